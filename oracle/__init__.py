@@ -1,0 +1,181 @@
+"""CPU oracle for the Spark-Attn forward and the Spark-Reblock partition.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg
+of ``bench.py`` may import it.  It never touches the HIP library and the HIP library never
+touches it: the two share no code.
+
+``spark_oracle.c`` holds the binary64 reference (built with gcc, OpenMP over independent
+(batch, head, block) units); ``brute.py`` holds a NumPy mask-matrix formulation for tiny inputs
+that pins it.  This module is the ctypes wrapper of the C part.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "spark_oracle.c")
+_LIB = os.path.join(_HERE, "libspark_oracle.so")
+
+
+class Params(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int), ("H", ctypes.c_int), ("N", ctypes.c_int), ("d", ctypes.c_int),
+        ("n_sink", ctypes.c_int), ("block", ctypes.c_int), ("topk_ratio", ctypes.c_float),
+        ("pool_mode", ctypes.c_int), ("scale", ctypes.c_double),
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the C oracle with gcc (binary64, no fp contraction, OpenMP)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           "-fno-fast-math", _SRC, "-o", _LIB + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.check_call(cmd)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.POINTER(Params)
+        f32, f64, i32 = (np.ctypeslib.ndpointer(t, flags="C_CONTIGUOUS")
+                         for t in (np.float32, np.float64, np.int32))
+        vp = ctypes.c_void_p
+        L.orc_num_blocks.argtypes = [P]
+        L.orc_topk_count.argtypes = [ctypes.c_int, ctypes.c_float]
+        L.orc_num_threads.argtypes = []
+        L.orc_pool.argtypes = [P, f32, f32, f32, f64, f64, f64, f64, f64, f64]
+        L.orc_scores.argtypes = [P, f64, f64, f64]
+        L.orc_select.argtypes = [P, f64, i32]
+        L.orc_dense.argtypes = [P, f32, f32, f32, f64, f64]
+        L.orc_attend_blocks.argtypes = [P, f32, f32, f32, f64, f64, f64, i32, ctypes.c_int, i32,
+                                        ctypes.c_int, f64, f64]
+        L.orc_forward.argtypes = [P, f32, f32, f32, vp, vp, f64, f64, vp]
+        L.orc_reblock_metric.argtypes = [P, f32, f32, f64, f64]
+        L.orc_reblock.argtypes = [P, f32, f32, i32]
+        for fn in (L.orc_pool, L.orc_scores, L.orc_select, L.orc_dense, L.orc_attend_blocks,
+                   L.orc_forward, L.orc_reblock_metric, L.orc_reblock):
+            fn.restype = None
+        _lib = L
+    return _lib
+
+
+def params(Q, n_sink, block, ratio=0.1, pool_mode=1, scale=0.0) -> Params:
+    B, H, N, d = Q.shape
+    return Params(B, H, N, d, n_sink, block, float(ratio), int(pool_mode), float(scale))
+
+
+def _f32(x):
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def num_blocks(p: Params) -> int:
+    return lib().orc_num_blocks(ctypes.byref(p))
+
+
+def topk_count(M: int, ratio: float) -> int:
+    return lib().orc_topk_count(M, ratio)
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()
+
+
+def pool(p: Params, Q, K, V):
+    """Returns dict q_mean, k_mean, k_sum, v_sum [B,H,M,d], bias [B,H,M], anchor [B,H,d]."""
+    M = num_blocks(p)
+    out = {k: np.empty((p.B, p.H, M, p.d)) for k in ("q_mean", "k_mean", "k_sum", "v_sum")}
+    out["bias"] = np.empty((p.B, p.H, M))
+    out["anchor"] = np.empty((p.B, p.H, p.d))
+    lib().orc_pool(ctypes.byref(p), _f32(Q), _f32(K), _f32(V), out["q_mean"], out["k_mean"],
+                   out["k_sum"], out["v_sum"], out["bias"], out["anchor"])
+    return out
+
+
+def scores(p: Params, q_mean, k_mean):
+    M = num_blocks(p)
+    S = np.empty((p.B, p.H, M, M))
+    lib().orc_scores(ctypes.byref(p), np.ascontiguousarray(q_mean, np.float64),
+                     np.ascontiguousarray(k_mean, np.float64), S)
+    return S
+
+
+def select(p: Params, S):
+    M = num_blocks(p)
+    K = topk_count(M, p.topk_ratio)
+    idx = np.empty((p.B, p.H, M, K), np.int32)
+    lib().orc_select(ctypes.byref(p), np.ascontiguousarray(S, np.float64), idx)
+    return idx
+
+
+def dense(p: Params, Q, K, V):
+    O = np.empty((p.B, p.H, p.N, p.d))
+    lse = np.empty((p.B, p.H, p.N))
+    lib().orc_dense(ctypes.byref(p), _f32(Q), _f32(K), _f32(V), O, lse)
+    return O, lse
+
+
+def forward(p: Params, Q, K, V, perm=None, idx=None):
+    """Full forward. Returns (O [B,H,N,d] f64, lse [B,H,N] f64, idx [B,H,M,K] int32)."""
+    M = num_blocks(p)
+    Ksel = topk_count(M, p.topk_ratio)
+    O = np.empty((p.B, p.H, p.N, p.d))
+    lse = np.empty((p.B, p.H, p.N))
+    idx_out = np.empty((p.B, p.H, M, Ksel), np.int32)
+    keep = []
+
+    def ptr(a, dt):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a, dtype=dt)
+        keep.append(a)
+        return a.ctypes.data
+
+    lib().orc_forward(ctypes.byref(p), _f32(Q), _f32(K), _f32(V), ptr(perm, np.int32),
+                      ptr(idx, np.int32), O, lse, idx_out.ctypes.data)
+    return O, lse, idx_out
+
+
+def attend_blocks(p: Params, Q, K, V, pooled, idx, qblocks):
+    """Attention rows of chosen query blocks. qblocks: int array [n, 2] of (b*H + h, I) where
+    I < M is a video query block and I >= M the sink row N_v + I - M.  Inputs are in the
+    (already permuted) block layout that ``idx`` refers to.  Returns O [n, block, d] and
+    lse [n, block] (rows past a partial block / past row 0 of a sink entry are NaN)."""
+    qb = np.ascontiguousarray(qblocks, dtype=np.int32).reshape(-1, 2)
+    n = qb.shape[0]
+    O = np.full((n, p.block, p.d), np.nan)
+    lse = np.full((n, p.block), np.nan)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    lib().orc_attend_blocks(ctypes.byref(p), _f32(Q), _f32(K), _f32(V),
+                            np.ascontiguousarray(pooled["k_sum"], np.float64),
+                            np.ascontiguousarray(pooled["v_sum"], np.float64),
+                            np.ascontiguousarray(pooled["bias"], np.float64), idx,
+                            idx.shape[-1], qb, n, O, lse)
+    return O, lse
+
+
+def reblock_metric(p: Params, Q, K):
+    Nv = p.N - p.n_sink
+    Sigma = np.empty((p.B, p.H, p.d, p.d))
+    nrm = np.empty((p.B, p.H, Nv))
+    lib().orc_reblock_metric(ctypes.byref(p), _f32(Q), _f32(K), Sigma, nrm)
+    return Sigma, nrm
+
+
+def reblock(p: Params, Q, K):
+    Nv = p.N - p.n_sink
+    perm = np.empty((p.B, p.H, Nv), np.int32)
+    lib().orc_reblock(ctypes.byref(p), _f32(Q), _f32(K), perm)
+    return perm
