@@ -1,0 +1,238 @@
+"""Python binding of libspark_attn.so (two-branch block-sparse attention forward for MI355X).
+
+Argument marshalling only: every step of the computation runs in the library's HIP kernels.
+PyTorch provides device memory and the current stream.  The library must be built
+(``python -m block_sparse_attention_score_amd.build``); loading fails loudly otherwise.
+
+Low-level functions carry the C names (``spark_attn_pool`` ...) and take pre-allocated tensors.
+The convenience functions ``pool``, ``select``, ``attend``, ``forward``, ``reblock`` and
+``gather_rows`` allocate their outputs with torch and call the same entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first so the library binds to the HIP runtime torch already uses
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspark_attn.so")
+
+BF16, FP32 = 0, 1
+POOL_MEAN, POOL_REWEIGHT = 0, 1
+
+
+class SparkAttnParams(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int), ("H", ctypes.c_int), ("N", ctypes.c_int), ("d", ctypes.c_int),
+        ("n_sink", ctypes.c_int), ("block", ctypes.c_int), ("topk_ratio", ctypes.c_float),
+        ("pool_mode", ctypes.c_int), ("dtype", ctypes.c_int), ("scale", ctypes.c_float),
+    ]
+
+
+class SparkAttnError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_str(status)} ({status})")
+
+
+EXPORTS = (
+    "spark_attn_num_blocks", "spark_attn_topk_count", "spark_attn_workspace_size",
+    "spark_attn_status_str", "spark_attn_pool", "spark_attn_select", "spark_attn_attend",
+    "spark_attn_forward", "spark_attn_reblock", "spark_attn_gather_rows",
+)
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_sparse_attention_score_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(SparkAttnParams)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        sig = {
+            "spark_attn_num_blocks": ([P], ctypes.c_int),
+            "spark_attn_topk_count": ([ctypes.c_int, ctypes.c_float], ctypes.c_int),
+            "spark_attn_workspace_size": ([P, ctypes.c_int], sz),
+            "spark_attn_status_str": ([ctypes.c_int], ctypes.c_char_p),
+            "spark_attn_pool": ([P] + [vp] * 9 + [vp], ctypes.c_int),
+            "spark_attn_select": ([P, vp, vp, vp, vp, vp], ctypes.c_int),
+            "spark_attn_attend": ([P] + [vp] * 10 + [vp], ctypes.c_int),
+            "spark_attn_forward": ([P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "spark_attn_reblock": ([P, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "spark_attn_gather_rows": ([P, vp, vp, vp, vp], ctypes.c_int),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes, fn.restype = args, res
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().spark_attn_status_str(status).decode()
+
+
+def params(Q: torch.Tensor, n_sink: int, block: int, topk_ratio: float = 0.1,
+           pool_mode: int = POOL_REWEIGHT, scale: float = 0.0) -> SparkAttnParams:
+    B, H, N, d = Q.shape
+    if Q.dtype == torch.bfloat16:
+        dt = BF16
+    elif Q.dtype == torch.float32:
+        dt = FP32
+    else:
+        raise TypeError(f"unsupported dtype {Q.dtype}")
+    return SparkAttnParams(B, H, N, d, n_sink, block, float(topk_ratio), int(pool_mode), dt,
+                           float(scale))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("tensors must be contiguous device tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(name, status):
+    if status != 0:
+        raise SparkAttnError(name, status)
+
+
+def num_blocks(p: SparkAttnParams) -> int:
+    m = lib().spark_attn_num_blocks(ctypes.byref(p))
+    _check("spark_attn_num_blocks", min(m, 0))
+    return m
+
+
+def topk_count(M: int, ratio: float) -> int:
+    k = lib().spark_attn_topk_count(M, ratio)
+    _check("spark_attn_topk_count", min(k, 0))
+    return k
+
+
+def workspace_size(p: SparkAttnParams, what: int) -> int:
+    return lib().spark_attn_workspace_size(ctypes.byref(p), what)
+
+
+# ---- C-named entry points (pre-allocated tensors) -------------------------------------------
+
+def spark_attn_pool(p, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, stream=None):
+    _check("spark_attn_pool", lib().spark_attn_pool(
+        ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(q_mean), _ptr(k_mean), _ptr(k_sum),
+        _ptr(v_sum), _ptr(bias), _ptr(anchor), _stream(stream)))
+
+
+def spark_attn_select(p, q_mean, k_mean, idx, scores=None, stream=None):
+    _check("spark_attn_select", lib().spark_attn_select(
+        ctypes.byref(p), _ptr(q_mean), _ptr(k_mean), _ptr(idx), _ptr(scores), _stream(stream)))
+
+
+def spark_attn_attend(p, Q, K, V, k_sum, v_sum, bias, idx, perm, O, lse=None, stream=None):
+    _check("spark_attn_attend", lib().spark_attn_attend(
+        ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(k_sum), _ptr(v_sum), _ptr(bias),
+        _ptr(idx), _ptr(perm), _ptr(O), _ptr(lse), _stream(stream)))
+
+
+def spark_attn_forward(p, Q, K, V, perm, O, lse, idx_out, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("spark_attn_forward", lib().spark_attn_forward(
+        ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(perm), _ptr(O), _ptr(lse),
+        _ptr(idx_out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def spark_attn_reblock(p, Q, K, perm, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("spark_attn_reblock", lib().spark_attn_reblock(
+        ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(perm), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def spark_attn_gather_rows(p, X, perm, Y, stream=None):
+    _check("spark_attn_gather_rows", lib().spark_attn_gather_rows(
+        ctypes.byref(p), _ptr(X), _ptr(perm), _ptr(Y), _stream(stream)))
+
+
+# ---- convenience wrappers (allocate outputs with torch) -------------------------------------
+
+def pool(Q, K, V, n_sink, block, pool_mode=POOL_REWEIGHT, scale=0.0, stream=None):
+    p = params(Q, n_sink, block, 1.0, pool_mode, scale)
+    M = num_blocks(p)
+    B, H, _, d = Q.shape
+    f = dict(device=Q.device, dtype=torch.float32)
+    out = {k: torch.empty(B, H, M, d, **f) for k in ("q_mean", "k_mean", "k_sum", "v_sum")}
+    out["bias"] = torch.empty(B, H, M, **f)
+    out["anchor"] = torch.empty(B, H, d, **f)
+    spark_attn_pool(p, Q, K, V, out["q_mean"], out["k_mean"], out["k_sum"], out["v_sum"],
+                    out["bias"], out["anchor"], stream)
+    return out
+
+
+def select(q_mean, k_mean, Q, n_sink, block, topk_ratio, with_scores=False, scale=0.0,
+           stream=None):
+    p = params(Q, n_sink, block, topk_ratio, POOL_REWEIGHT, scale)
+    M = num_blocks(p)
+    K = topk_count(M, topk_ratio)
+    B, H = q_mean.shape[:2]
+    idx = torch.empty(B, H, M, K, device=q_mean.device, dtype=torch.int32)
+    S = torch.empty(B, H, M, M, device=q_mean.device, dtype=torch.float32) if with_scores else None
+    spark_attn_select(p, q_mean, k_mean, idx, S, stream)
+    return (idx, S) if with_scores else idx
+
+
+def attend(Q, K, V, pooled, idx, n_sink, block, topk_ratio, perm=None, pool_mode=POOL_REWEIGHT,
+           scale=0.0, out=None, lse=None, stream=None):
+    p = params(Q, n_sink, block, topk_ratio, pool_mode, scale)
+    O = out if out is not None else torch.empty_like(Q)
+    spark_attn_attend(p, Q, K, V, pooled["k_sum"], pooled["v_sum"], pooled["bias"], idx, perm,
+                      O, lse, stream)
+    return O
+
+
+def forward(Q, K, V, n_sink, block, topk_ratio, pool_mode=POOL_REWEIGHT, perm=None, scale=0.0,
+            return_lse=False, return_idx=False, workspace=None, stream=None):
+    """Returns O (and lse [B,H,N] fp32, idx [B,H,M,K] int32 when asked)."""
+    p = params(Q, n_sink, block, topk_ratio, pool_mode, scale)
+    M = num_blocks(p)
+    Kk = topk_count(M, topk_ratio)
+    B, H, N, _ = Q.shape
+    O = torch.empty_like(Q)
+    lse = torch.empty(B, H, N, device=Q.device, dtype=torch.float32) if return_lse else None
+    idx = torch.empty(B, H, M, Kk, device=Q.device, dtype=torch.int32) if return_idx else None
+    if workspace is None:
+        workspace = torch.empty(workspace_size(p, 2 if perm is not None else 0), device=Q.device,
+                                dtype=torch.uint8)
+    spark_attn_forward(p, Q, K, V, perm, O, lse, idx, workspace, stream)
+    res = (O,)
+    if return_lse:
+        res += (lse,)
+    if return_idx:
+        res += (idx,)
+    return res[0] if len(res) == 1 else res
+
+
+def reblock(Q, K, n_sink, block, workspace=None, stream=None):
+    p = params(Q, n_sink, block)
+    B, H, N, _ = Q.shape
+    perm = torch.empty(B, H, N - n_sink, device=Q.device, dtype=torch.int32)
+    if workspace is None:
+        workspace = torch.empty(max(workspace_size(p, 1), 256), device=Q.device, dtype=torch.uint8)
+    spark_attn_reblock(p, Q, K, perm, workspace, stream)
+    return perm
+
+
+def gather_rows(X, perm, n_sink, block=128, stream=None):
+    p = params(X, n_sink, block)
+    Y = torch.empty_like(X)
+    spark_attn_gather_rows(p, X, perm, Y, stream)
+    return Y

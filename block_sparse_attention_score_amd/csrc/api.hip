@@ -1,0 +1,226 @@
+// C ABI of the library: argument validation, workspace layout and the launch sequence on the
+// caller's stream.  No allocation, no synchronisation, no fallback path.
+#include <math.h>
+#include <string.h>
+
+#include "kernels.hpp"
+
+namespace spark {
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int topk_count(int M, float ratio) {
+    if (M < 1 || !(ratio > 0.f) || !(ratio <= 1.f)) return SPARK_ATTN_INVALID_ARGUMENT;
+    double k = floor((double)ratio * (double)M + 0.5);
+    if (k < 1.0) k = 1.0;
+    if (k > (double)M) k = (double)M;
+    return (int)k;
+}
+
+// Select keeps R score rows of length M plus staging buffers in LDS; it needs at least one row.
+static bool select_fits(int d, int M) {
+    int dev = 0, lds = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || lds <= 0)
+        lds = 65536;
+    const size_t need = (size_t)4 * (d + 64 * (d + 4) + (size_t)M);
+    return need <= (size_t)lds;
+}
+
+static int make_ctx(const spark_attn_params* p, void* stream, LaunchCtx* L) {
+    if (!p) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (p->B < 1 || p->H < 1 || p->N < 1 || p->n_sink < 0 || p->n_sink >= p->N || p->block < 1 || p->d < 1)
+        return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!(p->topk_ratio > 0.f) || !(p->topk_ratio <= 1.f)) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (p->pool_mode != SPARK_ATTN_POOL_MEAN && p->pool_mode != SPARK_ATTN_POOL_REWEIGHT)
+        return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!(p->scale >= 0.f) || isinf(p->scale)) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (p->d != 64 && p->d != 128) return SPARK_ATTN_UNSUPPORTED;
+    if (p->block != 64 && p->block != 128) return SPARK_ATTN_UNSUPPORTED;
+    if (p->dtype != SPARK_ATTN_BF16 && p->dtype != SPARK_ATTN_FP32) return SPARK_ATTN_UNSUPPORTED;
+    const long long elems = (long long)p->B * p->H * p->N * p->d;
+    if (elems >= (1LL << 31)) return SPARK_ATTN_UNSUPPORTED;
+    L->B = p->B;
+    L->H = p->H;
+    L->BH = p->B * p->H;
+    L->N = p->N;
+    L->n_sink = p->n_sink;
+    L->Nv = p->N - p->n_sink;
+    L->d = p->d;
+    L->block = p->block;
+    L->M = (L->Nv + p->block - 1) / p->block;
+    if (L->M > kMaxBlocks) return SPARK_ATTN_UNSUPPORTED;
+    L->K = topk_count(L->M, p->topk_ratio);
+    L->pool_mode = p->pool_mode;
+    L->dtype = p->dtype;
+    L->scale = p->scale != 0.f ? p->scale : 1.0f / sqrtf((float)p->d);
+    L->stream = (hipStream_t)stream;
+    return SPARK_ATTN_OK;
+}
+
+static int launch_status() {
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SPARK_ATTN_OK : SPARK_ATTN_HIP_ERROR;
+}
+
+struct FwdWorkspace {
+    size_t q_mean, k_mean, k_sum, v_sum, bias, anchor, idx, qp, kp, vp, total;
+};
+
+static FwdWorkspace fwd_layout(const LaunchCtx& L, bool with_perm) {
+    FwdWorkspace w;
+    const size_t md = (size_t)L.BH * L.M * L.d * 4;
+    size_t o = 0;
+    w.q_mean = o; o = align256(o + md);
+    w.k_mean = o; o = align256(o + md);
+    w.k_sum = o; o = align256(o + md);
+    w.v_sum = o; o = align256(o + md);
+    w.bias = o; o = align256(o + (size_t)L.BH * L.M * 4);
+    w.anchor = o; o = align256(o + (size_t)L.BH * L.d * 4);
+    w.idx = o; o = align256(o + (size_t)L.BH * L.M * L.K * 4);
+    w.qp = w.kp = w.vp = 0;
+    if (with_perm) {
+        const size_t x = (size_t)L.BH * L.N * L.d * (L.dtype == SPARK_ATTN_BF16 ? 2 : 4);
+        w.qp = o; o = align256(o + x);
+        w.kp = o; o = align256(o + x);
+        w.vp = o; o = align256(o + x);
+    }
+    w.total = o;
+    return w;
+}
+
+}  // namespace spark
+
+using namespace spark;
+
+extern "C" {
+
+int spark_attn_num_blocks(const spark_attn_params* p) {
+    LaunchCtx L;
+    const int s = make_ctx(p, nullptr, &L);
+    return s < 0 ? s : L.M;
+}
+
+int spark_attn_topk_count(int M, float ratio) { return topk_count(M, ratio); }
+
+size_t spark_attn_workspace_size(const spark_attn_params* p, int what) {
+    LaunchCtx L;
+    if (make_ctx(p, nullptr, &L) < 0) return 0;
+    if (what == 1) return reblock_workspace_bytes(L);
+    if (what == 0 || what == 2) return fwd_layout(L, what == 2).total;
+    return 0;
+}
+
+const char* spark_attn_status_str(int status) {
+    switch (status) {
+        case SPARK_ATTN_OK: return "ok";
+        case SPARK_ATTN_INVALID_ARGUMENT: return "invalid argument";
+        case SPARK_ATTN_UNSUPPORTED: return "unsupported shape or dtype";
+        case SPARK_ATTN_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case SPARK_ATTN_HIP_ERROR: return "HIP launch error";
+        case SPARK_ATTN_MISALIGNED: return "pointer not 16-byte aligned";
+        default: return "unknown status";
+    }
+}
+
+int spark_attn_pool(const spark_attn_params* p, const void* Q, const void* K, const void* V, float* q_mean,
+                    float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor, void* stream) {
+    LaunchCtx L;
+    int s = make_ctx(p, stream, &L);
+    if (s < 0) return s;
+    if (!Q || !K || !V || !q_mean || !k_mean || !k_sum || !v_sum || !bias || !anchor)
+        return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(q_mean) || !aligned16(k_mean) ||
+        !aligned16(k_sum) || !aligned16(v_sum) || !aligned16(anchor))
+        return SPARK_ATTN_MISALIGNED;
+    launch_pool(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor);
+    return launch_status();
+}
+
+int spark_attn_select(const spark_attn_params* p, const float* q_mean, const float* k_mean, int32_t* idx,
+                      float* scores, void* stream) {
+    LaunchCtx L;
+    int s = make_ctx(p, stream, &L);
+    if (s < 0) return s;
+    if (!q_mean || !k_mean || !idx) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!aligned16(q_mean) || !aligned16(k_mean)) return SPARK_ATTN_MISALIGNED;
+    if (!select_fits(L.d, L.M)) return SPARK_ATTN_UNSUPPORTED;
+    launch_select(L, q_mean, k_mean, idx, scores);
+    return launch_status();
+}
+
+int spark_attn_attend(const spark_attn_params* p, const void* Q, const void* K, const void* V, const float* k_sum,
+                      const float* v_sum, const float* bias, const int32_t* idx, const int32_t* perm, void* O,
+                      float* lse, void* stream) {
+    LaunchCtx L;
+    int s = make_ctx(p, stream, &L);
+    if (s < 0) return s;
+    if (!Q || !K || !V || !k_sum || !v_sum || !bias || !idx || !O) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(k_sum) || !aligned16(v_sum) ||
+        !aligned16(bias) || !aligned16(O))
+        return SPARK_ATTN_MISALIGNED;
+    launch_attend(L, Q, K, V, k_sum, v_sum, bias, idx, perm, O, lse);
+    return launch_status();
+}
+
+int spark_attn_gather_rows(const spark_attn_params* p, const void* X, const int32_t* perm, void* Y, void* stream) {
+    LaunchCtx L;
+    int s = make_ctx(p, stream, &L);
+    if (s < 0) return s;
+    if (!X || !perm || !Y || X == Y) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!aligned16(X) || !aligned16(Y)) return SPARK_ATTN_MISALIGNED;
+    launch_gather_rows(L, X, perm, Y);
+    return launch_status();
+}
+
+int spark_attn_forward(const spark_attn_params* p, const void* Q, const void* K, const void* V, const int32_t* perm,
+                       void* O, float* lse, int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream) {
+    LaunchCtx L;
+    int s = make_ctx(p, stream, &L);
+    if (s < 0) return s;
+    if (!Q || !K || !V || !O) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(workspace))
+        return SPARK_ATTN_MISALIGNED;
+    if (!select_fits(L.d, L.M)) return SPARK_ATTN_UNSUPPORTED;
+    const FwdWorkspace w = fwd_layout(L, perm != nullptr);
+    if (!workspace || ws_bytes < w.total) return SPARK_ATTN_WORKSPACE_TOO_SMALL;
+    char* ws = (char*)workspace;
+    const void *q = Q, *k = K, *v = V;
+    if (perm) {
+        launch_gather_rows(L, Q, perm, ws + w.qp);
+        launch_gather_rows(L, K, perm, ws + w.kp);
+        launch_gather_rows(L, V, perm, ws + w.vp);
+        q = ws + w.qp;
+        k = ws + w.kp;
+        v = ws + w.vp;
+    }
+    float* q_mean = (float*)(ws + w.q_mean);
+    float* k_mean = (float*)(ws + w.k_mean);
+    float* k_sum = (float*)(ws + w.k_sum);
+    float* v_sum = (float*)(ws + w.v_sum);
+    float* bias = (float*)(ws + w.bias);
+    float* anchor = (float*)(ws + w.anchor);
+    int32_t* idx = idx_out ? idx_out : (int32_t*)(ws + w.idx);
+    launch_pool(L, q, k, v, q_mean, k_mean, k_sum, v_sum, bias, anchor);
+    launch_select(L, q_mean, k_mean, idx, nullptr);
+    launch_attend(L, q, k, v, k_sum, v_sum, bias, idx, perm, O, lse);
+    return launch_status();
+}
+
+int spark_attn_reblock(const spark_attn_params* p, const void* Q, const void* K, int32_t* perm, void* workspace,
+                       size_t ws_bytes, void* stream) {
+    LaunchCtx L;
+    int s = make_ctx(p, stream, &L);
+    if (s < 0) return s;
+    if (!Q || !K || !perm) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(workspace)) return SPARK_ATTN_MISALIGNED;
+    const size_t need = reblock_workspace_bytes(L);
+    if (need == 0) return SPARK_ATTN_UNSUPPORTED;
+    if (!workspace || ws_bytes < need) return SPARK_ATTN_WORKSPACE_TOO_SMALL;
+    launch_reblock(L, Q, K, perm, workspace);
+    return launch_status();
+}
+
+}  // extern "C"

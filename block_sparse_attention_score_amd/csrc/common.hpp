@@ -1,0 +1,86 @@
+// Shared device helpers for the gfx950 kernels (wave64, bf16 MFMA).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "spark_attn.h"
+
+namespace spark {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kMaxBlocks = 16384;  // largest M the select / attention LDS tables are sized for
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// Eight consecutive input elements (bf16 or fp32) widened to fp32.
+template <typename T> struct In;
+template <> struct In<__bf16> {
+    static constexpr int kBytes = 2;
+    __device__ __forceinline__ static void load8(const __bf16* p, float (&v)[8]) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = bf16_bits_to_f32(u[j] & 0xffffu);
+            v[2 * j + 1] = bf16_bits_to_f32(u[j] >> 16);
+        }
+    }
+};
+template <> struct In<float> {
+    static constexpr int kBytes = 4;
+    __device__ __forceinline__ static void load8(const float* p, float (&v)[8]) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { v[j] = a[j]; v[4 + j] = b[j]; }
+    }
+};
+
+// Eight consecutive elements as packed bf16 (16 bytes), rounding fp32 to nearest even.
+__device__ __forceinline__ u32x4 pack8_bf16(const float (&v)[8]) {
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const __bf16 lo = (__bf16)v[2 * j], hi = (__bf16)v[2 * j + 1];
+        r[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    return r;
+}
+
+template <typename T> __device__ __forceinline__ u32x4 load8_as_bf16(const T* p);
+template <> __device__ __forceinline__ u32x4 load8_as_bf16<__bf16>(const __bf16* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+template <> __device__ __forceinline__ u32x4 load8_as_bf16<float>(const float* p) {
+    float v[8];
+    In<float>::load8(p, v);
+    return pack8_bf16(v);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int lane = threadIdx.x & 63;
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+}  // namespace spark

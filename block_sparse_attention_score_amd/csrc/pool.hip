@@ -1,0 +1,231 @@
+// Block pooling: per-block means of Q and K, the per-head anchor, and the compressed K/V summary
+// with its log-mass bias (Spark-H3 page, section "Spark-Attnが変えるもの", Spark-Reweight bullet).
+//
+// HBM-bound: Q is read once by pool_q, K and V once by pool_kv.  One workgroup per (batch,
+// head, block) reads the block's rows with 16-byte loads (row-contiguous, fully coalesced);
+// every reduction runs in a fixed order, so results are deterministic.
+#include "kernels.hpp"
+
+namespace spark {
+
+// Rows of a block handled by one thread: thread (c, rg) owns the 8-element column chunk c of rows
+// rg, rg + RG, ... (RG row groups of CH chunk-threads).
+template <int D> struct PoolGeom {
+    static constexpr int CH = D / 8;
+    static constexpr int RG = 256 / CH;
+};
+
+template <typename T, int D, int BLK>
+__global__ __launch_bounds__(256) void pool_q_kernel(const T* __restrict__ Q, int N, int Nv, int M,
+                                                     float* __restrict__ q_mean) {
+    using G = PoolGeom<D>;
+    constexpr int RPT = (BLK + G::RG - 1) / G::RG;  // rows per thread
+    const int bh = blockIdx.x / M, J = blockIdx.x % M;
+    const int c = threadIdx.x % G::CH, rg = threadIdx.x / G::CH;
+    const int lo = J * BLK, n = min(BLK, Nv - lo);
+    const T* base = Q + ((size_t)bh * N + lo) * D + c * 8;
+
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+        const int r = rg + k * G::RG;
+        if (r < n) {
+            float v[8];
+            In<T>::load8(base + (size_t)r * D, v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] += v[j];
+        }
+    }
+    __shared__ float red[G::RG][D];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[rg][c * 8 + j] = acc[j];
+    __syncthreads();
+    for (int col = threadIdx.x; col < D; col += 256) {
+        float s = 0.f;
+        for (int g = 0; g < G::RG; ++g) s += red[g][col];
+        q_mean[((size_t)bh * M + J) * D + col] = s / (float)n;
+    }
+}
+
+// anchor = mean of all video queries = sum_J n_J * q_mean_J / N_v (binary64 accumulation).
+template <int D>
+__global__ __launch_bounds__(D) void anchor_kernel(const float* __restrict__ q_mean, int Nv, int M,
+                                                   int BLK, float* __restrict__ anchor) {
+    const int bh = blockIdx.x, col = threadIdx.x;
+    const float* qm = q_mean + (size_t)bh * M * D + col;
+    double s = 0.0;
+    for (int J = 0; J < M; ++J) {
+        const int n = min(BLK, Nv - J * BLK);
+        s += (double)n * (double)qm[(size_t)J * D];
+    }
+    anchor[(size_t)bh * D + col] = (float)(s / (double)Nv);
+}
+
+// Key/value block summaries.  REWEIGHT: x_i = s * a.k_i, m = max x, e_i = exp(x_i - m),
+// Z = sum e, k~ = sum e_i k_i / Z, v~ = sum e_i v_i / Z, bias = m + ln Z - s * a.k~.
+// MEAN: k~ = mean k, v~ = mean v, bias = ln n.  Both write the plain key mean for ranking.
+template <typename T, int D, int BLK, bool REWEIGHT>
+__global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, const T* __restrict__ V,
+                                                      const float* __restrict__ anchor, int N, int Nv,
+                                                      int M, float scale, float* __restrict__ k_mean,
+                                                      float* __restrict__ k_sum, float* __restrict__ v_sum,
+                                                      float* __restrict__ bias) {
+    using G = PoolGeom<D>;
+    constexpr int RPT = (BLK + G::RG - 1) / G::RG;
+    const int bh = blockIdx.x / M, J = blockIdx.x % M;
+    const int c = threadIdx.x % G::CH, rg = threadIdx.x / G::CH;
+    const int lo = J * BLK, n = min(BLK, Nv - lo);
+    const size_t off = ((size_t)bh * N + lo) * D + c * 8;
+
+    float kr[RPT][8], vr[RPT][8];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+        const int r = rg + k * G::RG;
+        if (r < n) {
+            In<T>::load8(K + off + (size_t)r * D, kr[k]);
+            In<T>::load8(V + off + (size_t)r * D, vr[k]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) { kr[k][j] = 0.f; vr[k][j] = 0.f; }
+        }
+    }
+
+    __shared__ float red_k[G::RG][D];
+    __shared__ float red_w[G::RG][D];
+    __shared__ float red_v[G::RG][D];
+    __shared__ float red_s[G::RG];
+    __shared__ float bcast[2];
+
+    float ks[8], wk[8], wv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        ks[j] = 0.f;
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) ks[j] += kr[k][j];
+    }
+
+    float m = 0.f, Z = (float)n;
+    if (REWEIGHT) {
+        float a[8];
+        In<float>::load8(anchor + (size_t)bh * D + c * 8, a);
+        float x[RPT];
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) {
+            float pd = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pd += a[j] * kr[k][j];
+            // the CH threads of one row group are consecutive lanes of one wave
+#pragma unroll
+            for (int o = 1; o < G::CH; o <<= 1) pd += __shfl_xor(pd, o);
+            const int r = rg + k * G::RG;
+            x[k] = r < n ? scale * pd : -INFINITY;
+            mloc = fmaxf(mloc, x[k]);
+        }
+        if (c == 0) red_s[rg] = mloc;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float mm = red_s[0];
+            for (int g = 1; g < G::RG; ++g) mm = fmaxf(mm, red_s[g]);
+            bcast[0] = mm;
+        }
+        __syncthreads();
+        m = bcast[0];
+        float zloc = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { wk[j] = 0.f; wv[j] = 0.f; }
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) {
+            const float e = rg + k * G::RG < n ? expf(x[k] - m) : 0.f;
+            zloc += e;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) { wk[j] += e * kr[k][j]; wv[j] += e * vr[k][j]; }
+        }
+        __syncthreads();  // red_s reuse
+        if (c == 0) red_s[rg] = zloc;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            wk[j] = ks[j];
+            wv[j] = 0.f;
+#pragma unroll
+            for (int k = 0; k < RPT; ++k) wv[j] += vr[k][j];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        red_k[rg][c * 8 + j] = ks[j];
+        red_w[rg][c * 8 + j] = wk[j];
+        red_v[rg][c * 8 + j] = wv[j];
+    }
+    __syncthreads();
+    if (REWEIGHT) {
+        if (threadIdx.x == 0) {
+            float z = 0.f;
+            for (int g = 0; g < G::RG; ++g) z += red_s[g];
+            bcast[1] = z;
+        }
+        __syncthreads();
+        Z = bcast[1];
+    }
+    const size_t o = ((size_t)bh * M + J) * D;
+    float dot = 0.f;  // a . k~ partial over this thread's columns
+    for (int col = threadIdx.x; col < D; col += 256) {
+        float sk = 0.f, sw = 0.f, sv = 0.f;
+        for (int g = 0; g < G::RG; ++g) { sk += red_k[g][col]; sw += red_w[g][col]; sv += red_v[g][col]; }
+        const float kt = sw / Z;
+        k_mean[o + col] = sk / (float)n;
+        k_sum[o + col] = kt;
+        v_sum[o + col] = sv / Z;
+        if (REWEIGHT) dot += anchor[(size_t)bh * D + col] * kt;
+    }
+    if (REWEIGHT) {
+        // D <= 256 columns live in the first D threads: waves 0 (and 1 for D = 128)
+        dot = wave_sum(dot);
+        __syncthreads();
+        if ((threadIdx.x & 63) == 0) red_s[threadIdx.x >> 6] = dot;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float t = 0.f;
+            for (int w = 0; w < 4; ++w) t += red_s[w];
+            bias[(size_t)bh * M + J] = m + logf(Z) - scale * t;
+        }
+    } else if (threadIdx.x == 0) {
+        bias[(size_t)bh * M + J] = logf((float)n);
+    }
+}
+
+template <typename T, int D, int BLK>
+static void launch_pool_t(const LaunchCtx& L, const void* Q, const void* K, const void* V, float* q_mean,
+                          float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor) {
+    const dim3 grid(L.BH * L.M);
+    hipLaunchKernelGGL((pool_q_kernel<T, D, BLK>), grid, dim3(256), 0, L.stream, (const T*)Q, L.N,
+                       L.Nv, L.M, q_mean);
+    hipLaunchKernelGGL((anchor_kernel<D>), dim3(L.BH), dim3(D), 0, L.stream, q_mean, L.Nv, L.M, BLK,
+                       anchor);
+    if (L.pool_mode == SPARK_ATTN_POOL_REWEIGHT)
+        hipLaunchKernelGGL((pool_kv_kernel<T, D, BLK, true>), grid, dim3(256), 0, L.stream, (const T*)K,
+                           (const T*)V, anchor, L.N, L.Nv, L.M, L.scale, k_mean, k_sum, v_sum, bias);
+    else
+        hipLaunchKernelGGL((pool_kv_kernel<T, D, BLK, false>), grid, dim3(256), 0, L.stream, (const T*)K,
+                           (const T*)V, anchor, L.N, L.Nv, L.M, L.scale, k_mean, k_sum, v_sum, bias);
+}
+
+void launch_pool(const LaunchCtx& L, const void* Q, const void* K, const void* V, float* q_mean,
+                 float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor) {
+#define SPARK_POOL_CASE(T, D, B)                                                                  \
+    if (L.d == D && L.block == B) {                                                               \
+        launch_pool_t<T, D, B>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor);           \
+        return;                                                                                   \
+    }
+    if (L.dtype == SPARK_ATTN_BF16) {
+        SPARK_POOL_CASE(__bf16, 64, 64) SPARK_POOL_CASE(__bf16, 64, 128)
+        SPARK_POOL_CASE(__bf16, 128, 64) SPARK_POOL_CASE(__bf16, 128, 128)
+    } else {
+        SPARK_POOL_CASE(float, 64, 64) SPARK_POOL_CASE(float, 64, 128)
+        SPARK_POOL_CASE(float, 128, 64) SPARK_POOL_CASE(float, 128, 128)
+    }
+#undef SPARK_POOL_CASE
+}
+
+}  // namespace spark

@@ -1,0 +1,179 @@
+/*
+ * spark_attn.h — C ABI of a gfx950 (MI355X) library for two-branch block-sparse video attention
+ * in the Spark-Attn style, forward only.
+ *
+ * The method (from the pages it is built from):
+ *  - Spark-H3 news page ("Spark-H3: ブロックスパースアテンションでComfyUIのMiniMax-H3を高速化",
+ *    comfyui-wiki, 2026-10-11), section "Spark-Attnが変えるもの" (what Spark-Attn changes):
+ *    attention over video tokens is split into an exact branch over the top-ranked key/value
+ *    blocks and a compressed branch covering the remaining blocks; the Spark-Reweight bullet
+ *    replaces the compressed branch's mean-pooled key/value with a summary weighted at one
+ *    anchor per head (the mean video query) plus a log-mass bias; the Spark-Reblock bullet
+ *    replaces fixed raster tiles by a hierarchical partition under a cosine measured in the
+ *    metric of the other side's second moment.  Section "ワークフロー" (workflows): the budget
+ *    is topk_mode=topk_ratio and keys reuse the query partition (reblock_layout=q_reuse_k).
+ *  - Core sparse-attention node page ("ComfyUI にコアのスパースアテンションノードと Comfy Compiler
+ *    が追加されました", comfyui-wiki, 2026-09-08), section "ブロックスパースアテンション：1 つの
+ *    ノード、3 つのバックエンド": every query block is routed to a subset of key blocks (top-k
+ *    keeps a fixed fraction of key blocks); sink_conditioning attends packed conditioning rows
+ *    exactly.
+ *  - "H3 Optimizations" README, section "Nodes": non-video queries stay dense; an explicitly
+ *    requested sparse backend that cannot run is an error, never a silent fallback.
+ *
+ * Conventions shared by every call
+ *  - Tensors are contiguous [B, H, N, d] (row = one token of one (batch, head)).  Rows
+ *    [0, N_v) are video tokens, rows [N_v, N) with N_v = N - n_sink are sink (conditioning)
+ *    rows.  Video rows are cut into M = ceil(N_v / block) blocks of `block` consecutive rows;
+ *    the last block may be shorter.  Blocks never include sink rows.
+ *  - Every pointer is a DEVICE pointer owned by the caller, 16-byte aligned.  The library
+ *    never allocates, frees or synchronises; all work is enqueued on `stream` (a hipStream_t
+ *    passed as void*, NULL = the null stream).  It keeps no state between calls.
+ *  - Return value: SPARK_ATTN_OK or a negative status.  Arguments are validated before any
+ *    work is enqueued, so an error return means nothing was launched (except
+ *    SPARK_ATTN_HIP_ERROR, which reports a failed launch).  Faults inside kernels surface at
+ *    the caller's next synchronisation.
+ *  - There is no fallback: an unsupported shape or dtype returns SPARK_ATTN_UNSUPPORTED.
+ *  - Supported: d in {64, 128}; block in {64, 128}; dtype bf16 or fp32 (fp32 inputs are
+ *    pooled and ranked in fp32 and rounded to bf16 for the matrix-core stages); M <= 16384;
+ *    B*H*N*d < 2^31.
+ */
+#ifndef SPARK_ATTN_H
+#define SPARK_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum spark_attn_status {
+    SPARK_ATTN_OK = 0,
+    SPARK_ATTN_INVALID_ARGUMENT = -1,   /* null required pointer, bad size, ratio outside (0,1] */
+    SPARK_ATTN_UNSUPPORTED = -2,        /* d, block, dtype or size outside the supported set */
+    SPARK_ATTN_WORKSPACE_TOO_SMALL = -3,
+    SPARK_ATTN_HIP_ERROR = -4,          /* a kernel launch failed */
+    SPARK_ATTN_MISALIGNED = -5          /* a pointer is not 16-byte aligned */
+};
+
+enum spark_attn_dtype { SPARK_ATTN_BF16 = 0, SPARK_ATTN_FP32 = 1 };
+enum spark_attn_pool_mode { SPARK_ATTN_POOL_MEAN = 0, SPARK_ATTN_POOL_REWEIGHT = 1 };
+
+typedef struct {
+    int B, H;          /* batch, heads */
+    int N;             /* rows per (batch, head): video rows followed by n_sink sink rows */
+    int d;             /* head dimension */
+    int n_sink;        /* sink rows at the tail of every (batch, head), 0 <= n_sink < N */
+    int block;         /* block size for queries and keys */
+    float topk_ratio;  /* kept fraction of key blocks, in (0, 1]; K = clamp(floor(r*M + 1/2), 1, M)
+                          evaluated in binary64 from this binary32 value */
+    int pool_mode;     /* spark_attn_pool_mode */
+    int dtype;         /* spark_attn_dtype of Q, K, V and O */
+    float scale;       /* softmax scale s; 0 means 1/sqrt(d) */
+} spark_attn_params;
+
+/* ---- host-only helpers (no GPU needed) ---------------------------------------------------- */
+
+/* M = ceil(N_v / block), or a negative status for invalid params. */
+int spark_attn_num_blocks(const spark_attn_params *p);
+
+/* Top-K budget of topk_mode=topk_ratio: clamp(floor(ratio*M + 0.5), 1, M) in binary64.
+ * Returns a negative status if M < 1 or ratio is outside (0, 1]. */
+int spark_attn_topk_count(int M, float ratio);
+
+/* Bytes of device workspace spark_attn_forward needs (with_perm != 0: a partition is given),
+ * or spark_attn_reblock needs (what = 1).  Returns 0 for invalid params.
+ *   what = 0: forward without perm; what = 1: reblock; what = 2: forward with perm. */
+size_t spark_attn_workspace_size(const spark_attn_params *p, int what);
+
+/* Static description of a status code. */
+const char *spark_attn_status_str(int status);
+
+/* ---- device calls --------------------------------------------------------------------------- */
+
+/*
+ * Block pooling (Spark-H3 page, "Spark-Attnが変えるもの", Spark-Reweight bullet).
+ * In:  Q, K, V [B,H,N,d] in p->dtype.
+ * Out (fp32, caller-allocated):
+ *   q_mean, k_mean [B,H,M,d]  per-block means of video queries / keys (used for ranking);
+ *   anchor [B,H,d]            mean of all video queries of the (batch, head);
+ *   k_sum, v_sum [B,H,M,d]    compressed summary of each key block;
+ *   bias [B,H,M]              its log-mass bias.
+ * pool_mode REWEIGHT: with x_i = s*anchor.k_i over the block's keys, w = softmax(x) inside the
+ *   block, k_sum = sum w_i k_i, v_sum = sum w_i v_i, bias = logsumexp(x) - s*anchor.k_sum, so that
+ *   exp(s*anchor.k_sum + bias) equals the block's exact attention mass at the anchor.
+ * pool_mode MEAN: k_sum = mean k, v_sum = mean v, bias = ln(block length).
+ */
+int spark_attn_pool(const spark_attn_params *p, const void *Q, const void *K, const void *V,
+                    float *q_mean, float *k_mean, float *k_sum, float *v_sum, float *bias,
+                    float *anchor, void *stream);
+
+/*
+ * Top-K key-block selection per query block (core node page, "ブロックスパースアテンション":
+ * route each query block to a subset of key blocks; top-k keeps a fixed fraction).
+ * In:  q_mean, k_mean [B,H,M,d] fp32 (from spark_attn_pool).
+ * Out: idx [B,H,M,K] int32: for query block I, the K key blocks J with the largest block scores
+ *      S_IJ = s * q_mean_I . k_mean_J (fp32), ties to the lower J, listed in ascending J.
+ *      scores [B,H,M,M] fp32, optional (NULL to skip): S itself.
+ */
+int spark_attn_select(const spark_attn_params *p, const float *q_mean, const float *k_mean,
+                      int32_t *idx, float *scores, void *stream);
+
+/*
+ * The attention stage alone (exact branch + sinks + compressed branch, one softmax).
+ * In:  Q, K, V [B,H,N,d] (already in the block layout idx refers to); k_sum, v_sum [B,H,M,d],
+ *      bias [B,H,M] fp32; idx [B,H,M,K] int32 ascending or not, distinct entries in [0, M).
+ *      perm [B,H,N_v] int32 or NULL: when given, output row q of the video part is written to
+ *      row perm[q] of O and lse (undoing a partition).
+ * Out: O [B,H,N,d] in p->dtype; lse [B,H,N] fp32 (natural log), optional.
+ * Video query i of block I attends in one softmax to every key of its K selected blocks, to
+ * every sink row, and to one pseudo-key per unselected block J (logit s*q.k_sum_J + bias_J,
+ * value v_sum_J).  Sink query rows attend densely to all N keys.
+ */
+int spark_attn_attend(const spark_attn_params *p, const void *Q, const void *K, const void *V,
+                      const float *k_sum, const float *v_sum, const float *bias,
+                      const int32_t *idx, const int32_t *perm, void *O, float *lse, void *stream);
+
+/*
+ * The whole forward: [gather rows by perm] -> pool -> select -> attend (-> un-permute).
+ * In:  Q, K, V [B,H,N,d] in p->dtype; perm [B,H,N_v] int32 or NULL (a permutation of [0,N_v)
+ *      per (batch, head), e.g. from spark_attn_reblock: block layout row q holds token perm[q];
+ *      keys and values reuse it).
+ * Out: O [B,H,N,d] in p->dtype (original token order); lse [B,H,N] fp32 or NULL;
+ *      idx_out [B,H,M,K] int32 or NULL: the route used (in the permuted block layout).
+ * workspace: device memory of at least spark_attn_workspace_size(p, perm ? 2 : 0) bytes.
+ */
+int spark_attn_forward(const spark_attn_params *p, const void *Q, const void *K, const void *V,
+                       const int32_t *perm, void *O, float *lse, int32_t *idx_out,
+                       void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Spark-Reblock partition (Spark-H3 page, "Spark-Attnが変えるもの", Spark-Reblock bullet) of the
+ * video queries of every (batch, head), with the metric Sigma = K^T K / N_v of the video keys:
+ *  - Sigma is summed exactly in 64-bit fixed point; n_i = sqrt(q_i^T Sigma q_i);
+ *  - a group holding c leaves splits (c > 1): pivot P0 = its lowest token; A = the token with
+ *    the smallest Sigma-cosine to P0, B = the one with the smallest to A (ties: lower index);
+ *    tokens ordered by cos(.,A) - cos(.,B) descending (then index ascending); the first
+ *    ceil(c/2)*block tokens form the left child, the rest the right child;
+ *  - perm lists leaves left to right, each leaf in ascending token order.
+ * All decisions are taken in binary64 with a fixed operation order, so the result is exact and
+ * reproducible.
+ * In:  Q, K [B,H,N,d] (only video rows are read).
+ * Out: perm [B,H,N_v] int32.
+ * workspace: at least spark_attn_workspace_size(p, 1) bytes.
+ */
+int spark_attn_reblock(const spark_attn_params *p, const void *Q, const void *K, int32_t *perm,
+                       void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Row gather used for the q_reuse_k layout: for every (batch, head), Y row q = X row perm[q]
+ * for q < N_v; sink rows are copied unchanged.  X, Y [B,H,N,d] in p->dtype, distinct buffers.
+ */
+int spark_attn_gather_rows(const spark_attn_params *p, const void *X, const int32_t *perm,
+                           void *Y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARK_ATTN_H */

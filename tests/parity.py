@@ -1,0 +1,59 @@
+"""Comparison rules shared by the GPU parity tests (HIP path vs the CPU oracle)."""
+from __future__ import annotations
+
+import numpy as np
+
+# Forward tolerances for bf16 matrix-core attention against the binary64 oracle.
+FWD_REL_L2 = 1e-2
+FWD_MAX_ABS = 2e-2
+# Pooled fp32 summaries against binary64 (fp32 accumulation over <= 128 rows).
+POOL_RTOL = 2e-5
+# Selection near-tie window: relative 1e-4 of the K-th / (K+1)-th scores, plus an absolute floor
+# of 1e-6 of the row's largest |score| where scores cross zero.
+SEL_REL = 1e-4
+SEL_FLOOR = 1e-6
+
+
+def check_selection_row(sel, S_row, K):
+    """True when `sel` (GPU, ascending) is a valid top-K of the oracle scores `S_row`: exactly K
+    distinct ascending blocks, containing every block clearly above the K-th score and none
+    clearly below it.  Where the K-th and (K+1)-th scores are further apart than the window the
+    set is forced to be the oracle's exact one."""
+    sel = np.asarray(sel)
+    M = S_row.shape[0]
+    if sel.shape != (K,) or not (np.diff(sel) > 0).all() or sel.min() < 0 or sel.max() >= M:
+        return False
+    order = np.lexsort((np.arange(M), -S_row))
+    sK = S_row[order[K - 1]]
+    sK1 = S_row[order[K]] if K < M else -np.inf
+    delta = SEL_REL * max(abs(sK), abs(sK1) if np.isfinite(sK1) else 0.0) + SEL_FLOOR * np.abs(S_row).max()
+    must = set(np.nonzero(S_row > sK + delta)[0].tolist())
+    allowed = set(np.nonzero(S_row >= sK - delta)[0].tolist())
+    G = set(sel.tolist())
+    return must <= G <= allowed
+
+
+def check_selection(idx, S):
+    """idx [..., M, K] GPU route vs oracle scores S [..., M, M]; returns (#rows bad, #rows not
+    equal to the oracle's exact top-K)."""
+    idx = np.asarray(idx)
+    S = np.asarray(S)
+    K = idx.shape[-1]
+    M = S.shape[-1]
+    bad = differ = 0
+    for sel, row in zip(idx.reshape(-1, K), S.reshape(-1, M)):
+        if not check_selection_row(sel, row, K):
+            bad += 1
+        ref = np.sort(np.lexsort((np.arange(M), -row))[:K])
+        differ += int(not np.array_equal(ref, sel))
+    return bad, differ
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def max_abs(a, b):
+    return float(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)).max())

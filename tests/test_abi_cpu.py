@@ -1,0 +1,133 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every declared symbol, its
+host helpers agree with the oracle's budget rule, and invalid arguments are rejected with their
+status before any device work (only fake, never-dereferenced addresses are passed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_score_amd as sa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spark_attn.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL, HIP_ERR, MISALIGNED = 0, -1, -2, -3, -4, -5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spark_attn_[a-z_]+)\s*\(", text)))
+
+
+def P(**kw):
+    base = dict(B=1, H=2, N=1000, d=128, n_sink=8, block=128, topk_ratio=0.1, pool_mode=1,
+                dtype=0, scale=0.0)
+    base.update(kw)
+    return sa.SparkAttnParams(**base)
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(sa.EXPORTS)
+    L = sa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_header_struct_matches_binding():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct \{(.*?)\} spark_attn_params;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"\b(int|float)\s+([A-Za-z_, ]+);", body)
+    names = [n.strip() for _, group in fields for n in group.split(",")]
+    assert names == [f[0] for f in sa.SparkAttnParams._fields_]
+
+
+@pytest.mark.parametrize("M,ratio,K", [(64, 0.1, 6), (240, 0.1, 24), (591, 0.1, 59), (591, 0.2, 118),
+                                       (591, 0.3, 177), (591, 1.0, 591), (1922, 0.1, 192),
+                                       (10, 0.01, 1), (7, 0.5, 4), (3, 1e-6, 1)])
+def test_topk_count_matches_oracle(orc, M, ratio, K):
+    assert sa.topk_count(M, ratio) == K == orc.topk_count(M, ratio)
+
+
+def test_topk_count_rejects_bad_ratio():
+    L = sa.lib()
+    assert L.spark_attn_topk_count(10, 0.0) == INVALID
+    assert L.spark_attn_topk_count(10, 1.5) == INVALID
+    assert L.spark_attn_topk_count(10, float("nan")) == INVALID
+    assert L.spark_attn_topk_count(0, 0.5) == INVALID
+
+
+def test_num_blocks():
+    L = sa.lib()
+    assert L.spark_attn_num_blocks(ctypes.byref(P(N=1000, n_sink=8, block=128))) == 8
+    assert L.spark_attn_num_blocks(ctypes.byref(P(N=30720 + 256, n_sink=256))) == 240
+    assert L.spark_attn_num_blocks(ctypes.byref(P(N=245952 + 512, n_sink=512))) == 1922
+    assert L.spark_attn_num_blocks(ctypes.byref(P(N=75600 + 512, n_sink=512))) == 591
+    assert L.spark_attn_num_blocks(ctypes.byref(P(N=5, n_sink=0, block=64, d=64))) == 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), INVALID), (dict(H=0), INVALID), (dict(N=0), INVALID), (dict(n_sink=-1), INVALID),
+    (dict(n_sink=1000), INVALID), (dict(topk_ratio=0.0), INVALID), (dict(topk_ratio=1.01), INVALID),
+    (dict(topk_ratio=float("nan")), INVALID), (dict(pool_mode=2), INVALID),
+    (dict(scale=-1.0), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(block=32), UNSUPPORTED),
+    (dict(block=256), UNSUPPORTED), (dict(dtype=2), UNSUPPORTED),
+    (dict(N=16384 * 128 + 2, n_sink=1, d=64, H=1), UNSUPPORTED),  # M > 16384
+    (dict(B=64, H=64, N=8192, d=128), UNSUPPORTED),                # B*H*N*d >= 2^31
+])
+def test_invalid_params_rejected_before_launch(kw, status):
+    L = sa.lib()
+    p = P(**kw)
+    fake = ctypes.c_void_p(0x100000)
+    assert L.spark_attn_num_blocks(ctypes.byref(p)) == status
+    assert L.spark_attn_workspace_size(ctypes.byref(p), 0) == 0
+    assert L.spark_attn_pool(ctypes.byref(p), *([fake] * 9), None) == status
+    assert L.spark_attn_select(ctypes.byref(p), fake, fake, fake, None, None) == status
+    assert L.spark_attn_attend(ctypes.byref(p), *([fake] * 7), None, fake, None, None) == status
+    assert L.spark_attn_forward(ctypes.byref(p), fake, fake, fake, None, fake, None, None, fake,
+                                1 << 40, None) == status
+    assert L.spark_attn_reblock(ctypes.byref(p), fake, fake, fake, fake, 1 << 40, None) == status
+    assert L.spark_attn_gather_rows(ctypes.byref(p), fake, fake, ctypes.c_void_p(0x200000), None) == status
+
+
+def test_null_and_misaligned_pointers_rejected():
+    L = sa.lib()
+    p = P()
+    a = ctypes.c_void_p(0x100000)
+    bad = ctypes.c_void_p(0x100008)
+    assert L.spark_attn_pool(ctypes.byref(p), None, a, a, a, a, a, a, a, a, None) == INVALID
+    assert L.spark_attn_pool(ctypes.byref(p), bad, a, a, a, a, a, a, a, a, None) == MISALIGNED
+    assert L.spark_attn_select(ctypes.byref(p), a, a, None, None, None) == INVALID
+    assert L.spark_attn_select(ctypes.byref(p), bad, a, a, None, None) == MISALIGNED
+    assert L.spark_attn_attend(ctypes.byref(p), a, a, a, a, a, a, None, None, a, None, None) == INVALID
+    assert L.spark_attn_attend(ctypes.byref(p), a, a, a, a, a, a, a, None, bad, None, None) == MISALIGNED
+    assert L.spark_attn_forward(ctypes.byref(p), a, a, a, None, None, None, None, a, 1 << 40, None) == INVALID
+    assert L.spark_attn_forward(ctypes.byref(p), a, bad, a, None, a, None, None, a, 1 << 40, None) == MISALIGNED
+    assert L.spark_attn_gather_rows(ctypes.byref(p), a, a, a, None) == INVALID  # in place
+    assert L.spark_attn_gather_rows(ctypes.byref(p), a, None, ctypes.c_void_p(0x200000), None) == INVALID
+    assert L.spark_attn_reblock(ctypes.byref(p), a, a, None, a, 1 << 40, None) == INVALID
+
+
+def test_workspace_sizes_and_too_small():
+    L = sa.lib()
+    p = P(N=245952 + 512, n_sink=512, H=24)
+    w0 = L.spark_attn_workspace_size(ctypes.byref(p), 0)
+    w2 = L.spark_attn_workspace_size(ctypes.byref(p), 2)
+    M, K, d, BH = 1922, 192, 128, 24
+    assert w0 >= 4 * BH * M * d * 4 + BH * M * 4 + BH * d * 4 + BH * M * K * 4
+    assert w0 < 4 * BH * M * d * 4 + BH * M * 4 + BH * d * 4 + BH * M * K * 4 + 8 * 256
+    assert w2 - w0 >= 3 * BH * (245952 + 512) * d * 2
+    a = ctypes.c_void_p(0x100000)
+    assert L.spark_attn_forward(ctypes.byref(p), a, a, a, None, a, None, None, a, w0 - 1, None) == WS_SMALL
+    assert L.spark_attn_forward(ctypes.byref(p), a, a, a, a, a, None, None, a, w2 - 1, None) == WS_SMALL
+    assert L.spark_attn_forward(ctypes.byref(p), a, a, a, None, a, None, None, None, w0, None) == WS_SMALL
+
+
+def test_status_strings():
+    for s in (OK, INVALID, UNSUPPORTED, WS_SMALL, HIP_ERR, MISALIGNED):
+        assert sa.status_str(s) and sa.status_str(s) != "unknown status"
+    assert sa.status_str(-99) == "unknown status"
