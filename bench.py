@@ -2,8 +2,8 @@
 """Benchmark of the two-branch block-sparse attention forward on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic video-shaped input resident
-in HBM: pool -> select -> attend, launched through the library's C entry points on the current
-stream (the same three launches spark_attn_forward makes without a partition).  HIP events on that
+in HBM: pool -> select -> pack -> attend, launched through the library's C entry points on the
+current stream (the same launches spark_attn_forward makes without a partition).  HIP events on that
 stream bracket every stage inside the timed region; the attention kernel's average duration gives
 the roofline figure.  Before timing, the route is checked against the oracle's block scores
 (every row, near-tie rule), and the oracle itself is timed on a bounded sample of the same
@@ -124,7 +124,10 @@ def main():
     ap.add_argument("--workload", default="fullclip")
     ap.add_argument("--ratio", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-blocks", type=int, default=48)
+    ap.add_argument("--cpu-sample-blocks", type=int, default=600)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run one device-to-device copy of this many MiB (a kernel of "
+                         "known traffic, used to scale hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -161,24 +164,27 @@ def main():
     idx = torch.empty(B, H, M, Kk, device="cuda", dtype=torch.int32)
     O = torch.empty_like(Q)
     lse = torch.empty(B, H, N, **f32)
+    sel_ws = torch.empty(sa.workspace_size(p, 3), device="cuda", dtype=torch.uint8)
+    packed = torch.empty(sa.workspace_size(p, 4), device="cuda", dtype=torch.uint8)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
         sa.spark_attn_pool(p, Q, K, V, pooled["q_mean"], pooled["k_mean"], pooled["k_sum"], pooled["v_sum"],
                            pooled["bias"], pooled["anchor"], stream)
         if ev: ev[1].record(stream)
-        sa.spark_attn_select(p, pooled["q_mean"], pooled["k_mean"], idx, None, stream)
+        sa.spark_attn_select(p, pooled["q_mean"], pooled["k_mean"], idx, None, sel_ws, stream)
         if ev: ev[2].record(stream)
-        sa.spark_attn_attend(p, Q, K, V, pooled["k_sum"], pooled["v_sum"], pooled["bias"], idx, None, O, lse,
-                             stream)
+        sa.spark_attn_pack(p, K, V, pooled["k_sum"], pooled["v_sum"], pooled["bias"], packed, stream)
         if ev: ev[3].record(stream)
+        sa.spark_attn_attend(p, Q, packed, idx, None, O, lse, stream)
+        if ev: ev[4].record(stream)
 
     log(f"M={M} K={Kk}; warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -187,10 +193,10 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    st = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in events])
-    ms_pool, ms_sel, ms_attn = (float(x) for x in st.mean(axis=0))
+    st = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in events])
+    ms_pool, ms_sel, ms_pack, ms_attn = (float(x) for x in st.mean(axis=0))
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (pool {ms_pool:.3f}, select {ms_sel:.3f}, "
-        f"attend {ms_attn:.3f})")
+        f"pack {ms_pack:.3f}, attend {ms_attn:.3f})")
 
     # cross-check: the single-call entry point over the same input
     ws = torch.empty(sa.workspace_size(p, 0), device="cuda", dtype=torch.uint8)
@@ -204,6 +210,13 @@ def main():
     torch.cuda.synchronize()
     ms_forward_call = fe[0].elapsed_time(fe[1]) / 3
     same_out = bool(torch.equal(O, O2))
+
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, device="cuda", dtype=torch.uint8)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     gidx = idx.cpu().numpy()
     F_sel, F_sink, F_comp, F_sinkq = algorithmic_flops(gidx, wl, Kk)
@@ -230,7 +243,8 @@ def main():
             "N_sink": wl.n_sink, "d": d, "block": wl.block, "topk_ratio": ratio, "M": M, "K": Kk,
             "compressed_branch": "anchor-weighted summary + log-mass bias", "parallelism": "none (1 GPU)",
         },
-        "stages_ms": {"pool": round(ms_pool, 4), "select": round(ms_sel, 4), "attend": round(ms_attn, 4),
+        "stages_ms": {"pool": round(ms_pool, 4), "select": round(ms_sel, 4), "pack": round(ms_pack, 4),
+                      "attend": round(ms_attn, 4),
                       "spark_attn_forward_call": round(ms_forward_call, 4)},
         "forward_call_output_identical": same_out,
         "flops": {"F_sel": F_sel, "F_sink": F_sink, "F_comp": F_comp, "F_sinkq": F_sinkq},
@@ -247,7 +261,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        del Q, K, V, O, O2, ws
+        del Q, K, V, O, O2, ws, sel_ws, packed
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(wl, ratio, Qh, Kh, Vh, gidx, F_sel, args.cpu_sample_blocks)
     print(json.dumps(out), flush=True)

@@ -38,8 +38,8 @@ class SparkAttnError(RuntimeError):
 
 EXPORTS = (
     "spark_attn_num_blocks", "spark_attn_topk_count", "spark_attn_workspace_size",
-    "spark_attn_status_str", "spark_attn_pool", "spark_attn_select", "spark_attn_attend",
-    "spark_attn_forward", "spark_attn_reblock", "spark_attn_gather_rows",
+    "spark_attn_status_str", "spark_attn_pool", "spark_attn_select", "spark_attn_pack",
+    "spark_attn_attend", "spark_attn_forward", "spark_attn_reblock", "spark_attn_gather_rows",
 )
 
 _lib = None
@@ -61,8 +61,9 @@ def lib():
             "spark_attn_workspace_size": ([P, ctypes.c_int], sz),
             "spark_attn_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "spark_attn_pool": ([P] + [vp] * 9 + [vp], ctypes.c_int),
-            "spark_attn_select": ([P, vp, vp, vp, vp, vp], ctypes.c_int),
-            "spark_attn_attend": ([P] + [vp] * 10 + [vp], ctypes.c_int),
+            "spark_attn_select": ([P, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "spark_attn_pack": ([P, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "spark_attn_attend": ([P, vp, vp, sz, vp, vp, vp, vp, vp], ctypes.c_int),
             "spark_attn_forward": ([P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "spark_attn_reblock": ([P, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "spark_attn_gather_rows": ([P, vp, vp, vp, vp], ctypes.c_int),
@@ -133,15 +134,27 @@ def spark_attn_pool(p, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, stre
         _ptr(v_sum), _ptr(bias), _ptr(anchor), _stream(stream)))
 
 
-def spark_attn_select(p, q_mean, k_mean, idx, scores=None, stream=None):
+def spark_attn_select(p, q_mean, k_mean, idx, scores=None, workspace=None, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("spark_attn_select", lib().spark_attn_select(
-        ctypes.byref(p), _ptr(q_mean), _ptr(k_mean), _ptr(idx), _ptr(scores), _stream(stream)))
+        ctypes.byref(p), _ptr(q_mean), _ptr(k_mean), _ptr(idx), _ptr(scores), _ptr(workspace),
+        ws_bytes, _stream(stream)))
 
 
-def spark_attn_attend(p, Q, K, V, k_sum, v_sum, bias, idx, perm, O, lse=None, stream=None):
+def _nbytes(t):
+    return t.numel() * t.element_size() if t is not None else 0
+
+
+def spark_attn_pack(p, K, V, k_sum, v_sum, bias, packed, stream=None):
+    _check("spark_attn_pack", lib().spark_attn_pack(
+        ctypes.byref(p), _ptr(K), _ptr(V), _ptr(k_sum), _ptr(v_sum), _ptr(bias), _ptr(packed),
+        _nbytes(packed), _stream(stream)))
+
+
+def spark_attn_attend(p, Q, packed, idx, perm, O, lse=None, stream=None):
     _check("spark_attn_attend", lib().spark_attn_attend(
-        ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(k_sum), _ptr(v_sum), _ptr(bias),
-        _ptr(idx), _ptr(perm), _ptr(O), _ptr(lse), _stream(stream)))
+        ctypes.byref(p), _ptr(Q), _ptr(packed), _nbytes(packed), _ptr(idx), _ptr(perm), _ptr(O),
+        _ptr(lse), _stream(stream)))
 
 
 def spark_attn_forward(p, Q, K, V, perm, O, lse, idx_out, workspace, stream=None):
@@ -185,17 +198,24 @@ def select(q_mean, k_mean, Q, n_sink, block, topk_ratio, with_scores=False, scal
     K = topk_count(M, topk_ratio)
     B, H = q_mean.shape[:2]
     idx = torch.empty(B, H, M, K, device=q_mean.device, dtype=torch.int32)
-    S = torch.empty(B, H, M, M, device=q_mean.device, dtype=torch.float32) if with_scores else None
-    spark_attn_select(p, q_mean, k_mean, idx, S, stream)
+    S = torch.empty(B, H, M, M, device=q_mean.device, dtype=torch.float32)
+    spark_attn_select(p, q_mean, k_mean, idx, S, None, stream)
     return (idx, S) if with_scores else idx
 
 
-def attend(Q, K, V, pooled, idx, n_sink, block, topk_ratio, perm=None, pool_mode=POOL_REWEIGHT,
-           scale=0.0, out=None, lse=None, stream=None):
-    p = params(Q, n_sink, block, topk_ratio, pool_mode, scale)
+def pack(K, V, pooled, n_sink, block, scale=0.0, stream=None):
+    p = params(K, n_sink, block, 1.0, POOL_REWEIGHT, scale)
+    packed = torch.empty(workspace_size(p, 4), device=K.device, dtype=torch.uint8)
+    spark_attn_pack(p, K, V, pooled["k_sum"], pooled["v_sum"], pooled["bias"], packed, stream)
+    return packed
+
+
+def attend(Q, K, V, pooled, idx, n_sink, block, topk_ratio, perm=None, scale=0.0, out=None,
+           lse=None, stream=None):
+    p = params(Q, n_sink, block, topk_ratio, POOL_REWEIGHT, scale)
+    packed = pack(K, V, pooled, n_sink, block, scale, stream)
     O = out if out is not None else torch.empty_like(Q)
-    spark_attn_attend(p, Q, K, V, pooled["k_sum"], pooled["v_sum"], pooled["bias"], idx, perm,
-                      O, lse, stream)
+    spark_attn_attend(p, Q, packed, idx, perm, O, lse, stream)
     return O
 
 

@@ -19,16 +19,6 @@ static int topk_count(int M, float ratio) {
     return (int)k;
 }
 
-// Select keeps R score rows of length M plus staging buffers in LDS; it needs at least one row.
-static bool select_fits(int d, int M) {
-    int dev = 0, lds = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || lds <= 0)
-        lds = 65536;
-    const size_t need = (size_t)4 * (d + 64 * (d + 4) + (size_t)M);
-    return need <= (size_t)lds;
-}
-
 static int make_ctx(const spark_attn_params* p, void* stream, LaunchCtx* L) {
     if (!p) return SPARK_ATTN_INVALID_ARGUMENT;
     if (p->B < 1 || p->H < 1 || p->N < 1 || p->n_sink < 0 || p->n_sink >= p->N || p->block < 1 || p->d < 1)
@@ -66,7 +56,7 @@ static int launch_status() {
 }
 
 struct FwdWorkspace {
-    size_t q_mean, k_mean, k_sum, v_sum, bias, anchor, idx, qp, kp, vp, total;
+    size_t q_mean, k_mean, k_sum, v_sum, bias, anchor, idx, scores, packed, qp, kp, vp, total;
 };
 
 static FwdWorkspace fwd_layout(const LaunchCtx& L, bool with_perm) {
@@ -80,6 +70,8 @@ static FwdWorkspace fwd_layout(const LaunchCtx& L, bool with_perm) {
     w.bias = o; o = align256(o + (size_t)L.BH * L.M * 4);
     w.anchor = o; o = align256(o + (size_t)L.BH * L.d * 4);
     w.idx = o; o = align256(o + (size_t)L.BH * L.M * L.K * 4);
+    w.scores = o; o = align256(o + select_workspace_bytes(L));
+    w.packed = o; o = align256(o + pack_geom(L).bytes);
     w.qp = w.kp = w.vp = 0;
     if (with_perm) {
         const size_t x = (size_t)L.BH * L.N * L.d * (L.dtype == SPARK_ATTN_BF16 ? 2 : 4);
@@ -110,6 +102,8 @@ size_t spark_attn_workspace_size(const spark_attn_params* p, int what) {
     if (make_ctx(p, nullptr, &L) < 0) return 0;
     if (what == 1) return reblock_workspace_bytes(L);
     if (what == 0 || what == 2) return fwd_layout(L, what == 2).total;
+    if (what == 3) return select_workspace_bytes(L);
+    if (what == 4) return pack_geom(L).bytes;
     return 0;
 }
 
@@ -140,28 +134,44 @@ int spark_attn_pool(const spark_attn_params* p, const void* Q, const void* K, co
 }
 
 int spark_attn_select(const spark_attn_params* p, const float* q_mean, const float* k_mean, int32_t* idx,
-                      float* scores, void* stream) {
+                      float* scores, void* workspace, size_t ws_bytes, void* stream) {
     LaunchCtx L;
     int s = make_ctx(p, stream, &L);
     if (s < 0) return s;
     if (!q_mean || !k_mean || !idx) return SPARK_ATTN_INVALID_ARGUMENT;
-    if (!aligned16(q_mean) || !aligned16(k_mean)) return SPARK_ATTN_MISALIGNED;
-    if (!select_fits(L.d, L.M)) return SPARK_ATTN_UNSUPPORTED;
-    launch_select(L, q_mean, k_mean, idx, scores);
+    if (!aligned16(q_mean) || !aligned16(k_mean) || !aligned16(scores) || !aligned16(workspace))
+        return SPARK_ATTN_MISALIGNED;
+    float* S = scores;
+    if (!S) {
+        if (!workspace || ws_bytes < select_workspace_bytes(L)) return SPARK_ATTN_WORKSPACE_TOO_SMALL;
+        S = (float*)workspace;
+    }
+    launch_select(L, q_mean, k_mean, idx, S);
     return launch_status();
 }
 
-int spark_attn_attend(const spark_attn_params* p, const void* Q, const void* K, const void* V, const float* k_sum,
-                      const float* v_sum, const float* bias, const int32_t* idx, const int32_t* perm, void* O,
-                      float* lse, void* stream) {
+int spark_attn_pack(const spark_attn_params* p, const void* K, const void* V, const float* k_sum, const float* v_sum,
+                    const float* bias, void* packed, size_t packed_bytes, void* stream) {
     LaunchCtx L;
     int s = make_ctx(p, stream, &L);
     if (s < 0) return s;
-    if (!Q || !K || !V || !k_sum || !v_sum || !bias || !idx || !O) return SPARK_ATTN_INVALID_ARGUMENT;
-    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(k_sum) || !aligned16(v_sum) ||
-        !aligned16(bias) || !aligned16(O))
+    if (!K || !V || !k_sum || !v_sum || !bias) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!aligned16(K) || !aligned16(V) || !aligned16(k_sum) || !aligned16(v_sum) || !aligned16(packed))
         return SPARK_ATTN_MISALIGNED;
-    launch_attend(L, Q, K, V, k_sum, v_sum, bias, idx, perm, O, lse);
+    if (!packed || packed_bytes < pack_geom(L).bytes) return SPARK_ATTN_WORKSPACE_TOO_SMALL;
+    launch_pack(L, K, V, k_sum, v_sum, bias, packed);
+    return launch_status();
+}
+
+int spark_attn_attend(const spark_attn_params* p, const void* Q, const void* packed, size_t packed_bytes,
+                      const int32_t* idx, const int32_t* perm, void* O, float* lse, void* stream) {
+    LaunchCtx L;
+    int s = make_ctx(p, stream, &L);
+    if (s < 0) return s;
+    if (!Q || !idx || !O) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!aligned16(Q) || !aligned16(packed) || !aligned16(O)) return SPARK_ATTN_MISALIGNED;
+    if (!packed || packed_bytes < pack_geom(L).bytes) return SPARK_ATTN_WORKSPACE_TOO_SMALL;
+    launch_attend(L, Q, packed, idx, perm, O, lse);
     return launch_status();
 }
 
@@ -183,7 +193,6 @@ int spark_attn_forward(const spark_attn_params* p, const void* Q, const void* K,
     if (!Q || !K || !V || !O) return SPARK_ATTN_INVALID_ARGUMENT;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(workspace))
         return SPARK_ATTN_MISALIGNED;
-    if (!select_fits(L.d, L.M)) return SPARK_ATTN_UNSUPPORTED;
     const FwdWorkspace w = fwd_layout(L, perm != nullptr);
     if (!workspace || ws_bytes < w.total) return SPARK_ATTN_WORKSPACE_TOO_SMALL;
     char* ws = (char*)workspace;
@@ -204,8 +213,9 @@ int spark_attn_forward(const spark_attn_params* p, const void* Q, const void* K,
     float* anchor = (float*)(ws + w.anchor);
     int32_t* idx = idx_out ? idx_out : (int32_t*)(ws + w.idx);
     launch_pool(L, q, k, v, q_mean, k_mean, k_sum, v_sum, bias, anchor);
-    launch_select(L, q_mean, k_mean, idx, nullptr);
-    launch_attend(L, q, k, v, k_sum, v_sum, bias, idx, perm, O, lse);
+    launch_select(L, q_mean, k_mean, idx, (float*)(ws + w.scores));
+    launch_pack(L, k, v, k_sum, v_sum, bias, ws + w.packed);
+    launch_attend(L, q, ws + w.packed, idx, perm, O, lse);
     return launch_status();
 }
 

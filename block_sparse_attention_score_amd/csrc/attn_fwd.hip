@@ -8,141 +8,88 @@
 // attended exactly by every query.  H3 Optimizations README, "Nodes": non-video (sink) queries are
 // dense over all keys.
 //
-// One workgroup = one query block (BLK rows) of one (batch, head); BLK/32 waves, each owning 32
-// query rows.  For every KV tile of 64 keys (a half or whole selected block, a sink tile, or 64
-// compressed pseudo-keys) the wave computes S^T = K_tile Q^T with v_mfma_f32_32x32x16_bf16, so
-// each lane ends up holding one query's logits (lane % 32 = query, 32 keys per lane): the row max
-// and row sum need only one cross-half shuffle, and P is already laid out as the B operand of
-// O^T += V^T P^T.  K tiles are staged row-major in LDS, V tiles transposed (d-major) in LDS; the
-// next tile's global loads are issued before the current tile's math (register prefetch).
+// Design (one workgroup = one query block of BLK rows of one (batch, head); BLK/32 waves, each
+// owning 32 query rows held in registers):
+//  * Keys and values arrive as packed 64-key tiles (K rows | V^T, bf16, plus a log2-domain bias
+//    row) written once per call by the pack kernels.  A workgroup's work is a list of tiles: its K
+//    selected blocks, the sink tiles, then the compressed tiles.
+//  * Tiles move HBM -> LDS with global_load_lds_dwordx4 (no register staging), into one of two LDS
+//    stages: tile t+1 streams in while tile t is computed; one barrier per tile.
+//  * LDS rows are XOR-swizzled by 16-byte chunk so the MFMA operand reads are conflict-free, and the
+//    K rows of each 32-key group are loaded in the order pi (bits 2 and 3 of the row index swapped):
+//    then the S^T accumulator of lane (i, h) holds, for query i, exactly the keys whose values form
+//    one contiguous 16-byte chunk of a V^T row, so P feeds O^T += V^T P^T straight from registers.
+//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: each lane holds one query's logits, so the row max
+//    and sum need one cross-half shuffle.  The running max is only raised when a tile's max exceeds
+//    it by more than 8 (log2 units); otherwise the accumulator is not rescaled.  Probabilities are
+//    then bounded by 2^8, and the result is unchanged because O and the normaliser share the max.
 #include "kernels.hpp"
 
 namespace spark {
 
-template <int D, int BLK> struct AttnGeom {
-    static constexpr int NW = BLK / 32;       // waves per workgroup
-    static constexpr int NT = NW * kWave;     // threads
-    static constexpr int TK = 64;             // keys per tile
-    static constexpr int NC = TK / 32;        // 32-key chunks per tile (one MFMA output tile each)
-    static constexpr int KST = D + 8;         // row stride of the K tile in LDS (bf16 elements)
-    static constexpr int VST = TK + 4;        // row stride of the V^T tile in LDS (bf16 elements)
-    static constexpr int KCHUNKS = TK * D / 8;           // 16-byte chunks of a K tile
-    static constexpr int VGROUPS = (TK / 4) * (D / 8);   // 4-key x 8-dim groups of a V tile
-    static constexpr int KCH = (KCHUNKS + NT - 1) / NT;  // per thread
-    static constexpr int VGR = (VGROUPS + NT - 1) / NT;  // per thread
-    static_assert(NT >= TK, "bias staging needs one thread per key");
+constexpr int kTK = 64;               // keys per tile
+constexpr float kRescaleSlack = 8.f;  // log2-domain slack before the running max is raised
+
+template <int D> struct TileGeom {
+    static constexpr int CK = D / 8;                  // 16-byte chunks per K row
+    static constexpr int ELEMS = 2 * kTK * D;         // bf16 elements of a packed tile
+    static constexpr int CHUNKS = ELEMS / 8;          // 16-byte chunks of a packed tile
+    static constexpr int K_CHUNKS = kTK * CK;         // chunks of the K part
+    static constexpr int V_CPR = kTK / 8;             // chunks per V^T row (8)
 };
 
-enum TileKind { kTileKV = 0, kTileCompressed = 1 };
-
-struct TileDesc {
-    int kind;
-    int row0;    // first key row (K/V rows) or first pseudo-key (compressed)
-    int nvalid;  // valid keys in the tile (<= 0: fully masked)
-};
-
-template <typename T, int D, int BLK>
-struct TileRegs {
-    using G = AttnGeom<D, BLK>;
-    u32x4 k[G::KCH];
-    u32x4 v[G::VGR][4];
-    float bias;  // per-key additive logit term (log2 units) for thread t < TK
-};
-
-template <typename T, int D, int BLK>
-__device__ __forceinline__ void load_tile(TileRegs<T, D, BLK>& R, const TileDesc& td, const T* Kh,
-                                          const T* Vh, const float* ksum_h, const float* vsum_h,
-                                          const float* bias_h, const uint32_t* sel_bits, int M) {
-    using G = AttnGeom<D, BLK>;
-    const int t = threadIdx.x;
-    constexpr int CPR = D / 8;  // 16-byte chunks per row
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    if (td.kind == kTileKV) {
-#pragma unroll
-        for (int i = 0; i < G::KCH; ++i) {
-            const int e = t + i * G::NT, r = e / CPR, c = e % CPR;
-            if (e >= G::KCHUNKS) break;
-            R.k[i] = r < td.nvalid ? load8_as_bf16<T>(Kh + (size_t)(td.row0 + r) * D + c * 8) : zero;
-        }
-#pragma unroll
-        for (int i = 0; i < G::VGR; ++i) {
-            const int g = t + i * G::NT, c = g % CPR, kg = g / CPR;
-            if (g >= G::VGROUPS) break;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = kg * 4 + j;
-                R.v[i][j] = r < td.nvalid ? load8_as_bf16<T>(Vh + (size_t)(td.row0 + r) * D + c * 8) : zero;
-            }
-        }
-        if (t < G::TK) R.bias = t < td.nvalid ? 0.f : -INFINITY;
-    } else {
-#pragma unroll
-        for (int i = 0; i < G::KCH; ++i) {
-            const int e = t + i * G::NT, r = e / CPR, c = e % CPR;
-            if (e >= G::KCHUNKS) break;
-            R.k[i] = r < td.nvalid ? load8_as_bf16<float>(ksum_h + (size_t)(td.row0 + r) * D + c * 8) : zero;
-        }
-#pragma unroll
-        for (int i = 0; i < G::VGR; ++i) {
-            const int g = t + i * G::NT, c = g % CPR, kg = g / CPR;
-            if (g >= G::VGROUPS) break;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = kg * 4 + j;
-                R.v[i][j] = r < td.nvalid ? load8_as_bf16<float>(vsum_h + (size_t)(td.row0 + r) * D + c * 8) : zero;
-            }
-        }
-        if (t < G::TK) {
-            const int J = td.row0 + t;
-            const bool live = t < td.nvalid && !((sel_bits[J >> 5] >> (J & 31)) & 1u);
-            R.bias = live ? bias_h[J] * 1.4426950408889634f : -INFINITY;
-        }
-    }
+// Chunk swizzle of an LDS row: rows of 16 chunks (256 B) use row % 16; rows of 8 chunks (128 B)
+// use (row / 2) % 8, so 16 consecutive rows read at one logical chunk hit 16 distinct bank groups.
+template <int CPR>
+__device__ __forceinline__ int swz(int row) {
+    return CPR == 16 ? (row & 15) : ((row >> 1) & 7);
 }
 
-template <typename T, int D, int BLK>
-__device__ __forceinline__ void store_tile(const TileRegs<T, D, BLK>& R, __bf16* Ks, __bf16* Vt, float* bias_s) {
-    using G = AttnGeom<D, BLK>;
-    const int t = threadIdx.x;
-    constexpr int CPR = D / 8;
+// Row order of K inside each 32-key group: swap bits 2 and 3.
+__device__ __forceinline__ int key_perm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+template <int D, int NT>
+__device__ __forceinline__ void issue_tile(const __bf16* __restrict__ gtile, const float* __restrict__ gbias,
+                                           __bf16* ltile, float* lbias) {
+    using G = TileGeom<D>;
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
 #pragma unroll
-    for (int i = 0; i < G::KCH; ++i) {
-        const int e = t + i * G::NT, r = e / CPR, c = e % CPR;
-        if (e >= G::KCHUNKS) break;
-        *reinterpret_cast<u32x4*>(Ks + r * G::KST + c * 8) = R.k[i];
-    }
-#pragma unroll
-    for (int i = 0; i < G::VGR; ++i) {
-        const int g = t + i * G::NT, c = g % CPR, kg = g / CPR;
-        if (g >= G::VGROUPS) break;
-        // rows kg*4 .. kg*4+3 of V, dims c*8 .. c*8+7  ->  V^T rows c*8+e, keys kg*4 .. kg*4+3
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int w = e >> 1, sh = (e & 1) * 16;
-            const uint32_t x0 = (R.v[i][0][w] >> sh) & 0xffffu, x1 = (R.v[i][1][w] >> sh) & 0xffffu;
-            const uint32_t x2 = (R.v[i][2][w] >> sh) & 0xffffu, x3 = (R.v[i][3][w] >> sh) & 0xffffu;
-            u32x2 pk;
-            pk[0] = x0 | (x1 << 16);
-            pk[1] = x2 | (x3 << 16);
-            *reinterpret_cast<u32x2*>(Vt + (c * 8 + e) * G::VST + kg * 4) = pk;
+    for (int i = 0; i < G::CHUNKS / NT; ++i) {
+        const int q = i * NT + t;  // LDS chunk this lane fills
+        int src;
+        if (q < G::K_CHUNKS) {
+            const int m = q / G::CK, pc = q % G::CK;
+            const int grow = (m & ~31) | key_perm(m & 31);
+            src = grow * G::CK + (pc ^ swz<G::CK>(m));
+        } else {
+            const int q2 = q - G::K_CHUNKS;
+            const int dr = q2 / G::V_CPR, pc = q2 % G::V_CPR;
+            src = G::K_CHUNKS + dr * G::V_CPR + (pc ^ swz<G::V_CPR>(dr));
         }
+        __builtin_amdgcn_global_load_lds((const void*)(gtile + (size_t)src * 8),
+                                         (lds_ptr)(ltile + (size_t)(i * NT + w * 64) * 8), 16, 0, 0);
     }
-    if (t < G::TK) bias_s[t] = R.bias;
+    if (w == 0) __builtin_amdgcn_global_load_lds((const void*)(gbias + lane), (lds_ptr)lbias, 4, 0, 0);
 }
 
 template <typename T, int D, int BLK>
 __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
-    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ k_sum,
-    const float* __restrict__ v_sum, const float* __restrict__ bias, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ perm, T* __restrict__ O, float* __restrict__ lse, int N, int Nv, int M,
-    int Ksel, int SQ, int BH, float c_log2) {
-    using G = AttnGeom<D, BLK>;
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[G::TK * G::KST];
-    __shared__ __attribute__((aligned(16))) __bf16 Vt[D * G::VST];
-    __shared__ __attribute__((aligned(16))) float bias_s[G::TK];
-    __shared__ uint32_t sel_bits[kMaxBlocks / 32];
+    const T* __restrict__ Q, const __bf16* __restrict__ packed, const float* __restrict__ bias2,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ perm, T* __restrict__ O, float* __restrict__ lse,
+    int N, int Nv, int M, int Ksel, int SQ, int BH, int C, int Tv, int Ts, int Tc, float c_log2) {
+    using G = TileGeom<D>;
+    constexpr int NT = BLK * 2;  // BLK / 32 waves
+    __shared__ __attribute__((aligned(16))) __bf16 lkv[2][G::ELEMS];
+    __shared__ __attribute__((aligned(16))) float lbias[2][kTK];
+    __shared__ uint32_t sel_bits[kMaxBlocks / 32 + 2];  // + the words a padded last tile can touch
 
-    // --- which query tile: sink-query tiles (dense, longest) come first in the grid
+    // --- which query tile.  Sink-query tiles (dense, the longest) come first in the grid.  Video
+    // query blocks are remapped so that each of the 8 XCDs (workgroup id w runs on XCD w % 8) walks
+    // its own contiguous run of C query blocks of the same head while all XCDs stay on one head:
+    // neighbouring query blocks select mostly the same key blocks, so concurrent workgroups of one
+    // XCD share tiles in its L2, and one head's tiles are the working set of the whole chip.
     int bh, qrow0, nq, ntiles;
     bool dense;
     {
@@ -152,62 +99,45 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
             bh = wg / SQ;
             qrow0 = Nv + (wg % SQ) * BLK;
             nq = min(BLK, N - qrow0);
-            ntiles = (N + G::TK - 1) / G::TK;
+            ntiles = Tv + Ts;
         } else {
             dense = false;
             const int v = wg - BH * SQ;
-            bh = v / M;
-            const int I = v % M;
+            const int xcd = wg & 7, slot = v >> 3;
+            bh = slot / C;
+            const int I = xcd * C + slot % C;
+            if (I >= M) return;  // padding slot (uniform for the workgroup, before any barrier)
             qrow0 = I * BLK;
             nq = min(BLK, Nv - qrow0);
-            ntiles = Ksel * (BLK / G::TK) + (N - Nv + G::TK - 1) / G::TK + (M + G::TK - 1) / G::TK;
+            ntiles = Ksel * (BLK / kTK) + Ts + Tc;
         }
     }
-    const size_t head = (size_t)bh * N * D;
-    const T* Qh = Q + head;
-    const T* Kh = K + head;
-    const T* Vh = V + head;
-    const float* ksum_h = k_sum + (size_t)bh * M * D;
-    const float* vsum_h = v_sum + (size_t)bh * M * D;
-    const float* bias_h = bias + (size_t)bh * M;
+    const int Tall = Tv + Ts + Tc;
+    const __bf16* ptile = packed + (size_t)bh * Tall * G::ELEMS;
+    const float* pbias = bias2 + (size_t)bh * Tall * kTK;
     const int32_t* sel = dense ? nullptr : idx + ((size_t)bh * M + qrow0 / BLK) * Ksel;
+    constexpr int nsub = BLK / kTK;
+    const int n_exact = dense ? 0 : Ksel * nsub;
+
+    // packed tile of list entry t: selected blocks, then sink tiles, then compressed tiles
+    auto tile_of = [&](int t) -> int {
+        if (dense) return t;
+        if (t >= n_exact) return Tv + (t - n_exact);
+        return sel[t / nsub] * nsub + t % nsub;
+    };
 
     if (!dense) {
-        for (int w = threadIdx.x; w < (M + 31) / 32; w += G::NT) sel_bits[w] = 0u;
+        for (int w = threadIdx.x; w < (M + 63) / 32 + 1; w += NT) sel_bits[w] = 0u;
         __syncthreads();
-        for (int k = threadIdx.x; k < Ksel; k += G::NT) {
+        for (int k = threadIdx.x; k < Ksel; k += NT) {
             const int J = sel[k];
             atomicOr(&sel_bits[J >> 5], 1u << (J & 31));
         }
-        __syncthreads();
     }
-
-    const int nsub = BLK / G::TK;
-    const int n_exact = dense ? 0 : Ksel * nsub;
-    const int n_sinkt = dense ? 0 : (N - Nv + G::TK - 1) / G::TK;
-    auto desc = [&](int t) -> TileDesc {
-        TileDesc td;
-        if (dense) {
-            td.kind = kTileKV;
-            td.row0 = t * G::TK;
-            td.nvalid = min(G::TK, N - td.row0);
-        } else if (t < n_exact) {
-            const int J = sel[t / nsub], sub = t % nsub;
-            const int nJ = min(BLK, Nv - J * BLK);
-            td.kind = kTileKV;
-            td.row0 = J * BLK + sub * G::TK;
-            td.nvalid = min(G::TK, nJ - sub * G::TK);
-        } else if (t < n_exact + n_sinkt) {
-            td.kind = kTileKV;
-            td.row0 = Nv + (t - n_exact) * G::TK;
-            td.nvalid = min(G::TK, N - td.row0);
-        } else {
-            td.kind = kTileCompressed;
-            td.row0 = (t - n_exact - n_sinkt) * G::TK;
-            td.nvalid = min(G::TK, M - td.row0);
-        }
-        return td;
-    };
+    {  // first tile in flight while Q is loaded
+        const int tl = tile_of(0);
+        issue_tile<D, NT>(ptile + (size_t)tl * G::ELEMS, pbias + (size_t)tl * kTK, lkv[0], lbias[0]);
+    }
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int i32 = lane & 31, h = lane >> 5;
@@ -217,7 +147,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     bf16x8 qreg[D / 16];
     {
         const int qr = w * 32 + i32;
-        const T* src = Qh + (size_t)(qrow0 + qr) * D;
+        const T* src = Q + ((size_t)bh * N + qrow0 + qr) * D;
 #pragma unroll
         for (int ds = 0; ds < D / 16; ++ds) {
             u32x4 u = {0u, 0u, 0u, 0u};
@@ -232,77 +162,90 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
-
-    TileRegs<T, D, BLK> R;
-    load_tile<T, D, BLK>(R, desc(0), Kh, Vh, ksum_h, vsum_h, bias_h, sel_bits, M);
+    const int first_cmp = dense ? ntiles : n_exact + Ts;  // first compressed tile in the list
 
     for (int t = 0; t < ntiles; ++t) {
-        __syncthreads();
-        store_tile<T, D, BLK>(R, Ks, Vt, bias_s);
-        __syncthreads();
-        if (t + 1 < ntiles) load_tile<T, D, BLK>(R, desc(t + 1), Kh, Vh, ksum_h, vsum_h, bias_h, sel_bits, M);
+        const int s = t & 1;
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's share of tile t has landed in LDS
+        __syncthreads();                // ... and everyone's; stage s^1 is free again
+        if (t + 1 < ntiles) {
+            const int tl = tile_of(t + 1);
+            issue_tile<D, NT>(ptile + (size_t)tl * G::ELEMS, pbias + (size_t)tl * kTK, lkv[s ^ 1], lbias[s ^ 1]);
+        }
+        const __bf16* Kl = lkv[s];
+        const __bf16* Vl = lkv[s] + kTK * D;
 
-        // ---- S^T = K_tile Q^T : G::NC chunks of 32 keys x 32 queries
-        f32x16 st[G::NC];
+        // ---- S^T = K_tile Q^T : two chunks of 32 keys x 32 queries
+        f32x16 st[2];
 #pragma unroll
-        for (int c = 0; c < G::NC; ++c) {
-            f32x16 s;
+        for (int c = 0; c < 2; ++c) {
+            f32x16 a16;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[r] = 0.f;
+            for (int r = 0; r < 16; ++r) a16[r] = 0.f;
+            const int m = c * 32 + i32;
 #pragma unroll
             for (int ds = 0; ds < D / 16; ++ds) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (c * 32 + i32) * G::KST + ds * 16 + 8 * h);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], s, 0, 0, 0);
+                const int pc = (2 * ds + h) ^ swz<G::CK>(m);
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kl + (m * G::CK + pc) * 8);
+                a16 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], a16, 0, 0, 0);
             }
-            st[c] = s;
+            st[c] = a16;
         }
-        // ---- logits in log2 units; lane holds keys c*32 + 8*(r/4) + 4*h + r%4 of query i32
+        // ---- logits (log2 units).  Register 4g+j of chunk c holds key c*32 + 16(g/2) + 8h + 4(g%2) + j.
+        const bool compressed = t >= first_cmp;
+        const int cbase = (t - first_cmp) * kTK;  // first pseudo-key of a compressed tile
         float mx = -INFINITY;
 #pragma unroll
-        for (int c = 0; c < G::NC; ++c)
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const f32x4 bb = *reinterpret_cast<const f32x4*>(bias_s + c * 32 + 8 * g + 4 * h);
+                const int key = c * 32 + 16 * (g >> 1) + 8 * h + 4 * (g & 1);
+                const f32x4 bb = *reinterpret_cast<const f32x4*>(lbias[s] + key);
+                uint32_t selw = 0;
+                if (compressed) selw = sel_bits[(cbase + key) >> 5] >> ((cbase + key) & 31);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float z = fmaf(st[c][4 * g + j], c_log2, bb[j]);
+                    float z = fmaf(st[c][4 * g + j], c_log2, bb[j]);
+                    if ((selw >> j) & 1u) z = -INFINITY;
                     st[c][4 * g + j] = z;
                     mx = fmaxf(mx, z);
                 }
             }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        const bool raise = mx > m_run + kRescaleSlack;
+        if (__ballot(raise)) {
+            const float m_new = raise ? mx : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
         float ls = 0.f;
 #pragma unroll
-        for (int c = 0; c < G::NC; ++c)
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float p = __builtin_amdgcn_exp2f(st[c][r] - m_use);
                 st[c][r] = p;
                 ls += p;
             }
-        l_run = l_run * alpha + ls;
-        m_run = m_new;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+        l_run += ls;
 
-        // ---- O^T += V^T P^T, 16 keys per MFMA step: P regs 8*(kt%2) .. +7 of chunk kt/2 hold keys
-        // 16*kt + 8*(e/4) + 4*h + e%4 (e = 0..7); V^T is read for exactly those keys.
+        // ---- O^T += V^T P^T, 16 keys per step: lane (i32, h) supplies keys 16kt + 8h + e (e = 0..7)
 #pragma unroll
-        for (int kt = 0; kt < G::TK / 16; ++kt) {
+        for (int kt = 0; kt < kTK / 16; ++kt) {
             bf16x8 b;
 #pragma unroll
             for (int e = 0; e < 8; ++e) b[e] = (__bf16)st[kt >> 1][8 * (kt & 1) + e];
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
-                const __bf16* vrow = Vt + (dt * 32 + i32) * G::VST + 16 * kt + 4 * h;
-                const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow);
-                const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 8);
-                const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                const int dr = dt * 32 + i32;
+                const int pc = (2 * kt + h) ^ swz<G::V_CPR>(dr);
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vl + (dr * G::V_CPR + pc) * 8);
                 acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[dt], 0, 0, 0);
             }
         }
@@ -315,7 +258,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     if (qr < nq) {
         const int row = qrow0 + qr;
         const int orow = (!dense && perm) ? perm[(size_t)bh * Nv + row] : row;
-        T* dst = O + head + (size_t)orow * D;
+        T* dst = O + ((size_t)bh * N + orow) * D;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -338,25 +281,24 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
 }
 
 template <typename T, int D, int BLK>
-static void launch_attend_t(const LaunchCtx& L, const void* Q, const void* K, const void* V, const float* k_sum,
-                            const float* v_sum, const float* bias, const int32_t* idx, const int32_t* perm,
-                            void* O, float* lse) {
-    using G = AttnGeom<D, BLK>;
+static void launch_attend_t(const LaunchCtx& L, const void* Q, const void* packed, const int32_t* idx,
+                            const int32_t* perm, void* O, float* lse) {
+    const PackGeom g = pack_geom(L);
     const int SQ = (L.n_sink + BLK - 1) / BLK;
-    const dim3 grid(L.BH * (SQ + L.M));
+    const int C = (L.M + 7) / 8;  // query blocks per XCD per head
+    const dim3 grid(L.BH * SQ + L.BH * 8 * C);
     const float c_log2 = L.scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, BLK>), grid, dim3(G::NT), 0, L.stream, (const T*)Q, (const T*)K,
-                       (const T*)V, k_sum, v_sum, bias, idx, perm, (T*)O, lse, L.N, L.Nv, L.M, L.K, SQ, L.BH,
-                       c_log2);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, BLK>), grid, dim3(BLK * 2), 0, L.stream, (const T*)Q,
+                       (const __bf16*)packed, (const float*)((const char*)packed + g.bias_off), idx, perm, (T*)O,
+                       lse, L.N, L.Nv, L.M, L.K, SQ, L.BH, C, g.Tv, g.Ts, g.Tc, c_log2);
 }
 
-void launch_attend(const LaunchCtx& L, const void* Q, const void* K, const void* V, const float* k_sum,
-                   const float* v_sum, const float* bias, const int32_t* idx, const int32_t* perm, void* O,
-                   float* lse) {
-#define SPARK_ATTN_CASE(T, D, B)                                                                  \
-    if (L.d == D && L.block == B) {                                                               \
-        launch_attend_t<T, D, B>(L, Q, K, V, k_sum, v_sum, bias, idx, perm, O, lse);              \
-        return;                                                                                   \
+void launch_attend(const LaunchCtx& L, const void* Q, const void* packed, const int32_t* idx, const int32_t* perm,
+                   void* O, float* lse) {
+#define SPARK_ATTN_CASE(T, D, B)                                          \
+    if (L.d == D && L.block == B) {                                       \
+        launch_attend_t<T, D, B>(L, Q, packed, idx, perm, O, lse);        \
+        return;                                                           \
     }
     if (L.dtype == SPARK_ATTN_BF16) {
         SPARK_ATTN_CASE(__bf16, 64, 64) SPARK_ATTN_CASE(__bf16, 64, 128)

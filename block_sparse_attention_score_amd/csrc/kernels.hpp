@@ -16,12 +16,26 @@ struct LaunchCtx {
 void launch_pool(const LaunchCtx& L, const void* Q, const void* K, const void* V, float* q_mean,
                  float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor);
 
+// Select writes the full score matrix S [BH, M, M] (fp32) to `scores`, then the route.
+size_t select_workspace_bytes(const LaunchCtx& L);
 void launch_select(const LaunchCtx& L, const float* q_mean, const float* k_mean, int32_t* idx,
                    float* scores);
 
-void launch_attend(const LaunchCtx& L, const void* Q, const void* K, const void* V, const float* k_sum,
-                   const float* v_sum, const float* bias, const int32_t* idx, const int32_t* perm,
-                   void* O, float* lse);
+// Packed 64-key tiles read by the attention kernel (layout in pack.hip).
+struct PackGeom {
+    int Tv, Ts, Tc, Tall;  // video, sink, compressed and total tiles per (batch, head)
+    size_t tile_elems;     // bf16 elements per tile (K rows + V^T)
+    size_t kv_bytes;       // all tiles of all heads
+    size_t bias_off;       // byte offset of the fp32 bias rows [BH][Tall][64]
+    size_t bytes;          // total
+};
+PackGeom pack_geom(const LaunchCtx& L);
+
+void launch_pack(const LaunchCtx& L, const void* K, const void* V, const float* k_sum, const float* v_sum,
+                 const float* bias, void* packed);
+
+void launch_attend(const LaunchCtx& L, const void* Q, const void* packed, const int32_t* idx,
+                   const int32_t* perm, void* O, float* lse);
 
 void launch_gather_rows(const LaunchCtx& L, const void* X, const int32_t* perm, void* Y);
 

@@ -1,0 +1,138 @@
+// Packing of the keys and values the attention stage reads, once per call, into 64-key tiles:
+//
+//   tile t of (batch, head) = [ K rows: 64 x d bf16, row-major | V^T: d x 64 bf16 ]  (contiguous)
+//   bias2[t][64] fp32: additive logit term in log2 units (0 or -inf for real keys, log2(e) * bias
+//                      for compressed pseudo-keys, -inf for padding)
+//
+// Tiles 0 .. Tv-1 hold the video keys (row r of the video part is tile r/64, slot r%64; Tv covers
+// M whole blocks, so a short last block ends in padding), tiles
+// Tv .. Tv+Ts-1 the sink keys, tiles Tv+Ts .. Tall-1 the compressed pseudo-keys (the per-block
+// summaries, Spark-H3 page, "Spark-Attnが変えるもの", Spark-Reweight bullet).  A selected block J
+// is the tiles J*block/64 .. (J+1)*block/64 - 1.  Padding rows are zero with bias -inf, so the
+// attention kernel reads whole tiles with no bounds logic.
+//
+// Every value tile is stored transposed: each selected block is used by ~K of the M query blocks,
+// so transposing once here replaces a transposition at every use inside the attention loop.
+#include "kernels.hpp"
+
+namespace spark {
+
+PackGeom pack_geom(const LaunchCtx& L) {
+    PackGeom g;
+    g.Tv = L.M * (L.block / 64);  // every block owns whole tiles (a short last block is padded)
+    g.Ts = (L.n_sink + 63) / 64;
+    g.Tc = (L.M + 63) / 64;
+    g.Tall = g.Tv + g.Ts + g.Tc;
+    g.tile_elems = (size_t)2 * 64 * L.d;
+    g.kv_bytes = (size_t)L.BH * g.Tall * g.tile_elems * 2;
+    g.bias_off = (g.kv_bytes + 255) & ~(size_t)255;
+    g.bytes = g.bias_off + (size_t)L.BH * g.Tall * 64 * 4;
+    return g;
+}
+
+// One workgroup per tile of 64 source rows: rows of X (real keys, type T) or of the fp32
+// summaries (compressed).  K rows are re-packed as bf16 rows; V rows go through LDS to be
+// written transposed with 16-byte stores.
+template <typename T, typename S, int D>
+__device__ __forceinline__ void pack_tile(const T* __restrict__ Ksrc, const T* __restrict__ Vsrc, int nvalid,
+                                          __bf16* __restrict__ tile, float* __restrict__ bias2,
+                                          const float* __restrict__ bias_src, float bias_scale) {
+    constexpr int CPR = D / 8;                 // 16-byte bf16 chunks per row
+    constexpr int ROWS_PER_PASS = 256 / CPR;   // rows covered by the 256 threads in one pass
+    __shared__ __attribute__((aligned(16))) __bf16 vs[64][D + 8];
+    const int t = threadIdx.x, c = t % CPR;
+    __bf16* kdst = tile;
+    __bf16* vdst = tile + 64 * D;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int r0 = 0; r0 < 64; r0 += ROWS_PER_PASS) {
+        const int r = r0 + t / CPR;
+        u32x4 kv = zero, vv = zero;
+        if (r < nvalid) {
+            kv = load8_as_bf16<S>(reinterpret_cast<const S*>(Ksrc) + (size_t)r * D + c * 8);
+            vv = load8_as_bf16<S>(reinterpret_cast<const S*>(Vsrc) + (size_t)r * D + c * 8);
+        }
+        *reinterpret_cast<u32x4*>(kdst + r * D + c * 8) = kv;
+        *reinterpret_cast<u32x4*>(&vs[r][c * 8]) = vv;
+    }
+    __syncthreads();
+    // V^T row dr = keys 0..63 of dimension dr: 8 chunks of 8 keys
+    for (int e = t; e < D * 8; e += 256) {
+        const int dr = e / 8, kc = e % 8;
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t lo = __builtin_bit_cast(uint16_t, vs[kc * 8 + 2 * j][dr]);
+            const uint32_t hi = __builtin_bit_cast(uint16_t, vs[kc * 8 + 2 * j + 1][dr]);
+            o[j] = lo | (hi << 16);
+        }
+        *reinterpret_cast<u32x4*>(vdst + dr * 64 + kc * 8) = o;
+    }
+    if (t < 64) {
+        float b = -INFINITY;
+        if (t < nvalid) b = bias_src ? bias_src[t] * bias_scale : 0.f;
+        bias2[t] = b;
+    }
+}
+
+// grid: BH * (Tv + Ts) tiles of real keys
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pack_keys_kernel(const T* __restrict__ K, const T* __restrict__ V, int N,
+                                                        int Nv, int Tv, int Ts, int Tall,
+                                                        __bf16* __restrict__ packed, float* __restrict__ bias2) {
+    const int per = Tv + Ts;
+    const int bh = blockIdx.x / per, t = blockIdx.x % per;
+    int row0, nvalid;
+    if (t < Tv) {
+        row0 = t * 64;
+        nvalid = min(64, Nv - row0);
+    } else {
+        row0 = Nv + (t - Tv) * 64;
+        nvalid = min(64, N - row0);
+    }
+    const size_t src = ((size_t)bh * N + row0) * D;
+    const size_t tile = (size_t)bh * Tall + t;
+    pack_tile<T, T, D>(K + src, V + src, nvalid, packed + tile * (2 * 64 * D), bias2 + tile * 64, nullptr, 0.f);
+}
+
+// grid: BH * Tc tiles of compressed pseudo-keys (fp32 summaries)
+template <int D>
+__global__ __launch_bounds__(256) void pack_compressed_kernel(const float* __restrict__ k_sum,
+                                                              const float* __restrict__ v_sum,
+                                                              const float* __restrict__ bias, int M, int Tv,
+                                                              int Ts, int Tc, int Tall,
+                                                              __bf16* __restrict__ packed, float* __restrict__ bias2) {
+    const int bh = blockIdx.x / Tc, c = blockIdx.x % Tc;
+    const int J0 = c * 64, nvalid = min(64, M - J0);
+    const size_t src = ((size_t)bh * M + J0) * D;
+    const size_t tile = (size_t)bh * Tall + Tv + Ts + c;
+    pack_tile<float, float, D>(k_sum + src, v_sum + src, nvalid, packed + tile * (2 * 64 * D), bias2 + tile * 64,
+                               bias + (size_t)bh * M + J0, 1.4426950408889634f);
+}
+
+template <typename T, int D>
+static void launch_pack_t(const LaunchCtx& L, const void* K, const void* V, const float* k_sum, const float* v_sum,
+                          const float* bias, void* packed) {
+    const PackGeom g = pack_geom(L);
+    __bf16* kv = (__bf16*)packed;
+    float* b2 = (float*)((char*)packed + g.bias_off);
+    if (K && V)
+        hipLaunchKernelGGL((pack_keys_kernel<T, D>), dim3(L.BH * (g.Tv + g.Ts)), dim3(256), 0, L.stream,
+                           (const T*)K, (const T*)V, L.N, L.Nv, g.Tv, g.Ts, g.Tall, kv, b2);
+    if (k_sum && v_sum && bias)
+        hipLaunchKernelGGL((pack_compressed_kernel<D>), dim3(L.BH * g.Tc), dim3(256), 0, L.stream, k_sum, v_sum,
+                           bias, L.M, g.Tv, g.Ts, g.Tc, g.Tall, kv, b2);
+}
+
+void launch_pack(const LaunchCtx& L, const void* K, const void* V, const float* k_sum, const float* v_sum,
+                 const float* bias, void* packed) {
+    if (L.dtype == SPARK_ATTN_BF16) {
+        if (L.d == 64) launch_pack_t<__bf16, 64>(L, K, V, k_sum, v_sum, bias, packed);
+        else launch_pack_t<__bf16, 128>(L, K, V, k_sum, v_sum, bias, packed);
+    } else {
+        if (L.d == 64) launch_pack_t<float, 64>(L, K, V, k_sum, v_sum, bias, packed);
+        else launch_pack_t<float, 128>(L, K, V, k_sum, v_sum, bias, packed);
+    }
+}
+
+}  // namespace spark

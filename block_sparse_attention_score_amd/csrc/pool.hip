@@ -47,18 +47,28 @@ __global__ __launch_bounds__(256) void pool_q_kernel(const T* __restrict__ Q, in
     }
 }
 
-// anchor = mean of all video queries = sum_J n_J * q_mean_J / N_v (binary64 accumulation).
+// anchor = mean of all video queries = sum_J n_J * q_mean_J / N_v, binary64 accumulation in a
+// fixed order: 1024 threads per (batch, head), P = 1024 / D interleaved partial sums per column,
+// combined in part order.
+constexpr int kAnchorThreads = 1024;
+
 template <int D>
-__global__ __launch_bounds__(D) void anchor_kernel(const float* __restrict__ q_mean, int Nv, int M,
-                                                   int BLK, float* __restrict__ anchor) {
-    const int bh = blockIdx.x, col = threadIdx.x;
+__global__ __launch_bounds__(kAnchorThreads) void anchor_kernel(const float* __restrict__ q_mean, int Nv, int M,
+                                                                int BLK, float* __restrict__ anchor) {
+    constexpr int P = kAnchorThreads / D;
+    __shared__ double red[P][D];
+    const int bh = blockIdx.x, col = threadIdx.x % D, part = threadIdx.x / D;
     const float* qm = q_mean + (size_t)bh * M * D + col;
     double s = 0.0;
-    for (int J = 0; J < M; ++J) {
-        const int n = min(BLK, Nv - J * BLK);
-        s += (double)n * (double)qm[(size_t)J * D];
+#pragma unroll 8
+    for (int J = part; J < M; J += P) s += (double)min(BLK, Nv - J * BLK) * (double)qm[(size_t)J * D];
+    red[part][col] = s;
+    __syncthreads();
+    if (threadIdx.x < D) {
+        double t = 0.0;
+        for (int q = 0; q < P; ++q) t += red[q][col];
+        anchor[(size_t)bh * D + col] = (float)(t / (double)Nv);
     }
-    anchor[(size_t)bh * D + col] = (float)(s / (double)Nv);
 }
 
 // Key/value block summaries.  REWEIGHT: x_i = s * a.k_i, m = max x, e_i = exp(x_i - m),
@@ -201,8 +211,8 @@ static void launch_pool_t(const LaunchCtx& L, const void* Q, const void* K, cons
     const dim3 grid(L.BH * L.M);
     hipLaunchKernelGGL((pool_q_kernel<T, D, BLK>), grid, dim3(256), 0, L.stream, (const T*)Q, L.N,
                        L.Nv, L.M, q_mean);
-    hipLaunchKernelGGL((anchor_kernel<D>), dim3(L.BH), dim3(D), 0, L.stream, q_mean, L.Nv, L.M, BLK,
-                       anchor);
+    hipLaunchKernelGGL((anchor_kernel<D>), dim3(L.BH), dim3(kAnchorThreads), 0, L.stream, q_mean, L.Nv, L.M,
+                       BLK, anchor);
     if (L.pool_mode == SPARK_ATTN_POOL_REWEIGHT)
         hipLaunchKernelGGL((pool_kv_kernel<T, D, BLK, true>), grid, dim3(256), 0, L.stream, (const T*)K,
                            (const T*)V, anchor, L.N, L.Nv, L.M, L.scale, k_mean, k_sum, v_sum, bias);

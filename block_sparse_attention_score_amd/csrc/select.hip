@@ -2,144 +2,151 @@
 // "ブロックスパースアテンション": each query block is routed to a subset of key blocks; the top-k
 // mode keeps a fixed fraction of them; Spark-H3 page, "ワークフロー": topk_mode=topk_ratio).
 //
-// One workgroup scores R query-block rows of one (batch, head) against every key block:
-// S_IJ = s * q_mean_I . k_mean_J in fp32 (the fp32 means are staged through LDS 64 key rows at a
-// time, so each k_mean row is read once per workgroup).  The R score rows stay in LDS; one wave
-// then finds each row's K-th largest score by a 32-step bisection on order-preserving integer
-// keys (wave ballots and sums), resolves ties toward lower block indices, and writes the chosen
-// blocks in ascending order with a ballot/popcount compaction.
+// Two kernels:
+//  1. block_scores: S_IJ = s * q_mean_I . k_mean_J for every (batch, head), a batched fp32 GEMM
+//     (64 x 64 output tile per workgroup, 4 x 4 per thread, d staged through LDS 32 at a time).
+//     Scores must be fp32-accurate: a near-tie between the K-th and (K+1)-th block is decided by
+//     them, so no bf16 rounding is allowed here.
+//  2. topk_rows: one wave per score row.  The row's scores live in registers as order-preserving
+//     integer keys (KPL per lane); the K-th largest key is found bit by bit from the top, counting
+//     keys >= candidate with wave ballots and popcounts; ties at the threshold go to the lower
+//     block index; the chosen blocks are written in ascending order by a ballot/popcount
+//     compaction.  Deterministic, no atomics.
 #include "kernels.hpp"
 
 namespace spark {
 
-constexpr int kSelChunk = 64;  // key rows staged per step
+constexpr int kGT = 64;   // score tile (rows and columns)
+constexpr int kGD = 32;   // d per LDS stage
 
-// Order-preserving map float -> uint32 (larger float, larger key); -0 is folded onto +0.
+__global__ __launch_bounds__(256) void block_scores_kernel(const float* __restrict__ q_mean,
+                                                           const float* __restrict__ k_mean, int M, int D,
+                                                           float scale, float* __restrict__ S) {
+    __shared__ float Qs[kGD][kGT + 4];
+    __shared__ float Ks[kGD][kGT + 4];
+    const int bh = blockIdx.z, I0 = blockIdx.y * kGT, J0 = blockIdx.x * kGT;
+    const int t = threadIdx.x, ty = t / 16, tx = t % 16;
+    const float* qb = q_mean + (size_t)bh * M * D;
+    const float* kb = k_mean + (size_t)bh * M * D;
+    float acc[4][4] = {};
+    for (int d0 = 0; d0 < D; d0 += kGD) {
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {  // 64 rows x 32 d = 512 float4 per operand
+            const int e = t + 256 * k, r = e / 8, c = (e % 8) * 4;
+            f32x4 qv = {0.f, 0.f, 0.f, 0.f}, kv = {0.f, 0.f, 0.f, 0.f};
+            if (I0 + r < M) qv = *reinterpret_cast<const f32x4*>(qb + (size_t)(I0 + r) * D + d0 + c);
+            if (J0 + r < M) kv = *reinterpret_cast<const f32x4*>(kb + (size_t)(J0 + r) * D + d0 + c);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                Qs[c + m][r] = qv[m];
+                Ks[c + m][r] = kv[m];
+            }
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int dd = 0; dd < kGD; ++dd) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(&Qs[dd][ty * 4]);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(&Ks[dd][tx * 4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int I = I0 + ty * 4 + i;
+        if (I >= M) break;
+        float* dst = S + ((size_t)bh * M + I) * M;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int J = J0 + tx * 4 + j;
+            if (J < M) dst[J] = scale * acc[i][j];
+        }
+    }
+}
+
+// Order-preserving map float -> uint32 (larger float, larger key); -0 is folded onto +0.  Every
+// finite score maps to a key >= 1, so 0 can pad a row.
 __device__ __forceinline__ uint32_t score_key(float f) {
     f = f + 0.0f;
     const uint32_t u = __float_as_uint(f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q_mean,
-                                                     const float* __restrict__ k_mean, int M, int K,
-                                                     int R, float scale, int32_t* __restrict__ idx,
-                                                     float* __restrict__ scores) {
-    extern __shared__ float smem[];
-    constexpr int KS = D + 4;  // padded stride of staged key rows
-    const int rowblocks = (M + R - 1) / R;
-    const int bh = blockIdx.x / rowblocks, I0 = (blockIdx.x % rowblocks) * R;
-    const int nr = min(R, M - I0);
-    float* qs = smem;                 // [R][D]
-    float* kc = qs + R * D;           // [kSelChunk][KS]
-    float* S = kc + kSelChunk * KS;   // [R][M]
-
-    const float* qsrc = q_mean + ((size_t)bh * M + I0) * D;
-    for (int e = threadIdx.x; e < nr * D; e += 256) qs[e] = qsrc[e];
-
-    const int jl = threadIdx.x & 63, rw = threadIdx.x >> 6;
-    const float* ksrc = k_mean + (size_t)bh * M * D;
-    for (int J0 = 0; J0 < M; J0 += kSelChunk) {
-        const int nj = min(kSelChunk, M - J0);
-        __syncthreads();
-        for (int e = threadIdx.x; e < kSelChunk * (D / 4); e += 256) {
-            const int r = e / (D / 4), c4 = (e % (D / 4)) * 4;
-            f32x4 v = {0.f, 0.f, 0.f, 0.f};
-            if (r < nj) v = *reinterpret_cast<const f32x4*>(ksrc + (size_t)(J0 + r) * D + c4);
-            *reinterpret_cast<f32x4*>(kc + r * KS + c4) = v;
-        }
-        __syncthreads();
-        if (jl < nj) {
-            const float* kr = kc + jl * KS;
-            for (int r = rw; r < nr; r += 4) {
-                const float* qr = qs + r * D;
-                float acc = 0.f;
-#pragma unroll 8
-                for (int c = 0; c < D; c += 4) {
-                    const f32x4 kv = *reinterpret_cast<const f32x4*>(kr + c);
-                    const f32x4 qv = *reinterpret_cast<const f32x4*>(qr + c);
-                    acc = fmaf(qv[0], kv[0], acc);
-                    acc = fmaf(qv[1], kv[1], acc);
-                    acc = fmaf(qv[2], kv[2], acc);
-                    acc = fmaf(qv[3], kv[3], acc);
-                }
-                S[r * M + J0 + jl] = scale * acc;
-            }
+// KPL > 0: the row is held in KPL registers per lane (M <= 64 * KPL).  KPL == 0: the row is
+// re-read from memory on every pass (any M).
+template <int KPL>
+__global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict__ S, int rows, int M, int K,
+                                                        int32_t* __restrict__ idx) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const float* Sr = S + (size_t)row * M;
+    constexpr int NREG = KPL > 0 ? KPL : 1;
+    uint32_t key[NREG];
+    if (KPL > 0) {
+#pragma unroll
+        for (int j = 0; j < NREG; ++j) {
+            const int J = lane + 64 * j;
+            key[j] = J < M ? score_key(Sr[J]) : 0u;
         }
     }
-    __syncthreads();
+    auto key_at = [&](int j) -> uint32_t {  // key of block lane + 64 j
+        if (KPL > 0) return key[j];
+        const int J = lane + 64 * j;
+        return J < M ? score_key(Sr[J]) : 0u;
+    };
+    const int chunks = KPL > 0 ? KPL : (M + 63) / 64;
 
-    if (scores) {
-        float* dst = scores + ((size_t)bh * M + I0) * M;
-        for (int e = threadIdx.x; e < nr * M; e += 256) dst[e] = S[e];
+    // largest T with #{J : key_J >= T} >= K, i.e. the K-th largest key
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        int cnt = 0;
+        for (int j = 0; j < chunks; ++j) cnt += __popcll(__ballot(key_at(j) >= cand));
+        if (cnt >= K) T = cand;
     }
+    int gt = 0;
+    for (int j = 0; j < chunks; ++j) gt += __popcll(__ballot(key_at(j) > T));
+    const int need = K - gt;  // keys equal to T still to take, lowest block index first
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const uint64_t below = lanemask_lt();
-    for (int r = w; r < nr; r += 4) {
-        const float* Sr = S + r * M;
-        // largest T with #{J : key_J >= T} >= K, i.e. the K-th largest key, bit by bit from the top
-        uint32_t T = 0;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cand = T | (1u << bit);
-            int cnt = 0;
-            for (int J = lane; J < M; J += 64) cnt += score_key(Sr[J]) >= cand;
-            if (wave_sum_int(cnt) >= K) T = cand;
-        }
-        int gt = 0;
-        for (int J = lane; J < M; J += 64) gt += score_key(Sr[J]) > T;
-        const int need = K - wave_sum_int(gt);  // keys equal to T still to take, lowest J first
-        int32_t* out = idx + ((size_t)bh * M + I0 + r) * K;
-        int pos = 0, eq_seen = 0;
-        for (int J0 = 0; J0 < M; J0 += 64) {
-            const int J = J0 + lane;
-            const uint32_t kk = J < M ? score_key(Sr[J]) : 0u;
-            const bool eq = J < M && kk == T;
-            const uint64_t eqb = __ballot(eq);
-            const int eq_rank = eq_seen + __popcll(eqb & below);
-            const bool sel = J < M && (kk > T || (eq && eq_rank < need));
-            const uint64_t sb = __ballot(sel);
-            if (sel) out[pos + __popcll(sb & below)] = J;
-            pos += __popcll(sb);
-            eq_seen += __popcll(eqb);
-        }
+    int32_t* out = idx + (size_t)row * K;
+    int pos = 0, eq_seen = 0;
+    for (int j = 0; j < chunks; ++j) {
+        const uint32_t kk = key_at(j);
+        const uint64_t eqb = __ballot(kk == T);
+        const int eq_rank = eq_seen + __popcll(eqb & below);
+        const bool sel = kk > T || (kk == T && eq_rank < need);
+        const uint64_t sb = __ballot(sel);
+        if (sel) out[pos + __popcll(sb & below)] = lane + 64 * j;
+        pos += __popcll(sb);
+        eq_seen += __popcll(eqb);
     }
 }
 
-static int max_lds_bytes() {
-    static int cached = 0;
-    if (!cached) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0)
-            cached = v;
-        else
-            cached = 65536;
-    }
-    return cached;
-}
+size_t select_workspace_bytes(const LaunchCtx& L) { return (size_t)L.BH * L.M * L.M * 4; }
 
-template <int D>
-static void launch_select_t(const LaunchCtx& L, const float* q_mean, const float* k_mean, int32_t* idx,
-                            float* scores) {
-    const int budget = max_lds_bytes();
-    const int fixed = kSelChunk * (D + 4) * 4;
-    int R = (budget - fixed) / (4 * (D + L.M));
-    R = R > 16 ? 16 : (R < 1 ? 1 : R);
-    const size_t lds = (size_t)4 * (R * D + kSelChunk * (D + 4) + (size_t)R * L.M);
-    if (lds > 65536)
-        (void)hipFuncSetAttribute((const void*)select_kernel<D>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    const int rowblocks = (L.M + R - 1) / R;
-    hipLaunchKernelGGL((select_kernel<D>), dim3(L.BH * rowblocks), dim3(256), lds, L.stream, q_mean, k_mean,
-                       L.M, L.K, R, L.scale, idx, scores);
-}
-
-void launch_select(const LaunchCtx& L, const float* q_mean, const float* k_mean, int32_t* idx,
-                   float* scores) {
-    if (L.d == 64) launch_select_t<64>(L, q_mean, k_mean, idx, scores);
-    else launch_select_t<128>(L, q_mean, k_mean, idx, scores);
+void launch_select(const LaunchCtx& L, const float* q_mean, const float* k_mean, int32_t* idx, float* scores) {
+    const dim3 sgrid((L.M + kGT - 1) / kGT, (L.M + kGT - 1) / kGT, L.BH);
+    hipLaunchKernelGGL(block_scores_kernel, sgrid, dim3(256), 0, L.stream, q_mean, k_mean, L.M, L.d, L.scale,
+                       scores);
+    const int rows = L.BH * L.M;
+    const dim3 tgrid((rows + 3) / 4);
+    const int need = (L.M + 63) / 64;
+#define SPARK_TOPK(KPL) \
+    hipLaunchKernelGGL((topk_rows_kernel<KPL>), tgrid, dim3(256), 0, L.stream, scores, rows, L.M, L.K, idx)
+    if (need <= 1) SPARK_TOPK(1);
+    else if (need <= 2) SPARK_TOPK(2);
+    else if (need <= 4) SPARK_TOPK(4);
+    else if (need <= 8) SPARK_TOPK(8);
+    else if (need <= 16) SPARK_TOPK(16);
+    else if (need <= 32) SPARK_TOPK(32);
+    else if (need <= 64) SPARK_TOPK(64);
+    else SPARK_TOPK(0);
+#undef SPARK_TOPK
 }
 
 }  // namespace spark

@@ -81,9 +81,10 @@ int spark_attn_num_blocks(const spark_attn_params *p);
  * Returns a negative status if M < 1 or ratio is outside (0, 1]. */
 int spark_attn_topk_count(int M, float ratio);
 
-/* Bytes of device workspace spark_attn_forward needs (with_perm != 0: a partition is given),
- * or spark_attn_reblock needs (what = 1).  Returns 0 for invalid params.
- *   what = 0: forward without perm; what = 1: reblock; what = 2: forward with perm. */
+/* Bytes of device workspace a call needs, or 0 for invalid params:
+ *   what = 0: spark_attn_forward without perm;  what = 2: spark_attn_forward with perm;
+ *   what = 1: spark_attn_reblock;               what = 3: spark_attn_select without `scores`;
+ *   what = 4: the packed key/value tiles of spark_attn_pack / spark_attn_attend. */
 size_t spark_attn_workspace_size(const spark_attn_params *p, int what);
 
 /* Static description of a status code. */
@@ -114,15 +115,29 @@ int spark_attn_pool(const spark_attn_params *p, const void *Q, const void *K, co
  * In:  q_mean, k_mean [B,H,M,d] fp32 (from spark_attn_pool).
  * Out: idx [B,H,M,K] int32: for query block I, the K key blocks J with the largest block scores
  *      S_IJ = s * q_mean_I . k_mean_J (fp32), ties to the lower J, listed in ascending J.
- *      scores [B,H,M,M] fp32, optional (NULL to skip): S itself.
+ *      scores [B,H,M,M] fp32, optional: receives S.  When NULL, S is kept in `workspace`, which
+ *      must then hold spark_attn_workspace_size(p, 3) bytes (ignored otherwise).
  */
 int spark_attn_select(const spark_attn_params *p, const float *q_mean, const float *k_mean,
-                      int32_t *idx, float *scores, void *stream);
+                      int32_t *idx, float *scores, void *workspace, size_t ws_bytes, void *stream);
 
 /*
- * The attention stage alone (exact branch + sinks + compressed branch, one softmax).
- * In:  Q, K, V [B,H,N,d] (already in the block layout idx refers to); k_sum, v_sum [B,H,M,d],
- *      bias [B,H,M] fp32; idx [B,H,M,K] int32 ascending or not, distinct entries in [0, M).
+ * Packing of the keys and values the attention stage reads.  `packed` (device memory of at least
+ * spark_attn_workspace_size(p, 4) bytes, caller-owned) receives, per (batch, head), 64-key tiles of
+ * bf16 K rows and transposed V for the video keys, the sink keys and the compressed pseudo-keys
+ * (k_sum / v_sum rows), plus one fp32 additive logit row per tile (log2 units: 0 for real keys,
+ * log2(e) * bias for pseudo-keys, -inf for padding).  The layout is private to the library: fill it
+ * with this call, read it with spark_attn_attend.
+ * In:  K, V [B,H,N,d] in p->dtype; k_sum, v_sum [B,H,M,d], bias [B,H,M] fp32 (spark_attn_pool).
+ */
+int spark_attn_pack(const spark_attn_params *p, const void *K, const void *V, const float *k_sum,
+                    const float *v_sum, const float *bias, void *packed, size_t packed_bytes,
+                    void *stream);
+
+/*
+ * The attention stage (exact branch + sinks + compressed branch, one softmax).
+ * In:  Q [B,H,N,d] (in the block layout idx refers to); packed (spark_attn_pack of the matching
+ *      K, V and summaries); idx [B,H,M,K] int32, distinct entries in [0, M) per row.
  *      perm [B,H,N_v] int32 or NULL: when given, output row q of the video part is written to
  *      row perm[q] of O and lse (undoing a partition).
  * Out: O [B,H,N,d] in p->dtype; lse [B,H,N] fp32 (natural log), optional.
@@ -130,12 +145,12 @@ int spark_attn_select(const spark_attn_params *p, const float *q_mean, const flo
  * every sink row, and to one pseudo-key per unselected block J (logit s*q.k_sum_J + bias_J,
  * value v_sum_J).  Sink query rows attend densely to all N keys.
  */
-int spark_attn_attend(const spark_attn_params *p, const void *Q, const void *K, const void *V,
-                      const float *k_sum, const float *v_sum, const float *bias,
-                      const int32_t *idx, const int32_t *perm, void *O, float *lse, void *stream);
+int spark_attn_attend(const spark_attn_params *p, const void *Q, const void *packed,
+                      size_t packed_bytes, const int32_t *idx, const int32_t *perm, void *O,
+                      float *lse, void *stream);
 
 /*
- * The whole forward: [gather rows by perm] -> pool -> select -> attend (-> un-permute).
+ * The whole forward: [gather rows by perm] -> pool -> select -> pack -> attend (-> un-permute).
  * In:  Q, K, V [B,H,N,d] in p->dtype; perm [B,H,N_v] int32 or NULL (a permutation of [0,N_v)
  *      per (batch, head), e.g. from spark_attn_reblock: block layout row q holds token perm[q];
  *      keys and values reuse it).

@@ -86,8 +86,9 @@ def test_invalid_params_rejected_before_launch(kw, status):
     assert L.spark_attn_num_blocks(ctypes.byref(p)) == status
     assert L.spark_attn_workspace_size(ctypes.byref(p), 0) == 0
     assert L.spark_attn_pool(ctypes.byref(p), *([fake] * 9), None) == status
-    assert L.spark_attn_select(ctypes.byref(p), fake, fake, fake, None, None) == status
-    assert L.spark_attn_attend(ctypes.byref(p), *([fake] * 7), None, fake, None, None) == status
+    assert L.spark_attn_select(ctypes.byref(p), fake, fake, fake, None, fake, 1 << 40, None) == status
+    assert L.spark_attn_pack(ctypes.byref(p), *([fake] * 6), 1 << 40, None) == status
+    assert L.spark_attn_attend(ctypes.byref(p), fake, fake, 1 << 40, fake, None, fake, None, None) == status
     assert L.spark_attn_forward(ctypes.byref(p), fake, fake, fake, None, fake, None, None, fake,
                                 1 << 40, None) == status
     assert L.spark_attn_reblock(ctypes.byref(p), fake, fake, fake, fake, 1 << 40, None) == status
@@ -101,10 +102,17 @@ def test_null_and_misaligned_pointers_rejected():
     bad = ctypes.c_void_p(0x100008)
     assert L.spark_attn_pool(ctypes.byref(p), None, a, a, a, a, a, a, a, a, None) == INVALID
     assert L.spark_attn_pool(ctypes.byref(p), bad, a, a, a, a, a, a, a, a, None) == MISALIGNED
-    assert L.spark_attn_select(ctypes.byref(p), a, a, None, None, None) == INVALID
-    assert L.spark_attn_select(ctypes.byref(p), bad, a, a, None, None) == MISALIGNED
-    assert L.spark_attn_attend(ctypes.byref(p), a, a, a, a, a, a, None, None, a, None, None) == INVALID
-    assert L.spark_attn_attend(ctypes.byref(p), a, a, a, a, a, a, a, None, bad, None, None) == MISALIGNED
+    assert L.spark_attn_select(ctypes.byref(p), a, a, None, None, a, 1 << 40, None) == INVALID
+    assert L.spark_attn_select(ctypes.byref(p), bad, a, a, None, a, 1 << 40, None) == MISALIGNED
+    assert L.spark_attn_select(ctypes.byref(p), a, a, a, None, None, 0, None) == WS_SMALL
+    assert L.spark_attn_select(ctypes.byref(p), a, a, a, None, a, 10, None) == WS_SMALL
+    assert L.spark_attn_attend(ctypes.byref(p), a, a, 1 << 40, None, None, a, None, None) == INVALID
+    assert L.spark_attn_attend(ctypes.byref(p), a, a, 1 << 40, a, None, bad, None, None) == MISALIGNED
+    assert L.spark_attn_attend(ctypes.byref(p), a, a, 10, a, None, a, None, None) == WS_SMALL
+    assert L.spark_attn_attend(ctypes.byref(p), a, None, 1 << 40, a, None, a, None, None) == WS_SMALL
+    assert L.spark_attn_pack(ctypes.byref(p), a, None, a, a, a, a, 1 << 40, None) == INVALID
+    assert L.spark_attn_pack(ctypes.byref(p), a, a, a, bad, a, a, 1 << 40, None) == MISALIGNED
+    assert L.spark_attn_pack(ctypes.byref(p), a, a, a, a, a, a, 10, None) == WS_SMALL
     assert L.spark_attn_forward(ctypes.byref(p), a, a, a, None, None, None, None, a, 1 << 40, None) == INVALID
     assert L.spark_attn_forward(ctypes.byref(p), a, bad, a, None, a, None, None, a, 1 << 40, None) == MISALIGNED
     assert L.spark_attn_gather_rows(ctypes.byref(p), a, a, a, None) == INVALID  # in place
@@ -118,8 +126,12 @@ def test_workspace_sizes_and_too_small():
     w0 = L.spark_attn_workspace_size(ctypes.byref(p), 0)
     w2 = L.spark_attn_workspace_size(ctypes.byref(p), 2)
     M, K, d, BH = 1922, 192, 128, 24
-    assert w0 >= 4 * BH * M * d * 4 + BH * M * 4 + BH * d * 4 + BH * M * K * 4
-    assert w0 < 4 * BH * M * d * 4 + BH * M * 4 + BH * d * 4 + BH * M * K * 4 + 8 * 256
+    Tall = 1922 * 2 + 8 + 31  # video (2 per block), sink and compressed 64-key tiles per head
+    packed = BH * Tall * 64 * (2 * d * 2 + 4)
+    assert packed <= L.spark_attn_workspace_size(ctypes.byref(p), 4) < packed + 256
+    need = 4 * BH * M * d * 4 + BH * M * 4 + BH * d * 4 + BH * M * K * 4 + BH * M * M * 4 + packed
+    assert need <= w0 < need + 11 * 256
+    assert L.spark_attn_workspace_size(ctypes.byref(p), 3) == BH * M * M * 4
     assert w2 - w0 >= 3 * BH * (245952 + 512) * d * 2
     a = ctypes.c_void_p(0x100000)
     assert L.spark_attn_forward(ctypes.byref(p), a, a, a, None, a, None, None, a, w0 - 1, None) == WS_SMALL

@@ -246,3 +246,19 @@ def test_720p_sampled(orc, ratio):
 
 def test_fullclip_sampled(orc):
     sampled_check(orc, W.WORKLOADS["fullclip"], 0.1, n_blocks=12, n_sink_rows=4)
+
+
+def test_stage_entry_points_match_forward():
+    """pool -> select -> pack -> attend through their own entry points gives exactly what
+    spark_attn_forward gives (same kernels, same inputs)."""
+    B, H, nv, ns, d, b, r = 1, 2, 7 * 128 + 19, 45, 128, 128, 0.2
+    Q, K, V = W.gaussian_qkv(B, H, nv, ns, d, seed=31, dtype="bf16")
+    Qd, Kd, Vd = to_dev(Q, "bf16"), to_dev(K, "bf16"), to_dev(V, "bf16")
+    note("stage entry points vs forward")
+    O, lse, idx = sa.forward(Qd, Kd, Vd, ns, b, r, return_lse=True, return_idx=True)
+    pooled = sa.pool(Qd, Kd, Vd, ns, b)
+    idx2 = sa.select(pooled["q_mean"], pooled["k_mean"], Qd, ns, b, r)
+    lse2 = torch.empty_like(lse)
+    O2 = sa.attend(Qd, Kd, Vd, pooled, idx2, ns, b, r, lse=lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(O, O2) and torch.equal(lse, lse2)
