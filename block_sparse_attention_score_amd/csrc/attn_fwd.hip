@@ -50,27 +50,33 @@ __device__ __forceinline__ int key_perm(int m) { return (m & ~12) | ((m & 4) << 
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// Source chunk (16 bytes) of the packed tile that lands in LDS chunk q: K rows in the order pi
+// with the row swizzle, then V^T rows with theirs.  Depends only on q, so each lane computes its
+// offsets once.
+template <int D>
+__device__ __forceinline__ int tile_src_chunk(int q) {
+    using G = TileGeom<D>;
+    if (q < G::K_CHUNKS) {
+        const int m = q / G::CK, pc = q % G::CK;
+        const int grow = (m & ~31) | key_perm(m & 31);
+        return grow * G::CK + (pc ^ swz<G::CK>(m));
+    }
+    const int q2 = q - G::K_CHUNKS;
+    const int dr = q2 / G::V_CPR, pc = q2 % G::V_CPR;
+    return G::K_CHUNKS + dr * G::V_CPR + (pc ^ swz<G::V_CPR>(dr));
+}
+
+// One packed tile (and its bias row) HBM -> LDS; every lane moves CHUNKS / NT chunks.
 template <int D, int NT>
 __device__ __forceinline__ void issue_tile(const __bf16* __restrict__ gtile, const float* __restrict__ gbias,
-                                           __bf16* ltile, float* lbias) {
+                                           const int (&src)[TileGeom<D>::CHUNKS / NT], __bf16* ltile,
+                                           float* lbias) {
     using G = TileGeom<D>;
-    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < G::CHUNKS / NT; ++i) {
-        const int q = i * NT + t;  // LDS chunk this lane fills
-        int src;
-        if (q < G::K_CHUNKS) {
-            const int m = q / G::CK, pc = q % G::CK;
-            const int grow = (m & ~31) | key_perm(m & 31);
-            src = grow * G::CK + (pc ^ swz<G::CK>(m));
-        } else {
-            const int q2 = q - G::K_CHUNKS;
-            const int dr = q2 / G::V_CPR, pc = q2 % G::V_CPR;
-            src = G::K_CHUNKS + dr * G::V_CPR + (pc ^ swz<G::V_CPR>(dr));
-        }
-        __builtin_amdgcn_global_load_lds((const void*)(gtile + (size_t)src * 8),
+    for (int i = 0; i < G::CHUNKS / NT; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(gtile + (size_t)src[i] * 8),
                                          (lds_ptr)(ltile + (size_t)(i * NT + w * 64) * 8), 16, 0, 0);
-    }
     if (w == 0) __builtin_amdgcn_global_load_lds((const void*)(gbias + lane), (lds_ptr)lbias, 4, 0, 0);
 }
 
@@ -134,10 +140,11 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
             atomicOr(&sel_bits[J >> 5], 1u << (J & 31));
         }
     }
-    {  // first tile in flight while Q is loaded
-        const int tl = tile_of(0);
-        issue_tile<D, NT>(ptile + (size_t)tl * G::ELEMS, pbias + (size_t)tl * kTK, lkv[0], lbias[0]);
-    }
+    int src[G::CHUNKS / NT];
+#pragma unroll
+    for (int i = 0; i < G::CHUNKS / NT; ++i) src[i] = tile_src_chunk<D>(i * NT + threadIdx.x);
+    int tl_cur = tile_of(0);  // first tile in flight while Q is loaded
+    issue_tile<D, NT>(ptile + (size_t)tl_cur * G::ELEMS, pbias + (size_t)tl_cur * kTK, src, lkv[0], lbias[0]);
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int i32 = lane & 31, h = lane >> 5;
@@ -164,13 +171,16 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     float m_run = -INFINITY, l_run = 0.f;
     const int first_cmp = dense ? ntiles : n_exact + Ts;  // first compressed tile in the list
 
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
     for (int t = 0; t < ntiles; ++t) {
         const int s = t & 1;
         __builtin_amdgcn_s_waitcnt(0);  // this thread's share of tile t has landed in LDS
         __syncthreads();                // ... and everyone's; stage s^1 is free again
+        int tl_next = 0;
         if (t + 1 < ntiles) {
-            const int tl = tile_of(t + 1);
-            issue_tile<D, NT>(ptile + (size_t)tl * G::ELEMS, pbias + (size_t)tl * kTK, lkv[s ^ 1], lbias[s ^ 1]);
+            tl_next = tile_of(t + 1);
+            issue_tile<D, NT>(ptile + (size_t)tl_next * G::ELEMS, pbias + (size_t)tl_next * kTK, src, lkv[s ^ 1],
+                              lbias[s ^ 1]);
         }
         const __bf16* Kl = lkv[s];
         const __bf16* Vl = lkv[s] + kTK * D;
@@ -191,26 +201,42 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
             }
             st[c] = a16;
         }
-        // ---- logits (log2 units).  Register 4g+j of chunk c holds key c*32 + 16(g/2) + 8h + 4(g%2) + j.
-        const bool compressed = t >= first_cmp;
-        const int cbase = (t - first_cmp) * kTK;  // first pseudo-key of a compressed tile
+
+        // ---- probabilities.  Register 4g+j of chunk c holds key c*32 + 16(g/2) + 8h + 4(g%2) + j.
+        // A plain tile (64 real keys, additive term 0) takes the short path: max over the raw
+        // scores and p = exp2(s * c - m) in one fma per key.  Other tiles (padded, compressed) add
+        // their bias row and, for compressed tiles, mask this query block's selected blocks.
+        const bool plain = tl_cur < Tv ? (tl_cur + 1) * kTK <= Nv
+                                       : (tl_cur < Tv + Ts && Nv + (tl_cur - Tv + 1) * kTK <= N);
         float mx = -INFINITY;
+        if (plain) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+            for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int key = c * 32 + 16 * (g >> 1) + 8 * h + 4 * (g & 1);
-                const f32x4 bb = *reinterpret_cast<const f32x4*>(lbias[s] + key);
-                uint32_t selw = 0;
-                if (compressed) selw = sel_bits[(cbase + key) >> 5] >> ((cbase + key) & 31);
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[c][r]);
+            mx *= c_log2;
+        } else {
+            const bool compressed = t >= first_cmp;
+            const int cbase = (t - first_cmp) * kTK;  // first pseudo-key of a compressed tile
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float z = fmaf(st[c][4 * g + j], c_log2, bb[j]);
-                    if ((selw >> j) & 1u) z = -INFINITY;
-                    st[c][4 * g + j] = z;
-                    mx = fmaxf(mx, z);
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int key = c * 32 + 16 * (g >> 1) + 8 * h + 4 * (g & 1);
+                    f32x4 bb = *reinterpret_cast<const f32x4*>(lbias[s] + key);
+                    // this query block's selected blocks leave the compressed branch: the mask goes
+                    // into the additive term with selects (no divergent writes to the scores)
+                    const uint32_t selw =
+                        compressed ? sel_bits[(cbase + key) >> 5] >> ((cbase + key) & 31) : 0u;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) bb[j] = ((selw >> j) & 1u) ? -INFINITY : bb[j];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        st[c][4 * g + j] = fmaf(st[c][4 * g + j], c_log2, bb[j]);
+                        mx = fmaxf(mx, st[c][4 * g + j]);
+                    }
                 }
-            }
+        }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const bool raise = mx > m_run + kRescaleSlack;
         if (__ballot(raise)) {
@@ -224,31 +250,44 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
             m_run = m_new;
         }
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        float ls = 0.f;
+        if (plain) {
+            const float nm = -m_use;
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+            for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(st[c][r] - m_use);
-                st[c][r] = p;
-                ls += p;
+                for (int r = 0; r < 16; ++r) st[c][r] = __builtin_amdgcn_exp2f(fmaf(st[c][r], c_log2, nm));
+        } else {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) st[c][r] = __builtin_amdgcn_exp2f(st[c][r] - m_use);
+        }
+        // P in bf16, 16 keys per PV step: lane (i32, h) supplies keys 16kt + 8h + e (e = 0..7).
+        // The normaliser sums the same bf16 values the PV product uses.
+        bf16x8 pk[kTK / 16];
+#pragma unroll
+        for (int kt = 0; kt < kTK / 16; ++kt)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pk[kt][e] = (__bf16)st[kt >> 1][8 * (kt & 1) + e];
+#pragma unroll
+        for (int kt = 0; kt < kTK / 16; ++kt)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const bf16x2 pr = {pk[kt][e], pk[kt][e + 1]};
+                l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
             }
-        l_run += ls;
 
-        // ---- O^T += V^T P^T, 16 keys per step: lane (i32, h) supplies keys 16kt + 8h + e (e = 0..7)
+        // ---- O^T += V^T P^T
 #pragma unroll
-        for (int kt = 0; kt < kTK / 16; ++kt) {
-            bf16x8 b;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) b[e] = (__bf16)st[kt >> 1][8 * (kt & 1) + e];
+        for (int kt = 0; kt < kTK / 16; ++kt)
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
                 const int dr = dt * 32 + i32;
                 const int pc = (2 * kt + h) ^ swz<G::V_CPR>(dr);
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vl + (dr * G::V_CPR + pc) * 8);
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[dt], 0, 0, 0);
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kt], acc[dt], 0, 0, 0);
             }
-        }
+        tl_cur = tl_next;
     }
 
     // ---- epilogue: lane (i32, h) holds query row w*32 + i32, dims dt*32 + 8*g + 4*h + (0..3)

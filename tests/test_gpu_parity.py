@@ -262,3 +262,34 @@ def test_stage_entry_points_match_forward():
     O2 = sa.attend(Qd, Kd, Vd, pooled, idx2, ns, b, r, lse=lse2)
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2) and torch.equal(O, O2) and torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("d,b,dt", [(128, 128, "bf16"), (128, 64, "bf16"), (64, 64, "bf16"), (64, 128, "bf16"),
+                                    (128, 64, "fp32"), (64, 64, "fp32")])
+def test_attend_explicit_routes(orc, d, b, dt):
+    """spark_attn_attend with routes chosen by the test: every selected-block position modulo 32
+    (the compressed-branch mask bits), the first and the ragged last block, and K up to M."""
+    B, H, ns = 1, 2, 37
+    M = 70
+    nv = (M - 1) * b + 13
+    Q, K, V = W.gaussian_qkv(B, H, nv, ns, d, seed=d + b, dtype=dt)
+    Qd, Kd, Vd = to_dev(Q, dt), to_dev(K, dt), to_dev(V, dt)
+    pooled = sa.pool(Qd, Kd, Vd, ns, b)
+    rng = np.random.default_rng(b + d)
+    for Ksel, ratio in ((3, 3 / M), (9, 9 / M)):
+        assert sa.topk_count(M, ratio) == Ksel
+        idx = np.empty((B, H, M, Ksel), np.int32)
+        for h in range(H):
+            for I in range(M):
+                fixed = [I % 32, (I * 7) % M, M - 1 if I % 3 == 0 else 0]
+                rest = rng.permutation(np.setdiff1d(np.arange(M), fixed))[:Ksel]
+                row = list(dict.fromkeys(fixed + list(rest)))[:Ksel]
+                idx[0, h, I] = np.sort(row)
+        note(f"attend explicit routes d={d} b={b} {dt} K={Ksel}")
+        lse = torch.empty(B, H, nv + ns, device="cuda", dtype=torch.float32)
+        O = sa.attend(Qd, Kd, Vd, pooled, torch.from_numpy(idx).cuda(), ns, b, ratio, lse=lse)
+        torch.cuda.synchronize()
+        Oref, lref, _ = orc.forward(orc.params(Q, ns, b, ratio, 1), Q, K, V, idx=idx)
+        e2, ea, el = rel_l2(host(O), Oref), max_abs(host(O), Oref), max_abs(host(lse), lref)
+        print(f"rel-L2 {e2:.3e} max-abs {ea:.3e} lse {el:.3e}")
+        assert e2 <= FWD_REL_L2 and ea <= FWD_MAX_ABS and el <= FWD_MAX_ABS
