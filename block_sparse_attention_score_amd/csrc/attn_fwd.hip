@@ -23,6 +23,8 @@
 //    and sum need one cross-half shuffle.  The running max is only raised when a tile's max exceeds
 //    it by more than 8 (log2 units); otherwise the accumulator is not rescaled.  Probabilities are
 //    then bounded by 2^8, and the result is unchanged because O and the normaliser share the max.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace spark {
@@ -50,34 +52,64 @@ __device__ __forceinline__ int key_perm(int m) { return (m & ~12) | ((m & 4) << 
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// Source chunk (16 bytes) of the packed tile that lands in LDS chunk q: K rows in the order pi
-// with the row swizzle, then V^T rows with theirs.  Depends only on q, so each lane computes its
-// offsets once.
+// Source chunks (16 bytes) of a packed tile for LDS chunk q: K rows in the order pi with the row
+// swizzle (K part), V^T rows with theirs (V part).  They depend only on q, so every lane computes
+// its offsets once.
 template <int D>
-__device__ __forceinline__ int tile_src_chunk(int q) {
+__device__ __forceinline__ int k_src_chunk(int q) {
     using G = TileGeom<D>;
-    if (q < G::K_CHUNKS) {
-        const int m = q / G::CK, pc = q % G::CK;
-        const int grow = (m & ~31) | key_perm(m & 31);
-        return grow * G::CK + (pc ^ swz<G::CK>(m));
-    }
-    const int q2 = q - G::K_CHUNKS;
-    const int dr = q2 / G::V_CPR, pc = q2 % G::V_CPR;
+    const int m = q / G::CK, pc = q % G::CK;
+    const int grow = (m & ~31) | key_perm(m & 31);
+    return grow * G::CK + (pc ^ swz<G::CK>(m));
+}
+template <int D>
+__device__ __forceinline__ int v_src_chunk(int q) {
+    using G = TileGeom<D>;
+    const int dr = q / G::V_CPR, pc = q % G::V_CPR;
     return G::K_CHUNKS + dr * G::V_CPR + (pc ^ swz<G::V_CPR>(dr));
 }
 
-// One packed tile (and its bias row) HBM -> LDS; every lane moves CHUNKS / NT chunks.
+// K part of a packed tile HBM -> LDS (every lane moves K_CHUNKS / NT chunks).
 template <int D, int NT>
-__device__ __forceinline__ void issue_tile(const __bf16* __restrict__ gtile, const float* __restrict__ gbias,
-                                           const int (&src)[TileGeom<D>::CHUNKS / NT], __bf16* ltile,
-                                           float* lbias) {
-    using G = TileGeom<D>;
+__device__ __forceinline__ void issue_k(const __bf16* __restrict__ gtile, const int (&src)[TileGeom<D>::K_CHUNKS / NT],
+                                        __bf16* lk) {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < TileGeom<D>::K_CHUNKS / NT; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(gtile + (size_t)src[i] * 8),
+                                         (lds_ptr)(lk + (size_t)(i * NT + w * 64) * 8), 16, 0, 0);
+}
+
+// V^T part of a packed tile and its bias row HBM -> LDS.
+template <int D, int NT>
+__device__ __forceinline__ void issue_v(const __bf16* __restrict__ gtile, const float* __restrict__ gbias,
+                                        const int (&src)[TileGeom<D>::K_CHUNKS / NT], __bf16* lv, float* lb) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < G::CHUNKS / NT; ++i)
+    for (int i = 0; i < TileGeom<D>::K_CHUNKS / NT; ++i)
         __builtin_amdgcn_global_load_lds((const void*)(gtile + (size_t)src[i] * 8),
-                                         (lds_ptr)(ltile + (size_t)(i * NT + w * 64) * 8), 16, 0, 0);
-    if (w == 0) __builtin_amdgcn_global_load_lds((const void*)(gbias + lane), (lds_ptr)lbias, 4, 0, 0);
+                                         (lds_ptr)(lv + (size_t)(i * NT + w * 64) * 8), 16, 0, 0);
+    if (w == 0) __builtin_amdgcn_global_load_lds((const void*)(gbias + lane), (lds_ptr)lb, 4, 0, 0);
+}
+
+// S^T = K_tile Q^T for two chunks of 32 keys x this wave's 32 queries.
+template <int D>
+__device__ __forceinline__ void scores(const __bf16* Kl, const bf16x8 (&qreg)[D / 16], int i32, int h, f32x16 (&st)[2]) {
+    using G = TileGeom<D>;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        f32x16 a16;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a16[r] = 0.f;
+        const int m = c * 32 + i32;
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) {
+            const int pc = (2 * ds + h) ^ swz<G::CK>(m);
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kl + (m * G::CK + pc) * 8);
+            a16 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], a16, 0, 0, 0);
+        }
+        st[c] = a16;
+    }
 }
 
 template <typename T, int D, int BLK>
@@ -87,7 +119,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     int N, int Nv, int M, int Ksel, int SQ, int BH, int C, int Tv, int Ts, int Tc, float c_log2) {
     using G = TileGeom<D>;
     constexpr int NT = BLK * 2;  // BLK / 32 waves
-    __shared__ __attribute__((aligned(16))) __bf16 lkv[2][G::ELEMS];
+    constexpr int NCH = G::K_CHUNKS / NT;  // DMA chunks per lane for one K (or V^T) part
+    __shared__ __attribute__((aligned(16))) __bf16 kbuf[2][kTK * D];
+    __shared__ __attribute__((aligned(16))) __bf16 vbuf[2][kTK * D];
     __shared__ __attribute__((aligned(16))) float lbias[2][kTK];
     __shared__ uint32_t sel_bits[kMaxBlocks / 32 + 2];  // + the words a padded last tile can touch
 
@@ -124,6 +158,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     const int32_t* sel = dense ? nullptr : idx + ((size_t)bh * M + qrow0 / BLK) * Ksel;
     constexpr int nsub = BLK / kTK;
     const int n_exact = dense ? 0 : Ksel * nsub;
+    const int first_cmp = dense ? ntiles : n_exact + Ts;  // first compressed tile in the list
 
     // packed tile of list entry t: selected blocks, then sink tiles, then compressed tiles
     auto tile_of = [&](int t) -> int {
@@ -140,11 +175,21 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
             atomicOr(&sel_bits[J >> 5], 1u << (J & 31));
         }
     }
-    int src[G::CHUNKS / NT];
+    int src_k[NCH], src_v[NCH];
 #pragma unroll
-    for (int i = 0; i < G::CHUNKS / NT; ++i) src[i] = tile_src_chunk<D>(i * NT + threadIdx.x);
-    int tl_cur = tile_of(0);  // first tile in flight while Q is loaded
-    issue_tile<D, NT>(ptile + (size_t)tl_cur * G::ELEMS, pbias + (size_t)tl_cur * kTK, src, lkv[0], lbias[0]);
+    for (int i = 0; i < NCH; ++i) {
+        src_k[i] = k_src_chunk<D>(i * NT + threadIdx.x);
+        src_v[i] = v_src_chunk<D>(i * NT + threadIdx.x);
+    }
+    // Pipeline: the K stream runs one tile ahead of the V stream.  Iteration t computes the scores of
+    // tile t+1 (K(t+1) resident) while it turns the scores of tile t into probabilities and applies
+    // V(t); K(t+2) and V(t+1) stream in meanwhile.  K(j) and V(j) live in buffer j % 2.
+    {
+        const int tl0 = tile_of(0);
+        issue_k<D, NT>(ptile + (size_t)tl0 * G::ELEMS, src_k, kbuf[0]);
+        if (ntiles > 1) issue_k<D, NT>(ptile + (size_t)tile_of(1) * G::ELEMS, src_k, kbuf[1]);
+        issue_v<D, NT>(ptile + (size_t)tl0 * G::ELEMS, pbias + (size_t)tl0 * kTK, src_v, vbuf[0], lbias[0]);
+    }
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int i32 = lane & 31, h = lane >> 5;
@@ -169,74 +214,48 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
-    const int first_cmp = dense ? ntiles : n_exact + Ts;  // first compressed tile in the list
-
     const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-    for (int t = 0; t < ntiles; ++t) {
-        const int s = t & 1;
-        __builtin_amdgcn_s_waitcnt(0);  // this thread's share of tile t has landed in LDS
-        __syncthreads();                // ... and everyone's; stage s^1 is free again
-        int tl_next = 0;
+
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // K(0), K(1), V(0) and the route bits are in LDS
+    f32x16 st[2];
+    scores<D>(kbuf[0], qreg, i32, h, st);
+
+    // One pipeline step.  MASKED: tile t is a compressed tile, whose pseudo-keys of this query
+    // block's selected blocks are excluded (the mask goes into the additive term with selects).
+    auto step = [&](int t, auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+        const int P = t & 1;
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's share of K(t+1), V(t) has landed
+        __syncthreads();                // ... everyone's; K(t) and V(t-1) buffers are free
+        if (t + 2 < ntiles) issue_k<D, NT>(ptile + (size_t)tile_of(t + 2) * G::ELEMS, src_k, kbuf[P]);
         if (t + 1 < ntiles) {
-            tl_next = tile_of(t + 1);
-            issue_tile<D, NT>(ptile + (size_t)tl_next * G::ELEMS, pbias + (size_t)tl_next * kTK, src, lkv[s ^ 1],
-                              lbias[s ^ 1]);
+            const int tl = tile_of(t + 1);
+            issue_v<D, NT>(ptile + (size_t)tl * G::ELEMS, pbias + (size_t)tl * kTK, src_v, vbuf[P ^ 1], lbias[P ^ 1]);
         }
-        const __bf16* Kl = lkv[s];
-        const __bf16* Vl = lkv[s] + kTK * D;
+        f32x16 sn[2];  // scores of tile t+1 (not used after the last tile)
+        scores<D>(kbuf[P ^ 1], qreg, i32, h, sn);
 
-        // ---- S^T = K_tile Q^T : two chunks of 32 keys x 32 queries
-        f32x16 st[2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            f32x16 a16;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) a16[r] = 0.f;
-            const int m = c * 32 + i32;
-#pragma unroll
-            for (int ds = 0; ds < D / 16; ++ds) {
-                const int pc = (2 * ds + h) ^ swz<G::CK>(m);
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kl + (m * G::CK + pc) * 8);
-                a16 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], a16, 0, 0, 0);
-            }
-            st[c] = a16;
-        }
-
-        // ---- probabilities.  Register 4g+j of chunk c holds key c*32 + 16(g/2) + 8h + 4(g%2) + j.
-        // A plain tile (64 real keys, additive term 0) takes the short path: max over the raw
-        // scores and p = exp2(s * c - m) in one fma per key.  Other tiles (padded, compressed) add
-        // their bias row and, for compressed tiles, mask this query block's selected blocks.
-        const bool plain = tl_cur < Tv ? (tl_cur + 1) * kTK <= Nv
-                                       : (tl_cur < Tv + Ts && Nv + (tl_cur - Tv + 1) * kTK <= N);
+        // ---- probabilities of tile t.  Register 4g+j of chunk c holds key c*32 + 16(g/2) + 8h + 4(g%2) + j.
+        const int cbase = (t - first_cmp) * kTK;  // first pseudo-key of a compressed tile
         float mx = -INFINITY;
-        if (plain) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[c][r]);
-            mx *= c_log2;
-        } else {
-            const bool compressed = t >= first_cmp;
-            const int cbase = (t - first_cmp) * kTK;  // first pseudo-key of a compressed tile
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int key = c * 32 + 16 * (g >> 1) + 8 * h + 4 * (g & 1);
-                    f32x4 bb = *reinterpret_cast<const f32x4*>(lbias[s] + key);
-                    // this query block's selected blocks leave the compressed branch: the mask goes
-                    // into the additive term with selects (no divergent writes to the scores)
-                    const uint32_t selw =
-                        compressed ? sel_bits[(cbase + key) >> 5] >> ((cbase + key) & 31) : 0u;
+            for (int g = 0; g < 4; ++g) {
+                const int key = c * 32 + 16 * (g >> 1) + 8 * h + 4 * (g & 1);
+                f32x4 bb = *reinterpret_cast<const f32x4*>(lbias[P] + key);
+                if constexpr (MASKED) {
+                    const uint32_t selw = sel_bits[(cbase + key) >> 5] >> ((cbase + key) & 31);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) bb[j] = ((selw >> j) & 1u) ? -INFINITY : bb[j];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        st[c][4 * g + j] = fmaf(st[c][4 * g + j], c_log2, bb[j]);
-                        mx = fmaxf(mx, st[c][4 * g + j]);
-                    }
                 }
-        }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    st[c][4 * g + j] = fmaf(st[c][4 * g + j], c_log2, bb[j]);
+                    mx = fmaxf(mx, st[c][4 * g + j]);
+                }
+            }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const bool raise = mx > m_run + kRescaleSlack;
         if (__ballot(raise)) {
@@ -250,45 +269,33 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
             m_run = m_new;
         }
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        if (plain) {
-            const float nm = -m_use;
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) st[c][r] = __builtin_amdgcn_exp2f(fmaf(st[c][r], c_log2, nm));
-        } else {
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) st[c][r] = __builtin_amdgcn_exp2f(st[c][r] - m_use);
-        }
         // P in bf16, 16 keys per PV step: lane (i32, h) supplies keys 16kt + 8h + e (e = 0..7).
         // The normaliser sums the same bf16 values the PV product uses.
-        bf16x8 pk[kTK / 16];
+        const __bf16* Vl = vbuf[P];
 #pragma unroll
-        for (int kt = 0; kt < kTK / 16; ++kt)
+        for (int kt = 0; kt < kTK / 16; ++kt) {
+            bf16x8 pk;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pk[kt][e] = (__bf16)st[kt >> 1][8 * (kt & 1) + e];
-#pragma unroll
-        for (int kt = 0; kt < kTK / 16; ++kt)
+            for (int e = 0; e < 8; ++e) pk[e] = (__bf16)__builtin_amdgcn_exp2f(st[kt >> 1][8 * (kt & 1) + e] - m_use);
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                const bf16x2 pr = {pk[kt][e], pk[kt][e + 1]};
+                const bf16x2 pr = {pk[e], pk[e + 1]};
                 l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
             }
-
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int kt = 0; kt < kTK / 16; ++kt)
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
                 const int dr = dt * 32 + i32;
                 const int pc = (2 * kt + h) ^ swz<G::V_CPR>(dr);
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vl + (dr * G::V_CPR + pc) * 8);
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kt], acc[dt], 0, 0, 0);
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk, acc[dt], 0, 0, 0);
             }
-        tl_cur = tl_next;
-    }
+        }
+        st[0] = sn[0];
+        st[1] = sn[1];
+    };
+    int t = 0;
+    for (; t < first_cmp; ++t) step(t, std::integral_constant<bool, false>{});
+    for (; t < ntiles; ++t) step(t, std::integral_constant<bool, true>{});
 
     // ---- epilogue: lane (i32, h) holds query row w*32 + i32, dims dt*32 + 8*g + 4*h + (0..3)
     const float l_tot = l_run + __shfl_xor(l_run, 32);
