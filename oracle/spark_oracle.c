@@ -466,9 +466,11 @@ void orc_forward(const orc_params *p, const float *Q, const float *K, const floa
  * hierarchical partitioner keeps splitting groups until every leaf holds the block size, in
  * O(N log N).  Readings (the pages give no formulas):
  *   R1  Sigma = K^T K / N_v over the video keys of the head (uncentred second moment), summed
- *       exactly: each product k_ia*k_ib (exact in binary64) is scaled by 2^e, rounded to the
- *       nearest integer (ties to even) and added in int64; e = 62 - ceil(log2 N_v) - 2*E where
- *       max|k| < 2^E, so no sum can overflow.  Sigma_ab = ((double)sum * 2^-e) / N_v.
+ *       exactly in fixed point: with max|k| < 2^E (E from frexp) and s = 21 - E, every key entry
+ *       becomes the integer k^ = rint(k * 2^s) (ties to even; |k^| <= 2^21, and k^ = k * 2^s exactly
+ *       for entries within 13 binades of the maximum when the keys are bf16), the products
+ *       k^_ia * k^_ib are added in int64 (no overflow for N_v <= 2^20), and
+ *       Sigma_ab = ((double)sum * 2^(-2s)) / N_v.
  *   R2  t(i) = Sigma q_i with t_a = fma(Sigma_ab, q_ib, t_a) for b = 0..d-1 from 0;
  *       r_i = fma(q_ia, t_a(i), r_i) for a = 0..d-1 from 0; n_i = sqrt(r_i) if r_i > 0 else 0.
  *   R3  Groups carry a leaf count c: one group of all N_v video tokens with c = M to start.
@@ -484,13 +486,6 @@ void orc_forward(const orc_params *p, const float *Q, const float *K, const floa
  * with -ffp-contract=off), so the result is fixed bit for bit.
  * ---------------------------------------------------------------------------------------- */
 
-static int ceil_log2(int n)
-{
-    int L = 0;
-    while ((1LL << L) < (long long)n) ++L;
-    return L;
-}
-
 /* R1 for one head; Kh points at its video rows. */
 static void reblock_sigma(const float *Kh, int Nv, int d, double *Sigma)
 {
@@ -502,15 +497,16 @@ static void reblock_sigma(const float *Kh, int Nv, int d, double *Sigma)
     if (mx == 0.0) { memset(Sigma, 0, sizeof(double) * (size_t)d * d); return; }
     int E;
     frexp(mx, &E); /* mx = f * 2^E with f in [0.5, 1), so mx < 2^E */
-    const int e = 62 - ceil_log2(Nv) - 2 * E;
+    const int sh = 21 - E;
     for (int a = 0; a < d; ++a)
         for (int c = 0; c < d; ++c) {
             int64_t acc = 0;
             for (int i = 0; i < Nv; ++i) {
-                const double prod = (double)Kh[(size_t)i * d + a] * (double)Kh[(size_t)i * d + c];
-                acc += (int64_t)rint(ldexp(prod, e));
+                const int64_t ka = (int64_t)rint(ldexp((double)Kh[(size_t)i * d + a], sh));
+                const int64_t kc = (int64_t)rint(ldexp((double)Kh[(size_t)i * d + c], sh));
+                acc += ka * kc;
             }
-            Sigma[(size_t)a * d + c] = ldexp((double)acc, -e) / (double)Nv;
+            Sigma[(size_t)a * d + c] = ldexp((double)acc, -2 * sh) / (double)Nv;
         }
 }
 

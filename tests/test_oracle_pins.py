@@ -250,13 +250,23 @@ def test_reblock_invariants(orc):
             leaf = pr[L * b:(L + 1) * b]
             assert (np.diff(leaf) > 0).all()  # ascending inside every leaf
         assert len(pr[(M - 1) * b:]) == nv - (M - 1) * b
-    # metric: Sigma = K^T K / N_v, n_i = |K q_i| / sqrt(N_v)
+    # metric: Sigma = K^T K / N_v up to the fixed-point grid of the keys (entries rounded to
+    # 2^(E-21), max|k| < 2^E): |error| <= 2^(2E-21); n_i = sqrt(q_i^T Sigma q_i)
     Sg, nrm = orc.reblock_metric(p, Q, K)
     kv = K[0, 0, :nv].astype(np.float64)
     qv = Q[0, 0, :nv].astype(np.float64)
     ref = kv.T @ kv / nv
-    assert np.abs(Sg[0, 0] - ref).max() <= 1e-13 * np.abs(ref).max()
-    assert np.allclose(nrm[0, 0], np.linalg.norm(qv @ kv.T, axis=1) / math.sqrt(nv), rtol=1e-12)
+    E = math.frexp(np.abs(kv).max())[1]
+    assert np.abs(Sg[0, 0] - ref).max() <= 2.0 ** (2 * E - 21)
+    assert np.allclose(nrm[0, 0], np.sqrt(np.einsum("ia,ab,ib->i", qv, Sg[0, 0], qv)), rtol=1e-12)
+    # keys on the grid (|k| >= 2^(E-13) or 0, bf16): the fixed-point sum is the exact K^T K / N_v
+    K4 = K.copy()
+    K4[np.abs(K4) < 2.0 ** (E - 13)] = 0.0
+    Sg4, nrm4 = orc.reblock_metric(p, Q, K4)
+    kv4 = K4[0, 0, :nv].astype(np.float64)
+    ref4 = kv4.T @ kv4 / nv
+    assert np.abs(Sg4[0, 0] - ref4).max() <= 1e-13 * np.abs(ref4).max()
+    assert np.allclose(nrm4[0, 0], np.linalg.norm(qv @ kv4.T, axis=1) / math.sqrt(nv), rtol=1e-12)
     # power-of-two scaling of query rows and of all keys leaves the partition unchanged
     Q2, K2 = Q.copy(), K.copy()
     Q2[0, 0, ::7] *= 8.0
