@@ -1,0 +1,134 @@
+"""GPU parity of the Spark-Reblock partition and of the forward on the partitioned layout.
+
+The permutation must equal the oracle's bit for bit (every decision is taken in binary64 with one
+fixed operation order on both sides).  The forward with the partition is held to the attention
+tolerances, with the oracle attending through the GPU's validated route.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_score_amd as sa
+import workloads as W
+from parity import FWD_MAX_ABS, FWD_REL_L2, check_selection, max_abs, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    sa.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def note(msg):
+    print(f"\n[gpu-case] {msg}", flush=True)
+
+
+def dev(x, dt):
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda", torch.bfloat16 if dt == "bf16" else torch.float32)
+
+
+# (name, B, H, n_video, n_sink, d, block, dtype)
+CASES = [
+    ("bf16-d128-b128", 1, 3, 11 * 128 + 37, 5, 128, 128, "bf16"),
+    ("bf16-d64-b64", 2, 2, 37 * 64 + 1, 0, 64, 64, "bf16"),
+    ("bf16-d128-b64", 1, 2, 16 * 64, 64, 128, 64, "bf16"),
+    ("fp32-d64-b128", 1, 2, 9 * 128 + 100, 7, 64, 128, "fp32"),
+    ("fp32-d128-b64", 1, 1, 25 * 64 + 63, 3, 128, 64, "fp32"),
+    ("one-block", 1, 2, 90, 4, 128, 128, "bf16"),
+    ("two-blocks", 1, 2, 129, 1, 128, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_reblock_bit_exact(orc, case):
+    name, B, H, nv, ns, d, b, dt = case
+    Q, K, V = W.gaussian_qkv(B, H, nv, ns, d, seed=nv + d, dtype=dt)
+    note(f"reblock {name}")
+    perm = sa.reblock(dev(Q, dt), dev(K, dt), ns, b)
+    torch.cuda.synchronize()
+    ref = orc.reblock(orc.params(Q, ns, b), Q, K)
+    got = perm.cpu().numpy()
+    assert (got == ref).all(), f"{(got != ref).sum()} positions differ"
+
+
+def test_reblock_structured_input_bit_exact(orc):
+    wl = W.WORKLOADS["tiny"].with_(dtype="bf16", d=64)
+    Q, K, V = W.make_qkv(wl)
+    note("reblock on the tiny positional workload")
+    perm = sa.reblock(dev(Q, "bf16"), dev(K, "bf16"), 0, 64)
+    torch.cuda.synchronize()
+    assert (perm.cpu().numpy() == orc.reblock(orc.params(Q, 0, 64), Q, K)).all()
+
+
+def test_reblock_degenerate_rows(orc):
+    """Zero query rows (norm 0: every cosine 0, ties decided by index) and a zero key set."""
+    Q, K, V = W.gaussian_qkv(1, 2, 6 * 64 + 10, 2, 64, seed=5, dtype="bf16")
+    Q[0, 0, ::3] = 0.0
+    K[0, 1, :] = 0.0
+    note("reblock with zero rows")
+    perm = sa.reblock(dev(Q, "bf16"), dev(K, "bf16"), 2, 64)
+    torch.cuda.synchronize()
+    assert (perm.cpu().numpy() == orc.reblock(orc.params(Q, 2, 64), Q, K)).all()
+
+
+def test_reblock_is_deterministic():
+    Q, K, V = W.gaussian_qkv(1, 4, 20 * 128 + 3, 8, 128, seed=8, dtype="bf16")
+    Qd, Kd = dev(Q, "bf16"), dev(K, "bf16")
+    note("reblock twice")
+    a = sa.reblock(Qd, Kd, 8, 128)
+    b = sa.reblock(Qd, Kd, 8, 128)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_reblock_720p_bit_exact_and_forward(orc):
+    """The 720p-like latent (75,600 video + 512 sink tokens, 24 heads) in full on the GPU; the oracle
+    checks the partition of 3 heads bit for bit, and the forward on sampled query blocks."""
+    wl = W.WORKLOADS["reblock720p"]
+    Q, K, V = W.make_qkv(wl)
+    note("reblock 720p")
+    Qd, Kd, Vd = dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16")
+    perm = sa.reblock(Qd, Kd, wl.n_sink, wl.block)
+    O, lse, idx = sa.forward(Qd, Kd, Vd, wl.n_sink, wl.block, 0.1, perm=perm, return_lse=True, return_idx=True)
+    torch.cuda.synchronize()
+    heads = [0, 11, 23]
+    Qs, Ks, Vs = (np.ascontiguousarray(x[:, heads]) for x in (Q, K, V))
+    p = orc.params(Qs, wl.n_sink, wl.block, 0.1, 1)
+    ref = orc.reblock(p, Qs, Ks)
+    gperm = perm.cpu().numpy()[:, heads]
+    assert (gperm == ref).all(), f"{(gperm != ref).sum()} positions differ"
+    # forward: the route is checked in the partitioned layout; sampled blocks are attended by the oracle
+    nv = wl.n_video
+
+    def permuted(X):
+        Y = X.copy()
+        for h in range(len(heads)):
+            Y[0, h, :nv] = X[0, h][ref[0, h]]
+        return Y
+
+    Qp, Kp, Vp = permuted(Qs), permuted(Ks), permuted(Vs)
+    pooled = orc.pool(p, Qp, Kp, Vp)
+    S = orc.scores(p, pooled["q_mean"], pooled["k_mean"])
+    gidx = idx.cpu().numpy()[:, heads]
+    bad, _ = check_selection(gidx, S)
+    assert bad == 0
+    M = gidx.shape[2]
+    rng = np.random.default_rng(3)
+    qb = np.array([(h, I) for h in range(len(heads)) for I in rng.choice(M, 4, replace=False)] + [(0, M - 1)])
+    Os, ls = orc.attend_blocks(p, Qp, Kp, Vp, pooled, gidx, qb)
+    Og, lg = O.float().cpu().numpy()[:, heads], lse.cpu().numpy()[:, heads]
+    g_rows, r_rows, gl, rl = [], [], [], []
+    for n, (h, I) in enumerate(qb):
+        lo, hi = I * wl.block, min(nv, (I + 1) * wl.block)
+        rows = ref[0, h, lo:hi]  # original token rows of this partitioned block
+        g_rows.append(Og[0, h, rows]); r_rows.append(Os[n, :hi - lo])
+        gl.append(lg[0, h, rows]); rl.append(ls[n, :hi - lo])
+    g_rows, r_rows = np.concatenate(g_rows), np.concatenate(r_rows)
+    e2, ea = rel_l2(g_rows, r_rows), max_abs(g_rows, r_rows)
+    el = max_abs(np.concatenate(gl), np.concatenate(rl))
+    print(f"reblocked forward: rel-L2 {e2:.3e} max-abs {ea:.3e} lse {el:.3e}")
+    assert e2 <= FWD_REL_L2 and ea <= FWD_MAX_ABS and el <= FWD_MAX_ABS
