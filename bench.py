@@ -169,24 +169,43 @@ def main():
     sel_ws = torch.empty(sa.workspace_size(p, 3), device="cuda", dtype=torch.uint8)
     packed = torch.empty(sa.workspace_size(p, 4), device="cuda", dtype=torch.uint8)
     stream = torch.cuda.current_stream()
+    perm = None
+    if wl.reblock:  # adaptive blocks: partition, gather, attend, scatter back (q_reuse_k)
+        perm = torch.empty(B, H, wl.n_video, device="cuda", dtype=torch.int32)
+        rb_ws = torch.empty(sa.workspace_size(p, 1), device="cuda", dtype=torch.uint8)
+        Qp, Kp, Vp = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    else:
+        Qp, Kp, Vp = Q, K, V
+
+    stage_names = (["reblock", "gather"] if wl.reblock else []) + ["pool", "select", "pack", "attend"]
 
     def step(ev=None):
-        sa.spark_attn_pool(p, Q, K, V, pooled["q_mean"], pooled["k_mean"], pooled["k_sum"], pooled["v_sum"],
+        k = 1
+        if wl.reblock:
+            sa.spark_attn_reblock(p, Q, K, perm, rb_ws, stream)
+            if ev: ev[k].record(stream)
+            k += 1
+            for X, Y in ((Q, Qp), (K, Kp), (V, Vp)):
+                sa.spark_attn_gather_rows(p, X, perm, Y, stream)
+            if ev: ev[k].record(stream)
+            k += 1
+        sa.spark_attn_pool(p, Qp, Kp, Vp, pooled["q_mean"], pooled["k_mean"], pooled["k_sum"], pooled["v_sum"],
                            pooled["bias"], pooled["anchor"], stream)
-        if ev: ev[1].record(stream)
+        if ev: ev[k].record(stream)
         sa.spark_attn_select(p, pooled["q_mean"], pooled["k_mean"], idx, None, sel_ws, stream)
-        if ev: ev[2].record(stream)
-        sa.spark_attn_pack(p, K, V, pooled["k_sum"], pooled["v_sum"], pooled["bias"], packed, stream)
-        if ev: ev[3].record(stream)
-        sa.spark_attn_attend(p, Q, packed, idx, None, O, lse, stream)
-        if ev: ev[4].record(stream)
+        if ev: ev[k + 1].record(stream)
+        sa.spark_attn_pack(p, Kp, Vp, pooled["k_sum"], pooled["v_sum"], pooled["bias"], packed, stream)
+        if ev: ev[k + 2].record(stream)
+        sa.spark_attn_attend(p, Qp, packed, idx, perm, O, lse, stream)
+        if ev: ev[k + 3].record(stream)
 
     log(f"M={M} K={Kk}; warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    ns = len(stage_names)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -195,21 +214,21 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    st = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in events])
-    ms_pool, ms_sel, ms_pack, ms_attn = (float(x) for x in st.mean(axis=0))
-    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (pool {ms_pool:.3f}, select {ms_sel:.3f}, "
-        f"pack {ms_pack:.3f}, attend {ms_attn:.3f})")
+    st = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(ns)] for e in events]).mean(axis=0)
+    stage_ms = {n: float(x) for n, x in zip(stage_names, st)}
+    ms_pool, ms_sel, ms_pack, ms_attn = (stage_ms[n] for n in ("pool", "select", "pack", "attend"))
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (" + ", ".join(f"{n} {v:.3f}" for n, v in stage_ms.items()) + ")")
 
     # cross-check: the single-call entry point over the same input
     ms_forward_call, same_out, ws, O2 = None, None, None, None
     if not args.no_forward_check:
-        ws = torch.empty(sa.workspace_size(p, 0), device="cuda", dtype=torch.uint8)
+        ws = torch.empty(sa.workspace_size(p, 2 if wl.reblock else 0), device="cuda", dtype=torch.uint8)
         O2 = torch.empty_like(Q)
-        sa.spark_attn_forward(p, Q, K, V, None, O2, None, None, ws, stream)
+        sa.spark_attn_forward(p, Q, K, V, perm, O2, None, None, ws, stream)
         fe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         fe[0].record(stream)
         for _ in range(3):
-            sa.spark_attn_forward(p, Q, K, V, None, O2, None, None, ws, stream)
+            sa.spark_attn_forward(p, Q, K, V, perm, O2, None, None, ws, stream)
         fe[1].record(stream)
         torch.cuda.synchronize()
         ms_forward_call = round(fe[0].elapsed_time(fe[1]) / 3, 4)
@@ -247,8 +266,8 @@ def main():
             "N_sink": wl.n_sink, "d": d, "block": wl.block, "topk_ratio": ratio, "M": M, "K": Kk,
             "compressed_branch": "anchor-weighted summary + log-mass bias", "parallelism": "none (1 GPU)",
         },
-        "stages_ms": {"pool": round(ms_pool, 4), "select": round(ms_sel, 4), "pack": round(ms_pack, 4),
-                      "attend": round(ms_attn, 4), "spark_attn_forward_call": ms_forward_call},
+        "stages_ms": dict({n: round(v, 4) for n, v in stage_ms.items()},
+                          spark_attn_forward_call=ms_forward_call),
         "forward_call_output_identical": same_out,
         "flops": {"F_sel": F_sel, "F_sink": F_sink, "F_comp": F_comp, "F_sinkq": F_sinkq},
         "roofline": {
@@ -264,7 +283,15 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        del Q, K, V, O, O2, ws, sel_ws, packed
+        del Q, K, V, O, O2, ws, sel_ws, packed, Qp, Kp, Vp
+        if wl.reblock:
+            perm_h = perm.cpu().numpy()
+            del perm, rb_ws
+            # the oracle runs on the partitioned layout the route refers to
+            for X in (Qh, Kh, Vh):
+                for b_ in range(B):
+                    for h_ in range(H):
+                        X[b_, h_, :wl.n_video] = X[b_, h_][perm_h[b_, h_]]
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(wl, ratio, Qh, Kh, Vh, gidx, F_sel, args.cpu_sample_blocks)
     print(json.dumps(out), flush=True)
