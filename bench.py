@@ -49,6 +49,24 @@ def algorithmic_flops(idx, wl, ratio_K):
     return F_sel, F_sink, F_comp, F_sinkq
 
 
+def committed_traffic(workload):
+    """HBM bytes per attention launch from the committed counter summary, or None when the kernel
+    source has changed since the counters were taken (or no summary exists for the workload)."""
+    import hashlib
+    import re
+
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}.md")
+    src = os.path.join(ROOT, "block_sparse_attention_score_amd", "csrc", "attn_fwd.hip")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"attn_fwd_kernel_source_sha256_16: ([0-9a-f]+)", text)
+    t = re.search(r"attn_fwd_kernel_traffic_bytes_per_launch: ([0-9.]+)", text)
+    if not h or not t or hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != h.group(1):
+        return None
+    return float(t.group(1))
+
+
 def route_check(idx, S, rel=1e-4, floor=1e-6):
     """Rows whose GPU route violates the near-tie rule against oracle scores S (vectorised)."""
     import numpy as np
@@ -273,7 +291,8 @@ def main():
         "roofline": {
             "kernel": "attn_fwd_kernel (exact + sink + compressed branches, sink queries)",
             "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": committed_traffic(wl.name), "traffic_unit": "bytes per launch (FETCH+WRITE, scaled)",
             "exact_branch_frac": round((F_sel + F_sink) / (ms_attn * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         },
         "pool_roofline": {"bound": "hbm", "achieved": round(pool_bytes / (ms_pool * 1e-3) / 1e9, 1),
