@@ -69,61 +69,88 @@ __device__ __forceinline__ int v_src_chunk(int q) {
     return G::K_CHUNKS + dr * G::V_CPR + (pc ^ swz<G::V_CPR>(dr));
 }
 
-// K part of a packed tile HBM -> LDS (every lane moves K_CHUNKS / NT chunks).
-template <int D, int NT>
-__device__ __forceinline__ void issue_k(const __bf16* __restrict__ gtile, const int (&src)[TileGeom<D>::K_CHUNKS / NT],
-                                        __bf16* lk) {
-    const int w = threadIdx.x >> 6;
-#pragma unroll
-    for (int i = 0; i < TileGeom<D>::K_CHUNKS / NT; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(gtile + (size_t)src[i] * 8),
-                                         (lds_ptr)(lk + (size_t)(i * NT + w * 64) * 8), 16, 0, 0);
+// HBM -> LDS copy of one half (K rows, or V^T rows) of a packed tile with buffer_load ... lds: every
+// lane moves NCH 16-byte chunks.  Chunk i of a lane is LDS chunk i*NT + tid, whose source chunk is
+// src(i*NT + tid).  Where src(i*NT + tid) = src(tid) + i*NT (every shape but d = 128 with 64-row
+// query blocks) a lane keeps one 32-bit byte offset and the chunk term goes into the scalar offset;
+// otherwise one offset per chunk.  The LDS destination of a wave's 64 chunks is contiguous (lane l
+// writes base + 16 l), the base is a scalar (M0).
+template <int D, int NT> struct DmaPlan {
+    static constexpr int NCH = TileGeom<D>::K_CHUNKS / NT;
+    static constexpr bool kAffine = (NT / TileGeom<D>::CK) % 16 == 0;
+    static constexpr int NOFF = kAffine ? 1 : NCH;
+};
+
+// Buffer resource of a byte range (CDNA3/CDNA4 ISA, buffer resource descriptor: base, zero stride,
+// size in bytes for the range check, word 3 as for untyped 32-bit data).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// V^T part of a packed tile and its bias row HBM -> LDS.
-template <int D, int NT>
-__device__ __forceinline__ void issue_v(const __bf16* __restrict__ gtile, const float* __restrict__ gbias,
-                                        const int (&src)[TileGeom<D>::K_CHUNKS / NT], __bf16* lv, float* lb) {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+template <int D, int NT, typename RS>
+__device__ __forceinline__ void issue_half(RS rs, uint32_t tile_byte,
+                                           const uint32_t (&off)[DmaPlan<D, NT>::NOFF], __bf16* l, int wv) {
+    using PL = DmaPlan<D, NT>;
 #pragma unroll
-    for (int i = 0; i < TileGeom<D>::K_CHUNKS / NT; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(gtile + (size_t)src[i] * 8),
-                                         (lds_ptr)(lv + (size_t)(i * NT + w * 64) * 8), 16, 0, 0);
-    if (w == 0) __builtin_amdgcn_global_load_lds((const void*)(gbias + lane), (lds_ptr)lb, 4, 0, 0);
+    for (int i = 0; i < PL::NCH; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(l + (size_t)(i * NT + wv * 64) * 8), 16,
+                                                 PL::kAffine ? off[0] : off[i],
+                                                 tile_byte + (PL::kAffine ? (uint32_t)(i * NT * 16) : 0u), 0, 0);
 }
 
-// S^T = K_tile Q^T for two chunks of 32 keys x this wave's 32 queries.
+// A zero the compiler cannot see through, taken once per pipeline step.  LDS addresses are formed
+// as stage base + (lane offset ^ zero): the lane offsets are computed once, the per-stage sums are
+// not hoisted out of the loop (which would hold one set of address registers per stage), and the
+// stage base, a constant, folds into the instruction's offset field.
+__device__ __forceinline__ int opaque_zero() {
+    int z;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+    return z;
+}
+
+// S^T = K_tile Q^T for two chunks of 32 keys x this wave's 32 queries.  koff[ds]: element offset of
+// lane (i32, h)'s A operand in row i32 of the tile for k step ds (row 32 + i32 is 32*D further).
 template <int D>
-__device__ __forceinline__ void scores(const __bf16* Kl, const bf16x8 (&qreg)[D / 16], int i32, int h, f32x16 (&st)[2]) {
-    using G = TileGeom<D>;
+__device__ __forceinline__ void scores(const __bf16* Kl, const int (&koff)[D / 16], int z, const bf16x8 (&qreg)[D / 16],
+                                       f32x16 (&st)[2]) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         f32x16 a16;
 #pragma unroll
         for (int r = 0; r < 16; ++r) a16[r] = 0.f;
-        const int m = c * 32 + i32;
 #pragma unroll
         for (int ds = 0; ds < D / 16; ++ds) {
-            const int pc = (2 * ds + h) ^ swz<G::CK>(m);
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kl + (m * G::CK + pc) * 8);
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kl + c * 32 * D + (koff[ds] ^ z));
             a16 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], a16, 0, 0, 0);
         }
         st[c] = a16;
     }
 }
 
+template <int V> using IC = std::integral_constant<int, V>;
+
 template <typename T, int D, int BLK>
 __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     const T* __restrict__ Q, const __bf16* __restrict__ packed, const float* __restrict__ bias2,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ perm, T* __restrict__ O, float* __restrict__ lse,
     int N, int Nv, int M, int Ksel, int SQ, int BH, int C, int Tv, int Ts, int Tc, float c_log2) {
+// The body uses buffer resources, a device-only type: the host pass sees an empty kernel.
+#if defined(__HIP_DEVICE_COMPILE__)
     using G = TileGeom<D>;
     constexpr int NT = BLK * 2;  // BLK / 32 waves
-    constexpr int NCH = G::K_CHUNKS / NT;  // DMA chunks per lane for one K (or V^T) part
-    __shared__ __attribute__((aligned(16))) __bf16 kbuf[2][kTK * D];
-    __shared__ __attribute__((aligned(16))) __bf16 vbuf[2][kTK * D];
-    __shared__ __attribute__((aligned(16))) float lbias[2][kTK];
+    // Each pipeline stage has LDS arrays of its own, always named statically (the stage parity is a
+    // template constant), so the compiler can see that the loads streaming into one stage do not
+    // write what the other stage reads, and does not wait for them before reading.
+    __shared__ __attribute__((aligned(16))) __bf16 kbuf0[kTK * D];
+    __shared__ __attribute__((aligned(16))) __bf16 kbuf1[kTK * D];
+    __shared__ __attribute__((aligned(16))) __bf16 vbuf0[kTK * D];
+    __shared__ __attribute__((aligned(16))) __bf16 vbuf1[kTK * D];
+    __shared__ __attribute__((aligned(16))) float lbias0[kTK];
+    __shared__ __attribute__((aligned(16))) float lbias1[kTK];
     __shared__ uint32_t sel_bits[kMaxBlocks / 32 + 2];  // + the words a padded last tile can touch
+    auto kbuf = [&](auto s) __attribute__((always_inline)) -> __bf16* { if constexpr (decltype(s)::value == 0) return kbuf0; else return kbuf1; };
+    auto vbuf = [&](auto s) __attribute__((always_inline)) -> __bf16* { if constexpr (decltype(s)::value == 0) return vbuf0; else return vbuf1; };
+    auto lbias = [&](auto s) __attribute__((always_inline)) -> float* { if constexpr (decltype(s)::value == 0) return lbias0; else return lbias1; };
 
     // --- which query tile.  Sink-query tiles (dense, the longest) come first in the grid.  Video
     // query blocks are remapped so that each of the 8 XCDs (workgroup id w runs on XCD w % 8) walks
@@ -152,6 +179,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
             ntiles = Ksel * (BLK / kTK) + Ts + Tc;
         }
     }
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int i32 = lane & 31, h = lane >> 5;
     const int Tall = Tv + Ts + Tc;
     const __bf16* ptile = packed + (size_t)bh * Tall * G::ELEMS;
     const float* pbias = bias2 + (size_t)bh * Tall * kTK;
@@ -160,39 +189,61 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     const int n_exact = dense ? 0 : Ksel * nsub;
     const int first_cmp = dense ? ntiles : n_exact + Ts;  // first compressed tile in the list
 
-    // packed tile of list entry t: selected blocks, then sink tiles, then compressed tiles
-    auto tile_of = [&](int t) -> int {
+    // Selected block ids are read 64 at a time into a register (lane l holds entry base + l) and
+    // taken out with readlane, so the tile loop issues no global loads besides the tile stream.
+    int win_base = 0, selw = 0;
+    if (!dense) selw = lane < Ksel ? sel[lane] : 0;
+    // packed tile of list entry t (called with increasing t): selected blocks, sinks, compressed
+    auto tile_of = [&](int t) __attribute__((always_inline)) -> int {
         if (dense) return t;
         if (t >= n_exact) return Tv + (t - n_exact);
-        return sel[t / nsub] * nsub + t % nsub;
+        const int k = t / nsub;
+        if (k >= win_base + 64) {
+            win_base = k & ~63;
+            selw = win_base + lane < Ksel ? sel[win_base + lane] : 0;
+        }
+        return __builtin_amdgcn_readlane(selw, k - win_base) * nsub + t % nsub;
     };
 
     if (!dense) {
-        for (int w = threadIdx.x; w < (M + 63) / 32 + 1; w += NT) sel_bits[w] = 0u;
+        for (int j = threadIdx.x; j < (M + 63) / 32 + 1; j += NT) sel_bits[j] = 0u;
         __syncthreads();
         for (int k = threadIdx.x; k < Ksel; k += NT) {
             const int J = sel[k];
             atomicOr(&sel_bits[J >> 5], 1u << (J & 31));
         }
     }
-    int src_k[NCH], src_v[NCH];
+    using PL = DmaPlan<D, NT>;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint32_t off_k[PL::NOFF], off_v[PL::NOFF];  // byte offsets inside a packed tile
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        src_k[i] = k_src_chunk<D>(i * NT + threadIdx.x);
-        src_v[i] = v_src_chunk<D>(i * NT + threadIdx.x);
+    for (int i = 0; i < PL::NOFF; ++i) {
+        off_k[i] = (uint32_t)k_src_chunk<D>(i * NT + threadIdx.x) * 16u;
+        off_v[i] = (uint32_t)v_src_chunk<D>(i * NT + threadIdx.x) * 16u;
     }
+    const __amdgpu_buffer_rsrc_t rs_tiles = byte_rsrc(ptile, (uint32_t)Tall * (G::ELEMS * 2));
+    const __amdgpu_buffer_rsrc_t rs_bias = byte_rsrc(pbias, (uint32_t)Tall * (kTK * 4));
+    // K half, V^T half plus the bias row, of packed tile tl into stage s
+    auto load_k = [&](int tl, auto s) __attribute__((always_inline)) {
+        issue_half<D, NT>(rs_tiles, (uint32_t)tl * (G::ELEMS * 2), off_k, kbuf(s), wv);
+    };
+    auto load_v = [&](int tl, auto s) __attribute__((always_inline)) {
+        issue_half<D, NT>(rs_tiles, (uint32_t)tl * (G::ELEMS * 2), off_v, vbuf(s), wv);
+        if (wv == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_bias, (lds_ptr)lbias(s), 4, (uint32_t)lane * 4u,
+                                                     (uint32_t)tl * (kTK * 4), 0, 0);
+    };
     // Pipeline: the K stream runs one tile ahead of the V stream.  Iteration t computes the scores of
     // tile t+1 (K(t+1) resident) while it turns the scores of tile t into probabilities and applies
-    // V(t); K(t+2) and V(t+1) stream in meanwhile.  K(j) and V(j) live in buffer j % 2.
+    // V(t); K(t+2) and V(t+1) stream in meanwhile.  K(j) and V(j) live in stage j % 2.
+    int tl_v;  // packed tile whose V part streams in next
     {
         const int tl0 = tile_of(0);
-        issue_k<D, NT>(ptile + (size_t)tl0 * G::ELEMS, src_k, kbuf[0]);
-        if (ntiles > 1) issue_k<D, NT>(ptile + (size_t)tile_of(1) * G::ELEMS, src_k, kbuf[1]);
-        issue_v<D, NT>(ptile + (size_t)tl0 * G::ELEMS, pbias + (size_t)tl0 * kTK, src_v, vbuf[0], lbias[0]);
+        load_k(tl0, IC<0>{});
+        tl_v = ntiles > 1 ? tile_of(1) : 0;
+        if (ntiles > 1) load_k(tl_v, IC<1>{});
+        load_v(tl0, IC<0>{});
     }
-
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int i32 = lane & 31, h = lane >> 5;
 
     // Q rows of this wave as the B operand of S^T = K Q^T: lane (i32, h) holds row w*32 + i32,
     // dims ds*16 + 8h .. +8 for each 16-wide k step ds.
@@ -208,6 +259,13 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
         }
     }
 
+    // LDS element offsets of this lane's MFMA operands: K rows (S^T) and V^T rows (O^T), XOR-swizzled.
+    int koff[D / 16], voff[kTK / 16];
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) koff[ds] = (i32 * G::CK + ((2 * ds + h) ^ swz<G::CK>(i32))) * 8;
+#pragma unroll
+    for (int kt = 0; kt < kTK / 16; ++kt) voff[kt] = (i32 * G::V_CPR + ((2 * kt + h) ^ swz<G::V_CPR>(i32))) * 8;
+
     f32x16 acc[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -219,36 +277,38 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // K(0), K(1), V(0) and the route bits are in LDS
     f32x16 st[2];
-    scores<D>(kbuf[0], qreg, i32, h, st);
+    scores<D>(kbuf(IC<0>{}), koff, 0, qreg, st);
 
-    // One pipeline step.  MASKED: tile t is a compressed tile, whose pseudo-keys of this query
-    // block's selected blocks are excluded (the mask goes into the additive term with selects).
-    auto step = [&](int t, auto masked) {
+    // One pipeline step on stage parity P = t % 2.  MASKED: tile t is a compressed tile, whose
+    // pseudo-keys of this query block's selected blocks are excluded (the mask goes into the additive
+    // term with selects).
+    auto step = [&](int t, auto masked, auto par) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked)::value;
-        const int P = t & 1;
+        constexpr int P = decltype(par)::value;
         __builtin_amdgcn_s_waitcnt(0);  // this thread's share of K(t+1), V(t) has landed
         __syncthreads();                // ... everyone's; K(t) and V(t-1) buffers are free
-        if (t + 2 < ntiles) issue_k<D, NT>(ptile + (size_t)tile_of(t + 2) * G::ELEMS, src_k, kbuf[P]);
-        if (t + 1 < ntiles) {
-            const int tl = tile_of(t + 1);
-            issue_v<D, NT>(ptile + (size_t)tl * G::ELEMS, pbias + (size_t)tl * kTK, src_v, vbuf[P ^ 1], lbias[P ^ 1]);
-        }
+        const int tl_k = t + 2 < ntiles ? tile_of(t + 2) : 0;
+        if (t + 2 < ntiles) load_k(tl_k, IC<P>{});
+        if (t + 1 < ntiles) load_v(tl_v, IC<P ^ 1>{});
+        tl_v = tl_k;
+        const int z = opaque_zero();
         f32x16 sn[2];  // scores of tile t+1 (not used after the last tile)
-        scores<D>(kbuf[P ^ 1], qreg, i32, h, sn);
+        scores<D>(kbuf(IC<P ^ 1>{}), koff, z, qreg, sn);
 
         // ---- probabilities of tile t.  Register 4g+j of chunk c holds key c*32 + 16(g/2) + 8h + 4(g%2) + j.
         const int cbase = (t - first_cmp) * kTK;  // first pseudo-key of a compressed tile
+        const float* lb = lbias(IC<P>{});
         float mx = -INFINITY;
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int key = c * 32 + 16 * (g >> 1) + 8 * h + 4 * (g & 1);
-                f32x4 bb = *reinterpret_cast<const f32x4*>(lbias[P] + key);
+                f32x4 bb = *reinterpret_cast<const f32x4*>(lb + key);
                 if constexpr (MASKED) {
-                    const uint32_t selw = sel_bits[(cbase + key) >> 5] >> ((cbase + key) & 31);
+                    const uint32_t selw_ = sel_bits[(cbase + key) >> 5] >> ((cbase + key) & 31);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) bb[j] = ((selw >> j) & 1u) ? -INFINITY : bb[j];
+                    for (int j = 0; j < 4; ++j) bb[j] = ((selw_ >> j) & 1u) ? -INFINITY : bb[j];
                 }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -271,7 +331,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
         // P in bf16, 16 keys per PV step: lane (i32, h) supplies keys 16kt + 8h + e (e = 0..7).
         // The normaliser sums the same bf16 values the PV product uses.
-        const __bf16* Vl = vbuf[P];
+        const __bf16* Vl = vbuf(IC<P>{});
 #pragma unroll
         for (int kt = 0; kt < kTK / 16; ++kt) {
             bf16x8 pk;
@@ -283,19 +343,26 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
                 l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
             }
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                const int dr = dt * 32 + i32;
-                const int pc = (2 * kt + h) ^ swz<G::V_CPR>(dr);
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vl + (dr * G::V_CPR + pc) * 8);
+            for (int dt = 0; dt < D / 32; ++dt) {  // V^T row dt*32 + i32 is 32*kTK elements past row i32
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vl + dt * 32 * kTK + (voff[kt] ^ z));
                 acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk, acc[dt], 0, 0, 0);
             }
         }
         st[0] = sn[0];
         st[1] = sn[1];
     };
-    int t = 0;
-    for (; t < first_cmp; ++t) step(t, std::integral_constant<bool, false>{});
-    for (; t < ntiles; ++t) step(t, std::integral_constant<bool, true>{});
+    // Steps over [t, end) with the stage parity a template constant: pairs (even, odd), plus one
+    // step at either end when the range starts odd or ends early.
+    auto run = [&](int t, int end, auto masked) __attribute__((always_inline)) {
+        if (t < end && (t & 1)) step(t++, masked, IC<1>{});
+        for (; t + 1 < end; t += 2) {
+            step(t, masked, IC<0>{});
+            step(t + 1, masked, IC<1>{});
+        }
+        if (t < end) step(t++, masked, IC<0>{});
+        return t;
+    };
+    run(run(0, first_cmp, std::false_type{}), ntiles, std::true_type{});
 
     // ---- epilogue: lane (i32, h) holds query row w*32 + i32, dims dt*32 + 8*g + 4*h + (0..3)
     const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -324,6 +391,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
             }
         if (lse && h == 0) lse[(size_t)bh * N + orow] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
     }
+#endif
 }
 
 template <typename T, int D, int BLK>
