@@ -13,8 +13,14 @@
 //  * Keys and values arrive as packed 64-key tiles (K rows | V^T, bf16, plus a log2-domain bias
 //    row) written once per call by the pack kernels.  A workgroup's work is a list of tiles: its K
 //    selected blocks, the sink tiles, then the compressed tiles.
-//  * Tiles move HBM -> LDS with global_load_lds_dwordx4 (no register staging), into one of two LDS
-//    stages: tile t+1 streams in while tile t is computed; one barrier per tile.
+//  * Tiles move HBM -> LDS with buffer_load ... lds (no register staging) into two LDS stages, the
+//    K half one tile ahead of the V^T half: iteration t computes the scores of tile t+1 while it
+//    turns those of tile t into probabilities and applies V(t); K(t+2) and V(t+1) stream in
+//    meanwhile; one barrier per tile.  Each stage is an LDS array of its own and the loop is
+//    unrolled by two, so the compiler can tell the arrays being read from those being written and
+//    does not wait for the stream before LDS reads.  Two workgroups per CU hide each other's waits.
+//  * A tile of real keys with no padding has an all-zero additive term: its exponents are taken
+//    straight from the raw scores (one FMA per key) and its bias row is not read.
 //  * LDS rows are XOR-swizzled by 16-byte chunk so the MFMA operand reads are conflict-free, and the
 //    K rows of each 32-key group are loaded in the order pi (bits 2 and 3 of the row index swapped):
 //    then the S^T accumulator of lane (i, h) holds, for query i, exactly the keys whose values form
@@ -102,17 +108,18 @@ __device__ __forceinline__ void issue_half(RS rs, uint32_t tile_byte,
 // as stage base + (lane offset ^ zero): the lane offsets are computed once, the per-stage sums are
 // not hoisted out of the loop (which would hold one set of address registers per stage), and the
 // stage base, a constant, folds into the instruction's offset field.
-__device__ __forceinline__ int opaque_zero() {
-    int z;
+__device__ __forceinline__ uint32_t opaque_zero() {
+    uint32_t z;
     asm volatile("s_mov_b32 %0, 0" : "=s"(z));
     return z;
 }
 
-// S^T = K_tile Q^T for two chunks of 32 keys x this wave's 32 queries.  koff[ds]: element offset of
-// lane (i32, h)'s A operand in row i32 of the tile for k step ds (row 32 + i32 is 32*D further).
+// S^T = K_tile Q^T for two chunks of 32 keys x this wave's 32 queries.  kboff[ds]: byte offset of
+// lane (i32, h)'s A operand in row i32 of the tile for k step ds (row 32 + i32 is 64*D bytes further).
 template <int D>
-__device__ __forceinline__ void scores(const __bf16* Kl, const int (&koff)[D / 16], int z, const bf16x8 (&qreg)[D / 16],
-                                       f32x16 (&st)[2]) {
+__device__ __forceinline__ void scores(const __bf16* Kl, const uint32_t (&kboff)[D / 16], uint32_t z,
+                                       const bf16x8 (&qreg)[D / 16], f32x16 (&st)[2]) {
+    const char* Kb = reinterpret_cast<const char*>(Kl);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         f32x16 a16;
@@ -120,7 +127,7 @@ __device__ __forceinline__ void scores(const __bf16* Kl, const int (&koff)[D / 1
         for (int r = 0; r < 16; ++r) a16[r] = 0.f;
 #pragma unroll
         for (int ds = 0; ds < D / 16; ++ds) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kl + c * 32 * D + (koff[ds] ^ z));
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + c * 64 * D + (kboff[ds] ^ z));
             a16 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], a16, 0, 0, 0);
         }
         st[c] = a16;
@@ -259,12 +266,17 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
         }
     }
 
-    // LDS element offsets of this lane's MFMA operands: K rows (S^T) and V^T rows (O^T), XOR-swizzled.
-    int koff[D / 16], voff[kTK / 16];
+    // LDS byte offsets of this lane's MFMA operands: K rows (S^T) and V^T rows (O^T), XOR-swizzled.
+    uint32_t kboff[D / 16], vboff[kTK / 16];
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) koff[ds] = (i32 * G::CK + ((2 * ds + h) ^ swz<G::CK>(i32))) * 8;
+    for (int ds = 0; ds < D / 16; ++ds) kboff[ds] = (i32 * G::CK + ((2 * ds + h) ^ swz<G::CK>(i32))) * 16;
 #pragma unroll
-    for (int kt = 0; kt < kTK / 16; ++kt) voff[kt] = (i32 * G::V_CPR + ((2 * kt + h) ^ swz<G::V_CPR>(i32))) * 8;
+    for (int kt = 0; kt < kTK / 16; ++kt) vboff[kt] = (i32 * G::V_CPR + ((2 * kt + h) ^ swz<G::V_CPR>(i32))) * 16;
+    // A tile of real keys needs no additive term when it holds no padding: its bias row is all zero.
+    const int Ns = N - Nv;
+    auto clean_of = [&](int tl) __attribute__((always_inline)) -> bool {
+        return tl < Tv ? (tl + 1) * kTK <= Nv : (tl - Tv + 1) * kTK <= Ns;
+    };
 
     f32x16 acc[D / 32];
 #pragma unroll
@@ -276,8 +288,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // K(0), K(1), V(0) and the route bits are in LDS
-    f32x16 st[2];
-    scores<D>(kbuf(IC<0>{}), koff, 0, qreg, st);
+    f32x16 sc[2][2];  // scores of tile t live in sc[t % 2]
+    scores<D>(kbuf(IC<0>{}), kboff, 0u, qreg, sc[0]);
+    bool clean_t = clean_of(tile_of(0)), clean_v = ntiles > 1 && clean_of(tl_v);  // tiles t and t+1
 
     // One pipeline step on stage parity P = t % 2.  MASKED: tile t is a compressed tile, whose
     // pseudo-keys of this query block's selected blocks are excluded (the mask goes into the additive
@@ -290,33 +303,48 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
         const int tl_k = t + 2 < ntiles ? tile_of(t + 2) : 0;
         if (t + 2 < ntiles) load_k(tl_k, IC<P>{});
         if (t + 1 < ntiles) load_v(tl_v, IC<P ^ 1>{});
+        const bool clean = !MASKED && clean_t;
+        clean_t = clean_v;
+        clean_v = t + 2 < ntiles && clean_of(tl_k);
         tl_v = tl_k;
-        const int z = opaque_zero();
-        f32x16 sn[2];  // scores of tile t+1 (not used after the last tile)
-        scores<D>(kbuf(IC<P ^ 1>{}), koff, z, qreg, sn);
+        const uint32_t z = opaque_zero();
+        scores<D>(kbuf(IC<P ^ 1>{}), kboff, z, qreg, sc[P ^ 1]);  // tile t+1 (unused after the last)
 
         // ---- probabilities of tile t.  Register 4g+j of chunk c holds key c*32 + 16(g/2) + 8h + 4(g%2) + j.
-        const int cbase = (t - first_cmp) * kTK;  // first pseudo-key of a compressed tile
-        const float* lb = lbias(IC<P>{});
-        float mx = -INFINITY;
+        // Exponent of key j: x_j * cc - m with x the raw score (cc = scale*log2 e) on a tile without
+        // an additive term, else x = raw*scale*log2 e + bias (cc = 1).
+        f32x16 (&st)[2] = sc[P];
+        float mx = -INFINITY, cc;
+        if (clean) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+            for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int key = c * 32 + 16 * (g >> 1) + 8 * h + 4 * (g & 1);
-                f32x4 bb = *reinterpret_cast<const f32x4*>(lb + key);
-                if constexpr (MASKED) {
-                    const uint32_t selw_ = sel_bits[(cbase + key) >> 5] >> ((cbase + key) & 31);
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[c][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32)) * c_log2;  // scale > 0: the max commutes with it
+            cc = c_log2;
+        } else {
+            const int cbase = (t - first_cmp) * kTK;  // first pseudo-key of a compressed tile
+            const float* lb = lbias(IC<P>{});
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) bb[j] = ((selw_ >> j) & 1u) ? -INFINITY : bb[j];
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int key = c * 32 + 16 * (g >> 1) + 8 * h + 4 * (g & 1);
+                    f32x4 bb = *reinterpret_cast<const f32x4*>(lb + key);
+                    if constexpr (MASKED) {
+                        const uint32_t selw_ = sel_bits[(cbase + key) >> 5] >> ((cbase + key) & 31);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) bb[j] = ((selw_ >> j) & 1u) ? -INFINITY : bb[j];
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        st[c][4 * g + j] = fmaf(st[c][4 * g + j], c_log2, bb[j]);
+                        mx = fmaxf(mx, st[c][4 * g + j]);
+                    }
                 }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    st[c][4 * g + j] = fmaf(st[c][4 * g + j], c_log2, bb[j]);
-                    mx = fmaxf(mx, st[c][4 * g + j]);
-                }
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            cc = 1.f;
+        }
         const bool raise = mx > m_run + kRescaleSlack;
         if (__ballot(raise)) {
             const float m_new = raise ? mx : m_run;
@@ -328,28 +356,27 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
                 for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
             m_run = m_new;
         }
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
         // P in bf16, 16 keys per PV step: lane (i32, h) supplies keys 16kt + 8h + e (e = 0..7).
         // The normaliser sums the same bf16 values the PV product uses.
-        const __bf16* Vl = vbuf(IC<P>{});
+        const char* Vb = reinterpret_cast<const char*>(vbuf(IC<P>{}));
 #pragma unroll
         for (int kt = 0; kt < kTK / 16; ++kt) {
             bf16x8 pk;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pk[e] = (__bf16)__builtin_amdgcn_exp2f(st[kt >> 1][8 * (kt & 1) + e] - m_use);
+            for (int e = 0; e < 8; ++e)
+                pk[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[kt >> 1][8 * (kt & 1) + e], cc, neg_m));
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
                 const bf16x2 pr = {pk[e], pk[e + 1]};
                 l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
             }
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {  // V^T row dt*32 + i32 is 32*kTK elements past row i32
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vl + dt * 32 * kTK + (voff[kt] ^ z));
+            for (int dt = 0; dt < D / 32; ++dt) {  // V^T row dt*32 + i32 is 64*kTK bytes past row i32
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vb + dt * 64 * kTK + (vboff[kt] ^ z));
                 acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk, acc[dt], 0, 0, 0);
             }
         }
-        st[0] = sn[0];
-        st[1] = sn[1];
     };
     // Steps over [t, end) with the stage parity a template constant: pairs (even, odd), plus one
     // step at either end when the range starts odd or ends early.
