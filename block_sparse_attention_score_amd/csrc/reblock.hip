@@ -15,11 +15,15 @@
 //            key = cos(., A) - cos(., B); the ceil(c/2)*block tokens first in (key desc, index asc)
 //            form the left child;
 //   perm   : leaves left to right, ascending token index inside each leaf.
-// Argmins use integer atomicMin on order-preserving keys and the balanced split is a radix select
-// on (key, index), so nothing depends on thread timing.
+// Argmins are lexicographic (order-preserving key, index) reductions and the balanced split is a
+// radix select on (key, index), so nothing depends on thread timing.
 //
-// Kernels: max|k| and the fixed-point Sigma and the norms are wide (all CUs); the level loop runs
-// in one persistent 1024-thread workgroup per (batch, head), with barriers between phases.
+// Kernels: max|k|, the fixed-point Sigma and the norms are wide (all CUs).  The partition keeps
+// an order array in which every group's tokens are contiguous, at the positions its leaves will
+// occupy in the permutation (leaves L0 .. L0+c-1 of a group own positions L0*block ..).  Each level
+// is one launch with one workgroup per group; a stable partition writes the next level's order,
+// so inside every leaf the tokens stay in ascending index and the last level writes the
+// permutation itself.
 #include <limits.h>
 
 #include "kernels.hpp"
@@ -33,13 +37,12 @@ constexpr int kRbSigmaRows = 2048;  // rows per exact binary64 partial sum (2^42
 constexpr int kRbMaxRows = 1 << 20; // int64 sums of <= 2^20 products of magnitude <= 2^42
 
 struct RbLayout {
-    size_t kmax, sint, sigma, nrm, grp, cbuf, dk, gstart, gc, gcnt, gp0, ga, gb, grem, gmin, gpre_hi, gpre_lo,
-        gvec, hist, total;
+    size_t kmax, sint, sigma, nrm, ord0, ord1, cbuf, dk, total;
 };
 
 static RbLayout rb_layout(const LaunchCtx& L) {
     RbLayout r;
-    const size_t BH = L.BH, Nv = L.Nv, M = L.M, d = L.d;
+    const size_t BH = L.BH, Nv = L.Nv, d = L.d;
     size_t o = 0;
     auto take = [&](size_t bytes) {
         const size_t at = o;
@@ -50,21 +53,10 @@ static RbLayout rb_layout(const LaunchCtx& L) {
     r.sint = take(BH * d * d * 8);
     r.sigma = take(BH * d * d * 8);
     r.nrm = take(BH * Nv * 8);
-    r.grp = take(BH * Nv * 4);
+    r.ord0 = take(BH * Nv * 4);
+    r.ord1 = take(BH * Nv * 4);
     r.cbuf = take(BH * Nv * 8);
     r.dk = take(BH * Nv * 8);
-    r.gstart = take(BH * M * 4);
-    r.gc = take(BH * M * 4);
-    r.gcnt = take(BH * M * 4);
-    r.gp0 = take(BH * M * 4);
-    r.ga = take(BH * M * 4);
-    r.gb = take(BH * M * 4);
-    r.grem = take(BH * M * 4);
-    r.gmin = take(BH * M * 8);
-    r.gpre_hi = take(BH * M * 8);
-    r.gpre_lo = take(BH * M * 8);
-    r.gvec = take(BH * M * d * 8);
-    r.hist = take(BH * M * 256 * 4);
     r.total = o;
     return r;
 }
@@ -83,10 +75,6 @@ __device__ __forceinline__ uint64_t asc_key(double x) {
     x = x + 0.0;
     const uint64_t u = (uint64_t)__double_as_longlong(x);
     return (u >> 63) ? ~u : (u | (1ull << 63));
-}
-
-template <typename U> __device__ __forceinline__ U aload(const U* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ __launch_bounds__(256) void rb_zero_kernel(uint64_t* __restrict__ p, size_t n) {
@@ -201,241 +189,258 @@ __global__ __launch_bounds__(256) void rb_norms_kernel(const T* __restrict__ Q, 
     nrm[(size_t)bh * Nv + i] = r > 0.0 ? sqrt(r) : 0.0;
 }
 
-struct RbHead {
-    const double* sigma;
-    const double* nrm;
-    int* grp;
-    double* cbuf;
-    uint64_t* dk;
-    int *gstart, *gc, *gcnt, *gp0, *ga, *gb, *grem;
-    uint64_t *gmin, *gpre_hi, *gpre_lo;
-    double* gvec;
-    unsigned* hist;
-};
-
-// g(P) = t(P) / n_P for the group starting at leaf G, computed by one wave (lane a-owners).
-template <typename T, int D>
-__device__ __forceinline__ void pivot_vec(const RbHead& s, const T* Qh, int P, int G) {
-    const int lane = threadIdx.x & 63;
-    const double nP = s.nrm[P];
-    const T* qp = Qh + (size_t)P * D;
-#pragma unroll
-    for (int k = 0; k < D / 64; ++k) {
-        const int a = lane + 64 * k;
+// g(P) = t(P) / n_P into gv[0..D): thread a computes t_a = fma chain over b of Sigma_ab q_Pb.
+template <typename T, int D, int NT>
+__device__ __forceinline__ void rb_pivot(const double* __restrict__ sigma, const double* __restrict__ nrm,
+                                         const T* __restrict__ Qh, int P, double* gv) {
+    for (int a = threadIdx.x; a < D; a += NT) {
+        const double nP = nrm[P];
         double g = 0.0;
         if (nP != 0.0) {
-            const double* Sa = s.sigma + (size_t)a * D;
+            const double* Sa = sigma + (size_t)a * D;
+            const T* qp = Qh + (size_t)P * D;
             double t = 0.0;
             for (int b = 0; b < D; ++b) t = fma(Sa[b], (double)elem_f<T>(qp + b), t);
             g = t / nP;
         }
-        s.gvec[(size_t)G * D + a] = g;
+        gv[a] = g;
     }
 }
 
+// cos(i, P) = (fma chain over a of q_ia g_a(P)) / n_i, 0 when n_i = 0.
 template <typename T, int D>
-__device__ __forceinline__ double cos_to(const RbHead& s, const T* Qh, int i, int G) {
-    const double ni = s.nrm[i];
+__device__ __forceinline__ double rb_cos(const T* __restrict__ Qh, const double* __restrict__ nrm, int i,
+                                         const double* gv) {
+    const double ni = nrm[i];
     if (ni == 0.0) return 0.0;
     const T* q = Qh + (size_t)i * D;
-    const double* g = s.gvec + (size_t)G * D;
     double acc = 0.0;
-    for (int a = 0; a < D; ++a) acc = fma((double)elem_f<T>(q + a), g[a], acc);
+#pragma unroll 8
+    for (int a = 0; a < D; ++a) acc = fma((double)elem_f<T>(q + a), gv[a], acc);
     return acc / ni;
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(kRbThreads) void rb_levels_kernel(const T* __restrict__ Q, int N, int Nv, int BLK,
-                                                               int M, RbLayout lay, char* ws, int32_t* __restrict__ perm) {
-    const int bh = blockIdx.x, tid = threadIdx.x, w = tid >> 6;
-    constexpr int NW = kRbThreads / 64;
+// Lexicographic minimum of (key, idx) over the workgroup (result in every thread).
+template <int NT>
+__device__ __forceinline__ void rb_argmin(uint64_t& key, int& idx, uint64_t* skey, int* sidx) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const uint64_t k2 = __shfl_xor(key, o);
+        const int i2 = __shfl_xor(idx, o);
+        if (k2 < key || (k2 == key && i2 < idx)) {
+            key = k2;
+            idx = i2;
+        }
+    }
+    if (lane == 0) {
+        skey[w] = key;
+        sidx[w] = idx;
+    }
+    __syncthreads();
+    key = skey[0];
+    idx = sidx[0];
+    for (int v = 1; v < NT / 64; ++v) {
+        const uint64_t k2 = skey[v];
+        const int i2 = sidx[v];
+        if (k2 < key || (k2 == key && i2 < idx)) {
+            key = k2;
+            idx = i2;
+        }
+    }
+    __syncthreads();
+}
+
+// One level of the partition: workgroup (group g of this level, (batch, head)).  The group's
+// leaves [L0, L0 + c) follow from g's bits (most significant first: 0 = left child, which takes
+// ceil(c/2) leaves).  A group of one leaf is copied; a group of more leaves is split.
+template <typename T, int D, int NT>
+__global__ __launch_bounds__(NT) void rb_level_kernel(const T* __restrict__ Q, int N, int Nv, int BLK, int M, int lev,
+                                                      const double* __restrict__ sigma_all,
+                                                      const double* __restrict__ nrm_all,
+                                                      const int32_t* __restrict__ ord_in_all,
+                                                      int32_t* __restrict__ ord_out_all, double* __restrict__ cbuf_all,
+                                                      uint64_t* __restrict__ dk_all) {
+    constexpr int NW = NT / 64;
+    __shared__ double gv[D];
+    __shared__ uint64_t skey[NW];
+    __shared__ int sidx[NW];
+    __shared__ unsigned hist[NW][256];
+    __shared__ int sel_digit, sel_rem, wcount[2][NW];
+
+    const int bh = blockIdx.y, g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int L0 = 0, c = M;
+    for (int b = lev - 1; b >= 0; --b) {
+        const int cl = (c + 1) / 2;
+        if ((g >> b) & 1) {
+            L0 += cl;
+            c -= cl;
+        } else {
+            c = cl;
+        }
+    }
+    if (c <= 0) return;
+    const int s0 = L0 * BLK, n = min(s0 + c * BLK, Nv) - s0;
+    const int32_t* seg = ord_in_all + (size_t)bh * Nv + s0;
+    int32_t* out = ord_out_all + (size_t)bh * Nv + s0;
+    if (c == 1) {
+        for (int j = tid; j < n; j += NT) out[j] = seg[j];
+        return;
+    }
     const T* Qh = Q + (size_t)bh * N * D;
-    RbHead s;
-    s.sigma = (const double*)(ws + lay.sigma) + (size_t)bh * D * D;
-    s.nrm = (const double*)(ws + lay.nrm) + (size_t)bh * Nv;
-    s.grp = (int*)(ws + lay.grp) + (size_t)bh * Nv;
-    s.cbuf = (double*)(ws + lay.cbuf) + (size_t)bh * Nv;
-    s.dk = (uint64_t*)(ws + lay.dk) + (size_t)bh * Nv;
-    s.gstart = (int*)(ws + lay.gstart) + (size_t)bh * M;
-    s.gc = (int*)(ws + lay.gc) + (size_t)bh * M;
-    s.gcnt = (int*)(ws + lay.gcnt) + (size_t)bh * M;
-    s.gp0 = (int*)(ws + lay.gp0) + (size_t)bh * M;
-    s.ga = (int*)(ws + lay.ga) + (size_t)bh * M;
-    s.gb = (int*)(ws + lay.gb) + (size_t)bh * M;
-    s.grem = (int*)(ws + lay.grem) + (size_t)bh * M;
-    s.gmin = (uint64_t*)(ws + lay.gmin) + (size_t)bh * M;
-    s.gpre_hi = (uint64_t*)(ws + lay.gpre_hi) + (size_t)bh * M;
-    s.gpre_lo = (uint64_t*)(ws + lay.gpre_lo) + (size_t)bh * M;
-    s.gvec = (double*)(ws + lay.gvec) + (size_t)bh * M * D;
-    s.hist = (unsigned*)(ws + lay.hist) + (size_t)bh * M * 256;
+    const double* sigma = sigma_all + (size_t)bh * D * D;
+    const double* nrm = nrm_all + (size_t)bh * Nv;
+    double* cb = cbuf_all + (size_t)bh * Nv + s0;
+    uint64_t* dk = dk_all + (size_t)bh * Nv + s0;
 
-    // one group of all N_v tokens holding M leaves
-    for (int i = tid; i < Nv; i += kRbThreads) s.grp[i] = 0;
-    for (int G = tid; G < M; G += kRbThreads) {
-        s.gstart[G] = G == 0;
-        s.gc[G] = G == 0 ? M : 0;
-        s.gcnt[G] = G == 0 ? Nv : 0;
+    // P0: lowest token index of the group
+    int P0 = INT_MAX;
+    for (int j = tid; j < n; j += NT) P0 = min(P0, (int)seg[j]);
+    {
+        uint64_t k0 = 0;
+        rb_argmin<NT>(k0, P0, skey, sidx);
+    }
+    rb_pivot<T, D, NT>(sigma, nrm, Qh, P0, gv);
+    __syncthreads();
+    // A = argmin cos(., P0), ties to the lower index
+    uint64_t kmin = ~0ull;
+    int A = INT_MAX;
+    for (int j = tid; j < n; j += NT) {
+        const int i = seg[j];
+        const uint64_t k = asc_key(rb_cos<T, D>(Qh, nrm, i, gv));
+        if (k < kmin || (k == kmin && i < A)) {
+            kmin = k;
+            A = i;
+        }
+    }
+    rb_argmin<NT>(kmin, A, skey, sidx);
+    rb_pivot<T, D, NT>(sigma, nrm, Qh, A, gv);
+    __syncthreads();
+    // B = argmin cos(., A); cos(., A) is kept for the key
+    kmin = ~0ull;
+    int B = INT_MAX;
+    for (int j = tid; j < n; j += NT) {
+        const int i = seg[j];
+        const double cA = rb_cos<T, D>(Qh, nrm, i, gv);
+        cb[j] = cA;
+        const uint64_t k = asc_key(cA);
+        if (k < kmin || (k == kmin && i < B)) {
+            kmin = k;
+            B = i;
+        }
+    }
+    rb_argmin<NT>(kmin, B, skey, sidx);
+    rb_pivot<T, D, NT>(sigma, nrm, Qh, B, gv);
+    __syncthreads();
+    // key = cos(., A) - cos(., B); order (key desc, index asc) = (~asc_key(key), index) asc
+    for (int j = tid; j < n; j += NT) {
+        const int i = seg[j];
+        dk[j] = ~asc_key(cb[j] - rb_cos<T, D>(Qh, nrm, i, gv));
     }
     __syncthreads();
-    int levels = 0;
-    while ((1 << levels) < M) ++levels;
-
-    auto splitting = [&](int G) { return s.gstart[G] && s.gc[G] > 1; };
-
-    for (int lev = 0; lev < levels; ++lev) {
-        // ---- group state for this level
-        for (int G = tid; G < M; G += kRbThreads)
-            if (splitting(G)) {
-                s.gp0[G] = INT_MAX;
-                s.ga[G] = INT_MAX;
-                s.gb[G] = INT_MAX;
-                s.gmin[G] = ~0ull;
-            }
+    // radix select of the nl-th smallest (dk, index): 8 digits of dk, then 3 of the index (< 2^24)
+    const int nl = ((c + 1) / 2) * BLK;
+    uint64_t pre_hi = 0;
+    uint32_t pre_lo = 0;
+    int rem = nl;
+    for (int pass = 0; pass < 11; ++pass) {
+        for (int b = lane; b < 256; b += 64) hist[w][b] = 0u;
         __syncthreads();
-        // ---- P0: lowest token index of the group
-        for (int i = tid; i < Nv; i += kRbThreads) {
-            const int G = s.grp[i];
-            if (s.gc[G] > 1) atomicMin(&s.gp0[G], i);
+        for (int j = tid; j < n; j += NT) {
+            const uint64_t k = dk[j];
+            const uint32_t i = (uint32_t)seg[j];
+            bool match;
+            unsigned digit;
+            if (pass < 8) {
+                match = pass == 0 || (k >> (64 - 8 * pass)) == pre_hi;
+                digit = (unsigned)(k >> (56 - 8 * pass)) & 255u;
+            } else {
+                const int p = pass - 8;
+                match = k == pre_hi && (p == 0 || (i >> (24 - 8 * p)) == pre_lo);
+                digit = (i >> (16 - 8 * p)) & 255u;
+            }
+            if (match) atomicAdd(&hist[w][digit], 1u);
         }
         __syncthreads();
-        for (int G = w; G < M; G += NW)
-            if (splitting(G)) pivot_vec<T, D>(s, Qh, aload(&s.gp0[G]), G);
-        __syncthreads();
-        // ---- A = argmin cos(., P0), ties to the lower index
-        for (int i = tid; i < Nv; i += kRbThreads) {
-            const int G = s.grp[i];
-            if (s.gc[G] > 1) {
-                const double c = cos_to<T, D>(s, Qh, i, G);
-                s.cbuf[i] = c;
-                atomicMin((unsigned long long*)&s.gmin[G], (unsigned long long)asc_key(c));
+        if (w == 0) {
+            // lane l owns bins 4l .. 4l+3
+            unsigned cnt[4], tot = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                unsigned v = 0;
+                for (int u = 0; u < NW; ++u) v += hist[u][4 * lane + q];
+                cnt[q] = v;
+                tot += v;
             }
-        }
-        __syncthreads();
-        for (int i = tid; i < Nv; i += kRbThreads) {
-            const int G = s.grp[i];
-            if (s.gc[G] > 1 && asc_key(s.cbuf[i]) == aload(&s.gmin[G])) atomicMin(&s.ga[G], i);
-        }
-        __syncthreads();
-        for (int G = w; G < M; G += NW)
-            if (splitting(G)) pivot_vec<T, D>(s, Qh, aload(&s.ga[G]), G);
-        for (int G = tid; G < M; G += kRbThreads)
-            if (splitting(G)) s.gmin[G] = ~0ull;
-        __syncthreads();
-        // ---- B = argmin cos(., A); cos(., A) is kept for the key
-        for (int i = tid; i < Nv; i += kRbThreads) {
-            const int G = s.grp[i];
-            if (s.gc[G] > 1) {
-                const double c = cos_to<T, D>(s, Qh, i, G);
-                s.cbuf[i] = c;
-                atomicMin((unsigned long long*)&s.gmin[G], (unsigned long long)asc_key(c));
+            unsigned inc = tot;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const unsigned y = __shfl_up(inc, o);
+                if (lane >= o) inc += y;
             }
-        }
-        __syncthreads();
-        for (int i = tid; i < Nv; i += kRbThreads) {
-            const int G = s.grp[i];
-            if (s.gc[G] > 1 && asc_key(s.cbuf[i]) == aload(&s.gmin[G])) atomicMin(&s.gb[G], i);
-        }
-        __syncthreads();
-        for (int G = w; G < M; G += NW)
-            if (splitting(G)) pivot_vec<T, D>(s, Qh, aload(&s.gb[G]), G);
-        __syncthreads();
-        // ---- key = cos(., A) - cos(., B); order (key desc, index asc) = (~asc_key(key), index) asc
-        for (int i = tid; i < Nv; i += kRbThreads) {
-            const int G = s.grp[i];
-            if (s.gc[G] > 1) {
-                const double key = s.cbuf[i] - cos_to<T, D>(s, Qh, i, G);
-                s.dk[i] = ~asc_key(key);
-            }
-        }
-        for (int G = tid; G < M; G += kRbThreads)
-            if (splitting(G)) {
-                s.grem[G] = ((s.gc[G] + 1) / 2) * BLK;  // rank of the last left token (1-based)
-                s.gpre_hi[G] = 0;
-                s.gpre_lo[G] = 0;
-            }
-        __syncthreads();
-        // ---- radix select of the grem-th smallest (dk, index): 8 digits of dk, then 4 of index
-        for (int pass = 0; pass < 12; ++pass) {
-            for (int G = w; G < M; G += NW)
-                if (splitting(G))
-                    for (int b = tid & 63; b < 256; b += 64) s.hist[(size_t)G * 256 + b] = 0u;
-            __syncthreads();
-            for (int i = tid; i < Nv; i += kRbThreads) {
-                const int G = s.grp[i];
-                if (s.gc[G] <= 1) continue;
-                const uint64_t k = s.dk[i];
-                bool match;
-                unsigned digit;
-                if (pass < 8) {
-                    match = pass == 0 || (k >> (64 - 8 * pass)) == s.gpre_hi[G];
-                    digit = (unsigned)(k >> (56 - 8 * pass)) & 255u;
-                } else {
-                    const int p = pass - 8;
-                    match = k == s.gpre_hi[G] && (p == 0 || ((uint64_t)i >> (32 - 8 * p)) == s.gpre_lo[G]);
-                    digit = ((unsigned)i >> (24 - 8 * p)) & 255u;
-                }
-                if (match) atomicAdd(&s.hist[(size_t)G * 256 + digit], 1u);
-            }
-            __syncthreads();
-            for (int G = tid; G < M; G += kRbThreads)
-                if (splitting(G)) {
-                    int rem = s.grem[G], cum = 0, dsel = 255;
-                    for (int b = 0; b < 256; ++b) {
-                        const int hcount = (int)aload(&s.hist[(size_t)G * 256 + b]);
-                        if (cum + hcount >= rem) {
-                            dsel = b;
-                            break;
-                        }
-                        cum += hcount;
+            const unsigned before = inc - tot;  // count of bins below 4*lane
+            // the lane whose range holds the rem-th element picks the bin
+            if ((int)before < rem && rem <= (int)inc) {
+                unsigned cum = before;
+                int dsel = 4 * lane + 3;
+                for (int q = 0; q < 4; ++q) {
+                    if ((int)(cum + cnt[q]) >= rem) {
+                        dsel = 4 * lane + q;
+                        break;
                     }
-                    s.grem[G] = rem - cum;
-                    if (pass < 8) s.gpre_hi[G] = (s.gpre_hi[G] << 8) | (uint64_t)dsel;
-                    else s.gpre_lo[G] = (s.gpre_lo[G] << 8) | (uint64_t)dsel;
+                    cum += cnt[q];
                 }
-            __syncthreads();
-        }
-        // ---- children: left = keys <= the selected one (ceil(c/2) leaves), right starts after
-        for (int i = tid; i < Nv; i += kRbThreads) {
-            const int G = s.grp[i];
-            const int c = s.gc[G];
-            if (c <= 1) continue;
-            const uint64_t k = s.dk[i], th = s.gpre_hi[G];
-            const bool left = k < th || (k == th && (uint64_t)i <= s.gpre_lo[G]);
-            if (!left) s.grp[i] = G + (c + 1) / 2;
-        }
-        __syncthreads();
-        for (int G = tid; G < M; G += kRbThreads)
-            if (splitting(G)) {
-                const int c = s.gc[G], cl = (c + 1) / 2, nl = cl * BLK;
-                s.gc[G + cl] = c - cl;
-                s.gcnt[G + cl] = s.gcnt[G] - nl;
-                s.gstart[G + cl] = 1;
-                s.gc[G] = cl;
-                s.gcnt[G] = nl;
+                sel_digit = dsel;
+                sel_rem = rem - (int)cum;
             }
-        __syncthreads();
-    }
-
-    // ---- perm: leaf L holds positions L*BLK .., tokens in ascending index (stable, chunked)
-    __shared__ int cnt[kMaxBlocks];
-    __shared__ int sleaf[kRbThreads];
-    for (int L = tid; L < M; L += kRbThreads) cnt[L] = 0;
-    __syncthreads();
-    int32_t* pr = perm + (size_t)bh * Nv;
-    for (int base = 0; base < Nv; base += kRbThreads) {
-        const int i = base + tid;
-        const int leaf = i < Nv ? s.grp[i] : -1;
-        sleaf[tid] = leaf;
-        __syncthreads();
-        if (i < Nv) {
-            int rank = 0;
-            for (int j = 0; j < tid; ++j) rank += sleaf[j] == leaf;
-            pr[(size_t)leaf * BLK + cnt[leaf] + rank] = i;
         }
         __syncthreads();
-        if (i < Nv) atomicAdd(&cnt[leaf], 1);
+        const unsigned dsel = (unsigned)sel_digit;
+        rem = sel_rem;
+        if (pass < 8) pre_hi = (pre_hi << 8) | dsel;
+        else pre_lo = (pre_lo << 8) | dsel;
         __syncthreads();
     }
+    // stable partition: the nl smallest (dk, index) first, in their current order, then the rest
+    int lbase = 0, rbase = 0;
+    for (int j0 = 0; j0 < n; j0 += NT) {
+        const int j = j0 + tid;
+        bool left = false;
+        int i = 0;
+        if (j < n) {
+            const uint64_t k = dk[j];
+            i = seg[j];
+            left = k < pre_hi || (k == pre_hi && (uint32_t)i <= pre_lo);
+        }
+        const uint64_t bl = __ballot(left && j < n), br = __ballot(!left && j < n);
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        if (lane == 0) {
+            wcount[0][w] = __popcll(bl);
+            wcount[1][w] = __popcll(br);
+        }
+        __syncthreads();
+        int lw = 0, rw = 0, lt = 0, rt = 0;
+        for (int v = 0; v < NW; ++v) {
+            if (v < w) {
+                lw += wcount[0][v];
+                rw += wcount[1][v];
+            }
+            lt += wcount[0][v];
+            rt += wcount[1][v];
+        }
+        if (j < n) {
+            if (left) out[lbase + lw + __popcll(bl & below)] = i;
+            else out[nl + rbase + rw + __popcll(br & below)] = i;
+        }
+        lbase += lt;
+        rbase += rt;
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(256) void rb_iota_kernel(int32_t* __restrict__ ord, int Nv) {
+    const int bh = blockIdx.y;
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < Nv; i += gridDim.x * 256) ord[(size_t)bh * Nv + i] = i;
 }
 
 template <typename T, int D>
@@ -456,8 +461,24 @@ static void launch_reblock_t(const LaunchCtx& L, const void* Q, const void* K, i
                        D, L.Nv, sigma);
     hipLaunchKernelGGL((rb_norms_kernel<T, D>), dim3((L.Nv + 255) / 256, L.BH), dim3(256), 0, L.stream, (const T*)Q,
                        L.N, L.Nv, sigma, nrm);
-    hipLaunchKernelGGL((rb_levels_kernel<T, D>), dim3(L.BH), dim3(kRbThreads), 0, L.stream, (const T*)Q, L.N, L.Nv,
-                       L.block, L.M, lay, w, perm);
+    int32_t* ord[2] = {(int32_t*)(w + lay.ord0), (int32_t*)(w + lay.ord1)};
+    double* cbuf = (double*)(w + lay.cbuf);
+    uint64_t* dk = (uint64_t*)(w + lay.dk);
+    hipLaunchKernelGGL(rb_iota_kernel, dim3((L.Nv + 255) / 256, L.BH), dim3(256), 0, L.stream, L.M > 1 ? ord[0] : perm,
+                       L.Nv);
+    int levels = 0;
+    while ((1 << levels) < L.M) ++levels;
+    for (int lev = 0; lev < levels; ++lev) {
+        int32_t* dst = lev + 1 == levels ? perm : ord[(lev + 1) & 1];
+        const dim3 grid(1u << lev, L.BH);
+        // wide workgroups while the groups are few and large, narrow ones once they are many
+        if ((1 << lev) <= 32)
+            hipLaunchKernelGGL((rb_level_kernel<T, D, 1024>), grid, dim3(1024), 0, L.stream, (const T*)Q, L.N, L.Nv,
+                               L.block, L.M, lev, sigma, nrm, ord[lev & 1], dst, cbuf, dk);
+        else
+            hipLaunchKernelGGL((rb_level_kernel<T, D, 256>), grid, dim3(256), 0, L.stream, (const T*)Q, L.N, L.Nv,
+                               L.block, L.M, lev, sigma, nrm, ord[lev & 1], dst, cbuf, dk);
+    }
 }
 
 void launch_reblock(const LaunchCtx& L, const void* Q, const void* K, int32_t* perm, void* ws) {
