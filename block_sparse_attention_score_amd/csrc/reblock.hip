@@ -190,6 +190,8 @@ __global__ __launch_bounds__(256) void rb_norms_kernel(const T* __restrict__ Q, 
 }
 
 // g(P) = t(P) / n_P into gv[0..D): thread a computes t_a = fma chain over b of Sigma_ab q_Pb.
+// Sigma is exactly symmetric, so Sigma_ab is read as Sigma[b][a]: at each b the lanes read one
+// contiguous row segment.
 template <typename T, int D, int NT>
 __device__ __forceinline__ void rb_pivot(const double* __restrict__ sigma, const double* __restrict__ nrm,
                                          const T* __restrict__ Qh, int P, double* gv) {
@@ -197,10 +199,10 @@ __device__ __forceinline__ void rb_pivot(const double* __restrict__ sigma, const
         const double nP = nrm[P];
         double g = 0.0;
         if (nP != 0.0) {
-            const double* Sa = sigma + (size_t)a * D;
             const T* qp = Qh + (size_t)P * D;
             double t = 0.0;
-            for (int b = 0; b < D; ++b) t = fma(Sa[b], (double)elem_f<T>(qp + b), t);
+#pragma unroll 16
+            for (int b = 0; b < D; ++b) t = fma(sigma[(size_t)b * D + a], (double)elem_f<T>(qp + b), t);
             g = t / nP;
         }
         gv[a] = g;
