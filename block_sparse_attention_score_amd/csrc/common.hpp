@@ -46,6 +46,32 @@ template <> struct In<float> {
     }
 };
 
+// Eight consecutive input elements kept as raw bits (loaded now, widened later), so that a
+// thread can have all of its loads in flight before it needs any value.
+template <typename T> struct Raw8;
+template <> struct Raw8<__bf16> {
+    u32x4 u;
+    __device__ __forceinline__ void load(const __bf16* p) { u = *reinterpret_cast<const u32x4*>(p); }
+    __device__ __forceinline__ void widen(float (&v)[8]) const {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = bf16_bits_to_f32(u[j] & 0xffffu);
+            v[2 * j + 1] = bf16_bits_to_f32(u[j] >> 16);
+        }
+    }
+};
+template <> struct Raw8<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = *reinterpret_cast<const f32x4*>(p);
+        b = *reinterpret_cast<const f32x4*>(p + 4);
+    }
+    __device__ __forceinline__ void widen(float (&v)[8]) const {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { v[j] = a[j]; v[4 + j] = b[j]; }
+    }
+};
+
 // Eight consecutive elements as packed bf16 (16 bytes), rounding fp32 to nearest even.
 __device__ __forceinline__ u32x4 pack8_bf16(const float (&v)[8]) {
     u32x4 r;

@@ -25,13 +25,16 @@ __global__ __launch_bounds__(256) void pool_q_kernel(const T* __restrict__ Q, in
     const int lo = J * BLK, n = min(BLK, Nv - lo);
     const T* base = Q + ((size_t)bh * N + lo) * D + c * 8;
 
+    // every row load is issued first (rows past the block end read its last row and are dropped)
+    Raw8<T> raw[RPT];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) raw[k].load(base + (size_t)min(rg + k * G::RG, n - 1) * D);
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
-        const int r = rg + k * G::RG;
-        if (r < n) {
+        if (rg + k * G::RG < n) {
             float v[8];
-            In<T>::load8(base + (size_t)r * D, v);
+            raw[k].widen(v);
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[j] += v[j];
         }
@@ -87,14 +90,20 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, c
     const int lo = J * BLK, n = min(BLK, Nv - lo);
     const size_t off = ((size_t)bh * N + lo) * D + c * 8;
 
+    // every row load is issued first (rows past the block end read its last row, then read as 0)
+    Raw8<T> kraw[RPT], vraw[RPT];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+        const size_t ro = (size_t)min(rg + k * G::RG, n - 1) * D;
+        kraw[k].load(K + off + ro);
+        vraw[k].load(V + off + ro);
+    }
     float kr[RPT][8], vr[RPT][8];
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
-        const int r = rg + k * G::RG;
-        if (r < n) {
-            In<T>::load8(K + off + (size_t)r * D, kr[k]);
-            In<T>::load8(V + off + (size_t)r * D, vr[k]);
-        } else {
+        kraw[k].widen(kr[k]);
+        vraw[k].widen(vr[k]);
+        if (rg + k * G::RG >= n) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) { kr[k][j] = 0.f; vr[k][j] = 0.f; }
         }
