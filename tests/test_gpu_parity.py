@@ -96,6 +96,50 @@ def test_select_parity(orc, case):
     print(f"rows differing from the exact oracle set (inside the near-tie window): {differ}")
 
 
+# (name, M, K ratio, kind): crafted block means drive the selection directly
+TOPK_CASES = [
+    ("random-1922", 1922, 0.1, "random"),
+    ("random-500", 500, 0.3, "random"),
+    ("ties-1922", 1922, 0.1, "ties"),
+    ("all-equal-1000", 1000, 0.1, "zero-q"),
+    ("few-values-700", 700, 0.2, "few"),
+    ("random-5000", 5000, 0.1, "random"),
+    ("ties-5000", 5000, 0.05, "ties"),
+    ("one-block", 1, 0.1, "random"),
+]
+
+
+@pytest.mark.parametrize("case", TOPK_CASES, ids=[c[0] for c in TOPK_CASES])
+def test_select_is_exact_topk_of_its_scores(case):
+    """The route must be exactly the K largest of the GPU's own score row by (score desc, J asc),
+    listed in ascending J, whatever the score distribution (ties decided by the lower index)."""
+    name, M, r, kind = case
+    B, H, d, b = 1, 2, 64, 64
+    rng = np.random.default_rng(M)
+    qm = rng.standard_normal((B, H, M, d)).astype(np.float32)
+    km = rng.standard_normal((B, H, M, d)).astype(np.float32)
+    if kind == "ties":  # key means drawn from five vectors: five distinct scores per row
+        km = rng.standard_normal((B, H, 5, d)).astype(np.float32)[:, :, rng.integers(0, 5, M)]
+    elif kind == "zero-q":  # every score 0: the K lowest indices
+        qm[:] = 0.0
+    elif kind == "few":  # small integer-valued means: many exact score ties
+        qm = rng.integers(-2, 3, (B, H, M, d)).astype(np.float32)
+        km = rng.integers(-1, 2, (B, H, M, d)).astype(np.float32)
+    Q = torch.zeros(B, H, M * b, d, device="cuda", dtype=torch.bfloat16)  # shapes only
+    note(f"topk {name}")
+    qm, km = np.ascontiguousarray(qm), np.ascontiguousarray(km)
+    idx, S = sa.select(torch.from_numpy(qm).cuda(), torch.from_numpy(km).cuda(), Q, 0, b, r, with_scores=True)
+    torch.cuda.synchronize()
+    Sh, gi = host(S), host(idx)
+    K = gi.shape[-1]
+    for bb in range(B):
+        for h in range(H):
+            for I in range(M):
+                row = Sh[bb, h, I]
+                top = np.sort(np.lexsort((np.arange(M), -row))[:K])
+                assert (gi[bb, h, I] == top).all(), (bb, h, I)
+
+
 def permute_rows(X, perm):
     Y = X.copy()
     nv = perm.shape[-1]
