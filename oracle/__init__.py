@@ -62,7 +62,7 @@ def lib():
         L.orc_dense.argtypes = [P, f32, f32, f32, f64, f64]
         L.orc_attend_blocks.argtypes = [P, f32, f32, f32, f64, f64, f64, i32, ctypes.c_int, i32,
                                         ctypes.c_int, f64, f64]
-        L.orc_forward.argtypes = [P, f32, f32, f32, vp, vp, f64, f64, vp]
+        L.orc_forward.argtypes = [P, f32, f32, f32, vp, vp, vp, f64, f64, vp]
         L.orc_reblock_metric.argtypes = [P, f32, f32, f64, f64]
         L.orc_reblock.argtypes = [P, f32, f32, i32]
         for fn in (L.orc_pool, L.orc_scores, L.orc_select, L.orc_dense, L.orc_attend_blocks,
@@ -127,8 +127,10 @@ def dense(p: Params, Q, K, V):
     return O, lse
 
 
-def forward(p: Params, Q, K, V, perm=None, idx=None):
-    """Full forward. Returns (O [B,H,N,d] f64, lse [B,H,N] f64, idx [B,H,M,K] int32)."""
+def forward(p: Params, Q, K, V, perm=None, idx=None, perm_k=None):
+    """Full forward. Returns (O [B,H,N,d] f64, lse [B,H,N] f64, idx [B,H,M,K] int32).
+    perm: query partition (and output rows); perm_k: separate key partition for K and V, or
+    None for keys and values reusing perm."""
     M = num_blocks(p)
     Ksel = topk_count(M, p.topk_ratio)
     O = np.empty((p.B, p.H, p.N, p.d))
@@ -144,7 +146,7 @@ def forward(p: Params, Q, K, V, perm=None, idx=None):
         return a.ctypes.data
 
     lib().orc_forward(ctypes.byref(p), _f32(Q), _f32(K), _f32(V), ptr(perm, np.int32),
-                      ptr(idx, np.int32), O, lse, idx_out.ctypes.data)
+                      ptr(perm_k, np.int32), ptr(idx, np.int32), O, lse, idx_out.ctypes.data)
     return O, lse, idx_out
 
 

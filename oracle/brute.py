@@ -66,8 +66,10 @@ def select_head(q_mean, k_mean, s, K):
     return S, idx
 
 
-def forward(Q, K, V, n_sink, block, ratio, pool_mode=1, scale=None, perm=None, idx=None):
-    """Q, K, V [B,H,N,d] (float arrays). Returns O, lse (binary64) and the route idx."""
+def forward(Q, K, V, n_sink, block, ratio, pool_mode=1, scale=None, perm=None, idx=None, perm_k=None):
+    """Q, K, V [B,H,N,d] (float arrays). Returns O, lse (binary64) and the route idx.
+    perm: query partition (and output rows); perm_k: separate key partition of K and V (None:
+    keys and values reuse perm)."""
     Q, K, V = (np.asarray(x, np.float64) for x in (Q, K, V))
     B, H, N, d = Q.shape
     n_video = N - n_sink
@@ -83,8 +85,11 @@ def forward(Q, K, V, n_sink, block, ratio, pool_mode=1, scale=None, perm=None, i
         for h in range(H):
             q, k, v = Q[b, h].copy(), K[b, h].copy(), V[b, h].copy()
             if perm is not None:
-                pm = np.asarray(perm[b, h])
-                q[:n_video], k[:n_video], v[:n_video] = q[pm], k[pm], v[pm]
+                q[:n_video] = q[np.asarray(perm[b, h])]
+            pk = perm_k if perm_k is not None else perm
+            if pk is not None:
+                pkm = np.asarray(pk[b, h])
+                k[:n_video], v[:n_video] = k[pkm], v[pkm]
             pooled = pool_head(q, k, v, n_video, block, pool_mode, s)
             if idx is None:
                 _, sel = select_head(pooled["q_mean"], pooled["k_mean"], s, Ksel)

@@ -395,23 +395,32 @@ static float *permute_rows(const orc_params *p, const float *X, const int32_t *p
 }
 
 /*
- * The whole forward: [gather by perm] -> pool -> scores -> top-K -> attention -> [un-permute].
- *   perm     [B*H][N_v] or NULL;
+ * The whole forward: [gather by the partitions] -> pool -> scores -> top-K -> attention ->
+ * [un-permute].
+ *   perm     [B*H][N_v] or NULL: the query partition (query blocks, and the output rows);
+ *   perm_k   [B*H][N_v] or NULL: a separate key partition for keys and values (key blocks and
+ *            their summaries are then taken over the key leaves); NULL means keys and values reuse
+ *            perm (reblock_layout=q_reuse_k [SH3 "ワークフロー"]);
  *   idx_in   [B*H][M][K] route to use instead of the oracle's own selection, or NULL;
  *   O [B,H,N,d], lse [B,H,N] binary64 outputs; idx_out [B*H][M][K] (may be NULL).
  */
 void orc_forward(const orc_params *p, const float *Q, const float *K, const float *V,
-                 const int32_t *perm, const int32_t *idx_in, double *O, double *lse,
-                 int32_t *idx_out)
+                 const int32_t *perm, const int32_t *perm_k, const int32_t *idx_in, double *O,
+                 double *lse, int32_t *idx_out)
 {
     const int d = p->d, N = p->N, Nv = n_video(p), M = orc_num_blocks(p);
     const int Ksel = orc_topk_count(M, p->topk_ratio);
     const size_t BH = (size_t)p->B * p->H, row = (size_t)N * d;
     const float *Qp = Q, *Kp = K, *Vp = V;
     float *tq = NULL, *tk = NULL, *tv = NULL;
+    const int32_t *pk = perm_k ? perm_k : perm;
     if (perm) {
-        tq = permute_rows(p, Q, perm); tk = permute_rows(p, K, perm); tv = permute_rows(p, V, perm);
-        Qp = tq; Kp = tk; Vp = tv;
+        tq = permute_rows(p, Q, perm);
+        Qp = tq;
+    }
+    if (pk) {
+        tk = permute_rows(p, K, pk); tv = permute_rows(p, V, pk);
+        Kp = tk; Vp = tv;
     }
     double *qm = (double *)malloc(sizeof(double) * BH * M * d);
     double *km = (double *)malloc(sizeof(double) * BH * M * d);

@@ -10,7 +10,8 @@ textbook routine, an invariant, a hand-worked example or a brute-force formulati
   P-e  every query equal to the anchor: Reweight == dense, mean-pool != dense
   P-f  oracle == NumPy mask-matrix brute force (partial block, sinks, B > 1)
   P-g  selection == numpy.lexsort ranking
-  P-h  reblocked forward at full density == dense (after un-permuting)
+  P-h  reblocked forward at full density == dense (after un-permuting), with the keys reusing
+       the query partition or partitioned on their own
   P-i  partition invariants; partition == score-vector brute force
   P-j  blocks of identical keys/values: compressed term exact, forward == dense
   P-k  hand-worked two-block example (tests/golden/hand_worked_example.json)
@@ -224,6 +225,35 @@ def test_reblocked_forward_matches_brute_force(orc):
     Ob, lb, ib = brute.forward(Q, K, V, 4, 64, 0.2, 1, perm=perm)
     assert (idx == ib).all()
     assert np.abs(O - Ob).max() < 1e-12
+
+
+def test_separate_key_partition_full_density_is_dense(orc):
+    """Queries and keys each in their own partition (keys bisected under the queries' second
+    moment): at full density the result is still dense attention, whatever the two orders."""
+    Q, K, V = small(seed=23, nv=700, ns=6)
+    p = orc.params(Q, 6, 32, 1.0, 1)
+    perm_q = orc.reblock(p, Q, K)
+    perm_k = orc.reblock(p, K, Q)
+    assert not (perm_q == perm_k).all()
+    O, _, _ = orc.forward(p, Q, K, V, perm=perm_q, perm_k=perm_k)
+    assert np.abs(O - sdpa_dense(Q, K, V)).max() < 1e-12
+    # only the key side partitioned
+    O2, _, _ = orc.forward(p, Q, K, V, perm_k=perm_k)
+    assert np.abs(O2 - sdpa_dense(Q, K, V)).max() < 1e-12
+
+
+def test_separate_key_partition_matches_brute_force(orc):
+    Q, K, V = small(seed=24, nv=900, ns=4)
+    p = orc.params(Q, 4, 64, 0.2, 1)
+    perm_q, perm_k = orc.reblock(p, Q, K), orc.reblock(p, K, Q)
+    O, lse, idx = orc.forward(p, Q, K, V, perm=perm_q, perm_k=perm_k)
+    Ob, lb, ib = brute.forward(Q, K, V, 4, 64, 0.2, 1, perm=perm_q, perm_k=perm_k)
+    assert (idx == ib).all()
+    assert np.abs(O - Ob).max() < 1e-12 and np.abs(lse - lb).max() < 1e-12
+    # the key partition is the query partition with the roles of Q and K exchanged: the
+    # score-vector brute force of the keys against the queries
+    for h in range(2):
+        assert (perm_k[0, h] == brute.reblock_head(K[0, h], Q[0, h], 900, 64)).all()
 
 
 @pytest.mark.parametrize("nv,block,dtype", [(1000, 64, "fp32"), (1500, 128, "bf16"),
