@@ -187,15 +187,18 @@ def main():
     sel_ws = torch.empty(sa.workspace_size(p, 3), device="cuda", dtype=torch.uint8)
     packed = torch.empty(sa.workspace_size(p, 4), device="cuda", dtype=torch.uint8)
     stream = torch.cuda.current_stream()
-    perm = None
-    if wl.reblock:  # adaptive blocks: partition, gather, attend, scatter back (q_reuse_k)
+    perm = perm_k = None
+    if wl.reblock:  # adaptive blocks: partition, gather, attend, scatter back
         perm = torch.empty(B, H, wl.n_video, device="cuda", dtype=torch.int32)
+        # q_reuse_k: keys and values reuse the query partition; else keys get their own
+        perm_k = torch.empty_like(perm) if wl.key_partition else perm
         rb_ws = torch.empty(sa.workspace_size(p, 1), device="cuda", dtype=torch.uint8)
         Qp, Kp, Vp = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
     else:
         Qp, Kp, Vp = Q, K, V
 
-    stage_names = (["reblock", "gather"] if wl.reblock else []) + ["pool", "select", "pack", "attend"]
+    stage_names = ((["reblock"] + (["reblock_k"] if wl.key_partition else []) + ["gather"]) if wl.reblock else []) \
+        + ["pool", "select", "pack", "attend"]
 
     def step(ev=None):
         k = 1
@@ -203,8 +206,12 @@ def main():
             sa.spark_attn_reblock(p, Q, K, perm, rb_ws, stream)
             if ev: ev[k].record(stream)
             k += 1
-            for X, Y in ((Q, Qp), (K, Kp), (V, Vp)):
-                sa.spark_attn_gather_rows(p, X, perm, Y, stream)
+            if wl.key_partition:  # keys bisected under the queries' second moment
+                sa.spark_attn_reblock(p, K, Q, perm_k, rb_ws, stream)
+                if ev: ev[k].record(stream)
+                k += 1
+            for X, Y, pm in ((Q, Qp, perm), (K, Kp, perm_k), (V, Vp, perm_k)):
+                sa.spark_attn_gather_rows(p, X, pm, Y, stream)
             if ev: ev[k].record(stream)
             k += 1
         sa.spark_attn_pool(p, Qp, Kp, Vp, pooled["q_mean"], pooled["k_mean"], pooled["k_sum"], pooled["v_sum"],
@@ -242,11 +249,11 @@ def main():
     if not args.no_forward_check:
         ws = torch.empty(sa.workspace_size(p, 2 if wl.reblock else 0), device="cuda", dtype=torch.uint8)
         O2 = torch.empty_like(Q)
-        sa.spark_attn_forward(p, Q, K, V, perm, O2, None, None, ws, stream)
+        sa.spark_attn_forward_kv(p, Q, K, V, perm, perm_k, O2, None, None, ws, stream)
         fe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         fe[0].record(stream)
         for _ in range(3):
-            sa.spark_attn_forward(p, Q, K, V, perm, O2, None, None, ws, stream)
+            sa.spark_attn_forward_kv(p, Q, K, V, perm, perm_k, O2, None, None, ws, stream)
         fe[1].record(stream)
         torch.cuda.synchronize()
         ms_forward_call = round(fe[0].elapsed_time(fe[1]) / 3, 4)
@@ -283,6 +290,8 @@ def main():
             "workload": wl.name, "description": wl.description, "B": B, "H": H, "N_video": wl.n_video,
             "N_sink": wl.n_sink, "d": d, "block": wl.block, "topk_ratio": ratio, "M": M, "K": Kk,
             "compressed_branch": "anchor-weighted summary + log-mass bias", "parallelism": "none (1 GPU)",
+            "layout": ("separate key partition" if wl.key_partition else "q_reuse_k") if wl.reblock
+            else "token order",
         },
         "stages_ms": dict({n: round(v, 4) for n, v in stage_ms.items()},
                           spark_attn_forward_call=ms_forward_call),
@@ -304,13 +313,13 @@ def main():
         log("cpu baseline (oracle) ...")
         del Q, K, V, O, O2, ws, sel_ws, packed, Qp, Kp, Vp
         if wl.reblock:
-            perm_h = perm.cpu().numpy()
-            del perm, rb_ws
-            # the oracle runs on the partitioned layout the route refers to
-            for X in (Qh, Kh, Vh):
+            perm_h, perm_kh = perm.cpu().numpy(), perm_k.cpu().numpy()
+            del perm, perm_k, rb_ws
+            # the oracle runs on the partitioned layouts the route refers to
+            for X, ph in ((Qh, perm_h), (Kh, perm_kh), (Vh, perm_kh)):
                 for b_ in range(B):
                     for h_ in range(H):
-                        X[b_, h_, :wl.n_video] = X[b_, h_][perm_h[b_, h_]]
+                        X[b_, h_, :wl.n_video] = X[b_, h_][ph[b_, h_]]
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(wl, ratio, Qh, Kh, Vh, gidx, F_sel, args.cpu_sample_blocks)
     print(json.dumps(out), flush=True)

@@ -39,7 +39,8 @@ class SparkAttnError(RuntimeError):
 EXPORTS = (
     "spark_attn_num_blocks", "spark_attn_topk_count", "spark_attn_workspace_size",
     "spark_attn_status_str", "spark_attn_pool", "spark_attn_select", "spark_attn_pack",
-    "spark_attn_attend", "spark_attn_forward", "spark_attn_reblock", "spark_attn_gather_rows",
+    "spark_attn_attend", "spark_attn_forward", "spark_attn_forward_kv", "spark_attn_reblock",
+    "spark_attn_gather_rows",
 )
 
 _lib = None
@@ -65,6 +66,7 @@ def lib():
             "spark_attn_pack": ([P, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "spark_attn_attend": ([P, vp, vp, sz, vp, vp, vp, vp, vp], ctypes.c_int),
             "spark_attn_forward": ([P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "spark_attn_forward_kv": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "spark_attn_reblock": ([P, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "spark_attn_gather_rows": ([P, vp, vp, vp, vp], ctypes.c_int),
         }
@@ -164,6 +166,13 @@ def spark_attn_forward(p, Q, K, V, perm, O, lse, idx_out, workspace, stream=None
         _ptr(idx_out), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def spark_attn_forward_kv(p, Q, K, V, perm_q, perm_k, O, lse, idx_out, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("spark_attn_forward_kv", lib().spark_attn_forward_kv(
+        ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(perm_q), _ptr(perm_k), _ptr(O), _ptr(lse),
+        _ptr(idx_out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 def spark_attn_reblock(p, Q, K, perm, workspace, stream=None):
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("spark_attn_reblock", lib().spark_attn_reblock(
@@ -220,8 +229,10 @@ def attend(Q, K, V, pooled, idx, n_sink, block, topk_ratio, perm=None, scale=0.0
 
 
 def forward(Q, K, V, n_sink, block, topk_ratio, pool_mode=POOL_REWEIGHT, perm=None, scale=0.0,
-            return_lse=False, return_idx=False, workspace=None, stream=None):
-    """Returns O (and lse [B,H,N] fp32, idx [B,H,M,K] int32 when asked)."""
+            return_lse=False, return_idx=False, workspace=None, stream=None, perm_k=None):
+    """Returns O (and lse [B,H,N] fp32, idx [B,H,M,K] int32 when asked).  perm: the partition of
+    the queries (and of keys and values unless perm_k is given); perm_k: a separate key
+    partition (spark_attn_forward_kv)."""
     p = params(Q, n_sink, block, topk_ratio, pool_mode, scale)
     M = num_blocks(p)
     Kk = topk_count(M, topk_ratio)
@@ -230,9 +241,13 @@ def forward(Q, K, V, n_sink, block, topk_ratio, pool_mode=POOL_REWEIGHT, perm=No
     lse = torch.empty(B, H, N, device=Q.device, dtype=torch.float32) if return_lse else None
     idx = torch.empty(B, H, M, Kk, device=Q.device, dtype=torch.int32) if return_idx else None
     if workspace is None:
-        workspace = torch.empty(workspace_size(p, 2 if perm is not None else 0), device=Q.device,
+        permuted = perm is not None or perm_k is not None
+        workspace = torch.empty(workspace_size(p, 2 if permuted else 0), device=Q.device,
                                 dtype=torch.uint8)
-    spark_attn_forward(p, Q, K, V, perm, O, lse, idx, workspace, stream)
+    if perm_k is None:
+        spark_attn_forward(p, Q, K, V, perm, O, lse, idx, workspace, stream)
+    else:
+        spark_attn_forward_kv(p, Q, K, V, perm, perm_k, O, lse, idx, workspace, stream)
     res = (O,)
     if return_lse:
         res += (lse,)

@@ -185,23 +185,26 @@ int spark_attn_gather_rows(const spark_attn_params* p, const void* X, const int3
     return launch_status();
 }
 
-int spark_attn_forward(const spark_attn_params* p, const void* Q, const void* K, const void* V, const int32_t* perm,
-                       void* O, float* lse, int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream) {
+int spark_attn_forward_kv(const spark_attn_params* p, const void* Q, const void* K, const void* V,
+                          const int32_t* perm_q, const int32_t* perm_k, void* O, float* lse, int32_t* idx_out,
+                          void* workspace, size_t ws_bytes, void* stream) {
     LaunchCtx L;
     int s = make_ctx(p, stream, &L);
     if (s < 0) return s;
     if (!Q || !K || !V || !O) return SPARK_ATTN_INVALID_ARGUMENT;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(workspace))
         return SPARK_ATTN_MISALIGNED;
-    const FwdWorkspace w = fwd_layout(L, perm != nullptr);
+    const FwdWorkspace w = fwd_layout(L, perm_q != nullptr || perm_k != nullptr);
     if (!workspace || ws_bytes < w.total) return SPARK_ATTN_WORKSPACE_TOO_SMALL;
     char* ws = (char*)workspace;
     const void *q = Q, *k = K, *v = V;
-    if (perm) {
-        launch_gather_rows(L, Q, perm, ws + w.qp);
-        launch_gather_rows(L, K, perm, ws + w.kp);
-        launch_gather_rows(L, V, perm, ws + w.vp);
+    if (perm_q) {
+        launch_gather_rows(L, Q, perm_q, ws + w.qp);
         q = ws + w.qp;
+    }
+    if (perm_k) {
+        launch_gather_rows(L, K, perm_k, ws + w.kp);
+        launch_gather_rows(L, V, perm_k, ws + w.vp);
         k = ws + w.kp;
         v = ws + w.vp;
     }
@@ -215,8 +218,13 @@ int spark_attn_forward(const spark_attn_params* p, const void* Q, const void* K,
     launch_pool(L, q, k, v, q_mean, k_mean, k_sum, v_sum, bias, anchor);
     launch_select(L, q_mean, k_mean, idx, (float*)(ws + w.scores));
     launch_pack(L, k, v, k_sum, v_sum, bias, ws + w.packed);
-    launch_attend(L, q, ws + w.packed, idx, perm, O, lse);
+    launch_attend(L, q, ws + w.packed, idx, perm_q, O, lse);
     return launch_status();
+}
+
+int spark_attn_forward(const spark_attn_params* p, const void* Q, const void* K, const void* V, const int32_t* perm,
+                       void* O, float* lse, int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream) {
+    return spark_attn_forward_kv(p, Q, K, V, perm, perm, O, lse, idx_out, workspace, ws_bytes, stream);
 }
 
 int spark_attn_reblock(const spark_attn_params* p, const void* Q, const void* K, int32_t* perm, void* workspace,

@@ -82,7 +82,8 @@ int spark_attn_num_blocks(const spark_attn_params *p);
 int spark_attn_topk_count(int M, float ratio);
 
 /* Bytes of device workspace a call needs, or 0 for invalid params:
- *   what = 0: spark_attn_forward without perm;  what = 2: spark_attn_forward with perm;
+ *   what = 0: spark_attn_forward without perm;  what = 2: spark_attn_forward with perm (or
+ *             spark_attn_forward_kv with either partition);
  *   what = 1: spark_attn_reblock;               what = 3: spark_attn_select without `scores`;
  *   what = 4: the packed key/value tiles of spark_attn_pack / spark_attn_attend. */
 size_t spark_attn_workspace_size(const spark_attn_params *p, int what);
@@ -161,6 +162,24 @@ int spark_attn_attend(const spark_attn_params *p, const void *Q, const void *pac
 int spark_attn_forward(const spark_attn_params *p, const void *Q, const void *K, const void *V,
                        const int32_t *perm, void *O, float *lse, int32_t *idx_out,
                        void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * The forward with a separate key partition (Spark-H3 page, Spark-Reblock bullet: each side is
+ * partitioned in the metric of the opposite side's second moment; "ワークフロー":
+ * reblock_layout=q_reuse_k is the layout where keys reuse the query partition, this call is the
+ * other one).  Query blocks and the output rows follow perm_q; key blocks, their compressed
+ * summaries and the values follow perm_k.  A key partition is spark_attn_reblock called with
+ * the roles exchanged: (p, K, Q, perm_k, ...), keys bisected under Sigma_Q = Q^T Q / N_v.
+ * In:  Q, K, V [B,H,N,d] in p->dtype; perm_q, perm_k [B,H,N_v] int32, each NULL or a permutation
+ *      of [0,N_v) per (batch, head) (row q of the block layout holds token perm[q]).
+ * Out: as spark_attn_forward (O and lse in the original token order, idx_out in the block
+ *      layouts: query block I of the perm_q order routed to key blocks of the perm_k order).
+ * workspace: at least spark_attn_workspace_size(p, (perm_q || perm_k) ? 2 : 0) bytes.
+ * spark_attn_forward(p, Q, K, V, perm, ...) equals spark_attn_forward_kv(p, Q, K, V, perm, perm, ...).
+ */
+int spark_attn_forward_kv(const spark_attn_params *p, const void *Q, const void *K, const void *V,
+                          const int32_t *perm_q, const int32_t *perm_k, void *O, float *lse,
+                          int32_t *idx_out, void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * Spark-Reblock partition (Spark-H3 page, "Spark-Attnが変えるもの", Spark-Reblock bullet) of the

@@ -91,6 +91,8 @@ def test_invalid_params_rejected_before_launch(kw, status):
     assert L.spark_attn_attend(ctypes.byref(p), fake, fake, 1 << 40, fake, None, fake, None, None) == status
     assert L.spark_attn_forward(ctypes.byref(p), fake, fake, fake, None, fake, None, None, fake,
                                 1 << 40, None) == status
+    assert L.spark_attn_forward_kv(ctypes.byref(p), fake, fake, fake, None, fake, fake, None, None, fake,
+                                   1 << 40, None) == status
     assert L.spark_attn_reblock(ctypes.byref(p), fake, fake, fake, fake, 1 << 40, None) == status
     assert L.spark_attn_gather_rows(ctypes.byref(p), fake, fake, ctypes.c_void_p(0x200000), None) == status
 
@@ -115,6 +117,8 @@ def test_null_and_misaligned_pointers_rejected():
     assert L.spark_attn_pack(ctypes.byref(p), a, a, a, a, a, a, 10, None) == WS_SMALL
     assert L.spark_attn_forward(ctypes.byref(p), a, a, a, None, None, None, None, a, 1 << 40, None) == INVALID
     assert L.spark_attn_forward(ctypes.byref(p), a, bad, a, None, a, None, None, a, 1 << 40, None) == MISALIGNED
+    assert L.spark_attn_forward_kv(ctypes.byref(p), a, a, None, None, None, a, None, None, a, 1 << 40, None) == INVALID
+    assert L.spark_attn_forward_kv(ctypes.byref(p), a, a, a, None, None, bad, None, None, a, 1 << 40, None) == MISALIGNED
     assert L.spark_attn_gather_rows(ctypes.byref(p), a, a, a, None) == INVALID  # in place
     assert L.spark_attn_gather_rows(ctypes.byref(p), a, None, ctypes.c_void_p(0x200000), None) == INVALID
     assert L.spark_attn_reblock(ctypes.byref(p), a, a, None, a, 1 << 40, None) == INVALID
@@ -137,6 +141,10 @@ def test_workspace_sizes_and_too_small():
     assert L.spark_attn_forward(ctypes.byref(p), a, a, a, None, a, None, None, a, w0 - 1, None) == WS_SMALL
     assert L.spark_attn_forward(ctypes.byref(p), a, a, a, a, a, None, None, a, w2 - 1, None) == WS_SMALL
     assert L.spark_attn_forward(ctypes.byref(p), a, a, a, None, a, None, None, None, w0, None) == WS_SMALL
+    # a separate key partition alone needs the permuted-layout workspace too
+    assert L.spark_attn_forward_kv(ctypes.byref(p), a, a, a, None, a, a, None, None, a, w2 - 1, None) == WS_SMALL
+    assert L.spark_attn_forward_kv(ctypes.byref(p), a, a, a, a, None, a, None, None, a, w2 - 1, None) == WS_SMALL
+    assert L.spark_attn_forward_kv(ctypes.byref(p), a, a, a, None, None, a, None, None, a, w0 - 1, None) == WS_SMALL
 
 
 def test_status_strings():

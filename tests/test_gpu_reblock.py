@@ -132,3 +132,106 @@ def test_reblock_720p_bit_exact_and_forward(orc):
     el = max_abs(np.concatenate(gl), np.concatenate(rl))
     print(f"reblocked forward: rel-L2 {e2:.3e} max-abs {ea:.3e} lse {el:.3e}")
     assert e2 <= FWD_REL_L2 and ea <= FWD_MAX_ABS and el <= FWD_MAX_ABS
+
+
+# ---- separate key partition: keys bisected under the queries' second moment (the same
+# partitioner with the roles of Q and K exchanged), keys and values in their own order
+KV_CASES = [
+    ("bf16-d128-b128", 1, 3, 11 * 128 + 37, 5, 128, 128, "bf16"),
+    ("bf16-d64-b64", 2, 2, 37 * 64 + 1, 0, 64, 64, "bf16"),
+    ("fp32-d64-b128", 1, 2, 9 * 128 + 100, 7, 64, 128, "fp32"),
+]
+
+
+@pytest.mark.parametrize("case", KV_CASES, ids=[c[0] for c in KV_CASES])
+def test_key_partition_bit_exact_and_forward(orc, case):
+    name, B, H, nv, ns, d, b, dt = case
+    Q, K, V = W.gaussian_qkv(B, H, nv, ns, d, seed=nv + 7, dtype=dt)
+    note(f"key partition {name}")
+    Qd, Kd, Vd = dev(Q, dt), dev(K, dt), dev(V, dt)
+    perm_q = sa.reblock(Qd, Kd, ns, b)
+    perm_k = sa.reblock(Kd, Qd, ns, b)
+    O, lse, idx = sa.forward(Qd, Kd, Vd, ns, b, 0.2, perm=perm_q, perm_k=perm_k, return_lse=True,
+                             return_idx=True)
+    torch.cuda.synchronize()
+    p = orc.params(Q, ns, b, 0.2, 1)
+    rq, rk = orc.reblock(p, Q, K), orc.reblock(p, K, Q)
+    assert (perm_q.cpu().numpy() == rq).all()
+    assert (perm_k.cpu().numpy() == rk).all()
+    # route validated against the oracle's scores in the two block layouts
+    Qp, Kp, Vp = Q.copy(), K.copy(), V.copy()
+    for bb in range(B):
+        for h in range(H):
+            Qp[bb, h, :nv] = Q[bb, h][rq[bb, h]]
+            Kp[bb, h, :nv], Vp[bb, h, :nv] = K[bb, h][rk[bb, h]], V[bb, h][rk[bb, h]]
+    pooled = orc.pool(p, Qp, Kp, Vp)
+    gidx = idx.cpu().numpy()
+    bad, _ = check_selection(gidx, orc.scores(p, pooled["q_mean"], pooled["k_mean"]))
+    assert bad == 0
+    Oref, lref, _ = orc.forward(p, Q, K, V, perm=rq, perm_k=rk, idx=gidx)
+    Og = O.float().cpu().numpy()
+    e2, ea, el = rel_l2(Og, Oref), max_abs(Og, Oref), max_abs(lse.cpu().numpy(), lref)
+    print(f"key-partitioned forward: rel-L2 {e2:.3e} max-abs {ea:.3e} lse {el:.3e}")
+    assert e2 <= FWD_REL_L2 and ea <= FWD_MAX_ABS and el <= FWD_MAX_ABS
+
+
+def test_key_partition_alone_equals_forward_kv_with_identity(orc):
+    """Only the keys partitioned (no query partition): spark_attn_forward_kv with perm_q = NULL."""
+    Q, K, V = W.gaussian_qkv(1, 2, 21 * 64 + 5, 3, 64, seed=41, dtype="bf16")
+    ns, b = 3, 64
+    Qd, Kd, Vd = dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16")
+    note("key partition only")
+    perm_k = sa.reblock(Kd, Qd, ns, b)
+    O, idx = sa.forward(Qd, Kd, Vd, ns, b, 0.25, perm_k=perm_k, return_idx=True)
+    torch.cuda.synchronize()
+    p = orc.params(Q, ns, b, 0.25, 1)
+    rk = perm_k.cpu().numpy()
+    gidx = idx.cpu().numpy()
+    Oref, _, _ = orc.forward(p, Q, K, V, perm_k=rk, idx=gidx)
+    Og = O.float().cpu().numpy()
+    assert rel_l2(Og, Oref) <= FWD_REL_L2 and max_abs(Og, Oref) <= FWD_MAX_ABS
+
+
+def test_key_partition_720p(orc):
+    """The 720p-like latent: the key partition of 3 heads bit for bit, and the doubly
+    partitioned forward on sampled query blocks."""
+    wl = W.WORKLOADS["reblock720p"]
+    Q, K, V = W.make_qkv(wl)
+    note("key partition 720p")
+    Qd, Kd, Vd = dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16")
+    perm_q = sa.reblock(Qd, Kd, wl.n_sink, wl.block)
+    perm_k = sa.reblock(Kd, Qd, wl.n_sink, wl.block)
+    O, lse, idx = sa.forward(Qd, Kd, Vd, wl.n_sink, wl.block, 0.1, perm=perm_q, perm_k=perm_k,
+                             return_lse=True, return_idx=True)
+    torch.cuda.synchronize()
+    heads = [0, 11, 23]
+    Qs, Ks, Vs = (np.ascontiguousarray(x[:, heads]) for x in (Q, K, V))
+    p = orc.params(Qs, wl.n_sink, wl.block, 0.1, 1)
+    rq, rk = orc.reblock(p, Qs, Ks), orc.reblock(p, Ks, Qs)
+    assert (perm_q.cpu().numpy()[:, heads] == rq).all()
+    assert (perm_k.cpu().numpy()[:, heads] == rk).all()
+    nv = wl.n_video
+    Qp, Kp, Vp = Qs.copy(), Ks.copy(), Vs.copy()
+    for h in range(len(heads)):
+        Qp[0, h, :nv] = Qs[0, h][rq[0, h]]
+        Kp[0, h, :nv], Vp[0, h, :nv] = Ks[0, h][rk[0, h]], Vs[0, h][rk[0, h]]
+    pooled = orc.pool(p, Qp, Kp, Vp)
+    gidx = idx.cpu().numpy()[:, heads]
+    bad, _ = check_selection(gidx, orc.scores(p, pooled["q_mean"], pooled["k_mean"]))
+    assert bad == 0
+    M = gidx.shape[2]
+    rng = np.random.default_rng(4)
+    qb = np.array([(h, I) for h in range(len(heads)) for I in rng.choice(M, 4, replace=False)] + [(0, M - 1)])
+    Os, ls = orc.attend_blocks(p, Qp, Kp, Vp, pooled, gidx, qb)
+    Og, lg = O.float().cpu().numpy()[:, heads], lse.cpu().numpy()[:, heads]
+    g_rows, r_rows, gl, rl = [], [], [], []
+    for n, (h, I) in enumerate(qb):
+        lo, hi = I * wl.block, min(nv, (I + 1) * wl.block)
+        rows = rq[0, h, lo:hi]
+        g_rows.append(Og[0, h, rows]); r_rows.append(Os[n, :hi - lo])
+        gl.append(lg[0, h, rows]); rl.append(ls[n, :hi - lo])
+    g_rows, r_rows = np.concatenate(g_rows), np.concatenate(r_rows)
+    e2, ea = rel_l2(g_rows, r_rows), max_abs(g_rows, r_rows)
+    el = max_abs(np.concatenate(gl), np.concatenate(rl))
+    print(f"doubly partitioned forward: rel-L2 {e2:.3e} max-abs {ea:.3e} lse {el:.3e}")
+    assert e2 <= FWD_REL_L2 and ea <= FWD_MAX_ABS and el <= FWD_MAX_ABS

@@ -49,6 +49,7 @@ class Workload:
     dtype: str = "bf16"  # "bf16" or "fp32"
     pool_modes: tuple = (1,)  # 0 = plain mean pool, 1 = anchor-weighted summary + log-mass bias
     reblock: bool = False
+    key_partition: bool = False  # with reblock: keys and values in their own partition
     description: str = ""
     extra: dict = field(default_factory=dict)
 
@@ -86,6 +87,11 @@ WORKLOADS = {
         "reblock720p", 5, B=1, H=24, d=128, grid=(21, 45, 80), n_sink=512, block=128,
         ratios=(0.1,), reblock=True,
         description="720p-like latent with adaptive blocks (q_reuse_k layout)"),
+    "reblockkv720p": Workload(
+        "reblockkv720p", 6, B=1, H=24, d=128, grid=(21, 45, 80), n_sink=512, block=128,
+        ratios=(0.1,), reblock=True, key_partition=True,
+        description="720p-like latent with adaptive blocks, queries and keys each partitioned under "
+                    "the other side's second moment"),
 }
 
 
