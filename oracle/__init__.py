@@ -63,10 +63,13 @@ def lib():
         L.orc_attend_blocks.argtypes = [P, f32, f32, f32, f64, f64, f64, i32, ctypes.c_int, i32,
                                         ctypes.c_int, f64, f64]
         L.orc_forward.argtypes = [P, f32, f32, f32, vp, vp, vp, f64, f64, vp]
+        L.orc_select_tau.argtypes = [P, ctypes.c_double, f64, i32, i32, vp]
+        L.orc_forward_tau.argtypes = [P, ctypes.c_double, f32, f32, f32, vp, vp, f64, f64, vp, vp]
         L.orc_reblock_metric.argtypes = [P, f32, f32, f64, f64]
         L.orc_reblock.argtypes = [P, f32, f32, i32]
         for fn in (L.orc_pool, L.orc_scores, L.orc_select, L.orc_dense, L.orc_attend_blocks,
-                   L.orc_forward, L.orc_reblock_metric, L.orc_reblock):
+                   L.orc_forward, L.orc_select_tau, L.orc_forward_tau, L.orc_reblock_metric,
+                   L.orc_reblock):
             fn.restype = None
         _lib = L
     return _lib
@@ -148,6 +151,41 @@ def forward(p: Params, Q, K, V, perm=None, idx=None, perm_k=None):
     lib().orc_forward(ctypes.byref(p), _f32(Q), _f32(K), _f32(V), ptr(perm, np.int32),
                       ptr(perm_k, np.int32), ptr(idx, np.int32), O, lse, idx_out.ctypes.data)
     return O, lse, idx_out
+
+
+def select_tau(p: Params, tau, S):
+    """Adaptive-tau routes from block scores S [B,H,M,M]: (idx [B,H,M,M] with row I's kept blocks
+    ascending in its first counts[I] entries (the rest -1), counts [B,H,M], stats [B,H,2] =
+    (mu, sigma))."""
+    M = num_blocks(p)
+    idx = np.full((p.B, p.H, M, M), -1, np.int32)
+    counts = np.empty((p.B, p.H, M), np.int32)
+    stats = np.empty((p.B, p.H, 2))
+    S = np.ascontiguousarray(S, dtype=np.float64)
+    lib().orc_select_tau(ctypes.byref(p), float(tau), S, idx, counts, stats.ctypes.data)
+    return idx, counts, stats
+
+
+def forward_tau(p: Params, tau, Q, K, V, idx=None, counts=None):
+    """Forward with adaptive-tau routes.  Returns (O, lse, idx [B,H,M,M], counts [B,H,M]); idx and
+    counts, when given, replace the oracle's own selection."""
+    M = num_blocks(p)
+    O = np.empty((p.B, p.H, p.N, p.d))
+    lse = np.empty((p.B, p.H, p.N))
+    idx_out = np.full((p.B, p.H, M, M), -1, np.int32)
+    cnt_out = np.empty((p.B, p.H, M), np.int32)
+    keep = []
+
+    def ptr(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a, dtype=np.int32)
+        keep.append(a)
+        return a.ctypes.data
+
+    lib().orc_forward_tau(ctypes.byref(p), float(tau), _f32(Q), _f32(K), _f32(V), ptr(idx), ptr(counts),
+                          O, lse, idx_out.ctypes.data, cnt_out.ctypes.data)
+    return O, lse, idx_out, cnt_out
 
 
 def attend_blocks(p: Params, Q, K, V, pooled, idx, qblocks):

@@ -66,10 +66,19 @@ def select_head(q_mean, k_mean, s, K):
     return S, idx
 
 
-def forward(Q, K, V, n_sink, block, ratio, pool_mode=1, scale=None, perm=None, idx=None, perm_k=None):
+def select_tau_head(S, tau):
+    """Adaptive-tau route of one head from its block scores: kept[I, J] = S_IJ > mean + tau * std
+    (NumPy's mean and population standard deviation over all entries)."""
+    S = np.asarray(S, np.float64)
+    return S > S.mean() + tau * S.std()
+
+
+def forward(Q, K, V, n_sink, block, ratio, pool_mode=1, scale=None, perm=None, idx=None, perm_k=None,
+            tau=None):
     """Q, K, V [B,H,N,d] (float arrays). Returns O, lse (binary64) and the route idx.
     perm: query partition (and output rows); perm_k: separate key partition of K and V (None:
-    keys and values reuse perm)."""
+    keys and values reuse perm).  tau: adaptive-tau routes instead of top-K (the returned idx is
+    then the boolean kept matrix [B,H,M,M])."""
     Q, K, V = (np.asarray(x, np.float64) for x in (Q, K, V))
     B, H, N, d = Q.shape
     n_video = N - n_sink
@@ -79,7 +88,7 @@ def forward(Q, K, V, n_sink, block, ratio, pool_mode=1, scale=None, perm=None, i
     Ksel = budget(M, ratio)
     O = np.empty((B, H, N, d))
     LSE = np.empty((B, H, N))
-    IDX = np.empty((B, H, M, Ksel), np.int64)
+    IDX = np.empty((B, H, M, Ksel), np.int64) if tau is None else np.empty((B, H, M, M), bool)
     blk = np.repeat(np.arange(M), sizes)  # video token -> block
     for b in range(B):
         for h in range(H):
@@ -91,13 +100,17 @@ def forward(Q, K, V, n_sink, block, ratio, pool_mode=1, scale=None, perm=None, i
                 pkm = np.asarray(pk[b, h])
                 k[:n_video], v[:n_video] = k[pkm], v[pkm]
             pooled = pool_head(q, k, v, n_video, block, pool_mode, s)
-            if idx is None:
-                _, sel = select_head(pooled["q_mean"], pooled["k_mean"], s, Ksel)
+            if tau is not None:
+                chosen = select_tau_head(s * (pooled["q_mean"] @ pooled["k_mean"].T), tau)
+                IDX[b, h] = chosen
             else:
-                sel = np.asarray(idx[b, h])
-            IDX[b, h] = sel
-            chosen = np.zeros((M, M), bool)  # chosen[I, J]
-            chosen[np.repeat(np.arange(M), Ksel), sel.reshape(-1)] = True
+                if idx is None:
+                    _, sel = select_head(pooled["q_mean"], pooled["k_mean"], s, Ksel)
+                else:
+                    sel = np.asarray(idx[b, h])
+                IDX[b, h] = sel
+                chosen = np.zeros((M, M), bool)  # chosen[I, J]
+                chosen[np.repeat(np.arange(M), Ksel), sel.reshape(-1)] = True
             logits = np.concatenate([s * (q @ k.T), s * (q @ pooled["k_sum"].T) + pooled["bias"]],
                                     axis=1)
             values = np.concatenate([v, pooled["v_sum"]], axis=0)

@@ -470,6 +470,91 @@ void orc_forward(const orc_params *p, const float *Q, const float *K, const floa
 }
 
 /* ------------------------------------------------------------------------------------------
+ * Adaptive-tau selection [core node page, "ブロックスパースアテンション", Sol-Attn bullet]: a per-head
+ * threshold placed in units of the spread of the head's score distribution, with no trained
+ * weights.  Reading: over all M x M block scores S_IJ of a (batch, head), mu = their mean and
+ * sigma = their population standard deviation (two passes); query block I keeps every key block J
+ * with S_IJ > mu + tau * sigma (strictly), so a row may keep any number of blocks, none included
+ * (its queries then see the compressed branch and the sinks only).  For Gaussian scores the kept
+ * fraction is the normal tail: tau 1.0 / 1.5 / 2.0 keep about 15.9% / 6.7% / 2.3% of the blocks.
+ *   S        [B*H][M][M] block scores (orc_scores);
+ *   idx      [B*H][M][M]: row I lists its kept blocks ascending in its first counts[I] entries;
+ *   counts   [B*H][M];  stats [B*H][2] = (mu, sigma), may be NULL.
+ */
+void orc_select_tau(const orc_params *p, double tau, const double *S, int32_t *idx, int32_t *counts,
+                    double *stats)
+{
+    const int M = orc_num_blocks(p);
+    const size_t MM = (size_t)M * M;
+#pragma omp parallel for schedule(static)
+    for (int bh = 0; bh < p->B * p->H; ++bh) {
+        const double *Sh = S + (size_t)bh * MM;
+        double sum = 0.0;
+        for (size_t e = 0; e < MM; ++e) sum += Sh[e];
+        const double mu = sum / (double)MM;
+        double sq = 0.0;
+        for (size_t e = 0; e < MM; ++e) sq += (Sh[e] - mu) * (Sh[e] - mu);
+        const double sigma = sqrt(sq / (double)MM);
+        const double thr = mu + tau * sigma;
+        if (stats) { stats[2 * bh] = mu; stats[2 * bh + 1] = sigma; }
+        for (int I = 0; I < M; ++I) {
+            int32_t *row = idx + ((size_t)bh * M + I) * M;
+            int c = 0;
+            for (int J = 0; J < M; ++J)
+                if (Sh[(size_t)I * M + J] > thr) row[c++] = J;
+            counts[(size_t)bh * M + I] = c;
+        }
+    }
+}
+
+/*
+ * The forward with adaptive-tau routes: pool -> scores -> tau selection -> attention.  Each video
+ * query block attends exactly to its counts[I] kept blocks, to every sink, and to one pseudo-key
+ * per other block, in one softmax; sink queries are dense.
+ *   idx_in / counts_in: a route to use instead of the oracle's own selection, or NULL;
+ *   idx_out [B*H][M][M], counts_out [B*H][M] (may be NULL).
+ */
+void orc_forward_tau(const orc_params *p, double tau, const float *Q, const float *K, const float *V,
+                     const int32_t *idx_in, const int32_t *counts_in, double *O, double *lse,
+                     int32_t *idx_out, int32_t *counts_out)
+{
+    const int d = p->d, N = p->N, Nv = n_video(p), M = orc_num_blocks(p);
+    const size_t BH = (size_t)p->B * p->H, row = (size_t)N * d;
+    double *qm = (double *)malloc(sizeof(double) * BH * M * d);
+    double *km = (double *)malloc(sizeof(double) * BH * M * d);
+    double *ks = (double *)malloc(sizeof(double) * BH * M * d);
+    double *vs = (double *)malloc(sizeof(double) * BH * M * d);
+    double *bias = (double *)malloc(sizeof(double) * BH * M);
+    double *anc = (double *)malloc(sizeof(double) * BH * d);
+    orc_pool(p, Q, K, V, qm, km, ks, vs, bias, anc);
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * BH * M * M);
+    int32_t *cnt = (int32_t *)malloc(sizeof(int32_t) * BH * M);
+    if (idx_in && counts_in) {
+        memcpy(idx, idx_in, sizeof(int32_t) * BH * M * M);
+        memcpy(cnt, counts_in, sizeof(int32_t) * BH * M);
+    } else {
+        double *S = (double *)malloc(sizeof(double) * BH * M * M);
+        orc_scores(p, qm, km, S);
+        orc_select_tau(p, tau, S, idx, cnt, NULL);
+        free(S);
+    }
+    if (idx_out) memcpy(idx_out, idx, sizeof(int32_t) * BH * M * M);
+    if (counts_out) memcpy(counts_out, cnt, sizeof(int32_t) * BH * M);
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int bh = 0; bh < (int)BH; ++bh)
+        for (int I = 0; I < M + p->n_sink; ++I) {
+            const float *Qh = Q + bh * row, *Kh = K + bh * row, *Vh = V + bh * row;
+            if (I < M)
+                attend_video_block(p, Qh, Kh, Vh, ks + (size_t)bh * M * d, vs + (size_t)bh * M * d,
+                                   bias + (size_t)bh * M, idx + ((size_t)bh * M + I) * M,
+                                   cnt[(size_t)bh * M + I], I, O + bh * row, lse + (size_t)bh * N);
+            else
+                attend_dense_row(p, Qh, Kh, Vh, Nv + (I - M), O + bh * row, lse + (size_t)bh * N);
+        }
+    free(idx); free(cnt); free(qm); free(km); free(ks); free(vs); free(bias); free(anc);
+}
+
+/* ------------------------------------------------------------------------------------------
  * Spark-Reblock [SH3, Reblock bullet]: two queries are alike when their score patterns against
  * the keys are alike, measured by the cosine under the metric of the keys' second moment; a
  * hierarchical partitioner keeps splitting groups until every leaf holds the block size, in

@@ -15,6 +15,8 @@ textbook routine, an invariant, a hand-worked example or a brute-force formulati
   P-i  partition invariants; partition == score-vector brute force
   P-j  blocks of identical keys/values: compressed term exact, forward == dense
   P-k  hand-worked two-block example (tests/golden/hand_worked_example.json)
+  P-l  adaptive-tau selection: the normal tail for Gaussian scores, NumPy mean/std threshold,
+       keep-all == dense, forward == brute force (moderate, all kept, none kept)
 """
 import json
 import math
@@ -377,3 +379,58 @@ def test_batches_and_heads_are_independent(orc):
     p1 = orc.params(Q[1:2, 2:3], 3, 64, 0.2, 1)
     O1, l1, i1 = orc.forward(p1, Q[1:2, 2:3], K[1:2, 2:3], V[1:2, 2:3])
     assert (O1[0, 0] == O[1, 2]).all() and (i1[0, 0] == idx[1, 2]).all()
+
+
+# ---------------------------------------------------------------- P-l adaptive-tau selection
+def _normal_tail(t):
+    return 0.5 * math.erfc(t / math.sqrt(2.0))
+
+
+@pytest.mark.parametrize("tau", [1.0, 1.5, 2.0])
+def test_tau_keeps_the_normal_tail_of_gaussian_scores(orc, tau):
+    """For normally distributed block scores the kept fraction is the normal tail beyond tau
+    (15.9% / 6.7% / 2.3%, the page's ~16 / ~7 / ~2.7%)."""
+    Q, K, V = small(seed=61, H=2, nv=600 * 16, ns=0, d=16)
+    p = orc.params(Q, 0, 16)
+    M = orc.num_blocks(p)
+    S = np.random.default_rng(62).standard_normal((1, 2, M, M)) * 3.0 + 0.7  # any mean and spread
+    _, counts, stats = orc.select_tau(p, tau, S)
+    frac = counts.sum(axis=2) / (M * M)
+    assert np.abs(frac - _normal_tail(tau)).max() < 3e-3, (frac, _normal_tail(tau))
+    assert np.allclose(stats[..., 0], S.mean(axis=(2, 3)), rtol=0, atol=1e-12)
+    assert np.allclose(stats[..., 1], S.std(axis=(2, 3)), rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("tau", [-0.5, 0.0, 0.7, 1.5])
+def test_tau_selection_matches_numpy(orc, tau):
+    Q, K, V = small(seed=63, H=2, nv=97 * 32 + 5, ns=0, d=16)
+    p = orc.params(Q, 0, 32)
+    M = orc.num_blocks(p)
+    rng = np.random.default_rng(64)
+    S = rng.standard_normal((1, 2, M, M))
+    S[0, 1, :, ::3] = 0.25  # ties in every row
+    idx, counts, _ = orc.select_tau(p, tau, S)
+    for h in range(2):
+        kept = brute.select_tau_head(S[0, h], tau)
+        assert (counts[0, h] == kept.sum(axis=1)).all()
+        for I in range(M):
+            assert (idx[0, h, I, :counts[0, h, I]] == np.nonzero(kept[I])[0]).all()
+
+
+def test_tau_keep_all_is_dense(orc):
+    Q, K, V = small(seed=65, nv=700, ns=6)
+    p = orc.params(Q, 6, 32, 0.1, 1)
+    O, _, _, counts = orc.forward_tau(p, -1e30, Q, K, V)
+    assert (counts == orc.num_blocks(p)).all()
+    assert np.abs(O - sdpa_dense(Q, K, V)).max() < 1e-12
+
+
+@pytest.mark.parametrize("tau", [0.8, -1e30, 1e30])
+def test_tau_forward_matches_brute_force(orc, tau):
+    """Moderate tau, everything kept, nothing kept (compressed branch and sinks only)."""
+    Q, K, V = small(seed=66, B=2, nv=900, ns=4)
+    p = orc.params(Q, 4, 64, 0.2, 1)
+    O, lse, idx, counts = orc.forward_tau(p, tau, Q, K, V)
+    Ob, lb, kept = brute.forward(Q, K, V, 4, 64, 0.2, 1, tau=tau)
+    assert (counts == kept.sum(axis=3)).all()
+    assert np.abs(O - Ob).max() < 1e-12 and np.abs(lse - lb).max() < 1e-12
