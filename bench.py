@@ -32,19 +32,26 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_flops(idx, wl, ratio_K):
+def algorithmic_flops(idx, wl, ratio_K, counts=None):
     """F_sel from the actual route, plus the sink, compressed and sink-query terms (4 d per
-    query-key pair: one multiply-add for the logit and one for the value)."""
+    query-key pair: one multiply-add for the logit and one for the value).  A variable route is
+    idx [B,H,M,M] with counts [B,H,M]."""
     import numpy as np
 
     b, nv, ns, d, N = wl.block, wl.n_video, wl.n_sink, wl.d, wl.N
     M = idx.shape[2]
     sizes = np.minimum(b, nv - np.arange(M) * b).astype(np.int64)
-    n_sel = sizes[idx].sum(axis=-1)  # [B,H,M] keys in the selected blocks of each query block
-    F_sel = 4.0 * d * float((n_sel * sizes[None, None, :]).sum())
     BH = wl.B * wl.H
+    if counts is None:
+        n_sel = sizes[idx].sum(axis=-1)  # [B,H,M] keys in the selected blocks of each query block
+        n_unsel = float(BH * nv * (M - ratio_K))
+    else:
+        valid = np.arange(M)[None, None, None, :] < counts[..., None]
+        n_sel = np.where(valid, sizes[np.clip(idx, 0, M - 1)], 0).sum(axis=-1)
+        n_unsel = float(((M - counts) * sizes[None, None, :]).sum())
+    F_sel = 4.0 * d * float((n_sel * sizes[None, None, :]).sum())
     F_sink = 4.0 * d * nv * ns * BH
-    F_comp = 4.0 * d * nv * (M - ratio_K) * BH
+    F_comp = 4.0 * d * n_unsel
     F_sinkq = 4.0 * d * ns * N * BH
     return F_sel, F_sink, F_comp, F_sinkq
 
@@ -141,6 +148,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="fullclip")
     ap.add_argument("--ratio", type=float, default=None)
+    ap.add_argument("--tau", type=float, default=None,
+                    help="adaptive-tau selection (per-head threshold mu + tau*sigma) instead of top-K")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-blocks", type=int, default=600)
     ap.add_argument("--no-forward-check", action="store_true",
@@ -181,10 +190,16 @@ def main():
     pooled = {k: torch.empty(B, H, M, d, **f32) for k in ("q_mean", "k_mean", "k_sum", "v_sum")}
     pooled["bias"] = torch.empty(B, H, M, **f32)
     pooled["anchor"] = torch.empty(B, H, d, **f32)
-    idx = torch.empty(B, H, M, Kk, device="cuda", dtype=torch.int32)
+    tau_mode = args.tau is not None
+    if tau_mode and wl.reblock:
+        print("--tau runs on token-order workloads only", file=sys.stderr)
+        sys.exit(2)
+    # adaptive tau: a variable route, row I of idx [B,H,M,M] holds counts[I] blocks
+    idx = torch.empty(B, H, M, M if tau_mode else Kk, device="cuda", dtype=torch.int32)
+    counts = torch.empty(B, H, M, device="cuda", dtype=torch.int32) if tau_mode else None
     O = torch.empty_like(Q)
     lse = torch.empty(B, H, N, **f32)
-    sel_ws = torch.empty(sa.workspace_size(p, 3), device="cuda", dtype=torch.uint8)
+    sel_ws = torch.empty(sa.workspace_size(p, 5 if tau_mode else 3), device="cuda", dtype=torch.uint8)
     packed = torch.empty(sa.workspace_size(p, 4), device="cuda", dtype=torch.uint8)
     stream = torch.cuda.current_stream()
     perm = perm_k = None
@@ -217,11 +232,18 @@ def main():
         sa.spark_attn_pool(p, Qp, Kp, Vp, pooled["q_mean"], pooled["k_mean"], pooled["k_sum"], pooled["v_sum"],
                            pooled["bias"], pooled["anchor"], stream)
         if ev: ev[k].record(stream)
-        sa.spark_attn_select(p, pooled["q_mean"], pooled["k_mean"], idx, None, sel_ws, stream)
+        if tau_mode:
+            sa.spark_attn_select_tau(p, args.tau, pooled["q_mean"], pooled["k_mean"], idx, counts, None, sel_ws,
+                                     stream)
+        else:
+            sa.spark_attn_select(p, pooled["q_mean"], pooled["k_mean"], idx, None, sel_ws, stream)
         if ev: ev[k + 1].record(stream)
         sa.spark_attn_pack(p, Kp, Vp, pooled["k_sum"], pooled["v_sum"], pooled["bias"], packed, stream)
         if ev: ev[k + 2].record(stream)
-        sa.spark_attn_attend(p, Qp, packed, idx, perm, O, lse, stream)
+        if tau_mode:
+            sa.spark_attn_attend_var(p, Qp, packed, idx, counts, perm, O, lse, stream)
+        else:
+            sa.spark_attn_attend(p, Qp, packed, idx, perm, O, lse, stream)
         if ev: ev[k + 3].record(stream)
 
     log(f"M={M} K={Kk}; warmup {args.warmup}")
@@ -247,13 +269,21 @@ def main():
     # cross-check: the single-call entry point over the same input
     ms_forward_call, same_out, ws, O2 = None, None, None, None
     if not args.no_forward_check:
-        ws = torch.empty(sa.workspace_size(p, 2 if wl.reblock else 0), device="cuda", dtype=torch.uint8)
+        ws = torch.empty(sa.workspace_size(p, 6 if tau_mode else (2 if wl.reblock else 0)), device="cuda",
+                         dtype=torch.uint8)
         O2 = torch.empty_like(Q)
-        sa.spark_attn_forward_kv(p, Q, K, V, perm, perm_k, O2, None, None, ws, stream)
+
+        def fwd_call():
+            if tau_mode:
+                sa.spark_attn_forward_tau(p, args.tau, Q, K, V, O2, None, None, None, ws, stream)
+            else:
+                sa.spark_attn_forward_kv(p, Q, K, V, perm, perm_k, O2, None, None, ws, stream)
+
+        fwd_call()
         fe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         fe[0].record(stream)
         for _ in range(3):
-            sa.spark_attn_forward_kv(p, Q, K, V, perm, perm_k, O2, None, None, ws, stream)
+            fwd_call()
         fe[1].record(stream)
         torch.cuda.synchronize()
         ms_forward_call = round(fe[0].elapsed_time(fe[1]) / 3, 4)
@@ -267,14 +297,16 @@ def main():
         del src, dst
 
     gidx = idx.cpu().numpy()
-    F_sel, F_sink, F_comp, F_sinkq = algorithmic_flops(gidx, wl, Kk)
+    gcounts = counts.cpu().numpy() if tau_mode else None
+    F_sel, F_sink, F_comp, F_sinkq = algorithmic_flops(gidx, wl, Kk, gcounts)
     F_attn = F_sel + F_sink + F_comp + F_sinkq
     value = F_sel / (ms_step * 1e-3) / 1e12
     achieved = F_attn / (ms_attn * 1e-3) / 1e12
     pool_bytes = 3.0 * B * H * wl.n_video * d * Q.element_size() + 4.0 * B * H * M * d * 4 + 4.0 * B * H * M
 
     out = {
-        "metric": "selected-block TFLOP/s of the sparse-attention forward at 10% density",
+        "metric": ("selected-block TFLOP/s of the sparse-attention forward at 10% density" if not tau_mode else
+                   f"selected-block TFLOP/s of the sparse-attention forward with adaptive-tau selection (tau={args.tau})"),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -288,7 +320,9 @@ def main():
         "data": "synthetic (seeded positional-feature Q/K/V of the clip's shape; no model weights)",
         "config": {
             "workload": wl.name, "description": wl.description, "B": B, "H": H, "N_video": wl.n_video,
-            "N_sink": wl.n_sink, "d": d, "block": wl.block, "topk_ratio": ratio, "M": M, "K": Kk,
+            "N_sink": wl.n_sink, "d": d, "block": wl.block, "M": M,
+            **({"topk_ratio": ratio, "K": Kk} if not tau_mode else
+               {"selection": "adaptive tau", "tau": args.tau, "kept_fraction": round(float(gcounts.mean()) / M, 4)}),
             "compressed_branch": "anchor-weighted summary + log-mass bias", "parallelism": "none (1 GPU)",
             "layout": ("separate key partition" if wl.key_partition else "q_reuse_k") if wl.reblock
             else "token order",
@@ -309,7 +343,9 @@ def main():
                           "frac": round(pool_bytes / (ms_pool * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and tau_mode:
+        log("cpu baseline: timed for the top-K route only")
+    if not args.no_cpu_baseline and not tau_mode:
         log("cpu baseline (oracle) ...")
         del Q, K, V, O, O2, ws, sel_ws, packed, Qp, Kp, Vp
         if wl.reblock:

@@ -40,7 +40,7 @@ EXPORTS = (
     "spark_attn_num_blocks", "spark_attn_topk_count", "spark_attn_workspace_size",
     "spark_attn_status_str", "spark_attn_pool", "spark_attn_select", "spark_attn_pack",
     "spark_attn_attend", "spark_attn_forward", "spark_attn_forward_kv", "spark_attn_reblock",
-    "spark_attn_gather_rows",
+    "spark_attn_gather_rows", "spark_attn_select_tau", "spark_attn_attend_var", "spark_attn_forward_tau",
 )
 
 _lib = None
@@ -69,6 +69,10 @@ def lib():
             "spark_attn_forward_kv": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "spark_attn_reblock": ([P, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "spark_attn_gather_rows": ([P, vp, vp, vp, vp], ctypes.c_int),
+            "spark_attn_select_tau": ([P, ctypes.c_float, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "spark_attn_attend_var": ([P, vp, vp, sz, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+            "spark_attn_forward_tau": ([P, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+                                       ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -173,6 +177,26 @@ def spark_attn_forward_kv(p, Q, K, V, perm_q, perm_k, O, lse, idx_out, workspace
         _ptr(idx_out), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def spark_attn_select_tau(p, tau, q_mean, k_mean, idx, counts, stats, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("spark_attn_select_tau", lib().spark_attn_select_tau(
+        ctypes.byref(p), float(tau), _ptr(q_mean), _ptr(k_mean), _ptr(idx), _ptr(counts), _ptr(stats),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def spark_attn_attend_var(p, Q, packed, idx, counts, perm, O, lse, stream=None):
+    _check("spark_attn_attend_var", lib().spark_attn_attend_var(
+        ctypes.byref(p), _ptr(Q), _ptr(packed), _nbytes(packed), _ptr(idx), _ptr(counts), _ptr(perm),
+        _ptr(O), _ptr(lse), _stream(stream)))
+
+
+def spark_attn_forward_tau(p, tau, Q, K, V, O, lse, idx_out, counts_out, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("spark_attn_forward_tau", lib().spark_attn_forward_tau(
+        ctypes.byref(p), float(tau), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(lse), _ptr(idx_out),
+        _ptr(counts_out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 def spark_attn_reblock(p, Q, K, perm, workspace, stream=None):
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("spark_attn_reblock", lib().spark_attn_reblock(
@@ -253,6 +277,42 @@ def forward(Q, K, V, n_sink, block, topk_ratio, pool_mode=POOL_REWEIGHT, perm=No
         res += (lse,)
     if return_idx:
         res += (idx,)
+    return res[0] if len(res) == 1 else res
+
+
+def select_tau(q_mean, k_mean, Q, n_sink, block, tau, scale=0.0, with_stats=False, stream=None):
+    """Adaptive-tau routes: (idx [B,H,M,M], counts [B,H,M]) (and stats [B,H,2] when asked)."""
+    p = params(Q, n_sink, block, 1.0, POOL_REWEIGHT, scale)
+    M = num_blocks(p)
+    B, H = q_mean.shape[:2]
+    idx = torch.full((B, H, M, M), -1, device=q_mean.device, dtype=torch.int32)
+    counts = torch.empty(B, H, M, device=q_mean.device, dtype=torch.int32)
+    stats = torch.empty(B, H, 2, device=q_mean.device, dtype=torch.float32)
+    ws = torch.empty(workspace_size(p, 5), device=q_mean.device, dtype=torch.uint8)
+    spark_attn_select_tau(p, tau, q_mean, k_mean, idx, counts, stats, ws, stream)
+    return (idx, counts, stats) if with_stats else (idx, counts)
+
+
+def forward_tau(Q, K, V, n_sink, block, tau, pool_mode=POOL_REWEIGHT, scale=0.0, return_lse=False,
+                return_route=False, workspace=None, stream=None):
+    """Forward with adaptive-tau routes.  Returns O (and lse, and (idx, counts) when asked)."""
+    p = params(Q, n_sink, block, 1.0, pool_mode, scale)
+    M = num_blocks(p)
+    B, H, N, _ = Q.shape
+    O = torch.empty_like(Q)
+    lse = torch.empty(B, H, N, device=Q.device, dtype=torch.float32) if return_lse else None
+    idx = counts = None
+    if return_route:
+        idx = torch.full((B, H, M, M), -1, device=Q.device, dtype=torch.int32)
+        counts = torch.empty(B, H, M, device=Q.device, dtype=torch.int32)
+    if workspace is None:
+        workspace = torch.empty(workspace_size(p, 6), device=Q.device, dtype=torch.uint8)
+    spark_attn_forward_tau(p, tau, Q, K, V, O, lse, idx, counts, workspace, stream)
+    res = (O,)
+    if return_lse:
+        res += (lse,)
+    if return_route:
+        res += (idx, counts)
     return res[0] if len(res) == 1 else res
 
 

@@ -83,6 +83,34 @@ static FwdWorkspace fwd_layout(const LaunchCtx& L, bool with_perm) {
     return w;
 }
 
+// workspace of spark_attn_select_tau: the score matrix, then the per-head partial sums
+static size_t tau_select_bytes(const LaunchCtx& L) {
+    return align256(select_workspace_bytes(L)) + tau_partials_bytes(L);
+}
+
+struct TauWorkspace {
+    size_t q_mean, k_mean, k_sum, v_sum, bias, anchor, idx, counts, scores, partials, packed, total;
+};
+
+static TauWorkspace tau_layout(const LaunchCtx& L) {
+    TauWorkspace w;
+    const size_t md = (size_t)L.BH * L.M * L.d * 4;
+    size_t o = 0;
+    w.q_mean = o; o = align256(o + md);
+    w.k_mean = o; o = align256(o + md);
+    w.k_sum = o; o = align256(o + md);
+    w.v_sum = o; o = align256(o + md);
+    w.bias = o; o = align256(o + (size_t)L.BH * L.M * 4);
+    w.anchor = o; o = align256(o + (size_t)L.BH * L.d * 4);
+    w.idx = o; o = align256(o + (size_t)L.BH * L.M * L.M * 4);
+    w.counts = o; o = align256(o + (size_t)L.BH * L.M * 4);
+    w.scores = o; o = align256(o + select_workspace_bytes(L));
+    w.partials = o; o = align256(o + tau_partials_bytes(L));
+    w.packed = o; o = align256(o + pack_geom(L).bytes);
+    w.total = o;
+    return w;
+}
+
 }  // namespace spark
 
 using namespace spark;
@@ -104,6 +132,8 @@ size_t spark_attn_workspace_size(const spark_attn_params* p, int what) {
     if (what == 0 || what == 2) return fwd_layout(L, what == 2).total;
     if (what == 3) return select_workspace_bytes(L);
     if (what == 4) return pack_geom(L).bytes;
+    if (what == 5) return tau_select_bytes(L);
+    if (what == 6) return tau_layout(L).total;
     return 0;
 }
 
@@ -171,7 +201,65 @@ int spark_attn_attend(const spark_attn_params* p, const void* Q, const void* pac
     if (!Q || !idx || !O) return SPARK_ATTN_INVALID_ARGUMENT;
     if (!aligned16(Q) || !aligned16(packed) || !aligned16(O)) return SPARK_ATTN_MISALIGNED;
     if (!packed || packed_bytes < pack_geom(L).bytes) return SPARK_ATTN_WORKSPACE_TOO_SMALL;
-    launch_attend(L, Q, packed, idx, perm, O, lse);
+    launch_attend(L, Q, packed, idx, nullptr, perm, O, lse);
+    return launch_status();
+}
+
+int spark_attn_attend_var(const spark_attn_params* p, const void* Q, const void* packed, size_t packed_bytes,
+                          const int32_t* idx, const int32_t* counts, const int32_t* perm, void* O, float* lse,
+                          void* stream) {
+    LaunchCtx L;
+    int s = make_ctx(p, stream, &L);
+    if (s < 0) return s;
+    if (!Q || !idx || !counts || !O) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!aligned16(Q) || !aligned16(packed) || !aligned16(O)) return SPARK_ATTN_MISALIGNED;
+    if (!packed || packed_bytes < pack_geom(L).bytes) return SPARK_ATTN_WORKSPACE_TOO_SMALL;
+    launch_attend(L, Q, packed, idx, counts, perm, O, lse);
+    return launch_status();
+}
+
+int spark_attn_select_tau(const spark_attn_params* p, float tau, const float* q_mean, const float* k_mean,
+                          int32_t* idx, int32_t* counts, float* stats, void* workspace, size_t ws_bytes,
+                          void* stream) {
+    LaunchCtx L;
+    int s = make_ctx(p, stream, &L);
+    if (s < 0) return s;
+    if (!(tau == tau) || tau == INFINITY || tau == -INFINITY) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!q_mean || !k_mean || !idx || !counts) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!aligned16(q_mean) || !aligned16(k_mean) || !aligned16(workspace)) return SPARK_ATTN_MISALIGNED;
+    if (!workspace || ws_bytes < tau_select_bytes(L)) return SPARK_ATTN_WORKSPACE_TOO_SMALL;
+    char* ws = (char*)workspace;
+    launch_select_tau(L, tau, q_mean, k_mean, idx, counts, stats, (float*)ws,
+                      (double*)(ws + align256(select_workspace_bytes(L))));
+    return launch_status();
+}
+
+int spark_attn_forward_tau(const spark_attn_params* p, float tau, const void* Q, const void* K, const void* V,
+                           void* O, float* lse, int32_t* idx_out, int32_t* counts_out, void* workspace,
+                           size_t ws_bytes, void* stream) {
+    LaunchCtx L;
+    int s = make_ctx(p, stream, &L);
+    if (s < 0) return s;
+    if (!(tau == tau) || tau == INFINITY || tau == -INFINITY) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!Q || !K || !V || !O) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(workspace))
+        return SPARK_ATTN_MISALIGNED;
+    const TauWorkspace w = tau_layout(L);
+    if (!workspace || ws_bytes < w.total) return SPARK_ATTN_WORKSPACE_TOO_SMALL;
+    char* ws = (char*)workspace;
+    float* q_mean = (float*)(ws + w.q_mean);
+    float* k_mean = (float*)(ws + w.k_mean);
+    float* k_sum = (float*)(ws + w.k_sum);
+    float* v_sum = (float*)(ws + w.v_sum);
+    float* bias = (float*)(ws + w.bias);
+    float* anchor = (float*)(ws + w.anchor);
+    int32_t* idx = idx_out ? idx_out : (int32_t*)(ws + w.idx);
+    int32_t* counts = counts_out ? counts_out : (int32_t*)(ws + w.counts);
+    launch_pool(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor);
+    launch_select_tau(L, tau, q_mean, k_mean, idx, counts, nullptr, (float*)(ws + w.scores),
+                      (double*)(ws + w.partials));
+    launch_pack(L, K, V, k_sum, v_sum, bias, ws + w.packed);
+    launch_attend(L, Q, ws + w.packed, idx, counts, nullptr, O, lse);
     return launch_status();
 }
 
@@ -218,7 +306,7 @@ int spark_attn_forward_kv(const spark_attn_params* p, const void* Q, const void*
     launch_pool(L, q, k, v, q_mean, k_mean, k_sum, v_sum, bias, anchor);
     launch_select(L, q_mean, k_mean, idx, (float*)(ws + w.scores));
     launch_pack(L, k, v, k_sum, v_sum, bias, ws + w.packed);
-    launch_attend(L, q, ws + w.packed, idx, perm_q, O, lse);
+    launch_attend(L, q, ws + w.packed, idx, nullptr, perm_q, O, lse);
     return launch_status();
 }
 

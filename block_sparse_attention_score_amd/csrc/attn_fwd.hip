@@ -139,8 +139,9 @@ template <int V> using IC = std::integral_constant<int, V>;
 template <typename T, int D, int BLK>
 __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     const T* __restrict__ Q, const __bf16* __restrict__ packed, const float* __restrict__ bias2,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ perm, T* __restrict__ O, float* __restrict__ lse,
-    int N, int Nv, int M, int Ksel, int SQ, int BH, int C, int Tv, int Ts, int Tc, float c_log2) {
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ counts, const int32_t* __restrict__ perm,
+    T* __restrict__ O, float* __restrict__ lse, int N, int Nv, int M, int Ksel, int kstride, int SQ, int BH, int C,
+    int Tv, int Ts, int Tc, float c_log2) {
 // The body uses buffer resources, a device-only type: the host pass sees an empty kernel.
 #if defined(__HIP_DEVICE_COMPILE__)
     using G = TileGeom<D>;
@@ -183,6 +184,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
             if (I >= M) return;  // padding slot (uniform for the workgroup, before any barrier)
             qrow0 = I * BLK;
             nq = min(BLK, Nv - qrow0);
+            // a variable route (counts given) lists counts[I] blocks in a row of kstride entries
+            if (counts) Ksel = counts[(size_t)bh * M + I];
             ntiles = Ksel * (BLK / kTK) + Ts + Tc;
         }
     }
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     const int Tall = Tv + Ts + Tc;
     const __bf16* ptile = packed + (size_t)bh * Tall * G::ELEMS;
     const float* pbias = bias2 + (size_t)bh * Tall * kTK;
-    const int32_t* sel = dense ? nullptr : idx + ((size_t)bh * M + qrow0 / BLK) * Ksel;
+    const int32_t* sel = dense ? nullptr : idx + ((size_t)bh * M + qrow0 / BLK) * kstride;
     constexpr int nsub = BLK / kTK;
     const int n_exact = dense ? 0 : Ksel * nsub;
     const int first_cmp = dense ? ntiles : n_exact + Ts;  // first compressed tile in the list
@@ -423,22 +426,22 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
 
 template <typename T, int D, int BLK>
 static void launch_attend_t(const LaunchCtx& L, const void* Q, const void* packed, const int32_t* idx,
-                            const int32_t* perm, void* O, float* lse) {
+                            const int32_t* counts, const int32_t* perm, void* O, float* lse) {
     const PackGeom g = pack_geom(L);
     const int SQ = (L.n_sink + BLK - 1) / BLK;
     const int C = (L.M + 7) / 8;  // query blocks per XCD per head
     const dim3 grid(L.BH * SQ + L.BH * 8 * C);
     const float c_log2 = L.scale * 1.4426950408889634f;
     hipLaunchKernelGGL((attn_fwd_kernel<T, D, BLK>), grid, dim3(BLK * 2), 0, L.stream, (const T*)Q,
-                       (const __bf16*)packed, (const float*)((const char*)packed + g.bias_off), idx, perm, (T*)O,
-                       lse, L.N, L.Nv, L.M, L.K, SQ, L.BH, C, g.Tv, g.Ts, g.Tc, c_log2);
+                       (const __bf16*)packed, (const float*)((const char*)packed + g.bias_off), idx, counts, perm,
+                       (T*)O, lse, L.N, L.Nv, L.M, L.K, counts ? L.M : L.K, SQ, L.BH, C, g.Tv, g.Ts, g.Tc, c_log2);
 }
 
-void launch_attend(const LaunchCtx& L, const void* Q, const void* packed, const int32_t* idx, const int32_t* perm,
-                   void* O, float* lse) {
+void launch_attend(const LaunchCtx& L, const void* Q, const void* packed, const int32_t* idx, const int32_t* counts,
+                   const int32_t* perm, void* O, float* lse) {
 #define SPARK_ATTN_CASE(T, D, B)                                          \
     if (L.d == D && L.block == B) {                                       \
-        launch_attend_t<T, D, B>(L, Q, packed, idx, perm, O, lse);        \
+        launch_attend_t<T, D, B>(L, Q, packed, idx, counts, perm, O, lse); \
         return;                                                           \
     }
     if (L.dtype == SPARK_ATTN_BF16) {

@@ -20,6 +20,11 @@ void launch_pool(const LaunchCtx& L, const void* Q, const void* K, const void* V
 size_t select_workspace_bytes(const LaunchCtx& L);
 void launch_select(const LaunchCtx& L, const float* q_mean, const float* k_mean, int32_t* idx,
                    float* scores);
+// adaptive-tau routes: idx [B,H,M,M] (row I's kept blocks ascending), counts [B,H,M], stats
+// [B,H,2] = (mu, sigma) or NULL; scores [B,H,M,M] and partials (tau_partials_bytes) are scratch
+size_t tau_partials_bytes(const LaunchCtx& L);
+void launch_select_tau(const LaunchCtx& L, float tau, const float* q_mean, const float* k_mean, int32_t* idx,
+                       int32_t* counts, float* stats, float* scores, double* partials);
 
 // Packed 64-key tiles read by the attention kernel (layout in pack.hip).
 struct PackGeom {
@@ -34,8 +39,9 @@ PackGeom pack_geom(const LaunchCtx& L);
 void launch_pack(const LaunchCtx& L, const void* K, const void* V, const float* k_sum, const float* v_sum,
                  const float* bias, void* packed);
 
+// idx [B,H,M,K] with counts == NULL, or a variable route: idx [B,H,M,M] with counts [B,H,M]
 void launch_attend(const LaunchCtx& L, const void* Q, const void* packed, const int32_t* idx,
-                   const int32_t* perm, void* O, float* lse);
+                   const int32_t* counts, const int32_t* perm, void* O, float* lse);
 
 void launch_gather_rows(const LaunchCtx& L, const void* X, const int32_t* perm, void* Y);
 

@@ -127,6 +127,101 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict_
     }
 }
 
+// ---- adaptive-tau selection (core node page, "ブロックスパースアテンション", Sol-Attn bullet: a
+// per-head threshold in sigma units of the score distribution).  Over the M x M scores of a
+// (batch, head): mu = mean, sigma = population standard deviation, both in binary64 from sums of
+// S and S^2 (per-workgroup partial sums in a fixed order, then the partials in a fixed order, so
+// the result does not depend on timing); row I keeps every J with S_IJ > mu + tau * sigma.
+constexpr int kTauParts = 64;
+
+size_t tau_partials_bytes(const LaunchCtx& L) { return (size_t)L.BH * kTauParts * 2 * sizeof(double); }
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// grid (kTauParts, BH): partial sums of S and S^2 over one contiguous part of a head's scores
+__global__ __launch_bounds__(256) void tau_partial_kernel(const float* __restrict__ S, int M,
+                                                          double* __restrict__ partial) {
+    __shared__ double red[2][4];
+    const int bh = blockIdx.y, part = blockIdx.x, t = threadIdx.x;
+    const size_t MM = (size_t)M * M, chunk = (MM + kTauParts - 1) / kTauParts;
+    const size_t lo = (size_t)part * chunk, hi = min(MM, lo + chunk);
+    const float* Sh = S + (size_t)bh * MM;
+    double s = 0.0, q = 0.0;
+    for (size_t e = lo + t; e < hi; e += 256) {
+        const double x = (double)Sh[e];
+        s += x;
+        q += x * x;
+    }
+    s = wave_sum_f64(s);
+    q = wave_sum_f64(q);
+    if ((t & 63) == 0) {
+        red[0][t >> 6] = s;
+        red[1][t >> 6] = q;
+    }
+    __syncthreads();
+    if (t == 0) {
+        double ts = 0.0, tq = 0.0;
+        for (int w = 0; w < 4; ++w) {
+            ts += red[0][w];
+            tq += red[1][w];
+        }
+        partial[((size_t)bh * kTauParts + part) * 2] = ts;
+        partial[((size_t)bh * kTauParts + part) * 2 + 1] = tq;
+    }
+}
+
+// one wave per score row: the head's threshold from the partials, then the kept blocks of the row
+// in ascending order (ballot compaction) and their count
+__global__ __launch_bounds__(256) void tau_rows_kernel(const float* __restrict__ S, int rows, int M, float tau,
+                                                       const double* __restrict__ partial,
+                                                       int32_t* __restrict__ idx, int32_t* __restrict__ counts,
+                                                       float* __restrict__ stats) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int bh = row / M;
+    const double* pp = partial + (size_t)bh * kTauParts * 2;
+    const double MM = (double)M * (double)M;
+    const double sum = wave_sum_f64(lane < kTauParts ? pp[2 * lane] : 0.0);
+    const double sumsq = wave_sum_f64(lane < kTauParts ? pp[2 * lane + 1] : 0.0);
+    const double mu = sum / MM;
+    const double sigma = sqrt(fmax(sumsq / MM - mu * mu, 0.0));
+    const double thr = mu + (double)tau * sigma;
+    const float* Sr = S + (size_t)row * M;
+    int32_t* out = idx + (size_t)row * M;
+    const uint64_t below = lanemask_lt();
+    int pos = 0;
+    for (int J0 = 0; J0 < M; J0 += 64) {
+        const int J = J0 + lane;
+        const bool keep = J < M && (double)Sr[J] > thr;
+        const uint64_t kb = __ballot(keep);
+        if (keep) out[pos + __popcll(kb & below)] = J;
+        pos += __popcll(kb);
+    }
+    if (lane == 0) {
+        counts[row] = pos;
+        if (stats && row % M == 0) {
+            stats[2 * bh] = (float)mu;
+            stats[2 * bh + 1] = (float)sigma;
+        }
+    }
+}
+
+void launch_select_tau(const LaunchCtx& L, float tau, const float* q_mean, const float* k_mean, int32_t* idx,
+                       int32_t* counts, float* stats, float* scores, double* partials) {
+    const dim3 sgrid((L.M + kGT - 1) / kGT, (L.M + kGT - 1) / kGT, L.BH);
+    hipLaunchKernelGGL(block_scores_kernel, sgrid, dim3(256), 0, L.stream, q_mean, k_mean, L.M, L.d, L.scale,
+                       scores);
+    hipLaunchKernelGGL(tau_partial_kernel, dim3(kTauParts, L.BH), dim3(256), 0, L.stream, scores, L.M, partials);
+    const int rows = L.BH * L.M;
+    hipLaunchKernelGGL(tau_rows_kernel, dim3((rows + 3) / 4), dim3(256), 0, L.stream, scores, rows, L.M, tau,
+                       partials, idx, counts, stats);
+}
+
 size_t select_workspace_bytes(const LaunchCtx& L) { return (size_t)L.BH * L.M * L.M * 4; }
 
 void launch_select(const LaunchCtx& L, const float* q_mean, const float* k_mean, int32_t* idx, float* scores) {

@@ -85,7 +85,8 @@ int spark_attn_topk_count(int M, float ratio);
  *   what = 0: spark_attn_forward without perm;  what = 2: spark_attn_forward with perm (or
  *             spark_attn_forward_kv with either partition);
  *   what = 1: spark_attn_reblock;               what = 3: spark_attn_select without `scores`;
- *   what = 4: the packed key/value tiles of spark_attn_pack / spark_attn_attend. */
+ *   what = 4: the packed key/value tiles of spark_attn_pack / spark_attn_attend;
+ *   what = 5: spark_attn_select_tau;            what = 6: spark_attn_forward_tau. */
 size_t spark_attn_workspace_size(const spark_attn_params *p, int what);
 
 /* Static description of a status code. */
@@ -149,6 +150,42 @@ int spark_attn_pack(const spark_attn_params *p, const void *K, const void *V, co
 int spark_attn_attend(const spark_attn_params *p, const void *Q, const void *packed,
                       size_t packed_bytes, const int32_t *idx, const int32_t *perm, void *O,
                       float *lse, void *stream);
+
+/*
+ * Adaptive-tau selection (core node page, "ブロックスパースアテンション", Sol-Attn bullet: a
+ * per-head threshold placed in sigma units of the score distribution, no trained weights).
+ * Over the M x M block scores S_IJ = s * q_mean_I . k_mean_J (fp32) of each (batch, head):
+ * mu = their mean and sigma = their population standard deviation (binary64, fixed summation
+ * order); query block I keeps every key block J with S_IJ > mu + tau * sigma, so the number of
+ * kept blocks varies per query block (none is allowed).
+ * In:  tau (finite); q_mean, k_mean [B,H,M,d] fp32 (from spark_attn_pool).
+ * Out: idx [B,H,M,M] int32: row I lists its kept blocks in ascending order in its first counts[I]
+ *      entries (the rest are left as they were); counts [B,H,M] int32; stats [B,H,2] fp32 =
+ *      (mu, sigma) per (batch, head), or NULL.
+ * workspace: at least spark_attn_workspace_size(p, 5) bytes.
+ */
+int spark_attn_select_tau(const spark_attn_params *p, float tau, const float *q_mean,
+                          const float *k_mean, int32_t *idx, int32_t *counts, float *stats,
+                          void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * The attention stage with a variable route (as spark_attn_attend otherwise): query block I
+ * attends exactly to the counts[I] blocks listed in row I of idx [B,H,M,M], to every sink, and
+ * to one pseudo-key per other block.  counts [B,H,M] int32 in [0, M]; perm as in
+ * spark_attn_attend or NULL.
+ */
+int spark_attn_attend_var(const spark_attn_params *p, const void *Q, const void *packed,
+                          size_t packed_bytes, const int32_t *idx, const int32_t *counts,
+                          const int32_t *perm, void *O, float *lse, void *stream);
+
+/*
+ * The forward with adaptive-tau routes: pool -> spark_attn_select_tau -> pack -> attend, in
+ * token order.  Out: O, lse (or NULL) as spark_attn_forward; idx_out [B,H,M,M] and counts_out
+ * [B,H,M] (each may be NULL): the route used.  workspace: spark_attn_workspace_size(p, 6) bytes.
+ */
+int spark_attn_forward_tau(const spark_attn_params *p, float tau, const void *Q, const void *K,
+                           const void *V, void *O, float *lse, int32_t *idx_out,
+                           int32_t *counts_out, void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * The whole forward: [gather rows by perm] -> pool -> select -> pack -> attend (-> un-permute).

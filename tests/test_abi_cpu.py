@@ -151,3 +151,31 @@ def test_status_strings():
     for s in (OK, INVALID, UNSUPPORTED, WS_SMALL, HIP_ERR, MISALIGNED):
         assert sa.status_str(s) and sa.status_str(s) != "unknown status"
     assert sa.status_str(-99) == "unknown status"
+
+
+def test_adaptive_tau_entry_points_validate_before_launch():
+    L = sa.lib()
+    p = P()
+    a = ctypes.c_void_p(0x100000)
+    bad = ctypes.c_void_p(0x100008)
+    f = ctypes.c_float
+    w5 = L.spark_attn_workspace_size(ctypes.byref(p), 5)
+    w6 = L.spark_attn_workspace_size(ctypes.byref(p), 6)
+    M = L.spark_attn_num_blocks(ctypes.byref(p))
+    BH = p.B * p.H
+    # select: the score matrix plus per-head partial sums
+    assert w5 >= BH * M * M * 4
+    assert w6 > w5
+    for t in (float("nan"), float("inf"), float("-inf")):
+        assert L.spark_attn_select_tau(ctypes.byref(p), f(t), a, a, a, a, None, a, w5, None) == INVALID
+        assert L.spark_attn_forward_tau(ctypes.byref(p), f(t), a, a, a, a, None, None, None, a, w6, None) == INVALID
+    assert L.spark_attn_select_tau(ctypes.byref(p), f(1.0), a, a, None, a, None, a, w5, None) == INVALID
+    assert L.spark_attn_select_tau(ctypes.byref(p), f(1.0), a, a, a, None, None, a, w5, None) == INVALID
+    assert L.spark_attn_select_tau(ctypes.byref(p), f(1.0), bad, a, a, a, None, a, w5, None) == MISALIGNED
+    assert L.spark_attn_select_tau(ctypes.byref(p), f(1.0), a, a, a, a, None, a, w5 - 1, None) == WS_SMALL
+    assert L.spark_attn_attend_var(ctypes.byref(p), a, a, 1 << 40, a, None, None, a, None, None) == INVALID
+    assert L.spark_attn_attend_var(ctypes.byref(p), a, a, 10, a, a, None, a, None, None) == WS_SMALL
+    assert L.spark_attn_forward_tau(ctypes.byref(p), f(1.0), a, a, a, a, None, None, None, a, w6 - 1, None) == WS_SMALL
+    assert L.spark_attn_forward_tau(ctypes.byref(p), f(1.0), a, None, a, a, None, None, None, a, w6, None) == INVALID
+    q = P(d=96)
+    assert L.spark_attn_select_tau(ctypes.byref(q), f(1.0), a, a, a, a, None, a, 1 << 40, None) == UNSUPPORTED
