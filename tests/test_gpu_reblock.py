@@ -40,6 +40,9 @@ CASES = [
     ("fp32-d128-b64", 1, 1, 25 * 64 + 63, 3, 128, 64, "fp32"),
     ("one-block", 1, 2, 90, 4, 128, 128, "bf16"),
     ("two-blocks", 1, 2, 129, 1, 128, 128, "bf16"),
+    # groups of several 2048-position chunks at the top levels, ragged last chunks
+    ("bf16-d128-b128-chunked", 1, 2, 70 * 128 + 77, 3, 128, 128, "bf16"),
+    ("fp32-d128-b64-chunked", 1, 1, 150 * 64 + 13, 2, 128, 64, "fp32"),
 ]
 
 
