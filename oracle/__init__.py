@@ -65,6 +65,11 @@ def lib():
         L.orc_forward.argtypes = [P, f32, f32, f32, vp, vp, vp, f64, f64, vp]
         L.orc_select_tau.argtypes = [P, ctypes.c_double, f64, i32, i32, vp]
         L.orc_forward_tau.argtypes = [P, ctypes.c_double, f32, f32, f32, vp, vp, f64, f64, vp, vp]
+        L.orc_e4m3.argtypes = [ctypes.c_float]
+        L.orc_e4m3.restype = ctypes.c_float
+        L.orc_e4m3_array.argtypes = [f32, f32, ctypes.c_size_t]
+        L.orc_fp8_scales.argtypes = [P, f32, f32, f32, f32]
+        L.orc_forward_fp8.argtypes = [P, f32, f32, f32, vp, vp, f64, f64, vp, vp]
         L.orc_reblock_metric.argtypes = [P, f32, f32, f64, f64]
         L.orc_reblock.argtypes = [P, f32, f32, i32]
         for fn in (L.orc_pool, L.orc_scores, L.orc_select, L.orc_dense, L.orc_attend_blocks,
@@ -186,6 +191,44 @@ def forward_tau(p: Params, tau, Q, K, V, idx=None, counts=None):
     lib().orc_forward_tau(ctypes.byref(p), float(tau), _f32(Q), _f32(K), _f32(V), ptr(idx), ptr(counts),
                           O, lse, idx_out.ctypes.data, cnt_out.ctypes.data)
     return O, lse, idx_out, cnt_out
+
+
+def e4m3(x):
+    """E4M3 rounding (OCP 8-bit float, 3 mantissa bits, ties to even) of binary32 values."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty_like(x)
+    lib().orc_e4m3_array(x.reshape(-1), y.reshape(-1), x.size)
+    return y
+
+
+def fp8_scales(p: Params, Q, K, V):
+    """Per (batch, head): [r_Q, s_Q, r_K, s_K, r_V, s_V] (binary32), r = 448/amax, s = amax/448."""
+    sc = np.empty((p.B, p.H, 6), np.float32)
+    lib().orc_fp8_scales(ctypes.byref(p), _f32(Q), _f32(K), _f32(V), sc.reshape(-1))
+    return sc
+
+
+def forward_fp8(p: Params, Q, K, V, perm=None, idx=None):
+    """Forward with Q, K, V and the pseudo-keys on per-head-scaled E4M3 carriers.  Returns
+    (O, lse, idx [B,H,M,K], scales [B,H,6])."""
+    M = num_blocks(p)
+    Ksel = topk_count(M, p.topk_ratio)
+    O = np.empty((p.B, p.H, p.N, p.d))
+    lse = np.empty((p.B, p.H, p.N))
+    idx_out = np.empty((p.B, p.H, M, Ksel), np.int32)
+    sc = np.empty((p.B, p.H, 6), np.float32)
+    keep = []
+
+    def ptr(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a, dtype=np.int32)
+        keep.append(a)
+        return a.ctypes.data
+
+    lib().orc_forward_fp8(ctypes.byref(p), _f32(Q), _f32(K), _f32(V), ptr(perm), ptr(idx), O, lse,
+                          idx_out.ctypes.data, sc.ctypes.data)
+    return O, lse, idx_out, sc
 
 
 def attend_blocks(p: Params, Q, K, V, pooled, idx, qblocks):

@@ -73,12 +73,32 @@ def select_tau_head(S, tau):
     return S > S.mean() + tau * S.std()
 
 
+def e4m3_torch(x):
+    """E4M3 rounding through PyTorch's float8_e4m3fn cast (a library routine, independent of the C
+    oracle's own rounding)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float8_e4m3fn).to(
+        torch.float32).numpy()
+
+
+def _fp8_carrier(x):
+    """Per-head E4M3 carrier of a [N, d] binary32 array: (decoded carrier, s) with r = 448/amax and
+    s = amax/448 in binary32."""
+    x = np.asarray(x, np.float32)
+    amax = np.float32(np.abs(x).max())
+    if amax == 0:
+        return x.copy(), np.float32(1)
+    r = np.float32(448) / amax
+    return e4m3_torch(x * r), amax / np.float32(448)
+
+
 def forward(Q, K, V, n_sink, block, ratio, pool_mode=1, scale=None, perm=None, idx=None, perm_k=None,
-            tau=None):
+            tau=None, fp8=False):
     """Q, K, V [B,H,N,d] (float arrays). Returns O, lse (binary64) and the route idx.
     perm: query partition (and output rows); perm_k: separate key partition of K and V (None:
     keys and values reuse perm).  tau: adaptive-tau routes instead of top-K (the returned idx is
-    then the boolean kept matrix [B,H,M,M])."""
+    then the boolean kept matrix [B,H,M,M]).  fp8: queries, keys, values and the pseudo-keys on
+    per-head E4M3 carriers (route and bias from the unquantized inputs)."""
     Q, K, V = (np.asarray(x, np.float64) for x in (Q, K, V))
     B, H, N, d = Q.shape
     n_video = N - n_sink
@@ -111,9 +131,23 @@ def forward(Q, K, V, n_sink, block, ratio, pool_mode=1, scale=None, perm=None, i
                 IDX[b, h] = sel
                 chosen = np.zeros((M, M), bool)  # chosen[I, J]
                 chosen[np.repeat(np.arange(M), Ksel), sel.reshape(-1)] = True
-            logits = np.concatenate([s * (q @ k.T), s * (q @ pooled["k_sum"].T) + pooled["bias"]],
-                                    axis=1)
-            values = np.concatenate([v, pooled["v_sum"]], axis=0)
+            qa, ka, va, kt, vt, sl, sv = q, k, v, pooled["k_sum"], pooled["v_sum"], s, 1.0
+            if fp8:
+                qa, sq = _fp8_carrier(q)
+                ka, sk = _fp8_carrier(k)
+                va, sv = _fp8_carrier(v)
+                # the pseudo-keys ride on the keys' and values' carriers
+                kmax, vmax = np.float32(np.abs(np.asarray(k, np.float32)).max()), np.float32(
+                    np.abs(np.asarray(v, np.float32)).max())
+                rk = np.float32(448) / kmax if kmax > 0 else np.float32(1)
+                rv = np.float32(448) / vmax if vmax > 0 else np.float32(1)
+                kt = e4m3_torch(np.asarray(kt, np.float32) * rk).astype(np.float64)
+                vt = e4m3_torch(np.asarray(vt, np.float32) * rv).astype(np.float64)
+                qa, ka, va = (np.asarray(x, np.float64) for x in (qa, ka, va))
+                sl = s * float(sq) * float(sk)
+                sv = float(sv)
+            logits = np.concatenate([sl * (qa @ ka.T), sl * (qa @ kt.T) + pooled["bias"]], axis=1)
+            values = sv * np.concatenate([va, vt], axis=0)
             mask = np.zeros((N, N + M), bool)
             # video queries: keys of chosen blocks, all sinks, pseudo-keys of unchosen blocks
             mask[:n_video, :n_video] = chosen[blk][:, blk]

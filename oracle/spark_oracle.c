@@ -15,7 +15,8 @@
  *  [CORE] "ComfyUI にコアのスパースアテンションノードと Comfy Compiler が追加されました" (comfyui-wiki
  *         news, 2026-09-08), section "ブロックスパースアテンション：1 つのノード、3 つのバックエンド":
  *         per-query-block routing, the top-k (SLA) fixed keep fraction, sink_conditioning.
- *  [H3O]  "H3 Optimizations" README, section "Nodes": non-video queries kept dense.
+ *  [H3O]  "H3 Optimizations" README, section "Nodes": non-video queries kept dense; section
+ *         "Manual Sparse Sage recovery": the FP8 carrier of the FlexAttention fallback.
  *
  * Where the pages leave a step open, the reading taken is stated at the function.
  */
@@ -552,6 +553,155 @@ void orc_forward_tau(const orc_params *p, double tau, const float *Q, const floa
                 attend_dense_row(p, Qh, Kh, Vh, Nv + (I - M), O + bh * row, lse + (size_t)bh * N);
         }
     free(idx); free(cnt); free(qm); free(km); free(ks); free(vs); free(bias); free(anc);
+}
+
+/* ------------------------------------------------------------------------------------------
+ * FP8 exact branch [H3O, section "Manual Sparse Sage recovery", the FP8 FlexAttention fallback]:
+ * Q, K and V are carried as E4M3 with one scale per head, the Q/K scale is restored before the
+ * softmax, the output returns in the original floating type, and the route is the same.
+ * Readings:
+ *  - E4M3 is the OCP 8-bit float with 4 exponent bits (bias 7) and 3 mantissa bits: normal
+ *    values 2^(e-7) (1 + m/8), subnormal spacing 2^-9, largest finite value 448.  A value goes to
+ *    the nearest representable one, ties to an even mantissa.
+ *  - Per (batch, head) and per tensor, amax = max |x| over all N rows (video and sinks); in
+ *    binary32, r = 448 / amax and s = amax / 448 (both 1 when amax = 0).  The carrier of x is
+ *    e4m3(x * r), the product rounded to binary32 first.
+ *  - The compressed pseudo-keys (k~, v~) travel with the keys' and values' scales: a convex
+ *    combination of a block's rows stays inside their range.  Their binary64 summaries are
+ *    rounded to binary32 before the scaling.  The bias beta and the route come from the
+ *    unquantized inputs, exactly as in the plain forward.
+ *  - Every logit is s_att * s_Q * s_K * (q8 . k8), plus beta for a pseudo-key; every value is
+ *    s_V * v8.  The softmax itself is exact (binary64).
+ */
+
+/* E4M3 rounding of x (the value, as binary32).  Magnitudes that round above 448 are outside the
+ * format: NaN. */
+float orc_e4m3(float x)
+{
+    if (x == 0.0f || isnan(x)) return x;
+    const double a = fabs((double)x);
+    int e;
+    (void)frexp(a, &e);       /* a = f 2^e with f in [1/2, 1): the leading bit is 2^(e-1) */
+    int lead = e - 1;
+    if (lead < -6) lead = -6; /* below the smallest normal binade the spacing stays 2^-9 */
+    const double q = ldexp(1.0, lead - 3);
+    const double y = rint(a / q) * q; /* a / q is exact; rint rounds ties to even */
+    if (y > 448.0) return NAN;
+    return (float)(x < 0.0f ? -y : y);
+}
+
+void orc_e4m3_array(const float *x, float *y, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) y[i] = orc_e4m3(x[i]);
+}
+
+/* Per (batch, head): scales[6] = r_Q, s_Q, r_K, s_K, r_V, s_V (binary32). */
+void orc_fp8_scales(const orc_params *p, const float *Q, const float *K, const float *V, float *scales)
+{
+    const size_t row = (size_t)p->N * p->d;
+    for (int bh = 0; bh < p->B * p->H; ++bh) {
+        const float *X[3] = {Q + bh * row, K + bh * row, V + bh * row};
+        for (int t = 0; t < 3; ++t) {
+            float amax = 0.0f;
+            for (size_t e = 0; e < row; ++e) amax = fmaxf(amax, fabsf(X[t][e]));
+            float r = 1.0f, sc = 1.0f;
+            if (amax > 0.0f) {
+                r = 448.0f / amax;
+                sc = amax / 448.0f;
+            }
+            scales[(size_t)bh * 6 + 2 * t] = r;
+            scales[(size_t)bh * 6 + 2 * t + 1] = sc;
+        }
+    }
+}
+
+/* The forward of orc_forward (reblock_layout=q_reuse_k when perm is given) with the exact branch,
+ * the sinks and the pseudo-keys on E4M3 carriers.  scales_out [B*H][6] may be NULL. */
+void orc_forward_fp8(const orc_params *p, const float *Q, const float *K, const float *V,
+                     const int32_t *perm, const int32_t *idx_in, double *O, double *lse,
+                     int32_t *idx_out, float *scales_out)
+{
+    const int d = p->d, N = p->N, Nv = n_video(p), M = orc_num_blocks(p);
+    const int Ksel = orc_topk_count(M, p->topk_ratio);
+    const size_t BH = (size_t)p->B * p->H, row = (size_t)N * d;
+    const float *Qp = Q, *Kp = K, *Vp = V;
+    float *tq = NULL, *tk = NULL, *tv = NULL;
+    if (perm) {
+        tq = permute_rows(p, Q, perm); tk = permute_rows(p, K, perm); tv = permute_rows(p, V, perm);
+        Qp = tq; Kp = tk; Vp = tv;
+    }
+    double *qm = (double *)malloc(sizeof(double) * BH * M * d);
+    double *km = (double *)malloc(sizeof(double) * BH * M * d);
+    double *ks = (double *)malloc(sizeof(double) * BH * M * d);
+    double *vs = (double *)malloc(sizeof(double) * BH * M * d);
+    double *bias = (double *)malloc(sizeof(double) * BH * M);
+    double *anc = (double *)malloc(sizeof(double) * BH * d);
+    orc_pool(p, Qp, Kp, Vp, qm, km, ks, vs, bias, anc);
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * BH * M * Ksel);
+    if (idx_in) {
+        memcpy(idx, idx_in, sizeof(int32_t) * BH * M * Ksel);
+    } else {
+        double *S = (double *)malloc(sizeof(double) * BH * M * M);
+        orc_scores(p, qm, km, S);
+        orc_select(p, S, idx);
+        free(S);
+    }
+    if (idx_out) memcpy(idx_out, idx, sizeof(int32_t) * BH * M * Ksel);
+
+    /* carriers, held as their (exact) binary32 / binary64 values */
+    float *sc = (float *)malloc(sizeof(float) * BH * 6);
+    orc_fp8_scales(p, Qp, Kp, Vp, sc);
+    if (scales_out) memcpy(scales_out, sc, sizeof(float) * BH * 6);
+    float *q8 = (float *)malloc(sizeof(float) * BH * row);
+    float *k8 = (float *)malloc(sizeof(float) * BH * row);
+    float *v8 = (float *)malloc(sizeof(float) * BH * row);
+    double *ks8 = (double *)malloc(sizeof(double) * BH * M * d);
+    double *vs8 = (double *)malloc(sizeof(double) * BH * M * d);
+    for (size_t bh = 0; bh < BH; ++bh) {
+        const float *s6 = sc + bh * 6;
+        for (size_t e = 0; e < row; ++e) {
+            q8[bh * row + e] = orc_e4m3(Qp[bh * row + e] * s6[0]);
+            k8[bh * row + e] = orc_e4m3(Kp[bh * row + e] * s6[2]);
+            v8[bh * row + e] = orc_e4m3(Vp[bh * row + e] * s6[4]);
+        }
+        for (size_t e = 0; e < (size_t)M * d; ++e) {
+            ks8[bh * M * d + e] = (double)orc_e4m3((float)ks[bh * M * d + e] * s6[2]);
+            vs8[bh * M * d + e] = (double)orc_e4m3((float)vs[bh * M * d + e] * s6[4]);
+        }
+    }
+
+    double *Op = (double *)malloc(sizeof(double) * BH * row);
+    double *lp = (double *)malloc(sizeof(double) * BH * N);
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int bh = 0; bh < (int)BH; ++bh)
+        for (int I = 0; I < M + p->n_sink; ++I) {
+            orc_params ph = *p;
+            ph.scale = scale_of(p) * (double)sc[(size_t)bh * 6 + 1] * (double)sc[(size_t)bh * 6 + 3];
+            const float *Qh = q8 + bh * row, *Kh = k8 + bh * row, *Vh = v8 + bh * row;
+            if (I < M)
+                attend_video_block(&ph, Qh, Kh, Vh, ks8 + (size_t)bh * M * d, vs8 + (size_t)bh * M * d,
+                                   bias + (size_t)bh * M, idx + ((size_t)bh * M + I) * Ksel, Ksel,
+                                   I, Op + bh * row, lp + (size_t)bh * N);
+            else
+                attend_dense_row(&ph, Qh, Kh, Vh, Nv + (I - M), Op + bh * row, lp + (size_t)bh * N);
+        }
+
+    /* values restored by s_V; video rows un-permuted: O[perm[q]] = O'[q] */
+    for (size_t bh = 0; bh < BH; ++bh) {
+        const double sV = (double)sc[bh * 6 + 5];
+        for (size_t e = 0; e < row; ++e) Op[bh * row + e] *= sV;
+        for (int q = 0; q < Nv; ++q) {
+            const int src = perm ? perm[bh * Nv + q] : q;
+            memcpy(O + bh * row + (size_t)src * d, Op + bh * row + (size_t)q * d, sizeof(double) * d);
+            lse[bh * N + src] = lp[bh * N + q];
+        }
+        memcpy(O + bh * row + (size_t)Nv * d, Op + bh * row + (size_t)Nv * d,
+               sizeof(double) * (size_t)(N - Nv) * d);
+        memcpy(lse + bh * N + Nv, lp + bh * N + Nv, sizeof(double) * (size_t)(N - Nv));
+    }
+    free(Op); free(lp); free(idx); free(qm); free(km); free(ks); free(vs); free(bias); free(anc);
+    free(sc); free(q8); free(k8); free(v8); free(ks8); free(vs8);
+    free(tq); free(tk); free(tv);
 }
 
 /* ------------------------------------------------------------------------------------------

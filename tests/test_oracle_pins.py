@@ -17,6 +17,9 @@ textbook routine, an invariant, a hand-worked example or a brute-force formulati
   P-k  hand-worked two-block example (tests/golden/hand_worked_example.json)
   P-l  adaptive-tau selection: the normal tail for Gaussian scores, NumPy mean/std threshold,
        keep-all == dense, forward == brute force (moderate, all kept, none kept)
+  P-m  FP8 carrier: E4M3 rounding == torch.float8_e4m3fn cast and the format's closed form
+       (every code maps to itself, midpoints go to the even mantissa); on-grid inputs at full
+       density == dense; power-of-two rescalings act exactly; forward == brute force
 """
 import json
 import math
@@ -434,3 +437,114 @@ def test_tau_forward_matches_brute_force(orc, tau):
     Ob, lb, kept = brute.forward(Q, K, V, 4, 64, 0.2, 1, tau=tau)
     assert (counts == kept.sum(axis=3)).all()
     assert np.abs(O - Ob).max() < 1e-12 and np.abs(lse - lb).max() < 1e-12
+
+
+# ---------------------------------------------------------------- P-m FP8 (E4M3) carrier
+def _e4m3_codes():
+    """Every finite E4M3 value from the format's definition (sign, 4-bit exponent with bias 7,
+    3-bit mantissa; exponent 15 with mantissa 7 is NaN)."""
+    vals = []
+    for code in range(256):
+        sgn, e, m = code >> 7, (code >> 3) & 15, code & 7
+        if e == 15 and m == 7:
+            continue
+        v = 2.0 ** (e - 7) * (1 + m / 8) if e else 2.0 ** -6 * (m / 8)
+        vals.append(-v if sgn else v)
+    return np.array(sorted(set(vals)), np.float64)
+
+
+def test_e4m3_matches_torch_cast(orc):
+    rng = np.random.default_rng(70)
+    mag = np.exp2(rng.uniform(-14, np.log2(448), 200000))
+    x = (mag * rng.choice([-1, 1], mag.size)).astype(np.float32)
+    grid = _e4m3_codes()
+    mids = ((grid[1:] + grid[:-1]) / 2).astype(np.float32)
+    x = np.concatenate([x, grid.astype(np.float32), mids, np.float32([0, -0.0, 448, -448])])
+    assert (orc.e4m3(x).view(np.uint32) == brute.e4m3_torch(x).view(np.uint32)).all()
+
+
+def test_e4m3_closed_form(orc):
+    grid = _e4m3_codes()
+    assert grid.max() == 448 and np.sort(np.abs(grid))[1] == 2.0 ** -9
+    g32 = grid.astype(np.float32)
+    assert (orc.e4m3(g32) == g32).all()
+    # a midpoint goes to the neighbour whose mantissa is even (its code is even)
+    pos = grid[grid >= 0]
+    for lo, hi in zip(pos[:-1], pos[1:]):
+        mid = np.float32((lo + hi) / 2)
+        got = float(orc.e4m3(np.float32([mid]))[0])
+        lo_code = list(pos).index(lo)  # codes of non-negative values ascend with the value
+        assert got == (lo if lo_code % 2 == 0 else hi), (lo, hi, got)
+        # anything strictly inside rounds to the nearer neighbour
+        q = np.float32(lo + 0.3 * (hi - lo))
+        assert float(orc.e4m3(np.float32([q]))[0]) == lo
+
+
+def _on_grid(rng, shape):
+    """Random values on the E4M3 grid with 448 reached in every (batch, head) slab, so that every
+    per-head scale is exactly 1."""
+    grid = _e4m3_codes()
+    grid = grid[np.abs(grid) >= 2.0 ** -3]
+    x = rng.choice(grid, size=shape).astype(np.float32)
+    x[..., 0, 0] = 448.0
+    return x
+
+
+def test_fp8_full_density_on_grid_is_dense(orc):
+    rng = np.random.default_rng(71)
+    B, H, nv, ns, d = 1, 2, 300, 3, 16
+    Q, K, V = (_on_grid(rng, (B, H, nv + ns, d)) * np.float32(1) for _ in range(3))
+    p = orc.params(Q, ns, 32, 1.0, 1)
+    p.scale = 1.0 / 512  # keeps the logits of 448-sized rows moderate
+    O, lse, idx, sc = orc.forward_fp8(p, Q, K, V)
+    assert (sc[..., 1::2] == 1).all() and (sc[..., 0::2] == 1).all()
+    Od, ld = orc.dense(p, Q, K, V)
+    assert np.abs(O - Od).max() < 1e-12 * np.abs(Od).max()
+    assert np.abs(lse - ld).max() < 1e-12
+
+
+def test_fp8_power_of_two_rescaling_is_exact(orc):
+    Q, K, V = small(seed=72, nv=600, ns=4)
+    p = orc.params(Q, 4, 64, 0.2, 1)
+    O, lse, idx, sc = orc.forward_fp8(p, Q, K, V)
+    # V * 4: the same carrier, s_V four times larger
+    O4, lse4, idx4, sc4 = orc.forward_fp8(p, Q, K, V * np.float32(4))
+    assert (idx4 == idx).all() and (O4 == 4 * O).all() and (lse4 == lse).all()
+    # Q * 2 and K / 2: the same carriers, the same s_Q s_K and route
+    O2, lse2, idx2, sc2 = orc.forward_fp8(p, Q * np.float32(2), K * np.float32(0.5), V)
+    assert (idx2 == idx).all()
+    assert (sc2[..., 1] * sc2[..., 3] == sc[..., 1] * sc[..., 3]).all()
+    assert np.abs(O2 - O).max() < 1e-12 and np.abs(lse2 - lse).max() < 1e-12
+
+
+def test_fp8_quantization_changes_the_result(orc):
+    """Off the grid the carrier is not the identity: the FP8 forward departs from the plain one by
+    about the E4M3 rounding (3 mantissa bits), not more."""
+    Q, K, V = small(seed=73, nv=800, ns=5)
+    p = orc.params(Q, 5, 64, 0.2, 1)
+    O8, _, idx8, _ = orc.forward_fp8(p, Q, K, V)
+    O, _, idx = orc.forward(p, Q, K, V)
+    assert (idx8 == idx).all()
+    rel = np.linalg.norm(O8 - O) / np.linalg.norm(O)
+    assert 1e-3 < rel < 2.0 ** -4
+
+
+@pytest.mark.parametrize("pool_mode,ratio", [(1, 0.2), (0, 0.2), (1, 1.0)])
+def test_fp8_forward_matches_brute_force(orc, pool_mode, ratio):
+    Q, K, V = small(seed=74, B=2, nv=1000 - 24, ns=5)
+    perm = None
+    p = orc.params(Q, 5, 64, ratio, pool_mode)
+    O, lse, idx, _ = orc.forward_fp8(p, Q, K, V)
+    Ob, lb, ib = brute.forward(Q, K, V, 5, 64, ratio, pool_mode, fp8=True)
+    assert (idx == ib).all()
+    assert np.abs(O - Ob).max() < 1e-12 and np.abs(lse - lb).max() < 1e-11
+
+
+def test_fp8_reblocked_forward_matches_brute_force(orc):
+    Q, K, V = small(seed=75, nv=640, ns=3)
+    p = orc.params(Q, 3, 64, 0.25, 1)
+    perm = orc.reblock(p, Q, K)
+    O, lse, idx, _ = orc.forward_fp8(p, Q, K, V, perm=perm)
+    Ob, lb, ib = brute.forward(Q, K, V, 3, 64, 0.25, 1, perm=perm, fp8=True)
+    assert (idx == ib).all()
+    assert np.abs(O - Ob).max() < 1e-12 and np.abs(lse - lb).max() < 1e-11
