@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (no sparsity)
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak (no sparsity)
 HBM_PEAK_GBS = 8000.0
 
 
@@ -56,14 +57,14 @@ def algorithmic_flops(idx, wl, ratio_K, counts=None):
     return F_sel, F_sink, F_comp, F_sinkq
 
 
-def committed_traffic(workload):
+def committed_traffic(workload, kernel="attn_fwd"):
     """HBM bytes per attention launch from the committed counter summary, or None when the kernel
     source has changed since the counters were taken (or no summary exists for the workload)."""
     import hashlib
     import re
 
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}.md")
-    src = os.path.join(ROOT, "block_sparse_attention_score_amd", "csrc", "attn_fwd.hip")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.md")
+    src = os.path.join(ROOT, "block_sparse_attention_score_amd", "csrc", f"{kernel}.hip")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -150,6 +151,8 @@ def main():
     ap.add_argument("--ratio", type=float, default=None)
     ap.add_argument("--tau", type=float, default=None,
                     help="adaptive-tau selection (per-head threshold mu + tau*sigma) instead of top-K")
+    ap.add_argument("--fp8", action="store_true",
+                    help="the exact branch, sinks and pseudo-keys on per-head E4M3 carriers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-blocks", type=int, default=600)
     ap.add_argument("--no-forward-check", action="store_true",
@@ -191,8 +194,12 @@ def main():
     pooled["bias"] = torch.empty(B, H, M, **f32)
     pooled["anchor"] = torch.empty(B, H, d, **f32)
     tau_mode = args.tau is not None
+    fp8 = args.fp8
     if tau_mode and wl.reblock:
         print("--tau runs on token-order workloads only", file=sys.stderr)
+        sys.exit(2)
+    if fp8 and (tau_mode or wl.key_partition):
+        print("--fp8 runs with top-K routes on token-order or q_reuse_k layouts", file=sys.stderr)
         sys.exit(2)
     # adaptive tau: a variable route, row I of idx [B,H,M,M] holds counts[I] blocks
     idx = torch.empty(B, H, M, M if tau_mode else Kk, device="cuda", dtype=torch.int32)
@@ -200,7 +207,8 @@ def main():
     O = torch.empty_like(Q)
     lse = torch.empty(B, H, N, **f32)
     sel_ws = torch.empty(sa.workspace_size(p, 5 if tau_mode else 3), device="cuda", dtype=torch.uint8)
-    packed = torch.empty(sa.workspace_size(p, 4), device="cuda", dtype=torch.uint8)
+    packed = torch.empty(sa.workspace_size(p, 9 if fp8 else 4), device="cuda", dtype=torch.uint8)
+    amax = torch.empty(B, H, 3, **f32) if fp8 else None
     stream = torch.cuda.current_stream()
     perm = perm_k = None
     if wl.reblock:  # adaptive blocks: partition, gather, attend, scatter back
@@ -213,7 +221,7 @@ def main():
         Qp, Kp, Vp = Q, K, V
 
     stage_names = ((["reblock"] + (["reblock_k"] if wl.key_partition else []) + ["gather"]) if wl.reblock else []) \
-        + ["pool", "select", "pack", "attend"]
+        + (["fp8_scales"] if fp8 else []) + ["pool", "select", "pack", "attend"]
 
     def step(ev=None):
         k = 1
@@ -229,6 +237,10 @@ def main():
                 sa.spark_attn_gather_rows(p, X, pm, Y, stream)
             if ev: ev[k].record(stream)
             k += 1
+        if fp8:
+            sa.spark_attn_fp8_scales(p, Qp, Kp, Vp, amax, stream)
+            if ev: ev[k].record(stream)
+            k += 1
         sa.spark_attn_pool(p, Qp, Kp, Vp, pooled["q_mean"], pooled["k_mean"], pooled["k_sum"], pooled["v_sum"],
                            pooled["bias"], pooled["anchor"], stream)
         if ev: ev[k].record(stream)
@@ -238,9 +250,14 @@ def main():
         else:
             sa.spark_attn_select(p, pooled["q_mean"], pooled["k_mean"], idx, None, sel_ws, stream)
         if ev: ev[k + 1].record(stream)
-        sa.spark_attn_pack(p, Kp, Vp, pooled["k_sum"], pooled["v_sum"], pooled["bias"], packed, stream)
+        if fp8:
+            sa.spark_attn_pack_fp8(p, Kp, Vp, pooled["k_sum"], pooled["v_sum"], pooled["bias"], amax, packed, stream)
+        else:
+            sa.spark_attn_pack(p, Kp, Vp, pooled["k_sum"], pooled["v_sum"], pooled["bias"], packed, stream)
         if ev: ev[k + 2].record(stream)
-        if tau_mode:
+        if fp8:
+            sa.spark_attn_attend_fp8(p, Qp, packed, idx, perm, amax, O, lse, stream)
+        elif tau_mode:
             sa.spark_attn_attend_var(p, Qp, packed, idx, counts, perm, O, lse, stream)
         else:
             sa.spark_attn_attend(p, Qp, packed, idx, perm, O, lse, stream)
@@ -269,12 +286,14 @@ def main():
     # cross-check: the single-call entry point over the same input
     ms_forward_call, same_out, ws, O2 = None, None, None, None
     if not args.no_forward_check:
-        ws = torch.empty(sa.workspace_size(p, 6 if tau_mode else (2 if wl.reblock else 0)), device="cuda",
-                         dtype=torch.uint8)
+        what = (8 if wl.reblock else 7) if fp8 else 6 if tau_mode else (2 if wl.reblock else 0)
+        ws = torch.empty(sa.workspace_size(p, what), device="cuda", dtype=torch.uint8)
         O2 = torch.empty_like(Q)
 
         def fwd_call():
-            if tau_mode:
+            if fp8:
+                sa.spark_attn_forward_fp8(p, Q, K, V, perm, O2, None, None, None, ws, stream)
+            elif tau_mode:
                 sa.spark_attn_forward_tau(p, args.tau, Q, K, V, O2, None, None, None, ws, stream)
             else:
                 sa.spark_attn_forward_kv(p, Q, K, V, perm, perm_k, O2, None, None, ws, stream)
@@ -304,8 +323,11 @@ def main():
     achieved = F_attn / (ms_attn * 1e-3) / 1e12
     pool_bytes = 3.0 * B * H * wl.n_video * d * Q.element_size() + 4.0 * B * H * M * d * 4 + 4.0 * B * H * M
 
+    peak = MFMA_FP8_PEAK_TFLOPS if fp8 else MFMA_BF16_PEAK_TFLOPS
+    kernel = "attn_fwd_fp8" if fp8 else "attn_fwd"
     out = {
-        "metric": ("selected-block TFLOP/s of the sparse-attention forward at 10% density" if not tau_mode else
+        "metric": ("selected-block TFLOP/s of the sparse-attention forward at 10% density"
+                   + (", E4M3 carriers" if fp8 else "") if not tau_mode else
                    f"selected-block TFLOP/s of the sparse-attention forward with adaptive-tau selection (tau={args.tau})"),
         "value": round(value, 3),
         "unit": "TFLOP/s",
@@ -316,7 +338,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "dtype": "fp8-e4m3 (bf16 in/out)" if fp8 else ("bf16" if wl.dtype == "bf16" else "f32"),
         "data": "synthetic (seeded positional-feature Q/K/V of the clip's shape; no model weights)",
         "config": {
             "workload": wl.name, "description": wl.description, "B": B, "H": H, "N_video": wl.n_video,
@@ -332,20 +354,20 @@ def main():
         "forward_call_output_identical": same_out,
         "flops": {"F_sel": F_sel, "F_sink": F_sink, "F_comp": F_comp, "F_sinkq": F_sinkq},
         "roofline": {
-            "kernel": "attn_fwd_kernel (exact + sink + compressed branches, sink queries)",
-            "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": committed_traffic(wl.name), "traffic_unit": "bytes per launch (FETCH+WRITE, scaled)",
-            "exact_branch_frac": round((F_sel + F_sink) / (ms_attn * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "kernel": f"{kernel}_kernel (exact + sink + compressed branches, sink queries)",
+            "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+            "traffic": committed_traffic(wl.name, kernel), "traffic_unit": "bytes per launch (FETCH+WRITE, scaled)",
+            "exact_branch_frac": round((F_sel + F_sink) / (ms_attn * 1e-3) / 1e12 / peak, 4),
         },
         "pool_roofline": {"bound": "hbm", "achieved": round(pool_bytes / (ms_pool * 1e-3) / 1e9, 1),
                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(pool_bytes / (ms_pool * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline and tau_mode:
-        log("cpu baseline: timed for the top-K route only")
-    if not args.no_cpu_baseline and not tau_mode:
+    if not args.no_cpu_baseline and (tau_mode or fp8):
+        log("cpu baseline: timed for the bf16 top-K path only")
+    if not args.no_cpu_baseline and not tau_mode and not fp8:
         log("cpu baseline (oracle) ...")
         del Q, K, V, O, O2, ws, sel_ws, packed, Qp, Kp, Vp
         if wl.reblock:

@@ -41,6 +41,7 @@ EXPORTS = (
     "spark_attn_status_str", "spark_attn_pool", "spark_attn_select", "spark_attn_pack",
     "spark_attn_attend", "spark_attn_forward", "spark_attn_forward_kv", "spark_attn_reblock",
     "spark_attn_gather_rows", "spark_attn_select_tau", "spark_attn_attend_var", "spark_attn_forward_tau",
+    "spark_attn_fp8_scales", "spark_attn_pack_fp8", "spark_attn_attend_fp8", "spark_attn_forward_fp8",
 )
 
 _lib = None
@@ -73,6 +74,10 @@ def lib():
             "spark_attn_attend_var": ([P, vp, vp, sz, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "spark_attn_forward_tau": ([P, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
                                        ctypes.c_int),
+            "spark_attn_fp8_scales": ([P, vp, vp, vp, vp, vp], ctypes.c_int),
+            "spark_attn_pack_fp8": ([P, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "spark_attn_attend_fp8": ([P, vp, vp, sz, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+            "spark_attn_forward_fp8": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -197,6 +202,29 @@ def spark_attn_forward_tau(p, tau, Q, K, V, O, lse, idx_out, counts_out, workspa
         _ptr(counts_out), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def spark_attn_fp8_scales(p, Q, K, V, amax, stream=None):
+    _check("spark_attn_fp8_scales", lib().spark_attn_fp8_scales(
+        ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(amax), _stream(stream)))
+
+
+def spark_attn_pack_fp8(p, K, V, k_sum, v_sum, bias, amax, packed, stream=None):
+    _check("spark_attn_pack_fp8", lib().spark_attn_pack_fp8(
+        ctypes.byref(p), _ptr(K), _ptr(V), _ptr(k_sum), _ptr(v_sum), _ptr(bias), _ptr(amax),
+        _ptr(packed), _nbytes(packed), _stream(stream)))
+
+
+def spark_attn_attend_fp8(p, Q, packed, idx, perm, amax, O, lse=None, stream=None):
+    _check("spark_attn_attend_fp8", lib().spark_attn_attend_fp8(
+        ctypes.byref(p), _ptr(Q), _ptr(packed), _nbytes(packed), _ptr(idx), _ptr(perm), _ptr(amax),
+        _ptr(O), _ptr(lse), _stream(stream)))
+
+
+def spark_attn_forward_fp8(p, Q, K, V, perm, O, lse, idx_out, amax_out, workspace, stream=None):
+    _check("spark_attn_forward_fp8", lib().spark_attn_forward_fp8(
+        ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(perm), _ptr(O), _ptr(lse), _ptr(idx_out),
+        _ptr(amax_out), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
 def spark_attn_reblock(p, Q, K, perm, workspace, stream=None):
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("spark_attn_reblock", lib().spark_attn_reblock(
@@ -313,6 +341,48 @@ def forward_tau(Q, K, V, n_sink, block, tau, pool_mode=POOL_REWEIGHT, scale=0.0,
         res += (lse,)
     if return_route:
         res += (idx, counts)
+    return res[0] if len(res) == 1 else res
+
+
+def fp8_scales(Q, K, V, n_sink, block, stream=None):
+    """amax [B,H,3] (Q, K, V) of the per-head E4M3 carriers."""
+    p = params(Q, n_sink, block)
+    B, H = Q.shape[:2]
+    amax = torch.empty(B, H, 3, device=Q.device, dtype=torch.float32)
+    spark_attn_fp8_scales(p, Q, K, V, amax, stream)
+    return amax
+
+
+def pack_fp8(K, V, pooled, amax, n_sink, block, scale=0.0, stream=None):
+    p = params(K, n_sink, block, 1.0, POOL_REWEIGHT, scale)
+    packed = torch.empty(workspace_size(p, 9), device=K.device, dtype=torch.uint8)
+    spark_attn_pack_fp8(p, K, V, pooled["k_sum"], pooled["v_sum"], pooled["bias"], amax, packed, stream)
+    return packed
+
+
+def forward_fp8(Q, K, V, n_sink, block, topk_ratio, pool_mode=POOL_REWEIGHT, perm=None, scale=0.0,
+                return_lse=False, return_idx=False, return_amax=False, workspace=None, stream=None):
+    """Forward with the exact branch, sinks and pseudo-keys on per-head E4M3 carriers.  Returns O
+    (and lse, idx [B,H,M,K], amax [B,H,3] when asked)."""
+    p = params(Q, n_sink, block, topk_ratio, pool_mode, scale)
+    M = num_blocks(p)
+    Kk = topk_count(M, topk_ratio)
+    B, H, N, _ = Q.shape
+    O = torch.empty_like(Q)
+    lse = torch.empty(B, H, N, device=Q.device, dtype=torch.float32) if return_lse else None
+    idx = torch.empty(B, H, M, Kk, device=Q.device, dtype=torch.int32) if return_idx else None
+    amax = torch.empty(B, H, 3, device=Q.device, dtype=torch.float32) if return_amax else None
+    if workspace is None:
+        workspace = torch.empty(workspace_size(p, 8 if perm is not None else 7), device=Q.device,
+                                dtype=torch.uint8)
+    spark_attn_forward_fp8(p, Q, K, V, perm, O, lse, idx, amax, workspace, stream)
+    res = (O,)
+    if return_lse:
+        res += (lse,)
+    if return_idx:
+        res += (idx,)
+    if return_amax:
+        res += (amax,)
     return res[0] if len(res) == 1 else res
 
 

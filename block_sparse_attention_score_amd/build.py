@@ -13,7 +13,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspark_attn.so")
 
-SOURCES = ["api.hip", "pool.hip", "select.hip", "pack.hip", "attn_fwd.hip", "permute.hip", "reblock.hip"]
+SOURCES = ["api.hip", "pool.hip", "select.hip", "pack.hip", "attn_fwd.hip", "attn_fwd_fp8.hip", "permute.hip",
+           "reblock.hip"]
 # reblock takes every decision in binary64 with a fixed operation order: no contraction there.
 PER_FILE = {"reblock.hip": ["-ffp-contract=off"]}
 

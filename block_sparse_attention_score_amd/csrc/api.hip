@@ -111,6 +111,35 @@ static TauWorkspace tau_layout(const LaunchCtx& L) {
     return w;
 }
 
+struct Fp8Workspace {
+    size_t q_mean, k_mean, k_sum, v_sum, bias, anchor, idx, scores, amax, packed, qp, kp, vp, total;
+};
+
+static Fp8Workspace fp8_layout(const LaunchCtx& L, bool with_perm) {
+    Fp8Workspace w;
+    const size_t md = (size_t)L.BH * L.M * L.d * 4;
+    size_t o = 0;
+    w.q_mean = o; o = align256(o + md);
+    w.k_mean = o; o = align256(o + md);
+    w.k_sum = o; o = align256(o + md);
+    w.v_sum = o; o = align256(o + md);
+    w.bias = o; o = align256(o + (size_t)L.BH * L.M * 4);
+    w.anchor = o; o = align256(o + (size_t)L.BH * L.d * 4);
+    w.idx = o; o = align256(o + (size_t)L.BH * L.M * L.K * 4);
+    w.scores = o; o = align256(o + select_workspace_bytes(L));
+    w.amax = o; o = align256(o + (size_t)L.BH * 3 * 4);
+    w.packed = o; o = align256(o + pack_geom_fp8(L).bytes);
+    w.qp = w.kp = w.vp = 0;
+    if (with_perm) {
+        const size_t x = (size_t)L.BH * L.N * L.d * (L.dtype == SPARK_ATTN_BF16 ? 2 : 4);
+        w.qp = o; o = align256(o + x);
+        w.kp = o; o = align256(o + x);
+        w.vp = o; o = align256(o + x);
+    }
+    w.total = o;
+    return w;
+}
+
 }  // namespace spark
 
 using namespace spark;
@@ -134,6 +163,8 @@ size_t spark_attn_workspace_size(const spark_attn_params* p, int what) {
     if (what == 4) return pack_geom(L).bytes;
     if (what == 5) return tau_select_bytes(L);
     if (what == 6) return tau_layout(L).total;
+    if (what == 7 || what == 8) return fp8_layout(L, what == 8).total;
+    if (what == 9) return pack_geom_fp8(L).bytes;
     return 0;
 }
 
@@ -313,6 +344,81 @@ int spark_attn_forward_kv(const spark_attn_params* p, const void* Q, const void*
 int spark_attn_forward(const spark_attn_params* p, const void* Q, const void* K, const void* V, const int32_t* perm,
                        void* O, float* lse, int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream) {
     return spark_attn_forward_kv(p, Q, K, V, perm, perm, O, lse, idx_out, workspace, ws_bytes, stream);
+}
+
+int spark_attn_fp8_scales(const spark_attn_params* p, const void* Q, const void* K, const void* V, float* amax,
+                          void* stream) {
+    LaunchCtx L;
+    int s = make_ctx(p, stream, &L);
+    if (s < 0) return s;
+    if (!Q || !K || !V || !amax) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V)) return SPARK_ATTN_MISALIGNED;
+    launch_fp8_scales(L, Q, K, V, (uint32_t*)amax);
+    return launch_status();
+}
+
+int spark_attn_pack_fp8(const spark_attn_params* p, const void* K, const void* V, const float* k_sum,
+                        const float* v_sum, const float* bias, const float* amax, void* packed, size_t packed_bytes,
+                        void* stream) {
+    LaunchCtx L;
+    int s = make_ctx(p, stream, &L);
+    if (s < 0) return s;
+    if (!K || !V || !k_sum || !v_sum || !bias || !amax) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!aligned16(K) || !aligned16(V) || !aligned16(k_sum) || !aligned16(v_sum) || !aligned16(packed))
+        return SPARK_ATTN_MISALIGNED;
+    if (!packed || packed_bytes < pack_geom_fp8(L).bytes) return SPARK_ATTN_WORKSPACE_TOO_SMALL;
+    launch_pack_fp8(L, K, V, k_sum, v_sum, bias, (const uint32_t*)amax, packed);
+    return launch_status();
+}
+
+int spark_attn_attend_fp8(const spark_attn_params* p, const void* Q, const void* packed, size_t packed_bytes,
+                          const int32_t* idx, const int32_t* perm, const float* amax, void* O, float* lse,
+                          void* stream) {
+    LaunchCtx L;
+    int s = make_ctx(p, stream, &L);
+    if (s < 0) return s;
+    if (!Q || !idx || !amax || !O) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!aligned16(Q) || !aligned16(packed) || !aligned16(O)) return SPARK_ATTN_MISALIGNED;
+    if (!packed || packed_bytes < pack_geom_fp8(L).bytes) return SPARK_ATTN_WORKSPACE_TOO_SMALL;
+    launch_attend_fp8(L, Q, packed, idx, perm, (const uint32_t*)amax, O, lse);
+    return launch_status();
+}
+
+int spark_attn_forward_fp8(const spark_attn_params* p, const void* Q, const void* K, const void* V,
+                           const int32_t* perm, void* O, float* lse, int32_t* idx_out, float* amax_out,
+                           void* workspace, size_t ws_bytes, void* stream) {
+    LaunchCtx L;
+    int s = make_ctx(p, stream, &L);
+    if (s < 0) return s;
+    if (!Q || !K || !V || !O) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(workspace))
+        return SPARK_ATTN_MISALIGNED;
+    const Fp8Workspace w = fp8_layout(L, perm != nullptr);
+    if (!workspace || ws_bytes < w.total) return SPARK_ATTN_WORKSPACE_TOO_SMALL;
+    char* ws = (char*)workspace;
+    const void *q = Q, *k = K, *v = V;
+    if (perm) {
+        launch_gather_rows(L, Q, perm, ws + w.qp);
+        launch_gather_rows(L, K, perm, ws + w.kp);
+        launch_gather_rows(L, V, perm, ws + w.vp);
+        q = ws + w.qp;
+        k = ws + w.kp;
+        v = ws + w.vp;
+    }
+    float* q_mean = (float*)(ws + w.q_mean);
+    float* k_mean = (float*)(ws + w.k_mean);
+    float* k_sum = (float*)(ws + w.k_sum);
+    float* v_sum = (float*)(ws + w.v_sum);
+    float* bias = (float*)(ws + w.bias);
+    float* anchor = (float*)(ws + w.anchor);
+    int32_t* idx = idx_out ? idx_out : (int32_t*)(ws + w.idx);
+    uint32_t* amax = amax_out ? (uint32_t*)amax_out : (uint32_t*)(ws + w.amax);
+    launch_fp8_scales(L, q, k, v, amax);
+    launch_pool(L, q, k, v, q_mean, k_mean, k_sum, v_sum, bias, anchor);
+    launch_select(L, q_mean, k_mean, idx, (float*)(ws + w.scores));
+    launch_pack_fp8(L, k, v, k_sum, v_sum, bias, amax, ws + w.packed);
+    launch_attend_fp8(L, q, ws + w.packed, idx, perm, amax, O, lse);
+    return launch_status();
 }
 
 int spark_attn_reblock(const spark_attn_params* p, const void* Q, const void* K, int32_t* perm, void* workspace,

@@ -45,6 +45,15 @@ void launch_attend(const LaunchCtx& L, const void* Q, const void* packed, const 
 
 void launch_gather_rows(const LaunchCtx& L, const void* X, const int32_t* perm, void* Y);
 
+// FP8 (E4M3) carriers: per-head amax [BH][3] (Q, K, V; float bits), packed fp8 tiles (layout in
+// attn_fwd_fp8.hip; same tile list and bias rows as pack_geom), and the attention on them.
+PackGeom pack_geom_fp8(const LaunchCtx& L);
+void launch_fp8_scales(const LaunchCtx& L, const void* Q, const void* K, const void* V, uint32_t* amax);
+void launch_pack_fp8(const LaunchCtx& L, const void* K, const void* V, const float* k_sum, const float* v_sum,
+                     const float* bias, const uint32_t* amax, void* packed);
+void launch_attend_fp8(const LaunchCtx& L, const void* Q, const void* packed, const int32_t* idx,
+                       const int32_t* perm, const uint32_t* amax, void* O, float* lse);
+
 // Reblock workspace layout (bytes), and its launch sequence.
 size_t reblock_workspace_bytes(const LaunchCtx& L);
 void launch_reblock(const LaunchCtx& L, const void* Q, const void* K, int32_t* perm, void* ws);

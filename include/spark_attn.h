@@ -86,7 +86,9 @@ int spark_attn_topk_count(int M, float ratio);
  *             spark_attn_forward_kv with either partition);
  *   what = 1: spark_attn_reblock;               what = 3: spark_attn_select without `scores`;
  *   what = 4: the packed key/value tiles of spark_attn_pack / spark_attn_attend;
- *   what = 5: spark_attn_select_tau;            what = 6: spark_attn_forward_tau. */
+ *   what = 5: spark_attn_select_tau;            what = 6: spark_attn_forward_tau;
+ *   what = 7: spark_attn_forward_fp8 without perm; what = 8: spark_attn_forward_fp8 with perm;
+ *   what = 9: the packed E4M3 tiles of spark_attn_pack_fp8 / spark_attn_attend_fp8. */
 size_t spark_attn_workspace_size(const spark_attn_params *p, int what);
 
 /* Static description of a status code. */
@@ -235,6 +237,40 @@ int spark_attn_forward_kv(const spark_attn_params *p, const void *Q, const void 
  */
 int spark_attn_reblock(const spark_attn_params *p, const void *Q, const void *K, int32_t *perm,
                        void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * FP8 carriers (H3 Optimizations README, section "Manual Sparse Sage recovery": the FP8
+ * FlexAttention fallback stores Q/K/V as per-head-scaled E4M3, restores the Q/K scale before the
+ * softmax, returns the output in the original floating type and consumes the same route).
+ * E4M3 is the OCP 8-bit float (4 exponent bits, bias 7, 3 mantissa bits, largest value 448).
+ * Per (batch, head) and tensor, amax = max |x| over all N rows; r = 448/amax and s = amax/448
+ * (binary32, both 1 when amax = 0); the carrier of x is e4m3(x * r), rounded to nearest even.
+ * Keys' and values' scales also carry the compressed pseudo-keys.  Every logit is
+ * scale * s_Q * s_K * (q8 . k8) (+ the pseudo-key bias), every value s_V * v8; the probabilities
+ * are rounded to E4M3 for the value product, the normaliser sums them unrounded.
+ *
+ * spark_attn_fp8_scales: amax [B,H,3] fp32 (Q, K, V), written with atomics after a clear.
+ * spark_attn_pack_fp8: the tiles of spark_attn_pack on E4M3 carriers (same tile list and fp32
+ *   bias rows; a tile is 64 key rows of d bytes, then d value rows of 64 bytes); `packed` holds
+ *   spark_attn_workspace_size(p, 9) bytes.
+ * spark_attn_attend_fp8: spark_attn_attend on those tiles; idx [B,H,M,K] (ascending rows), perm as
+ *   in spark_attn_attend; amax as written by spark_attn_fp8_scales for the same Q, K, V.
+ * spark_attn_forward_fp8: [gather by perm] -> scales -> pool -> select -> pack_fp8 -> attend_fp8;
+ *   pooling and selection see the unquantized inputs (the route equals spark_attn_forward's);
+ *   amax_out [B,H,3] or NULL; workspace of spark_attn_workspace_size(p, perm ? 8 : 7) bytes.
+ * Errors and ownership as for the bf16 calls; every pointer is device memory.
+ */
+int spark_attn_fp8_scales(const spark_attn_params *p, const void *Q, const void *K, const void *V,
+                          float *amax, void *stream);
+int spark_attn_pack_fp8(const spark_attn_params *p, const void *K, const void *V, const float *k_sum,
+                        const float *v_sum, const float *bias, const float *amax, void *packed,
+                        size_t packed_bytes, void *stream);
+int spark_attn_attend_fp8(const spark_attn_params *p, const void *Q, const void *packed,
+                          size_t packed_bytes, const int32_t *idx, const int32_t *perm,
+                          const float *amax, void *O, float *lse, void *stream);
+int spark_attn_forward_fp8(const spark_attn_params *p, const void *Q, const void *K, const void *V,
+                           const int32_t *perm, void *O, float *lse, int32_t *idx_out,
+                           float *amax_out, void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * Row gather used for the q_reuse_k layout: for every (batch, head), Y row q = X row perm[q]

@@ -18,7 +18,7 @@ OK, INVALID, UNSUPPORTED, WS_SMALL, HIP_ERR, MISALIGNED = 0, -1, -2, -3, -4, -5
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(spark_attn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(spark_attn_[a-z0-9_]+)\s*\(", text)))
 
 
 def P(**kw):
@@ -179,3 +179,33 @@ def test_adaptive_tau_entry_points_validate_before_launch():
     assert L.spark_attn_forward_tau(ctypes.byref(p), f(1.0), a, None, a, a, None, None, None, a, w6, None) == INVALID
     q = P(d=96)
     assert L.spark_attn_select_tau(ctypes.byref(q), f(1.0), a, a, a, a, None, a, 1 << 40, None) == UNSUPPORTED
+
+
+def test_fp8_entry_points_validate_before_launch():
+    L = sa.lib()
+    p = P()
+    a = ctypes.c_void_p(0x100000)
+    bad = ctypes.c_void_p(0x100008)
+    w7 = L.spark_attn_workspace_size(ctypes.byref(p), 7)
+    w8 = L.spark_attn_workspace_size(ctypes.byref(p), 8)
+    w9 = L.spark_attn_workspace_size(ctypes.byref(p), 9)
+    # E4M3 tiles are half the bf16 tiles' key/value bytes (same bias rows)
+    w4 = L.spark_attn_workspace_size(ctypes.byref(p), 4)
+    M = L.spark_attn_num_blocks(ctypes.byref(p))
+    Tall = M + (p.n_sink + 63) // 64 + (M + 63) // 64
+    BH = p.B * p.H
+    assert w9 >= BH * Tall * 128 * p.d and w9 < w4
+    assert w8 > w7 > w9
+    byref = ctypes.byref
+    assert L.spark_attn_fp8_scales(byref(p), a, a, a, None, None) == INVALID
+    assert L.spark_attn_fp8_scales(byref(p), a, bad, a, a, None) == MISALIGNED
+    assert L.spark_attn_pack_fp8(byref(p), a, a, a, a, a, None, a, w9, None) == INVALID
+    assert L.spark_attn_pack_fp8(byref(p), a, a, a, a, a, a, a, w9 - 1, None) == WS_SMALL
+    assert L.spark_attn_attend_fp8(byref(p), a, a, w9, a, None, None, a, None, None) == INVALID
+    assert L.spark_attn_attend_fp8(byref(p), a, a, w9 - 1, a, None, a, a, None, None) == WS_SMALL
+    assert L.spark_attn_attend_fp8(byref(p), a, bad, w9, a, None, a, a, None, None) == MISALIGNED
+    assert L.spark_attn_forward_fp8(byref(p), a, a, a, None, a, None, None, None, a, w7 - 1, None) == WS_SMALL
+    assert L.spark_attn_forward_fp8(byref(p), a, a, a, a, a, None, None, None, a, w8 - 1, None) == WS_SMALL
+    assert L.spark_attn_forward_fp8(byref(p), a, None, a, None, a, None, None, None, a, w7, None) == INVALID
+    q = P(d=96)
+    assert L.spark_attn_forward_fp8(byref(q), a, a, a, None, a, None, None, None, a, 1 << 40, None) == UNSUPPORTED
