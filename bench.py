@@ -68,8 +68,8 @@ def committed_traffic(workload, kernel="attn_fwd"):
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    h = re.search(r"attn_fwd_kernel_source_sha256_16: ([0-9a-f]+)", text)
-    t = re.search(r"attn_fwd_kernel_traffic_bytes_per_launch: ([0-9.]+)", text)
+    h = re.search(kernel + r"_kernel_source_sha256_16: ([0-9a-f]+)", text)
+    t = re.search(kernel + r"_kernel_traffic_bytes_per_launch: ([0-9.]+)", text)
     if not h or not t or hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != h.group(1):
         return None
     return float(t.group(1))
