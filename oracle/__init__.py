@@ -25,7 +25,7 @@ class Params(ctypes.Structure):
     _fields_ = [
         ("B", ctypes.c_int), ("H", ctypes.c_int), ("N", ctypes.c_int), ("d", ctypes.c_int),
         ("n_sink", ctypes.c_int), ("block", ctypes.c_int), ("topk_ratio", ctypes.c_float),
-        ("pool_mode", ctypes.c_int), ("scale", ctypes.c_double),
+        ("pool_mode", ctypes.c_int), ("scale", ctypes.c_double), ("block_k", ctypes.c_int),
     ]
 
 
@@ -54,6 +54,7 @@ def lib():
                          for t in (np.float32, np.float64, np.int32))
         vp = ctypes.c_void_p
         L.orc_num_blocks.argtypes = [P]
+        L.orc_num_key_blocks.argtypes = [P]
         L.orc_topk_count.argtypes = [ctypes.c_int, ctypes.c_float]
         L.orc_num_threads.argtypes = []
         L.orc_pool.argtypes = [P, f32, f32, f32, f64, f64, f64, f64, f64, f64]
@@ -80,9 +81,10 @@ def lib():
     return _lib
 
 
-def params(Q, n_sink, block, ratio=0.1, pool_mode=1, scale=0.0) -> Params:
+def params(Q, n_sink, block, ratio=0.1, pool_mode=1, scale=0.0, block_k=0) -> Params:
+    """block: query block size; block_k: key block size (0: the same as block)."""
     B, H, N, d = Q.shape
-    return Params(B, H, N, d, n_sink, block, float(ratio), int(pool_mode), float(scale))
+    return Params(B, H, N, d, n_sink, block, float(ratio), int(pool_mode), float(scale), int(block_k))
 
 
 def _f32(x):
@@ -90,7 +92,18 @@ def _f32(x):
 
 
 def num_blocks(p: Params) -> int:
+    """Query blocks M."""
     return lib().orc_num_blocks(ctypes.byref(p))
+
+
+def num_key_blocks(p: Params) -> int:
+    """Key blocks M_k (M when the key block size equals the query block size)."""
+    return lib().orc_num_key_blocks(ctypes.byref(p))
+
+
+def _equal_blocks(p: Params, what):
+    if p.block_k not in (0, p.block):
+        raise ValueError(f"{what} is defined for equal query and key blocks")
 
 
 def topk_count(M: int, ratio: float) -> int:
@@ -102,10 +115,12 @@ def num_threads() -> int:
 
 
 def pool(p: Params, Q, K, V):
-    """Returns dict q_mean, k_mean, k_sum, v_sum [B,H,M,d], bias [B,H,M], anchor [B,H,d]."""
-    M = num_blocks(p)
-    out = {k: np.empty((p.B, p.H, M, p.d)) for k in ("q_mean", "k_mean", "k_sum", "v_sum")}
-    out["bias"] = np.empty((p.B, p.H, M))
+    """Returns dict q_mean [B,H,M,d]; k_mean, k_sum, v_sum [B,H,M_k,d], bias [B,H,M_k];
+    anchor [B,H,d]."""
+    M, Mk = num_blocks(p), num_key_blocks(p)
+    out = {"q_mean": np.empty((p.B, p.H, M, p.d))}
+    out.update({k: np.empty((p.B, p.H, Mk, p.d)) for k in ("k_mean", "k_sum", "v_sum")})
+    out["bias"] = np.empty((p.B, p.H, Mk))
     out["anchor"] = np.empty((p.B, p.H, p.d))
     lib().orc_pool(ctypes.byref(p), _f32(Q), _f32(K), _f32(V), out["q_mean"], out["k_mean"],
                    out["k_sum"], out["v_sum"], out["bias"], out["anchor"])
@@ -113,8 +128,8 @@ def pool(p: Params, Q, K, V):
 
 
 def scores(p: Params, q_mean, k_mean):
-    M = num_blocks(p)
-    S = np.empty((p.B, p.H, M, M))
+    M, Mk = num_blocks(p), num_key_blocks(p)
+    S = np.empty((p.B, p.H, M, Mk))
     lib().orc_scores(ctypes.byref(p), np.ascontiguousarray(q_mean, np.float64),
                      np.ascontiguousarray(k_mean, np.float64), S)
     return S
@@ -122,7 +137,7 @@ def scores(p: Params, q_mean, k_mean):
 
 def select(p: Params, S):
     M = num_blocks(p)
-    K = topk_count(M, p.topk_ratio)
+    K = topk_count(num_key_blocks(p), p.topk_ratio)
     idx = np.empty((p.B, p.H, M, K), np.int32)
     lib().orc_select(ctypes.byref(p), np.ascontiguousarray(S, np.float64), idx)
     return idx
@@ -140,7 +155,7 @@ def forward(p: Params, Q, K, V, perm=None, idx=None, perm_k=None):
     perm: query partition (and output rows); perm_k: separate key partition for K and V, or
     None for keys and values reusing perm."""
     M = num_blocks(p)
-    Ksel = topk_count(M, p.topk_ratio)
+    Ksel = topk_count(num_key_blocks(p), p.topk_ratio)
     O = np.empty((p.B, p.H, p.N, p.d))
     lse = np.empty((p.B, p.H, p.N))
     idx_out = np.empty((p.B, p.H, M, Ksel), np.int32)
@@ -162,6 +177,7 @@ def select_tau(p: Params, tau, S):
     """Adaptive-tau routes from block scores S [B,H,M,M]: (idx [B,H,M,M] with row I's kept blocks
     ascending in its first counts[I] entries (the rest -1), counts [B,H,M], stats [B,H,2] =
     (mu, sigma))."""
+    _equal_blocks(p, "adaptive-tau selection")
     M = num_blocks(p)
     idx = np.full((p.B, p.H, M, M), -1, np.int32)
     counts = np.empty((p.B, p.H, M), np.int32)
@@ -174,6 +190,7 @@ def select_tau(p: Params, tau, S):
 def forward_tau(p: Params, tau, Q, K, V, idx=None, counts=None):
     """Forward with adaptive-tau routes.  Returns (O, lse, idx [B,H,M,M], counts [B,H,M]); idx and
     counts, when given, replace the oracle's own selection."""
+    _equal_blocks(p, "adaptive-tau selection")
     M = num_blocks(p)
     O = np.empty((p.B, p.H, p.N, p.d))
     lse = np.empty((p.B, p.H, p.N))
@@ -212,7 +229,7 @@ def forward_fp8(p: Params, Q, K, V, perm=None, idx=None):
     """Forward with Q, K, V and the pseudo-keys on per-head-scaled E4M3 carriers.  Returns
     (O, lse, idx [B,H,M,K], scales [B,H,6])."""
     M = num_blocks(p)
-    Ksel = topk_count(M, p.topk_ratio)
+    Ksel = topk_count(num_key_blocks(p), p.topk_ratio)
     O = np.empty((p.B, p.H, p.N, p.d))
     lse = np.empty((p.B, p.H, p.N))
     idx_out = np.empty((p.B, p.H, M, Ksel), np.int32)

@@ -33,10 +33,13 @@ def budget(M, ratio):
     return int(min(M, max(1, k)))
 
 
-def pool_head(q, k, v, n_video, block, pool_mode, s):
-    starts, sizes = _blocks(n_video, block)
+def pool_head(q, k, v, n_video, block, pool_mode, s, block_k=None):
+    """Query means over query blocks of `block` rows; key summaries over key blocks of `block_k`
+    keys (default: `block`)."""
+    qs, qz = _blocks(n_video, block)
+    starts, sizes = _blocks(n_video, block_k or block)
     qv, kv, vv = q[:n_video], k[:n_video], v[:n_video]
-    q_mean = np.add.reduceat(qv, starts, axis=0) / sizes[:, None]
+    q_mean = np.add.reduceat(qv, qs, axis=0) / qz[:, None]
     k_mean = np.add.reduceat(kv, starts, axis=0) / sizes[:, None]
     anchor = qv.mean(axis=0)
     if pool_mode == 0:
@@ -58,10 +61,10 @@ def pool_head(q, k, v, n_video, block, pool_mode, s):
 
 def select_head(q_mean, k_mean, s, K):
     S = s * (q_mean @ k_mean.T)
-    M = S.shape[0]
+    M, Mk = S.shape
     idx = np.empty((M, K), np.int64)
     for I in range(M):
-        order = np.lexsort((np.arange(M), -S[I]))
+        order = np.lexsort((np.arange(Mk), -S[I]))
         idx[I] = np.sort(order[:K])
     return S, idx
 
@@ -93,23 +96,29 @@ def _fp8_carrier(x):
 
 
 def forward(Q, K, V, n_sink, block, ratio, pool_mode=1, scale=None, perm=None, idx=None, perm_k=None,
-            tau=None, fp8=False):
+            tau=None, fp8=False, block_k=None):
     """Q, K, V [B,H,N,d] (float arrays). Returns O, lse (binary64) and the route idx.
     perm: query partition (and output rows); perm_k: separate key partition of K and V (None:
     keys and values reuse perm).  tau: adaptive-tau routes instead of top-K (the returned idx is
     then the boolean kept matrix [B,H,M,M]).  fp8: queries, keys, values and the pseudo-keys on
-    per-head E4M3 carriers (route and bias from the unquantized inputs)."""
+    per-head E4M3 carriers (route and bias from the unquantized inputs).  block_k: key block size
+    (default: block); the route, the budget and the compressed branch are per key block."""
     Q, K, V = (np.asarray(x, np.float64) for x in (Q, K, V))
     B, H, N, d = Q.shape
     n_video = N - n_sink
     s = 1.0 / math.sqrt(d) if not scale else float(scale)
+    bk = block_k or block
     starts, sizes = _blocks(n_video, block)
-    M = len(starts)
-    Ksel = budget(M, ratio)
+    kstarts, ksizes = _blocks(n_video, bk)
+    M, Mk = len(starts), len(kstarts)
+    if tau is not None and Mk != M:
+        raise ValueError("adaptive tau is defined for equal query and key blocks")
+    Ksel = budget(Mk, ratio)
     O = np.empty((B, H, N, d))
     LSE = np.empty((B, H, N))
     IDX = np.empty((B, H, M, Ksel), np.int64) if tau is None else np.empty((B, H, M, M), bool)
-    blk = np.repeat(np.arange(M), sizes)  # video token -> block
+    blk = np.repeat(np.arange(M), sizes)  # video token -> query block
+    kblk = np.repeat(np.arange(Mk), ksizes)  # video token -> key block
     for b in range(B):
         for h in range(H):
             q, k, v = Q[b, h].copy(), K[b, h].copy(), V[b, h].copy()
@@ -119,7 +128,7 @@ def forward(Q, K, V, n_sink, block, ratio, pool_mode=1, scale=None, perm=None, i
             if pk is not None:
                 pkm = np.asarray(pk[b, h])
                 k[:n_video], v[:n_video] = k[pkm], v[pkm]
-            pooled = pool_head(q, k, v, n_video, block, pool_mode, s)
+            pooled = pool_head(q, k, v, n_video, block, pool_mode, s, bk)
             if tau is not None:
                 chosen = select_tau_head(s * (pooled["q_mean"] @ pooled["k_mean"].T), tau)
                 IDX[b, h] = chosen
@@ -129,7 +138,7 @@ def forward(Q, K, V, n_sink, block, ratio, pool_mode=1, scale=None, perm=None, i
                 else:
                     sel = np.asarray(idx[b, h])
                 IDX[b, h] = sel
-                chosen = np.zeros((M, M), bool)  # chosen[I, J]
+                chosen = np.zeros((M, Mk), bool)  # chosen[I, J]
                 chosen[np.repeat(np.arange(M), Ksel), sel.reshape(-1)] = True
             qa, ka, va, kt, vt, sl, sv = q, k, v, pooled["k_sum"], pooled["v_sum"], s, 1.0
             if fp8:
@@ -148,9 +157,9 @@ def forward(Q, K, V, n_sink, block, ratio, pool_mode=1, scale=None, perm=None, i
                 sv = float(sv)
             logits = np.concatenate([sl * (qa @ ka.T), sl * (qa @ kt.T) + pooled["bias"]], axis=1)
             values = sv * np.concatenate([va, vt], axis=0)
-            mask = np.zeros((N, N + M), bool)
+            mask = np.zeros((N, N + Mk), bool)
             # video queries: keys of chosen blocks, all sinks, pseudo-keys of unchosen blocks
-            mask[:n_video, :n_video] = chosen[blk][:, blk]
+            mask[:n_video, :n_video] = chosen[blk][:, kblk]
             mask[:n_video, n_video:N] = True
             mask[:n_video, N:] = ~chosen[blk]
             # sink queries: every real key, no pseudo-key

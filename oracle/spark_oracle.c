@@ -33,6 +33,7 @@ typedef struct {
     float topk_ratio;  /* fraction of key blocks kept per query block (a binary32 value) */
     int pool_mode;     /* 0: plain mean pool, 1: anchor-weighted summary + log-mass bias */
     double scale;      /* softmax scale; 0 means 1/sqrt(d) */
+    int block_k;       /* key block size; 0 means the query block size `block` */
 } orc_params;
 
 static double scale_of(const orc_params *p) { return p->scale != 0.0 ? p->scale : 1.0 / sqrt((double)p->d); }
@@ -47,8 +48,13 @@ int orc_num_threads(void)
 #endif
 }
 
-/* Number of key blocks M = ceil(N_v / block); the last block may be partial. */
+/* Query blocks M = ceil(N_v / block) and key blocks M_k = ceil(N_v / block_k); a last block may be
+ * partial.  Reading of the asymmetric route [H3O, "Manual Sparse Sage recovery": the sparse
+ * backends consume a 128Q x 64KV route]: query blocks of `block` rows are routed to key blocks
+ * of `block_k` keys; pooling, scores, the budget and the compressed branch are per key block. */
+static int key_block(const orc_params *p) { return p->block_k > 0 ? p->block_k : p->block; }
 int orc_num_blocks(const orc_params *p) { return (n_video(p) + p->block - 1) / p->block; }
+int orc_num_key_blocks(const orc_params *p) { return (n_video(p) + key_block(p) - 1) / key_block(p); }
 
 /* Top-K budget from topk_mode=topk_ratio [SH3 "ワークフロー"], the fixed keep fraction of the
  * top-k mode [CORE]: K = floor(r*M + 1/2) in binary64, clamped to [1, M]. */
@@ -98,7 +104,8 @@ static void pool_head(const orc_params *p, const float *Qh, const float *Kh, con
                       double *q_mean, double *k_mean, double *k_sum, double *v_sum,
                       double *bias, double *anchor)
 {
-    const int d = p->d, b = p->block, Nv = n_video(p), M = orc_num_blocks(p);
+    const int d = p->d, bq = p->block, b = key_block(p), Nv = n_video(p), Mq = orc_num_blocks(p);
+    const int M = orc_num_key_blocks(p);
     const double s = scale_of(p);
 
     for (int c = 0; c < d; ++c) anchor[c] = 0.0;
@@ -106,18 +113,23 @@ static void pool_head(const orc_params *p, const float *Qh, const float *Kh, con
         for (int c = 0; c < d; ++c) anchor[c] += (double)Qh[(size_t)i * d + c];
     for (int c = 0; c < d; ++c) anchor[c] /= (double)Nv;
 
+    for (int I = 0; I < Mq; ++I) {
+        const int lo = I * bq, n = block_len(Nv, bq, I);
+        double *qm = q_mean + (size_t)I * d;
+        for (int c = 0; c < d; ++c) {
+            double sq = 0.0;
+            for (int i = lo; i < lo + n; ++i) sq += (double)Qh[(size_t)i * d + c];
+            qm[c] = sq / n;
+        }
+    }
     double *x = (double *)malloc(sizeof(double) * (size_t)b);
     for (int J = 0; J < M; ++J) {
         const int lo = J * b, n = block_len(Nv, b, J);
-        double *qm = q_mean + (size_t)J * d, *km = k_mean + (size_t)J * d;
+        double *km = k_mean + (size_t)J * d;
         double *ks = k_sum + (size_t)J * d, *vs = v_sum + (size_t)J * d;
         for (int c = 0; c < d; ++c) {
-            double sq = 0.0, sk = 0.0;
-            for (int i = lo; i < lo + n; ++i) {
-                sq += (double)Qh[(size_t)i * d + c];
-                sk += (double)Kh[(size_t)i * d + c];
-            }
-            qm[c] = sq / n;
+            double sk = 0.0;
+            for (int i = lo; i < lo + n; ++i) sk += (double)Kh[(size_t)i * d + c];
             km[c] = sk / n;
         }
         if (p->pool_mode == 0) {
@@ -156,12 +168,12 @@ void orc_pool(const orc_params *p, const float *Q, const float *K, const float *
               double *q_mean, double *k_mean, double *k_sum, double *v_sum, double *bias,
               double *anchor)
 {
-    const int M = orc_num_blocks(p), d = p->d;
+    const int Mq = orc_num_blocks(p), M = orc_num_key_blocks(p), d = p->d;
     const size_t row = (size_t)p->N * d;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int bh = 0; bh < p->B * p->H; ++bh) {
         const size_t o = (size_t)bh * M * d;
-        pool_head(p, Q + bh * row, K + bh * row, V + bh * row, q_mean + o, k_mean + o,
+        pool_head(p, Q + bh * row, K + bh * row, V + bh * row, q_mean + (size_t)bh * Mq * d, k_mean + o,
                   k_sum + o, v_sum + o, bias + (size_t)bh * M, anchor + (size_t)bh * d);
     }
 }
@@ -172,17 +184,17 @@ void orc_pool(const orc_params *p, const float *Q, const float *K, const float *
  * key blocks]. */
 void orc_scores(const orc_params *p, const double *q_mean, const double *k_mean, double *S)
 {
-    const int M = orc_num_blocks(p), d = p->d;
+    const int Mq = orc_num_blocks(p), M = orc_num_key_blocks(p), d = p->d;
     const double s = scale_of(p);
 #pragma omp parallel for collapse(2) schedule(static)
     for (int bh = 0; bh < p->B * p->H; ++bh)
-        for (int I = 0; I < M; ++I) {
-            const double *qi = q_mean + ((size_t)bh * M + I) * d;
+        for (int I = 0; I < Mq; ++I) {
+            const double *qi = q_mean + ((size_t)bh * Mq + I) * d;
             for (int J = 0; J < M; ++J) {
                 const double *kj = k_mean + ((size_t)bh * M + J) * d;
                 double acc = 0.0;
                 for (int c = 0; c < d; ++c) acc += qi[c] * kj[c];
-                S[((size_t)bh * M + I) * M + J] = s * acc;
+                S[((size_t)bh * Mq + I) * M + J] = s * acc;
             }
         }
 }
@@ -216,14 +228,14 @@ static void topk_row(const double *row, int M, int K, int32_t *out, keyed *tmp)
 
 void orc_select(const orc_params *p, const double *S, int32_t *idx)
 {
-    const int M = orc_num_blocks(p), K = orc_topk_count(M, p->topk_ratio);
+    const int Mq = orc_num_blocks(p), M = orc_num_key_blocks(p), K = orc_topk_count(M, p->topk_ratio);
 #pragma omp parallel
     {
         keyed *tmp = (keyed *)malloc(sizeof(keyed) * (size_t)M);
 #pragma omp for collapse(2) schedule(static)
         for (int bh = 0; bh < p->B * p->H; ++bh)
-            for (int I = 0; I < M; ++I)
-                topk_row(S + ((size_t)bh * M + I) * M, M, K, idx + ((size_t)bh * M + I) * K, tmp);
+            for (int I = 0; I < Mq; ++I)
+                topk_row(S + ((size_t)bh * Mq + I) * M, M, K, idx + ((size_t)bh * Mq + I) * K, tmp);
         free(tmp);
     }
 }
@@ -268,7 +280,8 @@ static void attend_video_block(const orc_params *p, const float *Qh, const float
                                const double *bias, const int32_t *sel, int K, int I,
                                double *Oh, double *lseh)
 {
-    const int d = p->d, b = p->block, Nv = n_video(p), M = orc_num_blocks(p), N = p->N;
+    const int d = p->d, bq = p->block, b = key_block(p), Nv = n_video(p), M = orc_num_key_blocks(p);
+    const int N = p->N;
     const double s = scale_of(p);
     const int cap = K * b + p->n_sink + M;
     logit_set L;
@@ -278,7 +291,7 @@ static void attend_video_block(const orc_params *p, const float *Qh, const float
     char *chosen = (char *)calloc((size_t)M, 1);
     for (int k = 0; k < K; ++k) chosen[sel[k]] = 1;
 
-    const int lo = I * b, n = block_len(Nv, b, I);
+    const int lo = I * bq, n = block_len(Nv, bq, I);
     for (int i = lo; i < lo + n; ++i) {
         const float *q = Qh + (size_t)i * d;
         L.n = 0;
@@ -340,7 +353,8 @@ void orc_dense(const orc_params *p, const float *Q, const float *K, const float 
  * Attention for selected query blocks only (sampled parity at full size, and the CPU baseline).
  * Inputs are already in the block layout the route refers to (permuted when a partition is
  * used).  qb[n] = (bh, I) pairs: I < M is a video query block, I >= M is sink row N_v + (I - M).
- * Pooled summaries (k_sum, v_sum, bias) and the route idx [B*H][M][K] are full arrays.
+ * Pooled key summaries (k_sum, v_sum, bias; M_k key blocks) and the route idx [B*H][M][K] are
+ * full arrays.
  * O_out[n][rows][d] / lse_out[n][rows] receive the block's rows (rows = block, or 1 for a sink
  * row); rows past a partial block are left untouched.
  */
@@ -349,7 +363,7 @@ void orc_attend_blocks(const orc_params *p, const float *Q, const float *K, cons
                        const int32_t *idx, int Ksel, const int32_t *qb, int nqb, double *O_out,
                        double *lse_out)
 {
-    const int d = p->d, b = p->block, M = orc_num_blocks(p), N = p->N;
+    const int d = p->d, b = p->block, M = orc_num_blocks(p), Mk = orc_num_key_blocks(p), N = p->N;
     const size_t row = (size_t)N * d;
 #pragma omp parallel
     {
@@ -360,8 +374,8 @@ void orc_attend_blocks(const orc_params *p, const float *Q, const float *K, cons
             const int bh = qb[2 * n], I = qb[2 * n + 1];
             const float *Qh = Q + bh * row, *Kh = K + bh * row, *Vh = V + bh * row;
             if (I < M) {
-                attend_video_block(p, Qh, Kh, Vh, k_sum + (size_t)bh * M * d,
-                                   v_sum + (size_t)bh * M * d, bias + (size_t)bh * M,
+                attend_video_block(p, Qh, Kh, Vh, k_sum + (size_t)bh * Mk * d,
+                                   v_sum + (size_t)bh * Mk * d, bias + (size_t)bh * Mk,
                                    idx + ((size_t)bh * M + I) * Ksel, Ksel, I, Oh, lh);
                 const int lo = I * b, rows = block_len(n_video(p), b, I);
                 memcpy(O_out + (size_t)n * b * d, Oh + (size_t)lo * d, sizeof(double) * (size_t)rows * d);
@@ -409,8 +423,8 @@ void orc_forward(const orc_params *p, const float *Q, const float *K, const floa
                  const int32_t *perm, const int32_t *perm_k, const int32_t *idx_in, double *O,
                  double *lse, int32_t *idx_out)
 {
-    const int d = p->d, N = p->N, Nv = n_video(p), M = orc_num_blocks(p);
-    const int Ksel = orc_topk_count(M, p->topk_ratio);
+    const int d = p->d, N = p->N, Nv = n_video(p), M = orc_num_blocks(p), Mk = orc_num_key_blocks(p);
+    const int Ksel = orc_topk_count(Mk, p->topk_ratio);
     const size_t BH = (size_t)p->B * p->H, row = (size_t)N * d;
     const float *Qp = Q, *Kp = K, *Vp = V;
     float *tq = NULL, *tk = NULL, *tv = NULL;
@@ -424,17 +438,17 @@ void orc_forward(const orc_params *p, const float *Q, const float *K, const floa
         Kp = tk; Vp = tv;
     }
     double *qm = (double *)malloc(sizeof(double) * BH * M * d);
-    double *km = (double *)malloc(sizeof(double) * BH * M * d);
-    double *ks = (double *)malloc(sizeof(double) * BH * M * d);
-    double *vs = (double *)malloc(sizeof(double) * BH * M * d);
-    double *bias = (double *)malloc(sizeof(double) * BH * M);
+    double *km = (double *)malloc(sizeof(double) * BH * Mk * d);
+    double *ks = (double *)malloc(sizeof(double) * BH * Mk * d);
+    double *vs = (double *)malloc(sizeof(double) * BH * Mk * d);
+    double *bias = (double *)malloc(sizeof(double) * BH * Mk);
     double *anc = (double *)malloc(sizeof(double) * BH * d);
     orc_pool(p, Qp, Kp, Vp, qm, km, ks, vs, bias, anc);
     int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * BH * M * Ksel);
     if (idx_in) {
         memcpy(idx, idx_in, sizeof(int32_t) * BH * M * Ksel);
     } else {
-        double *S = (double *)malloc(sizeof(double) * BH * M * M);
+        double *S = (double *)malloc(sizeof(double) * BH * M * Mk);
         orc_scores(p, qm, km, S);
         orc_select(p, S, idx);
         free(S);
@@ -448,8 +462,8 @@ void orc_forward(const orc_params *p, const float *Q, const float *K, const floa
         for (int I = 0; I < M + p->n_sink; ++I) {
             const float *Qh = Qp + bh * row, *Kh = Kp + bh * row, *Vh = Vp + bh * row;
             if (I < M)
-                attend_video_block(p, Qh, Kh, Vh, ks + (size_t)bh * M * d, vs + (size_t)bh * M * d,
-                                   bias + (size_t)bh * M, idx + ((size_t)bh * M + I) * Ksel, Ksel,
+                attend_video_block(p, Qh, Kh, Vh, ks + (size_t)bh * Mk * d, vs + (size_t)bh * Mk * d,
+                                   bias + (size_t)bh * Mk, idx + ((size_t)bh * M + I) * Ksel, Ksel,
                                    I, Op + bh * row, lp + (size_t)bh * N);
             else
                 attend_dense_row(p, Qh, Kh, Vh, Nv + (I - M), Op + bh * row, lp + (size_t)bh * N);
@@ -621,8 +635,8 @@ void orc_forward_fp8(const orc_params *p, const float *Q, const float *K, const 
                      const int32_t *perm, const int32_t *idx_in, double *O, double *lse,
                      int32_t *idx_out, float *scales_out)
 {
-    const int d = p->d, N = p->N, Nv = n_video(p), M = orc_num_blocks(p);
-    const int Ksel = orc_topk_count(M, p->topk_ratio);
+    const int d = p->d, N = p->N, Nv = n_video(p), M = orc_num_blocks(p), Mk = orc_num_key_blocks(p);
+    const int Ksel = orc_topk_count(Mk, p->topk_ratio);
     const size_t BH = (size_t)p->B * p->H, row = (size_t)N * d;
     const float *Qp = Q, *Kp = K, *Vp = V;
     float *tq = NULL, *tk = NULL, *tv = NULL;
@@ -631,17 +645,17 @@ void orc_forward_fp8(const orc_params *p, const float *Q, const float *K, const 
         Qp = tq; Kp = tk; Vp = tv;
     }
     double *qm = (double *)malloc(sizeof(double) * BH * M * d);
-    double *km = (double *)malloc(sizeof(double) * BH * M * d);
-    double *ks = (double *)malloc(sizeof(double) * BH * M * d);
-    double *vs = (double *)malloc(sizeof(double) * BH * M * d);
-    double *bias = (double *)malloc(sizeof(double) * BH * M);
+    double *km = (double *)malloc(sizeof(double) * BH * Mk * d);
+    double *ks = (double *)malloc(sizeof(double) * BH * Mk * d);
+    double *vs = (double *)malloc(sizeof(double) * BH * Mk * d);
+    double *bias = (double *)malloc(sizeof(double) * BH * Mk);
     double *anc = (double *)malloc(sizeof(double) * BH * d);
     orc_pool(p, Qp, Kp, Vp, qm, km, ks, vs, bias, anc);
     int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * BH * M * Ksel);
     if (idx_in) {
         memcpy(idx, idx_in, sizeof(int32_t) * BH * M * Ksel);
     } else {
-        double *S = (double *)malloc(sizeof(double) * BH * M * M);
+        double *S = (double *)malloc(sizeof(double) * BH * M * Mk);
         orc_scores(p, qm, km, S);
         orc_select(p, S, idx);
         free(S);
@@ -655,8 +669,8 @@ void orc_forward_fp8(const orc_params *p, const float *Q, const float *K, const 
     float *q8 = (float *)malloc(sizeof(float) * BH * row);
     float *k8 = (float *)malloc(sizeof(float) * BH * row);
     float *v8 = (float *)malloc(sizeof(float) * BH * row);
-    double *ks8 = (double *)malloc(sizeof(double) * BH * M * d);
-    double *vs8 = (double *)malloc(sizeof(double) * BH * M * d);
+    double *ks8 = (double *)malloc(sizeof(double) * BH * Mk * d);
+    double *vs8 = (double *)malloc(sizeof(double) * BH * Mk * d);
     for (size_t bh = 0; bh < BH; ++bh) {
         const float *s6 = sc + bh * 6;
         for (size_t e = 0; e < row; ++e) {
@@ -664,9 +678,9 @@ void orc_forward_fp8(const orc_params *p, const float *Q, const float *K, const 
             k8[bh * row + e] = orc_e4m3(Kp[bh * row + e] * s6[2]);
             v8[bh * row + e] = orc_e4m3(Vp[bh * row + e] * s6[4]);
         }
-        for (size_t e = 0; e < (size_t)M * d; ++e) {
-            ks8[bh * M * d + e] = (double)orc_e4m3((float)ks[bh * M * d + e] * s6[2]);
-            vs8[bh * M * d + e] = (double)orc_e4m3((float)vs[bh * M * d + e] * s6[4]);
+        for (size_t e = 0; e < (size_t)Mk * d; ++e) {
+            ks8[bh * Mk * d + e] = (double)orc_e4m3((float)ks[bh * Mk * d + e] * s6[2]);
+            vs8[bh * Mk * d + e] = (double)orc_e4m3((float)vs[bh * Mk * d + e] * s6[4]);
         }
     }
 
@@ -679,8 +693,8 @@ void orc_forward_fp8(const orc_params *p, const float *Q, const float *K, const 
             ph.scale = scale_of(p) * (double)sc[(size_t)bh * 6 + 1] * (double)sc[(size_t)bh * 6 + 3];
             const float *Qh = q8 + bh * row, *Kh = k8 + bh * row, *Vh = v8 + bh * row;
             if (I < M)
-                attend_video_block(&ph, Qh, Kh, Vh, ks8 + (size_t)bh * M * d, vs8 + (size_t)bh * M * d,
-                                   bias + (size_t)bh * M, idx + ((size_t)bh * M + I) * Ksel, Ksel,
+                attend_video_block(&ph, Qh, Kh, Vh, ks8 + (size_t)bh * Mk * d, vs8 + (size_t)bh * Mk * d,
+                                   bias + (size_t)bh * Mk, idx + ((size_t)bh * M + I) * Ksel, Ksel,
                                    I, Op + bh * row, lp + (size_t)bh * N);
             else
                 attend_dense_row(&ph, Qh, Kh, Vh, Nv + (I - M), Op + bh * row, lp + (size_t)bh * N);

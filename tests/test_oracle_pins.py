@@ -20,6 +20,10 @@ textbook routine, an invariant, a hand-worked example or a brute-force formulati
   P-m  FP8 carrier: E4M3 rounding == torch.float8_e4m3fn cast and the format's closed form
        (every code maps to itself, midpoints go to the even mantissa); on-grid inputs at full
        density == dense; power-of-two rescalings act exactly; forward == brute force
+  P-n  asymmetric route (query blocks of `block`, key blocks of `block_k`): one-token key blocks
+       == dense for any budget; full density == dense; block_k = block changes nothing; forward
+       == brute force (both pool modes, both orders of the sizes, FP8 carriers); selection ==
+       lexsort over the rectangular score matrix
 """
 import json
 import math
@@ -546,5 +550,70 @@ def test_fp8_reblocked_forward_matches_brute_force(orc):
     perm = orc.reblock(p, Q, K)
     O, lse, idx, _ = orc.forward_fp8(p, Q, K, V, perm=perm)
     Ob, lb, ib = brute.forward(Q, K, V, 3, 64, 0.25, 1, perm=perm, fp8=True)
+    assert (idx == ib).all()
+    assert np.abs(O - Ob).max() < 1e-12 and np.abs(lse - lb).max() < 1e-11
+
+
+# ---------------------------------------------------------------- P-n asymmetric route (query blocks of
+# `block` rows routed to key blocks of `block_k` keys)
+@pytest.mark.parametrize("pool_mode", [0, 1])
+def test_one_token_key_blocks_are_dense(orc, pool_mode):
+    """One-token key blocks: every pseudo-key is its own token exactly, so any budget gives dense
+    attention, whatever the query block size."""
+    Q, K, V = small(seed=80, nv=300, ns=4)
+    for ratio in (0.05, 0.3):
+        p = orc.params(Q, 4, 32, ratio, pool_mode, block_k=1)
+        O, lse, idx = orc.forward(p, Q, K, V)
+        assert idx.shape[-1] == orc.topk_count(300, ratio)
+        assert np.abs(O - sdpa_dense(Q, K, V)).max() < 1e-12
+
+
+def test_asymmetric_full_density_is_dense(orc):
+    Q, K, V = small(seed=81, nv=900, ns=7)
+    p = orc.params(Q, 7, 64, 1.0, 1, block_k=32)
+    O, lse, idx = orc.forward(p, Q, K, V)
+    assert idx.shape[-2:] == (orc.num_blocks(p), orc.num_key_blocks(p))
+    assert np.abs(O - sdpa_dense(Q, K, V)).max() < 1e-12
+
+
+def test_equal_key_blocks_change_nothing(orc):
+    Q, K, V = small(seed=82, nv=700, ns=3)
+    a = orc.forward(orc.params(Q, 3, 64, 0.2, 1), Q, K, V)
+    b = orc.forward(orc.params(Q, 3, 64, 0.2, 1, block_k=64), Q, K, V)
+    for x, y in zip(a, b):
+        assert (x == y).all()
+
+
+@pytest.mark.parametrize("block,block_k", [(64, 32), (32, 64), (128, 64)])
+@pytest.mark.parametrize("pool_mode", [0, 1])
+def test_asymmetric_forward_matches_brute_force(orc, block, block_k, pool_mode):
+    Q, K, V = small(seed=83, B=2, nv=2000 - 21, ns=5)
+    p = orc.params(Q, 5, block, 0.15, pool_mode, block_k=block_k)
+    O, lse, idx = orc.forward(p, Q, K, V)
+    Ob, lb, ib = brute.forward(Q, K, V, 5, block, 0.15, pool_mode, block_k=block_k)
+    assert (idx == ib).all()
+    assert np.abs(O - Ob).max() < 1e-12 and np.abs(lse - lb).max() < 1e-11
+
+
+def test_asymmetric_selection_is_lexsort_topk(orc):
+    Q, K, V = small(seed=84, nv=1500, ns=0)
+    p = orc.params(Q, 0, 128, 0.1, 1, block_k=64)
+    pooled = orc.pool(p, Q, K, V)
+    S = orc.scores(p, pooled["q_mean"], pooled["k_mean"])
+    M, Mk = orc.num_blocks(p), orc.num_key_blocks(p)
+    assert S.shape[-2:] == (M, Mk) == (12, 24)
+    idx = orc.select(p, S)
+    Kk = orc.topk_count(Mk, 0.1)
+    for h in range(2):
+        for I in range(M):
+            ref = np.sort(np.lexsort((np.arange(Mk), -S[0, h, I]))[:Kk])
+            assert (idx[0, h, I] == ref).all()
+
+
+def test_asymmetric_fp8_matches_brute_force(orc):
+    Q, K, V = small(seed=85, nv=1000 - 24, ns=5)
+    p = orc.params(Q, 5, 128, 0.2, 1, block_k=64)
+    O, lse, idx, _ = orc.forward_fp8(p, Q, K, V)
+    Ob, lb, ib = brute.forward(Q, K, V, 5, 128, 0.2, 1, fp8=True, block_k=64)
     assert (idx == ib).all()
     assert np.abs(O - Ob).max() < 1e-12 and np.abs(lse - lb).max() < 1e-11
