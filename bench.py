@@ -33,19 +33,22 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_flops(idx, wl, ratio_K, counts=None):
+def algorithmic_flops(idx, wl, ratio_K, counts=None, block_k=0):
     """F_sel from the actual route, plus the sink, compressed and sink-query terms (4 d per
     query-key pair: one multiply-add for the logit and one for the value).  A variable route is
-    idx [B,H,M,M] with counts [B,H,M]."""
+    idx [B,H,M,M] with counts [B,H,M].  block_k: key block size (0: the query block size)."""
     import numpy as np
 
     b, nv, ns, d, N = wl.block, wl.n_video, wl.n_sink, wl.d, wl.N
+    bk = block_k or b
     M = idx.shape[2]
-    sizes = np.minimum(b, nv - np.arange(M) * b).astype(np.int64)
+    Mk = -(-nv // bk)
+    sizes = np.minimum(b, nv - np.arange(M) * b).astype(np.int64)  # query block sizes
+    ksizes = np.minimum(bk, nv - np.arange(Mk) * bk).astype(np.int64)  # key block sizes
     BH = wl.B * wl.H
     if counts is None:
-        n_sel = sizes[idx].sum(axis=-1)  # [B,H,M] keys in the selected blocks of each query block
-        n_unsel = float(BH * nv * (M - ratio_K))
+        n_sel = ksizes[idx].sum(axis=-1)  # [B,H,M] keys in the selected blocks of each query block
+        n_unsel = float(BH * nv * (Mk - ratio_K))
     else:
         valid = np.arange(M)[None, None, None, :] < counts[..., None]
         n_sel = np.where(valid, sizes[np.clip(idx, 0, M - 1)], 0).sum(axis=-1)
@@ -96,14 +99,14 @@ def route_check(idx, S, rel=1e-4, floor=1e-6):
     return int((~ok).sum())
 
 
-def cpu_baseline(wl, ratio, Qh, Kh, Vh, gidx, F_sel_total, sample_blocks):
+def cpu_baseline(wl, ratio, Qh, Kh, Vh, gidx, F_sel_total, sample_blocks, block_k=0):
     """The oracle as it stands, on a bounded sample: full pool, full block scores and top-K, and
     the attention of `sample_blocks` video query blocks plus a few sink query rows; the full
     forward time is extrapolated from the per-block time."""
     import numpy as np
     import oracle
 
-    p = oracle.params(Qh, wl.n_sink, wl.block, ratio, 1)
+    p = oracle.params(Qh, wl.n_sink, wl.block, ratio, 1, block_k=block_k)
     threads = oracle.num_threads()
     t0 = time.perf_counter()
     pooled = oracle.pool(p, Qh, Kh, Vh)
@@ -113,7 +116,7 @@ def cpu_baseline(wl, ratio, Qh, Kh, Vh, gidx, F_sel_total, sample_blocks):
     t2 = time.perf_counter()
     bad = route_check(gidx, S)
     same = float((oidx == gidx).all(axis=-1).mean())
-    M = S.shape[-1]
+    M = S.shape[-2]  # query blocks
     rng = np.random.default_rng(7)
     BH = wl.B * wl.H
     qb = np.stack([rng.integers(0, BH, sample_blocks), rng.integers(0, M, sample_blocks)], 1)
@@ -151,6 +154,9 @@ def main():
     ap.add_argument("--ratio", type=float, default=None)
     ap.add_argument("--tau", type=float, default=None,
                     help="adaptive-tau selection (per-head threshold mu + tau*sigma) instead of top-K")
+    ap.add_argument("--block-k", type=int, default=0,
+                    help="key block size of the route (0: the workload's block); 64 with block 128 is the "
+                         "asymmetric 128Q x 64KV route")
     ap.add_argument("--fp8", action="store_true",
                     help="the exact branch, sinks and pseudo-keys on per-head E4M3 carriers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -185,18 +191,19 @@ def main():
     if args.no_cpu_baseline:
         del Qh, Kh, Vh
 
-    p = sa.params(Q, wl.n_sink, wl.block, ratio, sa.POOL_REWEIGHT)
-    M = sa.num_blocks(p)
-    Kk = sa.topk_count(M, ratio)
+    p = sa.params(Q, wl.n_sink, wl.block, ratio, sa.POOL_REWEIGHT, block_k=args.block_k)
+    M, Mk = sa.num_blocks(p), sa.num_key_blocks(p)
+    Kk = sa.topk_count(Mk, ratio)
     B, H, N, d = Q.shape
     f32 = dict(device="cuda", dtype=torch.float32)
-    pooled = {k: torch.empty(B, H, M, d, **f32) for k in ("q_mean", "k_mean", "k_sum", "v_sum")}
-    pooled["bias"] = torch.empty(B, H, M, **f32)
+    pooled = {"q_mean": torch.empty(B, H, M, d, **f32)}
+    pooled.update({k: torch.empty(B, H, Mk, d, **f32) for k in ("k_mean", "k_sum", "v_sum")})
+    pooled["bias"] = torch.empty(B, H, Mk, **f32)
     pooled["anchor"] = torch.empty(B, H, d, **f32)
     tau_mode = args.tau is not None
     fp8 = args.fp8
-    if tau_mode and wl.reblock:
-        print("--tau runs on token-order workloads only", file=sys.stderr)
+    if tau_mode and (wl.reblock or Mk != M):
+        print("--tau runs on token-order workloads with equal query and key blocks", file=sys.stderr)
         sys.exit(2)
     if fp8 and (tau_mode or wl.key_partition):
         print("--fp8 runs with top-K routes on token-order or q_reuse_k layouts", file=sys.stderr)
@@ -317,7 +324,7 @@ def main():
 
     gidx = idx.cpu().numpy()
     gcounts = counts.cpu().numpy() if tau_mode else None
-    F_sel, F_sink, F_comp, F_sinkq = algorithmic_flops(gidx, wl, Kk, gcounts)
+    F_sel, F_sink, F_comp, F_sinkq = algorithmic_flops(gidx, wl, Kk, gcounts, args.block_k)
     F_attn = F_sel + F_sink + F_comp + F_sinkq
     value = F_sel / (ms_step * 1e-3) / 1e12
     achieved = F_attn / (ms_attn * 1e-3) / 1e12
@@ -343,6 +350,7 @@ def main():
         "config": {
             "workload": wl.name, "description": wl.description, "B": B, "H": H, "N_video": wl.n_video,
             "N_sink": wl.n_sink, "d": d, "block": wl.block, "M": M,
+            **({"block_k": args.block_k, "M_k": Mk} if args.block_k not in (0, wl.block) else {}),
             **({"topk_ratio": ratio, "K": Kk} if not tau_mode else
                {"selection": "adaptive tau", "tau": args.tau, "kept_fraction": round(float(gcounts.mean()) / M, 4)}),
             "compressed_branch": "anchor-weighted summary + log-mass bias", "parallelism": "none (1 GPU)",
@@ -379,7 +387,8 @@ def main():
                     for h_ in range(H):
                         X[b_, h_, :wl.n_video] = X[b_, h_][ph[b_, h_]]
         torch.cuda.empty_cache()
-        out["cpu_baseline"] = cpu_baseline(wl, ratio, Qh, Kh, Vh, gidx, F_sel, args.cpu_sample_blocks)
+        out["cpu_baseline"] = cpu_baseline(wl, ratio, Qh, Kh, Vh, gidx, F_sel, args.cpu_sample_blocks,
+                                           args.block_k)
     print(json.dumps(out), flush=True)
 
 

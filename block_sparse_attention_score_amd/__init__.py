@@ -27,6 +27,7 @@ class SparkAttnParams(ctypes.Structure):
         ("B", ctypes.c_int), ("H", ctypes.c_int), ("N", ctypes.c_int), ("d", ctypes.c_int),
         ("n_sink", ctypes.c_int), ("block", ctypes.c_int), ("topk_ratio", ctypes.c_float),
         ("pool_mode", ctypes.c_int), ("dtype", ctypes.c_int), ("scale", ctypes.c_float),
+        ("block_k", ctypes.c_int),
     ]
 
 
@@ -37,7 +38,7 @@ class SparkAttnError(RuntimeError):
 
 
 EXPORTS = (
-    "spark_attn_num_blocks", "spark_attn_topk_count", "spark_attn_workspace_size",
+    "spark_attn_num_blocks", "spark_attn_num_key_blocks", "spark_attn_topk_count", "spark_attn_workspace_size",
     "spark_attn_status_str", "spark_attn_pool", "spark_attn_select", "spark_attn_pack",
     "spark_attn_attend", "spark_attn_forward", "spark_attn_forward_kv", "spark_attn_reblock",
     "spark_attn_gather_rows", "spark_attn_select_tau", "spark_attn_attend_var", "spark_attn_forward_tau",
@@ -59,6 +60,7 @@ def lib():
         vp, sz = ctypes.c_void_p, ctypes.c_size_t
         sig = {
             "spark_attn_num_blocks": ([P], ctypes.c_int),
+            "spark_attn_num_key_blocks": ([P], ctypes.c_int),
             "spark_attn_topk_count": ([ctypes.c_int, ctypes.c_float], ctypes.c_int),
             "spark_attn_workspace_size": ([P, ctypes.c_int], sz),
             "spark_attn_status_str": ([ctypes.c_int], ctypes.c_char_p),
@@ -91,7 +93,8 @@ def status_str(status: int) -> str:
 
 
 def params(Q: torch.Tensor, n_sink: int, block: int, topk_ratio: float = 0.1,
-           pool_mode: int = POOL_REWEIGHT, scale: float = 0.0) -> SparkAttnParams:
+           pool_mode: int = POOL_REWEIGHT, scale: float = 0.0, block_k: int = 0) -> SparkAttnParams:
+    """block: query block size; block_k: key block size (0: the same as block)."""
     B, H, N, d = Q.shape
     if Q.dtype == torch.bfloat16:
         dt = BF16
@@ -100,7 +103,7 @@ def params(Q: torch.Tensor, n_sink: int, block: int, topk_ratio: float = 0.1,
     else:
         raise TypeError(f"unsupported dtype {Q.dtype}")
     return SparkAttnParams(B, H, N, d, n_sink, block, float(topk_ratio), int(pool_mode), dt,
-                           float(scale))
+                           float(scale), int(block_k))
 
 
 def _ptr(t):
@@ -124,6 +127,12 @@ def _check(name, status):
 def num_blocks(p: SparkAttnParams) -> int:
     m = lib().spark_attn_num_blocks(ctypes.byref(p))
     _check("spark_attn_num_blocks", min(m, 0))
+    return m
+
+
+def num_key_blocks(p: SparkAttnParams) -> int:
+    m = lib().spark_attn_num_key_blocks(ctypes.byref(p))
+    _check("spark_attn_num_key_blocks", min(m, 0))
     return m
 
 
@@ -239,13 +248,15 @@ def spark_attn_gather_rows(p, X, perm, Y, stream=None):
 
 # ---- convenience wrappers (allocate outputs with torch) -------------------------------------
 
-def pool(Q, K, V, n_sink, block, pool_mode=POOL_REWEIGHT, scale=0.0, stream=None):
-    p = params(Q, n_sink, block, 1.0, pool_mode, scale)
-    M = num_blocks(p)
+def pool(Q, K, V, n_sink, block, pool_mode=POOL_REWEIGHT, scale=0.0, stream=None, block_k=0):
+    """q_mean [B,H,M,d]; k_mean, k_sum, v_sum [B,H,M_k,d], bias [B,H,M_k]; anchor [B,H,d]."""
+    p = params(Q, n_sink, block, 1.0, pool_mode, scale, block_k)
+    M, Mk = num_blocks(p), num_key_blocks(p)
     B, H, _, d = Q.shape
     f = dict(device=Q.device, dtype=torch.float32)
-    out = {k: torch.empty(B, H, M, d, **f) for k in ("q_mean", "k_mean", "k_sum", "v_sum")}
-    out["bias"] = torch.empty(B, H, M, **f)
+    out = {"q_mean": torch.empty(B, H, M, d, **f)}
+    out.update({k: torch.empty(B, H, Mk, d, **f) for k in ("k_mean", "k_sum", "v_sum")})
+    out["bias"] = torch.empty(B, H, Mk, **f)
     out["anchor"] = torch.empty(B, H, d, **f)
     spark_attn_pool(p, Q, K, V, out["q_mean"], out["k_mean"], out["k_sum"], out["v_sum"],
                     out["bias"], out["anchor"], stream)
@@ -253,41 +264,41 @@ def pool(Q, K, V, n_sink, block, pool_mode=POOL_REWEIGHT, scale=0.0, stream=None
 
 
 def select(q_mean, k_mean, Q, n_sink, block, topk_ratio, with_scores=False, scale=0.0,
-           stream=None):
-    p = params(Q, n_sink, block, topk_ratio, POOL_REWEIGHT, scale)
-    M = num_blocks(p)
-    K = topk_count(M, topk_ratio)
+           stream=None, block_k=0):
+    p = params(Q, n_sink, block, topk_ratio, POOL_REWEIGHT, scale, block_k)
+    M, Mk = num_blocks(p), num_key_blocks(p)
+    K = topk_count(Mk, topk_ratio)
     B, H = q_mean.shape[:2]
     idx = torch.empty(B, H, M, K, device=q_mean.device, dtype=torch.int32)
-    S = torch.empty(B, H, M, M, device=q_mean.device, dtype=torch.float32)
+    S = torch.empty(B, H, M, Mk, device=q_mean.device, dtype=torch.float32)
     spark_attn_select(p, q_mean, k_mean, idx, S, None, stream)
     return (idx, S) if with_scores else idx
 
 
-def pack(K, V, pooled, n_sink, block, scale=0.0, stream=None):
-    p = params(K, n_sink, block, 1.0, POOL_REWEIGHT, scale)
+def pack(K, V, pooled, n_sink, block, scale=0.0, stream=None, block_k=0):
+    p = params(K, n_sink, block, 1.0, POOL_REWEIGHT, scale, block_k)
     packed = torch.empty(workspace_size(p, 4), device=K.device, dtype=torch.uint8)
     spark_attn_pack(p, K, V, pooled["k_sum"], pooled["v_sum"], pooled["bias"], packed, stream)
     return packed
 
 
 def attend(Q, K, V, pooled, idx, n_sink, block, topk_ratio, perm=None, scale=0.0, out=None,
-           lse=None, stream=None):
-    p = params(Q, n_sink, block, topk_ratio, POOL_REWEIGHT, scale)
-    packed = pack(K, V, pooled, n_sink, block, scale, stream)
+           lse=None, stream=None, block_k=0):
+    p = params(Q, n_sink, block, topk_ratio, POOL_REWEIGHT, scale, block_k)
+    packed = pack(K, V, pooled, n_sink, block, scale, stream, block_k)
     O = out if out is not None else torch.empty_like(Q)
     spark_attn_attend(p, Q, packed, idx, perm, O, lse, stream)
     return O
 
 
 def forward(Q, K, V, n_sink, block, topk_ratio, pool_mode=POOL_REWEIGHT, perm=None, scale=0.0,
-            return_lse=False, return_idx=False, workspace=None, stream=None, perm_k=None):
+            return_lse=False, return_idx=False, workspace=None, stream=None, perm_k=None, block_k=0):
     """Returns O (and lse [B,H,N] fp32, idx [B,H,M,K] int32 when asked).  perm: the partition of
     the queries (and of keys and values unless perm_k is given); perm_k: a separate key
-    partition (spark_attn_forward_kv)."""
-    p = params(Q, n_sink, block, topk_ratio, pool_mode, scale)
+    partition (spark_attn_forward_kv); block_k: key block size (0: block)."""
+    p = params(Q, n_sink, block, topk_ratio, pool_mode, scale, block_k)
     M = num_blocks(p)
-    Kk = topk_count(M, topk_ratio)
+    Kk = topk_count(num_key_blocks(p), topk_ratio)
     B, H, N, _ = Q.shape
     O = torch.empty_like(Q)
     lse = torch.empty(B, H, N, device=Q.device, dtype=torch.float32) if return_lse else None
@@ -353,20 +364,21 @@ def fp8_scales(Q, K, V, n_sink, block, stream=None):
     return amax
 
 
-def pack_fp8(K, V, pooled, amax, n_sink, block, scale=0.0, stream=None):
-    p = params(K, n_sink, block, 1.0, POOL_REWEIGHT, scale)
+def pack_fp8(K, V, pooled, amax, n_sink, block, scale=0.0, stream=None, block_k=0):
+    p = params(K, n_sink, block, 1.0, POOL_REWEIGHT, scale, block_k)
     packed = torch.empty(workspace_size(p, 9), device=K.device, dtype=torch.uint8)
     spark_attn_pack_fp8(p, K, V, pooled["k_sum"], pooled["v_sum"], pooled["bias"], amax, packed, stream)
     return packed
 
 
 def forward_fp8(Q, K, V, n_sink, block, topk_ratio, pool_mode=POOL_REWEIGHT, perm=None, scale=0.0,
-                return_lse=False, return_idx=False, return_amax=False, workspace=None, stream=None):
+                return_lse=False, return_idx=False, return_amax=False, workspace=None, stream=None,
+                block_k=0):
     """Forward with the exact branch, sinks and pseudo-keys on per-head E4M3 carriers.  Returns O
     (and lse, idx [B,H,M,K], amax [B,H,3] when asked)."""
-    p = params(Q, n_sink, block, topk_ratio, pool_mode, scale)
+    p = params(Q, n_sink, block, topk_ratio, pool_mode, scale, block_k)
     M = num_blocks(p)
-    Kk = topk_count(M, topk_ratio)
+    Kk = topk_count(num_key_blocks(p), topk_ratio)
     B, H, N, _ = Q.shape
     O = torch.empty_like(Q)
     lse = torch.empty(B, H, N, device=Q.device, dtype=torch.float32) if return_lse else None

@@ -29,6 +29,8 @@ static int make_ctx(const spark_attn_params* p, void* stream, LaunchCtx* L) {
     if (!(p->scale >= 0.f) || isinf(p->scale)) return SPARK_ATTN_INVALID_ARGUMENT;
     if (p->d != 64 && p->d != 128) return SPARK_ATTN_UNSUPPORTED;
     if (p->block != 64 && p->block != 128) return SPARK_ATTN_UNSUPPORTED;
+    if (p->block_k < 0) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (p->block_k != 0 && p->block_k != 64 && p->block_k != 128) return SPARK_ATTN_UNSUPPORTED;
     if (p->dtype != SPARK_ATTN_BF16 && p->dtype != SPARK_ATTN_FP32) return SPARK_ATTN_UNSUPPORTED;
     const long long elems = (long long)p->B * p->H * p->N * p->d;
     if (elems >= (1LL << 31)) return SPARK_ATTN_UNSUPPORTED;
@@ -41,8 +43,10 @@ static int make_ctx(const spark_attn_params* p, void* stream, LaunchCtx* L) {
     L->d = p->d;
     L->block = p->block;
     L->M = (L->Nv + p->block - 1) / p->block;
-    if (L->M > kMaxBlocks) return SPARK_ATTN_UNSUPPORTED;
-    L->K = topk_count(L->M, p->topk_ratio);
+    L->block_k = p->block_k ? p->block_k : p->block;
+    L->Mk = (L->Nv + L->block_k - 1) / L->block_k;
+    if (L->M > kMaxBlocks || L->Mk > kMaxBlocks) return SPARK_ATTN_UNSUPPORTED;
+    L->K = topk_count(L->Mk, p->topk_ratio);
     L->pool_mode = p->pool_mode;
     L->dtype = p->dtype;
     L->scale = p->scale != 0.f ? p->scale : 1.0f / sqrtf((float)p->d);
@@ -61,13 +65,13 @@ struct FwdWorkspace {
 
 static FwdWorkspace fwd_layout(const LaunchCtx& L, bool with_perm) {
     FwdWorkspace w;
-    const size_t md = (size_t)L.BH * L.M * L.d * 4;
+    const size_t md = (size_t)L.BH * L.M * L.d * 4, mkd = (size_t)L.BH * L.Mk * L.d * 4;
     size_t o = 0;
     w.q_mean = o; o = align256(o + md);
-    w.k_mean = o; o = align256(o + md);
-    w.k_sum = o; o = align256(o + md);
-    w.v_sum = o; o = align256(o + md);
-    w.bias = o; o = align256(o + (size_t)L.BH * L.M * 4);
+    w.k_mean = o; o = align256(o + mkd);
+    w.k_sum = o; o = align256(o + mkd);
+    w.v_sum = o; o = align256(o + mkd);
+    w.bias = o; o = align256(o + (size_t)L.BH * L.Mk * 4);
     w.anchor = o; o = align256(o + (size_t)L.BH * L.d * 4);
     w.idx = o; o = align256(o + (size_t)L.BH * L.M * L.K * 4);
     w.scores = o; o = align256(o + select_workspace_bytes(L));
@@ -117,13 +121,13 @@ struct Fp8Workspace {
 
 static Fp8Workspace fp8_layout(const LaunchCtx& L, bool with_perm) {
     Fp8Workspace w;
-    const size_t md = (size_t)L.BH * L.M * L.d * 4;
+    const size_t md = (size_t)L.BH * L.M * L.d * 4, mkd = (size_t)L.BH * L.Mk * L.d * 4;
     size_t o = 0;
     w.q_mean = o; o = align256(o + md);
-    w.k_mean = o; o = align256(o + md);
-    w.k_sum = o; o = align256(o + md);
-    w.v_sum = o; o = align256(o + md);
-    w.bias = o; o = align256(o + (size_t)L.BH * L.M * 4);
+    w.k_mean = o; o = align256(o + mkd);
+    w.k_sum = o; o = align256(o + mkd);
+    w.v_sum = o; o = align256(o + mkd);
+    w.bias = o; o = align256(o + (size_t)L.BH * L.Mk * 4);
     w.anchor = o; o = align256(o + (size_t)L.BH * L.d * 4);
     w.idx = o; o = align256(o + (size_t)L.BH * L.M * L.K * 4);
     w.scores = o; o = align256(o + select_workspace_bytes(L));
@@ -150,6 +154,12 @@ int spark_attn_num_blocks(const spark_attn_params* p) {
     LaunchCtx L;
     const int s = make_ctx(p, nullptr, &L);
     return s < 0 ? s : L.M;
+}
+
+int spark_attn_num_key_blocks(const spark_attn_params* p) {
+    LaunchCtx L;
+    const int s = make_ctx(p, nullptr, &L);
+    return s < 0 ? s : L.Mk;
 }
 
 int spark_attn_topk_count(int M, float ratio) { return topk_count(M, ratio); }
@@ -242,6 +252,7 @@ int spark_attn_attend_var(const spark_attn_params* p, const void* Q, const void*
     LaunchCtx L;
     int s = make_ctx(p, stream, &L);
     if (s < 0) return s;
+    if (L.Mk != L.M) return SPARK_ATTN_UNSUPPORTED;  // adaptive tau: equal query and key blocks
     if (!Q || !idx || !counts || !O) return SPARK_ATTN_INVALID_ARGUMENT;
     if (!aligned16(Q) || !aligned16(packed) || !aligned16(O)) return SPARK_ATTN_MISALIGNED;
     if (!packed || packed_bytes < pack_geom(L).bytes) return SPARK_ATTN_WORKSPACE_TOO_SMALL;
@@ -255,6 +266,7 @@ int spark_attn_select_tau(const spark_attn_params* p, float tau, const float* q_
     LaunchCtx L;
     int s = make_ctx(p, stream, &L);
     if (s < 0) return s;
+    if (L.Mk != L.M) return SPARK_ATTN_UNSUPPORTED;  // adaptive tau: equal query and key blocks
     if (!(tau == tau) || tau == INFINITY || tau == -INFINITY) return SPARK_ATTN_INVALID_ARGUMENT;
     if (!q_mean || !k_mean || !idx || !counts) return SPARK_ATTN_INVALID_ARGUMENT;
     if (!aligned16(q_mean) || !aligned16(k_mean) || !aligned16(workspace)) return SPARK_ATTN_MISALIGNED;
@@ -271,6 +283,7 @@ int spark_attn_forward_tau(const spark_attn_params* p, float tau, const void* Q,
     LaunchCtx L;
     int s = make_ctx(p, stream, &L);
     if (s < 0) return s;
+    if (L.Mk != L.M) return SPARK_ATTN_UNSUPPORTED;  // adaptive tau: equal query and key blocks
     if (!(tau == tau) || tau == INFINITY || tau == -INFINITY) return SPARK_ATTN_INVALID_ARGUMENT;
     if (!Q || !K || !V || !O) return SPARK_ATTN_INVALID_ARGUMENT;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(workspace))

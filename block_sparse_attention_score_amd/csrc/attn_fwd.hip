@@ -140,7 +140,8 @@ template <typename T, int D, int BLK>
 __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     const T* __restrict__ Q, const __bf16* __restrict__ packed, const float* __restrict__ bias2,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ counts, const int32_t* __restrict__ perm,
-    T* __restrict__ O, float* __restrict__ lse, int N, int Nv, int M, int Ksel, int kstride, int SQ, int BH, int C,
+    T* __restrict__ O, float* __restrict__ lse, int N, int Nv, int M, int Mk, int nsh, int Ksel, int kstride, int SQ,
+    int BH, int C,
     int Tv, int Ts, int Tc, float c_log2) {
 // The body uses buffer resources, a device-only type: the host pass sees an empty kernel.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
             nq = min(BLK, Nv - qrow0);
             // a variable route (counts given) lists counts[I] blocks in a row of kstride entries
             if (counts) Ksel = counts[(size_t)bh * M + I];
-            ntiles = Ksel * (BLK / kTK) + Ts + Tc;
+            ntiles = (Ksel << nsh) + Ts + Tc;
         }
     }
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -195,8 +196,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     const __bf16* ptile = packed + (size_t)bh * Tall * G::ELEMS;
     const float* pbias = bias2 + (size_t)bh * Tall * kTK;
     const int32_t* sel = dense ? nullptr : idx + ((size_t)bh * M + qrow0 / BLK) * kstride;
-    constexpr int nsub = BLK / kTK;
-    const int n_exact = dense ? 0 : Ksel * nsub;
+    // a selected key block is 1 << nsh tiles (key blocks of 64 or 128 keys)
+    const int n_exact = dense ? 0 : Ksel << nsh;
     const int first_cmp = dense ? ntiles : n_exact + Ts;  // first compressed tile in the list
 
     // Selected block ids are read 64 at a time into a register (lane l holds entry base + l) and
@@ -207,16 +208,16 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     auto tile_of = [&](int t) __attribute__((always_inline)) -> int {
         if (dense) return t;
         if (t >= n_exact) return Tv + (t - n_exact);
-        const int k = t / nsub;
+        const int k = t >> nsh;
         if (k >= win_base + 64) {
             win_base = k & ~63;
             selw = win_base + lane < Ksel ? sel[win_base + lane] : 0;
         }
-        return __builtin_amdgcn_readlane(selw, k - win_base) * nsub + t % nsub;
+        return (__builtin_amdgcn_readlane(selw, k - win_base) << nsh) + (t & ((1 << nsh) - 1));
     };
 
     if (!dense) {
-        for (int j = threadIdx.x; j < (M + 63) / 32 + 1; j += NT) sel_bits[j] = 0u;
+        for (int j = threadIdx.x; j < (Mk + 63) / 32 + 1; j += NT) sel_bits[j] = 0u;
         __syncthreads();
         for (int k = threadIdx.x; k < Ksel; k += NT) {
             const int J = sel[k];
@@ -434,7 +435,8 @@ static void launch_attend_t(const LaunchCtx& L, const void* Q, const void* packe
     const float c_log2 = L.scale * 1.4426950408889634f;
     hipLaunchKernelGGL((attn_fwd_kernel<T, D, BLK>), grid, dim3(BLK * 2), 0, L.stream, (const T*)Q,
                        (const __bf16*)packed, (const float*)((const char*)packed + g.bias_off), idx, counts, perm,
-                       (T*)O, lse, L.N, L.Nv, L.M, L.K, counts ? L.M : L.K, SQ, L.BH, C, g.Tv, g.Ts, g.Tc, c_log2);
+                       (T*)O, lse, L.N, L.Nv, L.M, L.Mk, L.block_k == 128 ? 1 : 0, L.K, counts ? L.Mk : L.K, SQ,
+                       L.BH, C, g.Tv, g.Ts, g.Tc, c_log2);
 }
 
 void launch_attend(const LaunchCtx& L, const void* Q, const void* packed, const int32_t* idx, const int32_t* counts,

@@ -265,7 +265,8 @@ template <typename T, int D, int BLK>
 __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
     const T* __restrict__ Q, const uint8_t* __restrict__ packed, const float* __restrict__ bias2,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ perm, const uint32_t* __restrict__ amax,
-    T* __restrict__ O, float* __restrict__ lse, int N, int Nv, int M, int Ksel, int SQ, int BH, int C, int Tv,
+    T* __restrict__ O, float* __restrict__ lse, int N, int Nv, int M, int Mk, int nsh, int Ksel, int SQ, int BH, int C,
+    int Tv,
     int Ts, int Tc, float c_log2) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using G = TileGeom8<D>;
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
             if (I >= M) return;
             qrow0 = I * BLK;
             nq = min(BLK, Nv - qrow0);
-            ntiles = Ksel * (BLK / kTK8) + Ts + Tc;
+            ntiles = (Ksel << nsh) + Ts + Tc;
         }
     }
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -311,8 +312,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
     const uint8_t* ptile = packed + (size_t)bh * Tall * G::BYTES;
     const float* pbias = bias2 + (size_t)bh * Tall * kTK8;
     const int32_t* sel = dense ? nullptr : idx + ((size_t)bh * M + qrow0 / BLK) * Ksel;
-    constexpr int nsub = BLK / kTK8;
-    const int n_exact = dense ? 0 : Ksel * nsub;
+    // a selected key block is 1 << nsh tiles (key blocks of 64 or 128 keys)
+    const int n_exact = dense ? 0 : Ksel << nsh;
     const int first_cmp = dense ? ntiles : n_exact + Ts;
 
     int win_base = 0, selw = 0;
@@ -320,16 +321,16 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
     auto tile_of = [&](int t) __attribute__((always_inline)) -> int {
         if (dense) return t;
         if (t >= n_exact) return Tv + (t - n_exact);
-        const int k = t / nsub;
+        const int k = t >> nsh;
         if (k >= win_base + 64) {
             win_base = k & ~63;
             selw = win_base + lane < Ksel ? sel[win_base + lane] : 0;
         }
-        return __builtin_amdgcn_readlane(selw, k - win_base) * nsub + t % nsub;
+        return (__builtin_amdgcn_readlane(selw, k - win_base) << nsh) + (t & ((1 << nsh) - 1));
     };
 
     if (!dense) {
-        for (int j = threadIdx.x; j < (M + 63) / 32 + 1; j += NT) sel_bits[j] = 0u;
+        for (int j = threadIdx.x; j < (Mk + 63) / 32 + 1; j += NT) sel_bits[j] = 0u;
         __syncthreads();
         for (int k = threadIdx.x; k < Ksel; k += NT) {
             const int J = sel[k];
@@ -564,7 +565,7 @@ static void launch_pack_fp8_t(const LaunchCtx& L, const void* K, const void* V, 
     hipLaunchKernelGGL((pack_keys_fp8_kernel<T, D>), dim3(L.BH * (g.Tv + g.Ts)), dim3(256), 0, L.stream, (const T*)K,
                        (const T*)V, L.N, L.Nv, g.Tv, g.Ts, g.Tall, amax, kv, b2);
     hipLaunchKernelGGL((pack_compressed_fp8_kernel<D>), dim3(L.BH * g.Tc), dim3(256), 0, L.stream, k_sum, v_sum, bias,
-                       L.M, g.Tv, g.Ts, g.Tc, g.Tall, amax, kv, b2);
+                       L.Mk, g.Tv, g.Ts, g.Tc, g.Tall, amax, kv, b2);
 }
 
 void launch_pack_fp8(const LaunchCtx& L, const void* K, const void* V, const float* k_sum, const float* v_sum,
@@ -588,7 +589,8 @@ static void launch_attend_fp8_t(const LaunchCtx& L, const void* Q, const void* p
     const float c_log2 = L.scale * 1.4426950408889634f;
     hipLaunchKernelGGL((attn_fwd_fp8_kernel<T, D, BLK>), grid, dim3(BLK * 2), 0, L.stream, (const T*)Q,
                        (const uint8_t*)packed, (const float*)((const char*)packed + g.bias_off), idx, perm, amax,
-                       (T*)O, lse, L.N, L.Nv, L.M, L.K, SQ, L.BH, C, g.Tv, g.Ts, g.Tc, c_log2);
+                       (T*)O, lse, L.N, L.Nv, L.M, L.Mk, L.block_k == 128 ? 1 : 0, L.K, SQ, L.BH, C, g.Tv, g.Ts,
+                       g.Tc, c_log2);
 }
 
 void launch_attend_fp8(const LaunchCtx& L, const void* Q, const void* packed, const int32_t* idx,

@@ -8,6 +8,7 @@ namespace spark {
 // Validated sizes of one call, shared by every launcher.
 struct LaunchCtx {
     int B, H, BH, N, Nv, n_sink, d, block, M, K;
+    int block_k, Mk;  // key block size and key blocks (the route's columns); K is over Mk
     int pool_mode, dtype;
     float scale;
     hipStream_t stream;

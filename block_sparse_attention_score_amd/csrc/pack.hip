@@ -8,8 +8,8 @@
 // M whole blocks, so a short last block ends in padding), tiles
 // Tv .. Tv+Ts-1 the sink keys, tiles Tv+Ts .. Tall-1 the compressed pseudo-keys (the per-block
 // summaries, Spark-H3 page, "Spark-Attnが変えるもの", Spark-Reweight bullet).  A selected block J
-// is the tiles J*block/64 .. (J+1)*block/64 - 1.  Padding rows are zero with bias -inf, so the
-// attention kernel reads whole tiles with no bounds logic.
+// is the tiles J*block_k/64 .. (J+1)*block_k/64 - 1 (block_k: the key block size).  Padding rows
+// are zero with bias -inf, so the attention kernel reads whole tiles with no bounds logic.
 //
 // Every value tile is stored transposed: each selected block is used by ~K of the M query blocks,
 // so transposing once here replaces a transposition at every use inside the attention loop.
@@ -19,9 +19,9 @@ namespace spark {
 
 PackGeom pack_geom(const LaunchCtx& L) {
     PackGeom g;
-    g.Tv = L.M * (L.block / 64);  // every block owns whole tiles (a short last block is padded)
+    g.Tv = L.Mk * (L.block_k / 64);  // every key block owns whole tiles (a short last block is padded)
     g.Ts = (L.n_sink + 63) / 64;
-    g.Tc = (L.M + 63) / 64;
+    g.Tc = (L.Mk + 63) / 64;
     g.Tall = g.Tv + g.Ts + g.Tc;
     g.tile_elems = (size_t)2 * 64 * L.d;
     g.kv_bytes = (size_t)L.BH * g.Tall * g.tile_elems * 2;
@@ -121,7 +121,7 @@ static void launch_pack_t(const LaunchCtx& L, const void* K, const void* V, cons
                            (const T*)K, (const T*)V, L.N, L.Nv, g.Tv, g.Ts, g.Tall, kv, b2);
     if (k_sum && v_sum && bias)
         hipLaunchKernelGGL((pack_compressed_kernel<D>), dim3(L.BH * g.Tc), dim3(256), 0, L.stream, k_sum, v_sum,
-                           bias, L.M, g.Tv, g.Ts, g.Tc, g.Tall, kv, b2);
+                           bias, L.Mk, g.Tv, g.Ts, g.Tc, g.Tall, kv, b2);
 }
 
 void launch_pack(const LaunchCtx& L, const void* K, const void* V, const float* k_sum, const float* v_sum,

@@ -214,37 +214,46 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, c
     }
 }
 
+// Query means (and the anchor) over the L.M query blocks of L.block rows; key summaries over the
+// L.Mk key blocks of L.block_k keys.
 template <typename T, int D, int BLK>
-static void launch_pool_t(const LaunchCtx& L, const void* Q, const void* K, const void* V, float* q_mean,
-                          float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor) {
-    const dim3 grid(L.BH * L.M);
-    hipLaunchKernelGGL((pool_q_kernel<T, D, BLK>), grid, dim3(256), 0, L.stream, (const T*)Q, L.N,
+static void launch_pool_q_t(const LaunchCtx& L, const void* Q, float* q_mean, float* anchor) {
+    hipLaunchKernelGGL((pool_q_kernel<T, D, BLK>), dim3(L.BH * L.M), dim3(256), 0, L.stream, (const T*)Q, L.N,
                        L.Nv, L.M, q_mean);
     hipLaunchKernelGGL((anchor_kernel<D>), dim3(L.BH), dim3(kAnchorThreads), 0, L.stream, q_mean, L.Nv, L.M,
                        BLK, anchor);
+}
+
+template <typename T, int D, int BLK>
+static void launch_pool_kv_t(const LaunchCtx& L, const void* K, const void* V, const float* anchor,
+                             float* k_mean, float* k_sum, float* v_sum, float* bias) {
+    const dim3 grid(L.BH * L.Mk);
     if (L.pool_mode == SPARK_ATTN_POOL_REWEIGHT)
         hipLaunchKernelGGL((pool_kv_kernel<T, D, BLK, true>), grid, dim3(256), 0, L.stream, (const T*)K,
-                           (const T*)V, anchor, L.N, L.Nv, L.M, L.scale, k_mean, k_sum, v_sum, bias);
+                           (const T*)V, anchor, L.N, L.Nv, L.Mk, L.scale, k_mean, k_sum, v_sum, bias);
     else
         hipLaunchKernelGGL((pool_kv_kernel<T, D, BLK, false>), grid, dim3(256), 0, L.stream, (const T*)K,
-                           (const T*)V, anchor, L.N, L.Nv, L.M, L.scale, k_mean, k_sum, v_sum, bias);
+                           (const T*)V, anchor, L.N, L.Nv, L.Mk, L.scale, k_mean, k_sum, v_sum, bias);
+}
+
+template <typename T, int D>
+static void launch_pool_t(const LaunchCtx& L, const void* Q, const void* K, const void* V, float* q_mean,
+                          float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor) {
+    if (L.block == 64) launch_pool_q_t<T, D, 64>(L, Q, q_mean, anchor);
+    else launch_pool_q_t<T, D, 128>(L, Q, q_mean, anchor);
+    if (L.block_k == 64) launch_pool_kv_t<T, D, 64>(L, K, V, anchor, k_mean, k_sum, v_sum, bias);
+    else launch_pool_kv_t<T, D, 128>(L, K, V, anchor, k_mean, k_sum, v_sum, bias);
 }
 
 void launch_pool(const LaunchCtx& L, const void* Q, const void* K, const void* V, float* q_mean,
                  float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor) {
-#define SPARK_POOL_CASE(T, D, B)                                                                  \
-    if (L.d == D && L.block == B) {                                                               \
-        launch_pool_t<T, D, B>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor);           \
-        return;                                                                                   \
-    }
     if (L.dtype == SPARK_ATTN_BF16) {
-        SPARK_POOL_CASE(__bf16, 64, 64) SPARK_POOL_CASE(__bf16, 64, 128)
-        SPARK_POOL_CASE(__bf16, 128, 64) SPARK_POOL_CASE(__bf16, 128, 128)
+        if (L.d == 64) launch_pool_t<__bf16, 64>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor);
+        else launch_pool_t<__bf16, 128>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor);
     } else {
-        SPARK_POOL_CASE(float, 64, 64) SPARK_POOL_CASE(float, 64, 128)
-        SPARK_POOL_CASE(float, 128, 64) SPARK_POOL_CASE(float, 128, 128)
+        if (L.d == 64) launch_pool_t<float, 64>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor);
+        else launch_pool_t<float, 128>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor);
     }
-#undef SPARK_POOL_CASE
 }
 
 }  // namespace spark

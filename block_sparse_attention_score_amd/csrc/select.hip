@@ -19,14 +19,15 @@ namespace spark {
 constexpr int kGT = 64;   // score tile (rows and columns)
 constexpr int kGD = 32;   // d per LDS stage
 
+// S [BH][Mq][Mk]: query-block means against key-block means.
 __global__ __launch_bounds__(256) void block_scores_kernel(const float* __restrict__ q_mean,
-                                                           const float* __restrict__ k_mean, int M, int D,
-                                                           float scale, float* __restrict__ S) {
+                                                           const float* __restrict__ k_mean, int Mq, int M,
+                                                           int D, float scale, float* __restrict__ S) {
     __shared__ float Qs[kGD][kGT + 4];
     __shared__ float Ks[kGD][kGT + 4];
     const int bh = blockIdx.z, I0 = blockIdx.y * kGT, J0 = blockIdx.x * kGT;
     const int t = threadIdx.x, ty = t / 16, tx = t % 16;
-    const float* qb = q_mean + (size_t)bh * M * D;
+    const float* qb = q_mean + (size_t)bh * Mq * D;
     const float* kb = k_mean + (size_t)bh * M * D;
     float acc[4][4] = {};
     for (int d0 = 0; d0 < D; d0 += kGD) {
@@ -35,7 +36,7 @@ __global__ __launch_bounds__(256) void block_scores_kernel(const float* __restri
         for (int k = 0; k < 2; ++k) {  // 64 rows x 32 d = 512 float4 per operand
             const int e = t + 256 * k, r = e / 8, c = (e % 8) * 4;
             f32x4 qv = {0.f, 0.f, 0.f, 0.f}, kv = {0.f, 0.f, 0.f, 0.f};
-            if (I0 + r < M) qv = *reinterpret_cast<const f32x4*>(qb + (size_t)(I0 + r) * D + d0 + c);
+            if (I0 + r < Mq) qv = *reinterpret_cast<const f32x4*>(qb + (size_t)(I0 + r) * D + d0 + c);
             if (J0 + r < M) kv = *reinterpret_cast<const f32x4*>(kb + (size_t)(J0 + r) * D + d0 + c);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
@@ -57,8 +58,8 @@ __global__ __launch_bounds__(256) void block_scores_kernel(const float* __restri
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int I = I0 + ty * 4 + i;
-        if (I >= M) break;
-        float* dst = S + ((size_t)bh * M + I) * M;
+        if (I >= Mq) break;
+        float* dst = S + ((size_t)bh * Mq + I) * M;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int J = J0 + tx * 4 + j;
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(256) void tau_rows_kernel(const float* __restrict__
 void launch_select_tau(const LaunchCtx& L, float tau, const float* q_mean, const float* k_mean, int32_t* idx,
                        int32_t* counts, float* stats, float* scores, double* partials) {
     const dim3 sgrid((L.M + kGT - 1) / kGT, (L.M + kGT - 1) / kGT, L.BH);
-    hipLaunchKernelGGL(block_scores_kernel, sgrid, dim3(256), 0, L.stream, q_mean, k_mean, L.M, L.d, L.scale,
+    hipLaunchKernelGGL(block_scores_kernel, sgrid, dim3(256), 0, L.stream, q_mean, k_mean, L.M, L.M, L.d, L.scale,
                        scores);
     hipLaunchKernelGGL(tau_partial_kernel, dim3(kTauParts, L.BH), dim3(256), 0, L.stream, scores, L.M, partials);
     const int rows = L.BH * L.M;
@@ -222,17 +223,17 @@ void launch_select_tau(const LaunchCtx& L, float tau, const float* q_mean, const
                        partials, idx, counts, stats);
 }
 
-size_t select_workspace_bytes(const LaunchCtx& L) { return (size_t)L.BH * L.M * L.M * 4; }
+size_t select_workspace_bytes(const LaunchCtx& L) { return (size_t)L.BH * L.M * L.Mk * 4; }
 
 void launch_select(const LaunchCtx& L, const float* q_mean, const float* k_mean, int32_t* idx, float* scores) {
-    const dim3 sgrid((L.M + kGT - 1) / kGT, (L.M + kGT - 1) / kGT, L.BH);
-    hipLaunchKernelGGL(block_scores_kernel, sgrid, dim3(256), 0, L.stream, q_mean, k_mean, L.M, L.d, L.scale,
-                       scores);
+    const dim3 sgrid((L.Mk + kGT - 1) / kGT, (L.M + kGT - 1) / kGT, L.BH);
+    hipLaunchKernelGGL(block_scores_kernel, sgrid, dim3(256), 0, L.stream, q_mean, k_mean, L.M, L.Mk, L.d,
+                       L.scale, scores);
     const int rows = L.BH * L.M;
     const dim3 tgrid((rows + 3) / 4);
-    const int need = (L.M + 63) / 64;
+    const int need = (L.Mk + 63) / 64;
 #define SPARK_TOPK(KPL) \
-    hipLaunchKernelGGL((topk_rows_kernel<KPL>), tgrid, dim3(256), 0, L.stream, scores, rows, L.M, L.K, idx)
+    hipLaunchKernelGGL((topk_rows_kernel<KPL>), tgrid, dim3(256), 0, L.stream, scores, rows, L.Mk, L.K, idx)
     if (need <= 1) SPARK_TOPK(1);
     else if (need <= 2) SPARK_TOPK(2);
     else if (need <= 4) SPARK_TOPK(4);

@@ -64,18 +64,26 @@ typedef struct {
     int N;             /* rows per (batch, head): video rows followed by n_sink sink rows */
     int d;             /* head dimension */
     int n_sink;        /* sink rows at the tail of every (batch, head), 0 <= n_sink < N */
-    int block;         /* block size for queries and keys */
-    float topk_ratio;  /* kept fraction of key blocks, in (0, 1]; K = clamp(floor(r*M + 1/2), 1, M)
-                          evaluated in binary64 from this binary32 value */
+    int block;         /* query block size (and key block size when block_k is 0) */
+    float topk_ratio;  /* kept fraction of key blocks, in (0, 1]; K = clamp(floor(r*M_k + 1/2), 1,
+                          M_k) evaluated in binary64 from this binary32 value */
     int pool_mode;     /* spark_attn_pool_mode */
     int dtype;         /* spark_attn_dtype of Q, K, V and O */
     float scale;       /* softmax scale s; 0 means 1/sqrt(d) */
+    int block_k;       /* key block size; 0 means `block`.  The asymmetric route (H3 Optimizations
+                          README, "Manual Sparse Sage recovery": the sparse backends consume a
+                          128Q x 64KV route): query blocks of `block` rows are routed to key blocks
+                          of `block_k` keys; key summaries, scores' columns, the budget and the
+                          compressed branch are per key block.  Adaptive tau needs block_k =
+                          block; reblock leaves are query blocks. */
 } spark_attn_params;
 
 /* ---- host-only helpers (no GPU needed) ---------------------------------------------------- */
 
-/* M = ceil(N_v / block), or a negative status for invalid params. */
+/* M = ceil(N_v / block) query blocks, or a negative status for invalid params. */
 int spark_attn_num_blocks(const spark_attn_params *p);
+/* M_k = ceil(N_v / block_k) key blocks (M when block_k is 0 or block), or a negative status. */
+int spark_attn_num_key_blocks(const spark_attn_params *p);
 
 /* Top-K budget of topk_mode=topk_ratio: clamp(floor(ratio*M + 0.5), 1, M) in binary64.
  * Returns a negative status if M < 1 or ratio is outside (0, 1]. */

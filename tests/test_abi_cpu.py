@@ -209,3 +209,23 @@ def test_fp8_entry_points_validate_before_launch():
     assert L.spark_attn_forward_fp8(byref(p), a, None, a, None, a, None, None, None, a, w7, None) == INVALID
     q = P(d=96)
     assert L.spark_attn_forward_fp8(byref(q), a, a, a, None, a, None, None, None, a, 1 << 40, None) == UNSUPPORTED
+
+
+def test_key_block_size_validation_and_counts():
+    L = sa.lib()
+    byref = ctypes.byref
+    p = P(N=1000, n_sink=8, block=128, block_k=64)
+    nv = 1000 - 8
+    assert L.spark_attn_num_blocks(byref(p)) == -(-nv // 128)
+    assert L.spark_attn_num_key_blocks(byref(p)) == -(-nv // 64)
+    assert L.spark_attn_num_key_blocks(byref(P())) == L.spark_attn_num_blocks(byref(P()))
+    assert L.spark_attn_num_key_blocks(byref(P(block_k=32))) == UNSUPPORTED
+    assert L.spark_attn_num_key_blocks(byref(P(block_k=-1))) == INVALID
+    # the score matrix is query blocks x key blocks; the compressed tiles cover the key blocks
+    M, Mk = -(-nv // 128), -(-nv // 64)
+    assert L.spark_attn_workspace_size(byref(p), 3) == p.B * p.H * M * Mk * 4
+    a = ctypes.c_void_p(0x100000)
+    # adaptive tau is defined for equal query and key blocks
+    assert L.spark_attn_select_tau(byref(p), ctypes.c_float(1.0), a, a, a, a, None, a, 1 << 40, None) == UNSUPPORTED
+    assert L.spark_attn_forward_tau(byref(p), ctypes.c_float(1.0), a, a, a, a, None, None, None, a, 1 << 40,
+                                    None) == UNSUPPORTED

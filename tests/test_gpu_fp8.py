@@ -63,13 +63,13 @@ CASES = [
 ]
 
 
-def fp8_check(orc, Q, K, V, ns, b, r, pool_mode, dt, perm=None):
+def fp8_check(orc, Q, K, V, ns, b, r, pool_mode, dt, perm=None, block_k=0):
     Q, K, V = (rounded(x, dt) for x in (Q, K, V))
     permd = torch.from_numpy(perm).cuda() if perm is not None else None
     O, lse, idx, amax = sa.forward_fp8(dev(Q, dt), dev(K, dt), dev(V, dt), ns, b, r, pool_mode, perm=permd,
-                                       return_lse=True, return_idx=True, return_amax=True)
+                                       return_lse=True, return_idx=True, return_amax=True, block_k=block_k)
     torch.cuda.synchronize()
-    p = orc.params(Q, ns, b, r, pool_mode)
+    p = orc.params(Q, ns, b, r, pool_mode, block_k=block_k)
     gidx = idx.cpu().numpy()
     Qp, Kp, Vp = (permute_rows(x, perm) for x in (Q, K, V)) if perm is not None else (Q, K, V)
     ref = orc.pool(p, Qp, Kp, Vp)
@@ -101,6 +101,13 @@ def test_fp8_forward_reblocked(orc):
     note("fp8 forward on the reblocked layout")
     perm = sa.reblock(dev(Q, "bf16"), dev(K, "bf16"), ns, b).cpu().numpy()
     fp8_check(orc, Q, K, V, ns, b, 0.3, 1, "bf16", perm=perm)
+
+
+@pytest.mark.parametrize("b,bk", [(128, 64), (64, 128)])
+def test_fp8_asymmetric_route(orc, b, bk):
+    Q, K, V = W.gaussian_qkv(1, 2, 10 * 128 + 33, 9, 128, seed=b + bk, dtype="bf16")
+    note(f"fp8 forward, query blocks {b}, key blocks {bk}")
+    fp8_check(orc, Q, K, V, 9, b, 0.2, 1, "bf16", block_k=bk)
 
 
 def test_fp8_structured_workload(orc):

@@ -149,12 +149,13 @@ def permute_rows(X, perm):
     return Y
 
 
-def forward_check(orc, Q, K, V, ns, b, r, pool_mode, dt, perm=None):
+def forward_check(orc, Q, K, V, ns, b, r, pool_mode, dt, perm=None, block_k=0):
     Qd, Kd, Vd = to_dev(Q, dt), to_dev(K, dt), to_dev(V, dt)
     permd = torch.from_numpy(perm).cuda() if perm is not None else None
-    O, lse, idx = sa.forward(Qd, Kd, Vd, ns, b, r, pool_mode, perm=permd, return_lse=True, return_idx=True)
+    O, lse, idx = sa.forward(Qd, Kd, Vd, ns, b, r, pool_mode, perm=permd, return_lse=True, return_idx=True,
+                             block_k=block_k)
     torch.cuda.synchronize()
-    p = orc.params(Q, ns, b, r, pool_mode)
+    p = orc.params(Q, ns, b, r, pool_mode, block_k=block_k)
     gidx = host(idx)
     # validate the route against the oracle's scores (in the permuted layout when a perm is given)
     Qp, Kp, Vp = (permute_rows(x, perm) for x in (Q, K, V)) if perm is not None else (Q, K, V)
@@ -203,6 +204,44 @@ def test_forward_with_permutation(orc):
     perm = np.stack([[rng.permutation(nv) for _ in range(H)] for _ in range(B)]).astype(np.int32)
     note("forward with a permutation")
     forward_check(orc, Q, K, V, ns, b, 0.3, 1, "bf16", perm=perm)
+
+
+# asymmetric route: query blocks of `block` rows, key blocks of `block_k` keys
+ASYM = [
+    ("q128-k64", 1, 2, 11 * 128 + 37, 5, 128, 128, 64, 0.15, "bf16"),
+    ("q64-k128", 1, 2, 23 * 64 + 5, 70, 128, 64, 128, 0.2, "bf16"),
+    ("q128-k64-d64", 2, 1, 6 * 128 + 1, 0, 64, 128, 64, 0.3, "bf16"),
+    ("q128-k64-fp32", 1, 1, 5 * 128 + 90, 3, 128, 128, 64, 0.25, "fp32"),
+]
+
+
+@pytest.mark.parametrize("pool_mode", [0, 1])
+@pytest.mark.parametrize("case", ASYM, ids=[c[0] for c in ASYM])
+def test_forward_asymmetric_route(orc, case, pool_mode):
+    name, B, H, nv, ns, d, b, bk, r, dt = case
+    Q, K, V = W.gaussian_qkv(B, H, nv, ns, d, seed=nv + bk, dtype=dt)
+    note(f"forward asymmetric {name} mode={pool_mode}")
+    forward_check(orc, Q, K, V, ns, b, r, pool_mode, dt, block_k=bk)
+
+
+def test_asymmetric_pool_and_scores(orc):
+    B, H, nv, ns, d, b, bk = 1, 2, 9 * 128 + 40, 6, 128, 128, 64
+    Q, K, V = W.gaussian_qkv(B, H, nv, ns, d, seed=31, dtype="bf16")
+    Qd, Kd, Vd = to_dev(Q, "bf16"), to_dev(K, "bf16"), to_dev(V, "bf16")
+    note("asymmetric pool and block scores")
+    out = sa.pool(Qd, Kd, Vd, ns, b, block_k=bk)
+    idx, S = sa.select(out["q_mean"], out["k_mean"], Qd, ns, b, 0.2, with_scores=True, block_k=bk)
+    torch.cuda.synchronize()
+    p = orc.params(Q.astype(np.float32), ns, b, 0.2, 1, block_k=bk)
+    ref = orc.pool(p, host(Qd), host(Kd), host(Vd))
+    assert out["k_mean"].shape[2] == orc.num_key_blocks(p) and out["q_mean"].shape[2] == orc.num_blocks(p)
+    for key in ("q_mean", "k_mean", "k_sum", "v_sum", "anchor"):
+        g, o = host(out[key]), ref[key]
+        assert np.abs(g - o).max() / np.abs(o).max() < POOL_RTOL, key
+    Sref = orc.scores(p, ref["q_mean"], ref["k_mean"])
+    assert np.abs(host(S) - Sref).max() <= 1e-5 * np.abs(Sref).max()
+    bad, _ = check_selection(idx.cpu().numpy(), Sref)
+    assert bad == 0
 
 
 def test_gather_rows_bit_exact():
