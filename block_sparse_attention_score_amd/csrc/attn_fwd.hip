@@ -324,7 +324,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
             for (int c = 0; c < 2; ++c)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[c][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32)) * c_log2;  // scale > 0: the max commutes with it
+            mx = half_max(mx) * c_log2;  // scale > 0: the max commutes with it
             cc = c_log2;
         } else {
             const int cbase = (t - first_cmp) * kTK;  // first pseudo-key of a compressed tile
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
                         mx = fmaxf(mx, st[c][4 * g + j]);
                     }
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = half_max(mx);
             cc = 1.f;
         }
         const bool raise = mx > m_run + kRescaleSlack;

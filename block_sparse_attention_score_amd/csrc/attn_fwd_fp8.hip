@@ -443,7 +443,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
             for (int c = 0; c < 2; ++c)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[c][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32)) * cl;  // cl > 0: the max commutes with it
+            mx = half_max(mx) * cl;  // cl > 0: the max commutes with it
             cc = cl;
         } else {
             const int cbase = (t - first_cmp) * kTK8;
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
                         mx = fmaxf(mx, st[c][4 * g + j]);
                     }
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = half_max(mx);
             cc = 1.f;
         }
         const bool raise = mx > m_run + kRescaleSlack8;

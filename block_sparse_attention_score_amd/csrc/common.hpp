@@ -19,6 +19,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 constexpr int kMaxBlocks = 16384;  // largest M the select / attention LDS tables are sized for
 
+// Maximum of v over lanes l and l ^ 32 (the two 32-lane halves of the wave), in one VALU swap
+// (v_permlane32_swap) instead of a round trip through the LDS crossbar.  Whichever way the swap
+// assigns its two results, together they hold v of both lanes.
+__device__ __forceinline__ float half_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
