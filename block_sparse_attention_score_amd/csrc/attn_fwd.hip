@@ -104,20 +104,10 @@ __device__ __forceinline__ void issue_half(RS rs, uint32_t tile_byte,
                                                  tile_byte + (PL::kAffine ? (uint32_t)(i * NT * 16) : 0u), 0, 0);
 }
 
-// A zero the compiler cannot see through, taken once per pipeline step.  LDS addresses are formed
-// as stage base + (lane offset ^ zero): the lane offsets are computed once, the per-stage sums are
-// not hoisted out of the loop (which would hold one set of address registers per stage), and the
-// stage base, a constant, folds into the instruction's offset field.
-__device__ __forceinline__ uint32_t opaque_zero() {
-    uint32_t z;
-    asm volatile("s_mov_b32 %0, 0" : "=s"(z));
-    return z;
-}
-
 // S^T = K_tile Q^T for two chunks of 32 keys x this wave's 32 queries.  kboff[ds]: byte offset of
 // lane (i32, h)'s A operand in row i32 of the tile for k step ds (row 32 + i32 is 64*D bytes further).
 template <int D>
-__device__ __forceinline__ void scores(const __bf16* Kl, const uint32_t (&kboff)[D / 16], uint32_t z,
+__device__ __forceinline__ void scores(const __bf16* Kl, const uint32_t (&kboff)[D / 16],
                                        const bf16x8 (&qreg)[D / 16], f32x16 (&st)[2]) {
     const char* Kb = reinterpret_cast<const char*>(Kl);
 #pragma unroll
@@ -127,7 +117,7 @@ __device__ __forceinline__ void scores(const __bf16* Kl, const uint32_t (&kboff)
         for (int r = 0; r < 16; ++r) a16[r] = 0.f;
 #pragma unroll
         for (int ds = 0; ds < D / 16; ++ds) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + c * 64 * D + (kboff[ds] ^ z));
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + c * 64 * D + kboff[ds]);
             a16 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], a16, 0, 0, 0);
         }
         st[c] = a16;
@@ -293,7 +283,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // K(0), K(1), V(0) and the route bits are in LDS
     f32x16 sc[2][2];  // scores of tile t live in sc[t % 2]
-    scores<D>(kbuf(IC<0>{}), kboff, 0u, qreg, sc[0]);
+    scores<D>(kbuf(IC<0>{}), kboff, qreg, sc[0]);
     bool clean_t = clean_of(tile_of(0)), clean_v = ntiles > 1 && clean_of(tl_v);  // tiles t and t+1
 
     // One pipeline step on stage parity P = t % 2.  MASKED: tile t is a compressed tile, whose
@@ -311,8 +301,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
         clean_t = clean_v;
         clean_v = t + 2 < ntiles && clean_of(tl_k);
         tl_v = tl_k;
-        const uint32_t z = opaque_zero();
-        scores<D>(kbuf(IC<P ^ 1>{}), kboff, z, qreg, sc[P ^ 1]);  // tile t+1 (unused after the last)
+        scores<D>(kbuf(IC<P ^ 1>{}), kboff, qreg, sc[P ^ 1]);  // tile t+1 (unused after the last)
 
         // ---- probabilities of tile t.  Register 4g+j of chunk c holds key c*32 + 16(g/2) + 8h + 4(g%2) + j.
         // Exponent of key j: x_j * cc - m with x the raw score (cc = scale*log2 e) on a tile without
@@ -377,7 +366,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
             }
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {  // V^T row dt*32 + i32 is 64*kTK bytes past row i32
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vb + dt * 64 * kTK + (vboff[kt] ^ z));
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vb + dt * 64 * kTK + vboff[kt]);
                 acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk, acc[dt], 0, 0, 0);
             }
         }

@@ -221,12 +221,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc8(const void* base, u
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ uint32_t opaque_zero8() {
-    uint32_t z;
-    asm volatile("s_mov_b32 %0, 0" : "=s"(z));
-    return z;
-}
-
 // 32 bytes of an LDS row at two 16-byte chunks as one MFMA operand.
 __device__ __forceinline__ i32x8 lds32(const char* p0, const char* p1) {
     const u32x4 a = *reinterpret_cast<const u32x4*>(p0);
@@ -242,7 +236,7 @@ __device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
 // S^T = K_tile Q^T for two chunks of 32 keys x this wave's 32 queries.  kboff[ds][u]: byte offset of
 // lane (i32, h)'s chunk u (of 2) of k step ds in row i32 (row 32 + i32 is 32*D bytes further).
 template <int D>
-__device__ __forceinline__ void scores8(const uint8_t* Kl, const uint32_t (&kboff)[D / 64][2], uint32_t z,
+__device__ __forceinline__ void scores8(const uint8_t* Kl, const uint32_t (&kboff)[D / 64][2],
                                         const i32x8 (&qreg)[D / 64], f32x16 (&st)[2]) {
     const char* Kb = reinterpret_cast<const char*>(Kl);
 #pragma unroll
@@ -252,7 +246,7 @@ __device__ __forceinline__ void scores8(const uint8_t* Kl, const uint32_t (&kbof
         for (int r = 0; r < 16; ++r) a16[r] = 0.f;
 #pragma unroll
         for (int ds = 0; ds < D / 64; ++ds) {
-            const i32x8 a = lds32(Kb + c * 32 * D + (kboff[ds][0] ^ z), Kb + c * 32 * D + (kboff[ds][1] ^ z));
+            const i32x8 a = lds32(Kb + c * 32 * D + kboff[ds][0], Kb + c * 32 * D + kboff[ds][1]);
             a16 = mfma8(a, qreg[ds], a16);
         }
         st[c] = a16;
@@ -417,7 +411,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x16 sc[2][2];
-    scores8<D>(kbuf(IC8<0>{}), kboff, 0u, qreg, sc[0]);
+    scores8<D>(kbuf(IC8<0>{}), kboff, qreg, sc[0]);
     bool clean_t = clean_of(tile_of(0)), clean_v = ntiles > 1 && clean_of(tl_v);
 
     auto step = [&](int t, auto masked, auto par) __attribute__((always_inline)) {
@@ -432,8 +426,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
         clean_t = clean_v;
         clean_v = t + 2 < ntiles && clean_of(tl_k);
         tl_v = tl_k;
-        const uint32_t z = opaque_zero8();
-        scores8<D>(kbuf(IC8<P ^ 1>{}), kboff, z, qreg, sc[P ^ 1]);
+        scores8<D>(kbuf(IC8<P ^ 1>{}), kboff, qreg, sc[P ^ 1]);
 
         // probabilities of tile t; register 4g+j of chunk c holds key 32c + 8g + 4h + j
         f32x16 (&st)[2] = sc[P];
@@ -497,7 +490,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
         const char* Vb = reinterpret_cast<const char*>(vbuf(IC8<P>{}));
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {  // V^T row dt*32 + i32 is 32*64 bytes past row i32
-            const i32x8 a = lds32(Vb + dt * 32 * kTK8 + (vboff[0] ^ z), Vb + dt * 32 * kTK8 + (vboff[1] ^ z));
+            const i32x8 a = lds32(Vb + dt * 32 * kTK8 + vboff[0], Vb + dt * 32 * kTK8 + vboff[1]);
             acc[dt] = mfma8(a, pf, acc[dt]);
         }
     };
