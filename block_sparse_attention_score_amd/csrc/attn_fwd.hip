@@ -289,7 +289,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     // One pipeline step on stage parity P = t % 2.  MASKED: tile t is a compressed tile, whose
     // pseudo-keys of this query block's selected blocks are excluded (the mask goes into the additive
     // term with selects).
-    auto step = [&](int t, auto masked, auto par) __attribute__((always_inline)) {
+    auto step = [&](int t, auto masked, auto par, auto known_clean) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked)::value;
         constexpr int P = decltype(par)::value;
         __builtin_amdgcn_s_waitcnt(0);  // this thread's share of K(t+1), V(t) has landed
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
         const int tl_k = t + 2 < ntiles ? tile_of(t + 2) : 0;
         if (t + 2 < ntiles) load_k(tl_k, IC<P>{});
         if (t + 1 < ntiles) load_v(tl_v, IC<P ^ 1>{});
-        const bool clean = !MASKED && clean_t;
+        const bool clean = decltype(known_clean)::value || (!MASKED && clean_t);
         clean_t = clean_v;
         clean_v = t + 2 < ntiles && clean_of(tl_k);
         tl_v = tl_k;
@@ -374,12 +374,20 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     // Steps over [t, end) with the stage parity a template constant: pairs (even, odd), plus one
     // step at either end when the range starts odd or ends early.
     auto run = [&](int t, int end, auto masked) __attribute__((always_inline)) {
-        if (t < end && (t & 1)) step(t++, masked, IC<1>{});
-        for (; t + 1 < end; t += 2) {
-            step(t, masked, IC<0>{});
-            step(t + 1, masked, IC<1>{});
+        constexpr std::false_type any{};
+        if (t < end && (t & 1)) step(t++, masked, IC<1>{}, any);
+        if constexpr (!decltype(masked)::value) {
+            // leading pairs of tiles known to need no additive term (all but ragged edge tiles)
+            for (; t + 1 < end && clean_t && clean_v; t += 2) {
+                step(t, masked, IC<0>{}, std::true_type{});
+                step(t + 1, masked, IC<1>{}, std::true_type{});
+            }
         }
-        if (t < end) step(t++, masked, IC<0>{});
+        for (; t + 1 < end; t += 2) {
+            step(t, masked, IC<0>{}, any);
+            step(t + 1, masked, IC<1>{}, any);
+        }
+        if (t < end) step(t++, masked, IC<0>{}, any);
         return t;
     };
     run(run(0, first_cmp, std::false_type{}), ntiles, std::true_type{});

@@ -414,7 +414,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
     scores8<D>(kbuf(IC8<0>{}), kboff, qreg, sc[0]);
     bool clean_t = clean_of(tile_of(0)), clean_v = ntiles > 1 && clean_of(tl_v);
 
-    auto step = [&](int t, auto masked, auto par) __attribute__((always_inline)) {
+    auto step = [&](int t, auto masked, auto par, auto known_clean) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked)::value;
         constexpr int P = decltype(par)::value;
         __builtin_amdgcn_s_waitcnt(0);
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
         const int tl_k = t + 2 < ntiles ? tile_of(t + 2) : 0;
         if (t + 2 < ntiles) load_k(tl_k, IC8<P>{});
         if (t + 1 < ntiles) load_v(tl_v, IC8<P ^ 1>{});
-        const bool clean = !MASKED && clean_t;
+        const bool clean = decltype(known_clean)::value || (!MASKED && clean_t);
         clean_t = clean_v;
         clean_v = t + 2 < ntiles && clean_of(tl_k);
         tl_v = tl_k;
@@ -495,12 +495,20 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
         }
     };
     auto run = [&](int t, int end, auto masked) __attribute__((always_inline)) {
-        if (t < end && (t & 1)) step(t++, masked, IC8<1>{});
-        for (; t + 1 < end; t += 2) {
-            step(t, masked, IC8<0>{});
-            step(t + 1, masked, IC8<1>{});
+        constexpr std::false_type any{};
+        if (t < end && (t & 1)) step(t++, masked, IC8<1>{}, any);
+        if constexpr (!decltype(masked)::value) {
+            // leading pairs of tiles known to need no additive term (all but ragged edge tiles)
+            for (; t + 1 < end && clean_t && clean_v; t += 2) {
+                step(t, masked, IC8<0>{}, std::true_type{});
+                step(t + 1, masked, IC8<1>{}, std::true_type{});
+            }
         }
-        if (t < end) step(t++, masked, IC8<0>{});
+        for (; t + 1 < end; t += 2) {
+            step(t, masked, IC8<0>{}, any);
+            step(t + 1, masked, IC8<1>{}, any);
+        }
+        if (t < end) step(t++, masked, IC8<0>{}, any);
         return t;
     };
     run(run(0, first_cmp, std::false_type{}), ntiles, std::true_type{});
