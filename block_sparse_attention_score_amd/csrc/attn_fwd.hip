@@ -353,6 +353,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
         // P in bf16, 16 keys per PV step: lane (i32, h) supplies keys 16kt + 8h + e (e = 0..7).
         // The normaliser sums the same bf16 values the PV product uses.
         const char* Vb = reinterpret_cast<const char*>(vbuf(IC<P>{}));
+        // The probability/PV phase runs at raised wave priority: the SIMD's other wave is then most
+        // often in its score or row-max phase, so the two keep both the VALU and the matrix pipe fed.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kt = 0; kt < kTK / 16; ++kt) {
             bf16x8 pk;
@@ -370,6 +373,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
                 acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk, acc[dt], 0, 0, 0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     };
     // Steps over [t, end) with the stage parity a template constant: pairs (even, odd), plus one
     // step at either end when the range starts odd or ends early.
