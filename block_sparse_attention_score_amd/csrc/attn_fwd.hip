@@ -191,17 +191,22 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     const int first_cmp = dense ? ntiles : n_exact + Ts;  // first compressed tile in the list
 
     // Selected block ids are read 64 at a time into a register (lane l holds entry base + l) and
-    // taken out with readlane, so the tile loop issues no global loads besides the tile stream.
-    int win_base = 0, selw = 0;
-    if (!dense) selw = lane < Ksel ? sel[lane] : 0;
+    // taken out with readlane, so the tile loop issues no global loads besides the tile stream.  The
+    // next 64 are loaded one window ahead, so moving to them never waits for memory.
+    int win_base = 0, selw = 0, selw_next = 0;
+    if (!dense) {
+        selw = lane < Ksel ? sel[lane] : 0;
+        selw_next = 64 + lane < Ksel ? sel[64 + lane] : 0;
+    }
     // packed tile of list entry t (called with increasing t): selected blocks, sinks, compressed
     auto tile_of = [&](int t) __attribute__((always_inline)) -> int {
         if (dense) return t;
         if (t >= n_exact) return Tv + (t - n_exact);
         const int k = t >> nsh;
-        if (k >= win_base + 64) {
-            win_base = k & ~63;
-            selw = win_base + lane < Ksel ? sel[win_base + lane] : 0;
+        if (k >= win_base + 64) {  // k grows by at most one per call: this is the next window
+            win_base += 64;
+            selw = selw_next;
+            selw_next = win_base + 64 + lane < Ksel ? sel[win_base + 64 + lane] : 0;
         }
         return (__builtin_amdgcn_readlane(selw, k - win_base) << nsh) + (t & ((1 << nsh) - 1));
     };

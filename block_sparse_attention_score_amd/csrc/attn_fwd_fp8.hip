@@ -310,15 +310,21 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
     const int n_exact = dense ? 0 : Ksel << nsh;
     const int first_cmp = dense ? ntiles : n_exact + Ts;
 
-    int win_base = 0, selw = 0;
-    if (!dense) selw = lane < Ksel ? sel[lane] : 0;
+    // selected block ids, 64 per register window (lane l holds entry base + l), the next window
+    // loaded one ahead so that moving to it never waits for memory
+    int win_base = 0, selw = 0, selw_next = 0;
+    if (!dense) {
+        selw = lane < Ksel ? sel[lane] : 0;
+        selw_next = 64 + lane < Ksel ? sel[64 + lane] : 0;
+    }
     auto tile_of = [&](int t) __attribute__((always_inline)) -> int {
         if (dense) return t;
         if (t >= n_exact) return Tv + (t - n_exact);
         const int k = t >> nsh;
-        if (k >= win_base + 64) {
-            win_base = k & ~63;
-            selw = win_base + lane < Ksel ? sel[win_base + lane] : 0;
+        if (k >= win_base + 64) {  // k grows by at most one per call: this is the next window
+            win_base += 64;
+            selw = selw_next;
+            selw_next = win_base + 64 + lane < Ksel ? sel[win_base + 64 + lane] : 0;
         }
         return (__builtin_amdgcn_readlane(selw, k - win_base) << nsh) + (t & ((1 << nsh) - 1));
     };
