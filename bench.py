@@ -365,7 +365,11 @@ def main():
             "kernel": f"{kernel}_kernel (exact + sink + compressed branches, sink queries)",
             "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
             "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-            "traffic": committed_traffic(wl.name, kernel), "traffic_unit": "bytes per launch (FETCH+WRITE, scaled)",
+            # the committed counters were taken on the workload's default route (top-K at its first
+            # ratio, key blocks of `block` keys); any other route streams other tiles
+            "traffic": (committed_traffic(wl.name, kernel)
+                        if args.block_k == 0 and not tau_mode and ratio == wl.ratios[0] else None),
+            "traffic_unit": "bytes per launch (FETCH+WRITE, scaled)",
             "exact_branch_frac": round((F_sel + F_sink) / (ms_attn * 1e-3) / 1e12 / peak, 4),
         },
         "pool_roofline": {"bound": "hbm", "achieved": round(pool_bytes / (ms_pool * 1e-3) / 1e9, 1),
