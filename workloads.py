@@ -103,6 +103,9 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32)
 
 
+N_FEATURES = 48  # 3 raster axes x 8 frequencies x (sin, cos)
+
+
 def positional_features(grid) -> np.ndarray:
     """F (N_v x 48) float64: sin/cos of each raster coordinate at 8 frequencies per axis."""
     T, Y, X = grid
@@ -116,15 +119,39 @@ def positional_features(grid) -> np.ndarray:
     return np.stack(cols, axis=1).astype(np.float64)
 
 
+def _positional_base(grid, W: np.ndarray) -> np.ndarray:
+    """positional_features(grid) @ W in binary64, in a fixed summation order.  Columns 16a ..
+    16a+15 of the features depend on raster axis a alone, so the product is A_t[t] + A_y[y] +
+    A_x[x] with A_a the product of axis a's 16 columns (taken per coordinate value, summed in
+    column order), added as (A_t + A_y) + A_x.  Scalar libm sin/cos and elementwise IEEE
+    operations only: the same bits on every run, thread count and machine with this C library (a
+    BLAS product may split its sums differently from call to call, which flips the last bit of
+    some values and now and then a bf16 rounding)."""
+    parts = []
+    for a, L in enumerate(grid):
+        acc = None
+        for f in range(8):
+            w = math.pi * float(L) ** ((f - 7) / 7.0)
+            # the C library's scalar sin and cos (a vectorised form may take CPU-specific paths)
+            for j, fn in enumerate((math.sin, math.cos)):
+                col = np.array([fn(w * v) for v in range(L)], np.float64)
+                term = col[:, None] * W[16 * a + 2 * f + j]
+                acc = term if acc is None else acc + term
+        parts.append(acc)
+    At, Ay, Ax = parts
+    base = (At[:, None, None, :] + Ay[None, :, None, :]) + Ax[None, None, :, :]
+    return base.reshape(-1, W.shape[1])
+
+
 def _rng(cfg_id, b, h, tid):
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg_id, b, h, tid])))
 
 
-def _head(wl: Workload, F: np.ndarray, b: int, h: int, seed_offset: int):
+def _head(wl: Workload, b: int, h: int, seed_offset: int):
     cid = wl.config_id + seed_offset
     d, nv, ns = wl.d, wl.n_video, wl.n_sink
-    W = _rng(cid, b, h, _T_W).standard_normal((F.shape[1], d))
-    base = (F @ W).astype(np.float32)
+    W = _rng(cid, b, h, _T_W).standard_normal((N_FEATURES, d))
+    base = _positional_base(wl.grid, W).astype(np.float32)
     inv = np.float32(1.0 / math.sqrt(d))
     out = []
     for tn, ts in ((_T_QN, _T_QS), (_T_KN, _T_KS), (_T_VN, _T_VS)):
@@ -141,7 +168,6 @@ def _head(wl: Workload, F: np.ndarray, b: int, h: int, seed_offset: int):
 
 def make_qkv(wl: Workload, seed_offset: int = 0, threads: int = 8):
     """Q, K, V as float32 numpy arrays [B, H, N, d] (bf16-exact values for bf16 workloads)."""
-    F = positional_features(wl.grid)
     shape = (wl.B, wl.H, wl.N, wl.d)
     Q = np.empty(shape, np.float32)
     K = np.empty(shape, np.float32)
@@ -149,7 +175,7 @@ def make_qkv(wl: Workload, seed_offset: int = 0, threads: int = 8):
 
     def one(bh):
         b, h = bh
-        q, k, v = _head(wl, F, b, h, seed_offset)
+        q, k, v = _head(wl, b, h, seed_offset)
         Q[b, h], K[b, h], V[b, h] = q, k, v
 
     jobs = [(b, h) for b in range(wl.B) for h in range(wl.H)]
