@@ -88,11 +88,13 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict_
     constexpr int NREG = KPL > 0 ? KPL : 1;
     uint32_t key[NREG];
     if (KPL > 0) {
+        // every load is unconditional (from a clamped column) so that all of them are in flight
+        // together; columns past the row end are then replaced by the padding key
+        float f[NREG];
 #pragma unroll
-        for (int j = 0; j < NREG; ++j) {
-            const int J = lane + 64 * j;
-            key[j] = J < M ? score_key(Sr[J]) : 0u;
-        }
+        for (int j = 0; j < NREG; ++j) f[j] = Sr[min(lane + 64 * j, M - 1)];
+#pragma unroll
+        for (int j = 0; j < NREG; ++j) key[j] = lane + 64 * j < M ? score_key(f[j]) : 0u;
     }
     auto key_at = [&](int j) -> uint32_t {  // key of block lane + 64 j
         if (KPL > 0) return key[j];
