@@ -27,6 +27,10 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (no sparsity)
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak (no sparsity)
 HBM_PEAK_GBS = 8000.0
+# fp32 vector peak, 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2 (packed FMA) x 2.4 GHz; the
+# kernels are built without packed fp32 instructions, which halves what they can reach
+VALU_FP32_PEAK_TFLOPS = 157.3
+VALU_FP32_UNPACKED_TFLOPS = 78.6
 
 
 def log(msg):
@@ -328,6 +332,7 @@ def main():
     F_attn = F_sel + F_sink + F_comp + F_sinkq
     value = F_sel / (ms_step * 1e-3) / 1e12
     achieved = F_attn / (ms_attn * 1e-3) / 1e12
+    sel_flops = 2.0 * B * H * M * Mk * d
     pool_bytes = 3.0 * B * H * wl.n_video * d * Q.element_size() + 4.0 * B * H * M * d * 4 + 4.0 * B * H * M
 
     peak = MFMA_FP8_PEAK_TFLOPS if fp8 else MFMA_BF16_PEAK_TFLOPS
@@ -375,6 +380,13 @@ def main():
         "pool_roofline": {"bound": "hbm", "achieved": round(pool_bytes / (ms_pool * 1e-3) / 1e9, 1),
                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(pool_bytes / (ms_pool * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        # select = block-score product (fp32 FMA, 2*M*M_k*d flops per head) + row top-K; its
+        # compulsory bytes (block means in, route out) take ~10 us at HBM peak, so the ALU bounds it
+        "select_roofline": {"bound": "alu", "achieved": round(sel_flops / (ms_sel * 1e-3) / 1e12, 2),
+                            "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(sel_flops / (ms_sel * 1e-3) / 1e12 / VALU_FP32_PEAK_TFLOPS, 4),
+                            "frac_of_unpacked_fp32": round(sel_flops / (ms_sel * 1e-3) / 1e12
+                                                           / VALU_FP32_UNPACKED_TFLOPS, 4)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline and (tau_mode or fp8):
