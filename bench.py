@@ -232,7 +232,7 @@ def main():
         Qp, Kp, Vp = Q, K, V
 
     stage_names = ((["reblock"] + (["reblock_k"] if wl.key_partition else []) + ["gather"]) if wl.reblock else []) \
-        + (["fp8_scales"] if fp8 else []) + ["pool", "select", "pack", "attend"]
+        + (["fp8_scales", "pool", "select", "pack", "attend"] if fp8 else ["pool_pack", "select", "attend"])
 
     def step(ev=None):
         k = 1
@@ -252,27 +252,32 @@ def main():
             sa.spark_attn_fp8_scales(p, Qp, Kp, Vp, amax, stream)
             if ev: ev[k].record(stream)
             k += 1
-        sa.spark_attn_pool(p, Qp, Kp, Vp, pooled["q_mean"], pooled["k_mean"], pooled["k_sum"], pooled["v_sum"],
-                           pooled["bias"], pooled["anchor"], stream)
+        if fp8:
+            sa.spark_attn_pool(p, Qp, Kp, Vp, pooled["q_mean"], pooled["k_mean"], pooled["k_sum"],
+                               pooled["v_sum"], pooled["bias"], pooled["anchor"], stream)
+        else:  # pooling and packing in one pass over K and V
+            sa.spark_attn_pool_pack(p, Qp, Kp, Vp, pooled["q_mean"], pooled["k_mean"], pooled["k_sum"],
+                                    pooled["v_sum"], pooled["bias"], pooled["anchor"], packed, stream)
         if ev: ev[k].record(stream)
+        k += 1
         if tau_mode:
             sa.spark_attn_select_tau(p, args.tau, pooled["q_mean"], pooled["k_mean"], idx, counts, None, sel_ws,
                                      stream)
         else:
             sa.spark_attn_select(p, pooled["q_mean"], pooled["k_mean"], idx, None, sel_ws, stream)
-        if ev: ev[k + 1].record(stream)
+        if ev: ev[k].record(stream)
+        k += 1
         if fp8:
             sa.spark_attn_pack_fp8(p, Kp, Vp, pooled["k_sum"], pooled["v_sum"], pooled["bias"], amax, packed, stream)
-        else:
-            sa.spark_attn_pack(p, Kp, Vp, pooled["k_sum"], pooled["v_sum"], pooled["bias"], packed, stream)
-        if ev: ev[k + 2].record(stream)
+            if ev: ev[k].record(stream)
+            k += 1
         if fp8:
             sa.spark_attn_attend_fp8(p, Qp, packed, idx, perm, amax, O, lse, stream)
         elif tau_mode:
             sa.spark_attn_attend_var(p, Qp, packed, idx, counts, perm, O, lse, stream)
         else:
             sa.spark_attn_attend(p, Qp, packed, idx, perm, O, lse, stream)
-        if ev: ev[k + 3].record(stream)
+        if ev: ev[k].record(stream)
 
     log(f"M={M} K={Kk}; warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -291,7 +296,8 @@ def main():
     ms_step = (t1 - t0) * 1e3 / args.steps
     st = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(ns)] for e in events]).mean(axis=0)
     stage_ms = {n: float(x) for n, x in zip(stage_names, st)}
-    ms_pool, ms_sel, ms_pack, ms_attn = (stage_ms[n] for n in ("pool", "select", "pack", "attend"))
+    ms_pool = stage_ms["pool"] if fp8 else stage_ms["pool_pack"]
+    ms_sel, ms_attn = stage_ms["select"], stage_ms["attend"]
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (" + ", ".join(f"{n} {v:.3f}" for n, v in stage_ms.items()) + ")")
 
     # cross-check: the single-call entry point over the same input
@@ -334,6 +340,8 @@ def main():
     achieved = F_attn / (ms_attn * 1e-3) / 1e12
     sel_flops = 2.0 * B * H * M * Mk * d
     pool_bytes = 3.0 * B * H * wl.n_video * d * Q.element_size() + 4.0 * B * H * M * d * 4 + 4.0 * B * H * M
+    if not fp8:  # the fused stage also reads the sink keys/values and writes every packed tile
+        pool_bytes += 2.0 * B * H * wl.n_sink * d * Q.element_size() + float(packed.numel())
 
     peak = MFMA_FP8_PEAK_TFLOPS if fp8 else MFMA_BF16_PEAK_TFLOPS
     kernel = "attn_fwd_fp8" if fp8 else "attn_fwd"
@@ -377,7 +385,8 @@ def main():
             "traffic_unit": "bytes per launch (FETCH+WRITE, scaled)",
             "exact_branch_frac": round((F_sel + F_sink) / (ms_attn * 1e-3) / 1e12 / peak, 4),
         },
-        "pool_roofline": {"bound": "hbm", "achieved": round(pool_bytes / (ms_pool * 1e-3) / 1e9, 1),
+        "pool_roofline": {"stage": "pool" if fp8 else "pool_pack (pooling + packed tiles, one pass over K, V)",
+                          "bound": "hbm", "achieved": round(pool_bytes / (ms_pool * 1e-3) / 1e9, 1),
                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(pool_bytes / (ms_pool * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         # select = block-score product (fp32 FMA, 2*M*M_k*d flops per head) + row top-K; its

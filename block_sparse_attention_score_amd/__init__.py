@@ -39,7 +39,7 @@ class SparkAttnError(RuntimeError):
 
 EXPORTS = (
     "spark_attn_num_blocks", "spark_attn_num_key_blocks", "spark_attn_topk_count", "spark_attn_workspace_size",
-    "spark_attn_status_str", "spark_attn_pool", "spark_attn_select", "spark_attn_pack",
+    "spark_attn_status_str", "spark_attn_pool", "spark_attn_select", "spark_attn_pack", "spark_attn_pool_pack",
     "spark_attn_attend", "spark_attn_forward", "spark_attn_forward_kv", "spark_attn_reblock",
     "spark_attn_gather_rows", "spark_attn_select_tau", "spark_attn_attend_var", "spark_attn_forward_tau",
     "spark_attn_fp8_scales", "spark_attn_pack_fp8", "spark_attn_attend_fp8", "spark_attn_forward_fp8",
@@ -67,6 +67,7 @@ def lib():
             "spark_attn_pool": ([P] + [vp] * 9 + [vp], ctypes.c_int),
             "spark_attn_select": ([P, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "spark_attn_pack": ([P, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "spark_attn_pool_pack": ([P] + [vp] * 10 + [sz, vp], ctypes.c_int),
             "spark_attn_attend": ([P, vp, vp, sz, vp, vp, vp, vp, vp], ctypes.c_int),
             "spark_attn_forward": ([P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "spark_attn_forward_kv": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
@@ -171,6 +172,12 @@ def spark_attn_pack(p, K, V, k_sum, v_sum, bias, packed, stream=None):
         _nbytes(packed), _stream(stream)))
 
 
+def spark_attn_pool_pack(p, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, packed, stream=None):
+    _check("spark_attn_pool_pack", lib().spark_attn_pool_pack(
+        ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(q_mean), _ptr(k_mean), _ptr(k_sum),
+        _ptr(v_sum), _ptr(bias), _ptr(anchor), _ptr(packed), _nbytes(packed), _stream(stream)))
+
+
 def spark_attn_attend(p, Q, packed, idx, perm, O, lse=None, stream=None):
     _check("spark_attn_attend", lib().spark_attn_attend(
         ctypes.byref(p), _ptr(Q), _ptr(packed), _nbytes(packed), _ptr(idx), _ptr(perm), _ptr(O),
@@ -261,6 +268,22 @@ def pool(Q, K, V, n_sink, block, pool_mode=POOL_REWEIGHT, scale=0.0, stream=None
     spark_attn_pool(p, Q, K, V, out["q_mean"], out["k_mean"], out["k_sum"], out["v_sum"],
                     out["bias"], out["anchor"], stream)
     return out
+
+
+def pool_pack(Q, K, V, n_sink, block, pool_mode=POOL_REWEIGHT, scale=0.0, stream=None, block_k=0):
+    """pool() and pack() in one pass over K and V: (pooled dict as pool() returns, packed)."""
+    p = params(Q, n_sink, block, 1.0, pool_mode, scale, block_k)
+    M, Mk = num_blocks(p), num_key_blocks(p)
+    B, H, _, d = Q.shape
+    f = dict(device=Q.device, dtype=torch.float32)
+    out = {"q_mean": torch.empty(B, H, M, d, **f)}
+    out.update({k: torch.empty(B, H, Mk, d, **f) for k in ("k_mean", "k_sum", "v_sum")})
+    out["bias"] = torch.empty(B, H, Mk, **f)
+    out["anchor"] = torch.empty(B, H, d, **f)
+    packed = torch.empty(workspace_size(p, 4), device=Q.device, dtype=torch.uint8)
+    spark_attn_pool_pack(p, Q, K, V, out["q_mean"], out["k_mean"], out["k_sum"], out["v_sum"],
+                         out["bias"], out["anchor"], packed, stream)
+    return out, packed
 
 
 def select(q_mean, k_mean, Q, n_sink, block, topk_ratio, with_scores=False, scale=0.0,

@@ -234,6 +234,22 @@ int spark_attn_pack(const spark_attn_params* p, const void* K, const void* V, co
     return launch_status();
 }
 
+int spark_attn_pool_pack(const spark_attn_params* p, const void* Q, const void* K, const void* V, float* q_mean,
+                         float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor, void* packed,
+                         size_t packed_bytes, void* stream) {
+    LaunchCtx L;
+    int s = make_ctx(p, stream, &L);
+    if (s < 0) return s;
+    if (!Q || !K || !V || !q_mean || !k_mean || !k_sum || !v_sum || !bias || !anchor)
+        return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(q_mean) || !aligned16(k_mean) ||
+        !aligned16(k_sum) || !aligned16(v_sum) || !aligned16(anchor) || !aligned16(packed))
+        return SPARK_ATTN_MISALIGNED;
+    if (!packed || packed_bytes < pack_geom(L).bytes) return SPARK_ATTN_WORKSPACE_TOO_SMALL;
+    launch_pool_pack(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, packed);
+    return launch_status();
+}
+
 int spark_attn_attend(const spark_attn_params* p, const void* Q, const void* packed, size_t packed_bytes,
                       const int32_t* idx, const int32_t* perm, void* O, float* lse, void* stream) {
     LaunchCtx L;
@@ -299,10 +315,9 @@ int spark_attn_forward_tau(const spark_attn_params* p, float tau, const void* Q,
     float* anchor = (float*)(ws + w.anchor);
     int32_t* idx = idx_out ? idx_out : (int32_t*)(ws + w.idx);
     int32_t* counts = counts_out ? counts_out : (int32_t*)(ws + w.counts);
-    launch_pool(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor);
+    launch_pool_pack(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, ws + w.packed);
     launch_select_tau(L, tau, q_mean, k_mean, idx, counts, nullptr, (float*)(ws + w.scores),
                       (double*)(ws + w.partials));
-    launch_pack(L, K, V, k_sum, v_sum, bias, ws + w.packed);
     launch_attend(L, Q, ws + w.packed, idx, counts, nullptr, O, lse);
     return launch_status();
 }
@@ -347,9 +362,8 @@ int spark_attn_forward_kv(const spark_attn_params* p, const void* Q, const void*
     float* bias = (float*)(ws + w.bias);
     float* anchor = (float*)(ws + w.anchor);
     int32_t* idx = idx_out ? idx_out : (int32_t*)(ws + w.idx);
-    launch_pool(L, q, k, v, q_mean, k_mean, k_sum, v_sum, bias, anchor);
+    launch_pool_pack(L, q, k, v, q_mean, k_mean, k_sum, v_sum, bias, anchor, ws + w.packed);
     launch_select(L, q_mean, k_mean, idx, (float*)(ws + w.scores));
-    launch_pack(L, k, v, k_sum, v_sum, bias, ws + w.packed);
     launch_attend(L, q, ws + w.packed, idx, nullptr, perm_q, O, lse);
     return launch_status();
 }

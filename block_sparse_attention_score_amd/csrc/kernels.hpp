@@ -16,6 +16,10 @@ struct LaunchCtx {
 
 void launch_pool(const LaunchCtx& L, const void* Q, const void* K, const void* V, float* q_mean,
                  float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor);
+// launch_pool followed by launch_pack, with K and V read once: the pooling kernel also writes the
+// video key tiles.
+void launch_pool_pack(const LaunchCtx& L, const void* Q, const void* K, const void* V, float* q_mean,
+                      float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor, void* packed);
 
 // Select writes the full score matrix S [BH, M, M] (fp32) to `scores`, then the route.
 size_t select_workspace_bytes(const LaunchCtx& L);
@@ -39,6 +43,9 @@ PackGeom pack_geom(const LaunchCtx& L);
 
 void launch_pack(const LaunchCtx& L, const void* K, const void* V, const float* k_sum, const float* v_sum,
                  const float* bias, void* packed);
+// the sink tiles and the compressed tiles only
+void launch_pack_rest(const LaunchCtx& L, const void* K, const void* V, const float* k_sum, const float* v_sum,
+                      const float* bias, void* packed);
 
 // idx [B,H,M,K] with counts == NULL, or a variable route: idx [B,H,M,M] with counts [B,H,M]
 void launch_attend(const LaunchCtx& L, const void* Q, const void* packed, const int32_t* idx,

@@ -75,13 +75,12 @@ __device__ __forceinline__ void pack_tile(const T* __restrict__ Ksrc, const T* _
     }
 }
 
-// grid: BH * (Tv + Ts) tiles of real keys
+// grid: BH * cnt tiles of real keys, tiles t0 .. t0+cnt-1 of each (batch, head)
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pack_keys_kernel(const T* __restrict__ K, const T* __restrict__ V, int N,
-                                                        int Nv, int Tv, int Ts, int Tall,
+                                                        int Nv, int Tv, int Tall, int t0, int cnt,
                                                         __bf16* __restrict__ packed, float* __restrict__ bias2) {
-    const int per = Tv + Ts;
-    const int bh = blockIdx.x / per, t = blockIdx.x % per;
+    const int bh = blockIdx.x / cnt, t = t0 + blockIdx.x % cnt;
     int row0, nvalid;
     if (t < Tv) {
         row0 = t * 64;
@@ -112,27 +111,39 @@ __global__ __launch_bounds__(256) void pack_compressed_kernel(const float* __res
 
 template <typename T, int D>
 static void launch_pack_t(const LaunchCtx& L, const void* K, const void* V, const float* k_sum, const float* v_sum,
-                          const float* bias, void* packed) {
+                          const float* bias, void* packed, bool sinks_only) {
     const PackGeom g = pack_geom(L);
     __bf16* kv = (__bf16*)packed;
     float* b2 = (float*)((char*)packed + g.bias_off);
-    if (K && V)
-        hipLaunchKernelGGL((pack_keys_kernel<T, D>), dim3(L.BH * (g.Tv + g.Ts)), dim3(256), 0, L.stream,
-                           (const T*)K, (const T*)V, L.N, L.Nv, g.Tv, g.Ts, g.Tall, kv, b2);
+    const int t0 = sinks_only ? g.Tv : 0, cnt = g.Tv + g.Ts - t0;
+    if (K && V && cnt > 0)
+        hipLaunchKernelGGL((pack_keys_kernel<T, D>), dim3(L.BH * cnt), dim3(256), 0, L.stream, (const T*)K,
+                           (const T*)V, L.N, L.Nv, g.Tv, g.Tall, t0, cnt, kv, b2);
     if (k_sum && v_sum && bias)
         hipLaunchKernelGGL((pack_compressed_kernel<D>), dim3(L.BH * g.Tc), dim3(256), 0, L.stream, k_sum, v_sum,
                            bias, L.Mk, g.Tv, g.Ts, g.Tc, g.Tall, kv, b2);
 }
 
+static void launch_pack_any(const LaunchCtx& L, const void* K, const void* V, const float* k_sum,
+                            const float* v_sum, const float* bias, void* packed, bool sinks_only) {
+    if (L.dtype == SPARK_ATTN_BF16) {
+        if (L.d == 64) launch_pack_t<__bf16, 64>(L, K, V, k_sum, v_sum, bias, packed, sinks_only);
+        else launch_pack_t<__bf16, 128>(L, K, V, k_sum, v_sum, bias, packed, sinks_only);
+    } else {
+        if (L.d == 64) launch_pack_t<float, 64>(L, K, V, k_sum, v_sum, bias, packed, sinks_only);
+        else launch_pack_t<float, 128>(L, K, V, k_sum, v_sum, bias, packed, sinks_only);
+    }
+}
+
 void launch_pack(const LaunchCtx& L, const void* K, const void* V, const float* k_sum, const float* v_sum,
                  const float* bias, void* packed) {
-    if (L.dtype == SPARK_ATTN_BF16) {
-        if (L.d == 64) launch_pack_t<__bf16, 64>(L, K, V, k_sum, v_sum, bias, packed);
-        else launch_pack_t<__bf16, 128>(L, K, V, k_sum, v_sum, bias, packed);
-    } else {
-        if (L.d == 64) launch_pack_t<float, 64>(L, K, V, k_sum, v_sum, bias, packed);
-        else launch_pack_t<float, 128>(L, K, V, k_sum, v_sum, bias, packed);
-    }
+    launch_pack_any(L, K, V, k_sum, v_sum, bias, packed, false);
+}
+
+// the sink tiles and the compressed tiles (the video tiles come from the pooling kernel)
+void launch_pack_rest(const LaunchCtx& L, const void* K, const void* V, const float* k_sum, const float* v_sum,
+                      const float* bias, void* packed) {
+    launch_pack_any(L, K, V, k_sum, v_sum, bias, packed, true);
 }
 
 }  // namespace spark

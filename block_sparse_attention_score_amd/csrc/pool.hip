@@ -4,6 +4,8 @@
 // HBM-bound: Q is read once by pool_q, K and V once by pool_kv.  One workgroup per (batch,
 // head, block) reads the block's rows with 16-byte loads (row-contiguous, fully coalesced);
 // every reduction runs in a fixed order, so results are deterministic.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace spark {
@@ -77,12 +79,17 @@ __global__ __launch_bounds__(kAnchorThreads) void anchor_kernel(const float* __r
 // Key/value block summaries.  REWEIGHT: x_i = s * a.k_i, m = max x, e_i = exp(x_i - m),
 // Z = sum e, k~ = sum e_i k_i / Z, v~ = sum e_i v_i / Z, bias = m + ln Z - s * a.k~.
 // MEAN: k~ = mean k, v~ = mean v, bias = ln n.  Both write the plain key mean for ranking.
-template <typename T, int D, int BLK, bool REWEIGHT>
+//
+// PACK: the same kernel also writes the block's keys and values into their packed 64-key tiles
+// (the layout of pack.hip: K rows as they are, bf16; V^T through LDS; additive term 0 for real
+// keys, -inf for padding), so that K and V are read from HBM once for both.
+template <typename T, int D, int BLK, bool REWEIGHT, bool PACK>
 __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, const T* __restrict__ V,
                                                       const float* __restrict__ anchor, int N, int Nv,
                                                       int M, float scale, float* __restrict__ k_mean,
                                                       float* __restrict__ k_sum, float* __restrict__ v_sum,
-                                                      float* __restrict__ bias) {
+                                                      float* __restrict__ bias, __bf16* __restrict__ packed,
+                                                      float* __restrict__ bias2, int Tall) {
     using G = PoolGeom<D>;
     constexpr int RPT = (BLK + G::RG - 1) / G::RG;
     const int bh = blockIdx.x / M, J = blockIdx.x % M;
@@ -106,6 +113,32 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, c
         if (rg + k * G::RG >= n) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) { kr[k][j] = 0.f; vr[k][j] = 0.f; }
+        }
+    }
+
+    // packed tiles of this key block: K rows straight from the registers, V rows into LDS
+    constexpr int TPB = BLK / 64;  // tiles per key block
+    __shared__ __attribute__((aligned(16))) __bf16 vs[PACK ? BLK : 1][D + 8];
+    const size_t tile0 = (size_t)bh * Tall + (size_t)J * TPB;
+    if constexpr (PACK) {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) {
+            const int r = rg + k * G::RG;
+            if (r < BLK) {
+                u32x4 kb = zero, vb = zero;
+                if (r < n) {
+                    if constexpr (std::is_same<T, __bf16>::value) {
+                        kb = kraw[k].u;  // the input bits, unchanged
+                        vb = vraw[k].u;
+                    } else {
+                        kb = pack8_bf16(kr[k]);
+                        vb = pack8_bf16(vr[k]);
+                    }
+                }
+                *reinterpret_cast<u32x4*>(packed + (tile0 + (r >> 6)) * (2 * 64 * D) + (r & 63) * D + c * 8) = kb;
+                *reinterpret_cast<u32x4*>(&vs[r][c * 8]) = vb;
+            }
         }
     }
 
@@ -212,6 +245,26 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, c
     } else if (threadIdx.x == 0) {
         bias[(size_t)bh * M + J] = logf((float)n);
     }
+    if constexpr (PACK) {
+        __syncthreads();  // every V row is in LDS
+        // V^T row dr of tile tt = keys 0..63 of dimension dr: 8 chunks of 8 keys
+#pragma unroll
+        for (int tt = 0; tt < TPB; ++tt) {
+            __bf16* vdst = packed + (tile0 + tt) * (2 * 64 * D) + 64 * D;
+            for (int e = threadIdx.x; e < D * 8; e += 256) {
+                const int dr = e / 8, kc = e % 8;
+                u32x4 o;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t lo = __builtin_bit_cast(uint16_t, vs[tt * 64 + kc * 8 + 2 * j][dr]);
+                    const uint32_t hi = __builtin_bit_cast(uint16_t, vs[tt * 64 + kc * 8 + 2 * j + 1][dr]);
+                    o[j] = lo | (hi << 16);
+                }
+                *reinterpret_cast<u32x4*>(vdst + dr * 64 + kc * 8) = o;
+            }
+            if (threadIdx.x < 64) bias2[(tile0 + tt) * 64 + threadIdx.x] = tt * 64 + (int)threadIdx.x < n ? 0.f : -INFINITY;
+        }
+    }
 }
 
 // Query means (and the anchor) over the L.M query blocks of L.block rows; key summaries over the
@@ -224,36 +277,63 @@ static void launch_pool_q_t(const LaunchCtx& L, const void* Q, float* q_mean, fl
                        BLK, anchor);
 }
 
-template <typename T, int D, int BLK>
+template <typename T, int D, int BLK, bool PACK>
 static void launch_pool_kv_t(const LaunchCtx& L, const void* K, const void* V, const float* anchor,
-                             float* k_mean, float* k_sum, float* v_sum, float* bias) {
+                             float* k_mean, float* k_sum, float* v_sum, float* bias, void* packed) {
     const dim3 grid(L.BH * L.Mk);
+    __bf16* kv = nullptr;
+    float* b2 = nullptr;
+    int Tall = 0;
+    if (PACK) {
+        const PackGeom g = pack_geom(L);
+        kv = (__bf16*)packed;
+        b2 = (float*)((char*)packed + g.bias_off);
+        Tall = g.Tall;
+    }
     if (L.pool_mode == SPARK_ATTN_POOL_REWEIGHT)
-        hipLaunchKernelGGL((pool_kv_kernel<T, D, BLK, true>), grid, dim3(256), 0, L.stream, (const T*)K,
-                           (const T*)V, anchor, L.N, L.Nv, L.Mk, L.scale, k_mean, k_sum, v_sum, bias);
+        hipLaunchKernelGGL((pool_kv_kernel<T, D, BLK, true, PACK>), grid, dim3(256), 0, L.stream, (const T*)K,
+                           (const T*)V, anchor, L.N, L.Nv, L.Mk, L.scale, k_mean, k_sum, v_sum, bias, kv, b2, Tall);
     else
-        hipLaunchKernelGGL((pool_kv_kernel<T, D, BLK, false>), grid, dim3(256), 0, L.stream, (const T*)K,
-                           (const T*)V, anchor, L.N, L.Nv, L.Mk, L.scale, k_mean, k_sum, v_sum, bias);
+        hipLaunchKernelGGL((pool_kv_kernel<T, D, BLK, false, PACK>), grid, dim3(256), 0, L.stream, (const T*)K,
+                           (const T*)V, anchor, L.N, L.Nv, L.Mk, L.scale, k_mean, k_sum, v_sum, bias, kv, b2, Tall);
 }
 
 template <typename T, int D>
 static void launch_pool_t(const LaunchCtx& L, const void* Q, const void* K, const void* V, float* q_mean,
-                          float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor) {
+                          float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor, void* packed) {
     if (L.block == 64) launch_pool_q_t<T, D, 64>(L, Q, q_mean, anchor);
     else launch_pool_q_t<T, D, 128>(L, Q, q_mean, anchor);
-    if (L.block_k == 64) launch_pool_kv_t<T, D, 64>(L, K, V, anchor, k_mean, k_sum, v_sum, bias);
-    else launch_pool_kv_t<T, D, 128>(L, K, V, anchor, k_mean, k_sum, v_sum, bias);
+    if (packed) {
+        if (L.block_k == 64) launch_pool_kv_t<T, D, 64, true>(L, K, V, anchor, k_mean, k_sum, v_sum, bias, packed);
+        else launch_pool_kv_t<T, D, 128, true>(L, K, V, anchor, k_mean, k_sum, v_sum, bias, packed);
+    } else {
+        if (L.block_k == 64) launch_pool_kv_t<T, D, 64, false>(L, K, V, anchor, k_mean, k_sum, v_sum, bias, nullptr);
+        else launch_pool_kv_t<T, D, 128, false>(L, K, V, anchor, k_mean, k_sum, v_sum, bias, nullptr);
+    }
+}
+
+static void launch_pool_any(const LaunchCtx& L, const void* Q, const void* K, const void* V, float* q_mean,
+                            float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor, void* packed) {
+    if (L.dtype == SPARK_ATTN_BF16) {
+        if (L.d == 64) launch_pool_t<__bf16, 64>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, packed);
+        else launch_pool_t<__bf16, 128>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, packed);
+    } else {
+        if (L.d == 64) launch_pool_t<float, 64>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, packed);
+        else launch_pool_t<float, 128>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, packed);
+    }
 }
 
 void launch_pool(const LaunchCtx& L, const void* Q, const void* K, const void* V, float* q_mean,
                  float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor) {
-    if (L.dtype == SPARK_ATTN_BF16) {
-        if (L.d == 64) launch_pool_t<__bf16, 64>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor);
-        else launch_pool_t<__bf16, 128>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor);
-    } else {
-        if (L.d == 64) launch_pool_t<float, 64>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor);
-        else launch_pool_t<float, 128>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor);
-    }
+    launch_pool_any(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, nullptr);
+}
+
+// Pool and pack in one pass over K and V: the video key tiles are written by the pooling kernel,
+// then the sink tiles and the compressed tiles (which need the summaries) by the pack kernels.
+void launch_pool_pack(const LaunchCtx& L, const void* Q, const void* K, const void* V, float* q_mean,
+                      float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor, void* packed) {
+    launch_pool_any(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, packed);
+    launch_pack_rest(L, K, V, k_sum, v_sum, bias, packed);
 }
 
 }  // namespace spark

@@ -147,6 +147,17 @@ int spark_attn_pack(const spark_attn_params *p, const void *K, const void *V, co
                     void *stream);
 
 /*
+ * spark_attn_pool followed by spark_attn_pack, with K and V read from memory once: the kernel
+ * that pools a key block also writes its packed tiles (same outputs, same layout, same values).
+ * Arguments as in those two calls; every pointer is required.  Error behaviour as theirs:
+ * SPARK_ATTN_INVALID_ARGUMENT for a NULL pointer, SPARK_ATTN_MISALIGNED, and
+ * SPARK_ATTN_WORKSPACE_TOO_SMALL when packed_bytes < spark_attn_workspace_size(p, 4).
+ */
+int spark_attn_pool_pack(const spark_attn_params *p, const void *Q, const void *K, const void *V,
+                         float *q_mean, float *k_mean, float *k_sum, float *v_sum, float *bias,
+                         float *anchor, void *packed, size_t packed_bytes, void *stream);
+
+/*
  * The attention stage (exact branch + sinks + compressed branch, one softmax).
  * In:  Q [B,H,N,d] (in the block layout idx refers to); packed (spark_attn_pack of the matching
  *      K, V and summaries); idx [B,H,M,K] int32, distinct entries in [0, M) per row.

@@ -229,3 +229,24 @@ def test_key_block_size_validation_and_counts():
     assert L.spark_attn_select_tau(byref(p), ctypes.c_float(1.0), a, a, a, a, None, a, 1 << 40, None) == UNSUPPORTED
     assert L.spark_attn_forward_tau(byref(p), ctypes.c_float(1.0), a, a, a, a, None, None, None, a, 1 << 40,
                                     None) == UNSUPPORTED
+
+
+def test_pool_pack_validates_before_launch():
+    L = sa.lib()
+    p = P()
+    a = ctypes.c_void_p(0x100000)
+    bad = ctypes.c_void_p(0x100008)
+    byref = ctypes.byref
+    w4 = L.spark_attn_workspace_size(byref(p), 4)
+    args = [a] * 9  # Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor
+    assert L.spark_attn_pool_pack(byref(p), *args, a, w4 - 1, None) == WS_SMALL
+    assert L.spark_attn_pool_pack(byref(p), *args, None, w4, None) == WS_SMALL
+    for i in range(9):
+        miss = list(args)
+        miss[i] = None
+        assert L.spark_attn_pool_pack(byref(p), *miss, a, w4, None) == INVALID
+    mis = list(args)
+    mis[1] = bad
+    assert L.spark_attn_pool_pack(byref(p), *mis, a, w4, None) == MISALIGNED
+    assert L.spark_attn_pool_pack(byref(p), *args, bad, w4, None) == MISALIGNED
+    assert L.spark_attn_pool_pack(byref(P(d=96)), *args, a, 1 << 40, None) == UNSUPPORTED

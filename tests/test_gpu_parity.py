@@ -376,3 +376,31 @@ def test_attend_explicit_routes(orc, d, b, dt):
         e2, ea, el = rel_l2(host(O), Oref), max_abs(host(O), Oref), max_abs(host(lse), lref)
         print(f"rel-L2 {e2:.3e} max-abs {ea:.3e} lse {el:.3e}")
         assert e2 <= FWD_REL_L2 and ea <= FWD_MAX_ABS and el <= FWD_MAX_ABS
+
+
+POOL_PACK = [(c[0], c[1], c[2], c[3], c[4], c[5], c[6], 0, c[8]) for c in SMALL] + [
+    (c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[7], c[9]) for c in ASYM]
+
+
+@pytest.mark.parametrize("pool_mode", [0, 1])
+@pytest.mark.parametrize("case", POOL_PACK, ids=[c[0] for c in POOL_PACK])
+def test_pool_pack_equals_pool_then_pack(case, pool_mode):
+    """spark_attn_pool_pack writes the same summaries and the same packed bytes as spark_attn_pool
+    followed by spark_attn_pack (the fused kernel runs the pooling arithmetic unchanged)."""
+    name, B, H, nv, ns, d, b, bk, dt = case
+    note(f"pool_pack {name} mode={pool_mode}")
+    Q, K, V = W.gaussian_qkv(B, H, nv, ns, d, seed=nv + 3 * bk + pool_mode, dtype=dt)
+    Qd, Kd, Vd = (to_dev(x, dt) for x in (Q, K, V))
+    p = sa.params(Qd, ns, b, 0.1, pool_mode, block_k=bk)
+    ref = sa.pool(Qd, Kd, Vd, ns, b, pool_mode, block_k=bk)
+    nbytes = sa.workspace_size(p, 4)
+    packed_ref = torch.zeros(nbytes, device="cuda", dtype=torch.uint8)
+    sa.spark_attn_pack(p, Kd, Vd, ref["k_sum"], ref["v_sum"], ref["bias"], packed_ref)
+    got = {k: torch.full_like(v, float("nan")) for k, v in ref.items()}
+    packed = torch.zeros(nbytes, device="cuda", dtype=torch.uint8)
+    sa.spark_attn_pool_pack(p, Qd, Kd, Vd, got["q_mean"], got["k_mean"], got["k_sum"], got["v_sum"],
+                            got["bias"], got["anchor"], packed)
+    torch.cuda.synchronize()
+    for k in ref:
+        assert torch.equal(got[k], ref[k]), k
+    assert torch.equal(packed, packed_ref)
