@@ -232,7 +232,7 @@ def main():
         Qp, Kp, Vp = Q, K, V
 
     stage_names = ((["reblock"] + (["reblock_k"] if wl.key_partition else []) + ["gather"]) if wl.reblock else []) \
-        + (["fp8_scales", "pool", "select", "pack", "attend"] if fp8 else ["pool_pack", "select", "attend"])
+        + (["pool_scales", "select", "pack", "attend"] if fp8 else ["pool_pack", "select", "attend"])
 
     def step(ev=None):
         k = 1
@@ -248,13 +248,9 @@ def main():
                 sa.spark_attn_gather_rows(p, X, pm, Y, stream)
             if ev: ev[k].record(stream)
             k += 1
-        if fp8:
-            sa.spark_attn_fp8_scales(p, Qp, Kp, Vp, amax, stream)
-            if ev: ev[k].record(stream)
-            k += 1
-        if fp8:
-            sa.spark_attn_pool(p, Qp, Kp, Vp, pooled["q_mean"], pooled["k_mean"], pooled["k_sum"],
-                               pooled["v_sum"], pooled["bias"], pooled["anchor"], stream)
+        if fp8:  # pooling and the per-head E4M3 scales in one pass over Q, K, V
+            sa.spark_attn_pool_fp8_scales(p, Qp, Kp, Vp, pooled["q_mean"], pooled["k_mean"], pooled["k_sum"],
+                                          pooled["v_sum"], pooled["bias"], pooled["anchor"], amax, stream)
         else:  # pooling and packing in one pass over K and V
             sa.spark_attn_pool_pack(p, Qp, Kp, Vp, pooled["q_mean"], pooled["k_mean"], pooled["k_sum"],
                                     pooled["v_sum"], pooled["bias"], pooled["anchor"], packed, stream)
@@ -296,7 +292,7 @@ def main():
     ms_step = (t1 - t0) * 1e3 / args.steps
     st = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(ns)] for e in events]).mean(axis=0)
     stage_ms = {n: float(x) for n, x in zip(stage_names, st)}
-    ms_pool = stage_ms["pool"] if fp8 else stage_ms["pool_pack"]
+    ms_pool = stage_ms["pool_scales"] if fp8 else stage_ms["pool_pack"]
     ms_sel, ms_attn = stage_ms["select"], stage_ms["attend"]
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (" + ", ".join(f"{n} {v:.3f}" for n, v in stage_ms.items()) + ")")
 
@@ -340,7 +336,9 @@ def main():
     achieved = F_attn / (ms_attn * 1e-3) / 1e12
     sel_flops = 2.0 * B * H * M * Mk * d
     pool_bytes = 3.0 * B * H * wl.n_video * d * Q.element_size() + 4.0 * B * H * M * d * 4 + 4.0 * B * H * M
-    if not fp8:  # the fused stage also reads the sink keys/values and writes every packed tile
+    if fp8:  # the sink rows of Q, K, V for their maxima
+        pool_bytes += 3.0 * B * H * wl.n_sink * d * Q.element_size()
+    else:  # the fused stage also reads the sink keys/values and writes every packed tile
         pool_bytes += 2.0 * B * H * wl.n_sink * d * Q.element_size() + float(packed.numel())
 
     peak = MFMA_FP8_PEAK_TFLOPS if fp8 else MFMA_BF16_PEAK_TFLOPS
@@ -385,7 +383,8 @@ def main():
             "traffic_unit": "bytes per launch (FETCH+WRITE, scaled)",
             "exact_branch_frac": round((F_sel + F_sink) / (ms_attn * 1e-3) / 1e12 / peak, 4),
         },
-        "pool_roofline": {"stage": "pool" if fp8 else "pool_pack (pooling + packed tiles, one pass over K, V)",
+        "pool_roofline": {"stage": "pool_scales (pooling + E4M3 amax, one pass over Q, K, V)" if fp8
+                          else "pool_pack (pooling + packed tiles, one pass over K, V)",
                           "bound": "hbm", "achieved": round(pool_bytes / (ms_pool * 1e-3) / 1e9, 1),
                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(pool_bytes / (ms_pool * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},

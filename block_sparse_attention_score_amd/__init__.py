@@ -43,6 +43,7 @@ EXPORTS = (
     "spark_attn_attend", "spark_attn_forward", "spark_attn_forward_kv", "spark_attn_reblock",
     "spark_attn_gather_rows", "spark_attn_select_tau", "spark_attn_attend_var", "spark_attn_forward_tau",
     "spark_attn_fp8_scales", "spark_attn_pack_fp8", "spark_attn_attend_fp8", "spark_attn_forward_fp8",
+    "spark_attn_pool_fp8_scales",
 )
 
 _lib = None
@@ -78,6 +79,7 @@ def lib():
             "spark_attn_forward_tau": ([P, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
                                        ctypes.c_int),
             "spark_attn_fp8_scales": ([P, vp, vp, vp, vp, vp], ctypes.c_int),
+            "spark_attn_pool_fp8_scales": ([P] + [vp] * 10 + [vp], ctypes.c_int),
             "spark_attn_pack_fp8": ([P, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "spark_attn_attend_fp8": ([P, vp, vp, sz, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "spark_attn_forward_fp8": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
@@ -221,6 +223,12 @@ def spark_attn_forward_tau(p, tau, Q, K, V, O, lse, idx_out, counts_out, workspa
 def spark_attn_fp8_scales(p, Q, K, V, amax, stream=None):
     _check("spark_attn_fp8_scales", lib().spark_attn_fp8_scales(
         ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(amax), _stream(stream)))
+
+
+def spark_attn_pool_fp8_scales(p, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, amax, stream=None):
+    _check("spark_attn_pool_fp8_scales", lib().spark_attn_pool_fp8_scales(
+        ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(q_mean), _ptr(k_mean), _ptr(k_sum),
+        _ptr(v_sum), _ptr(bias), _ptr(anchor), _ptr(amax), _stream(stream)))
 
 
 def spark_attn_pack_fp8(p, K, V, k_sum, v_sum, bias, amax, packed, stream=None):

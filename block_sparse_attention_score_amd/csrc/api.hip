@@ -384,6 +384,21 @@ int spark_attn_fp8_scales(const spark_attn_params* p, const void* Q, const void*
     return launch_status();
 }
 
+int spark_attn_pool_fp8_scales(const spark_attn_params* p, const void* Q, const void* K, const void* V,
+                               float* q_mean, float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor,
+                               float* amax, void* stream) {
+    LaunchCtx L;
+    int s = make_ctx(p, stream, &L);
+    if (s < 0) return s;
+    if (!Q || !K || !V || !q_mean || !k_mean || !k_sum || !v_sum || !bias || !anchor || !amax)
+        return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(q_mean) || !aligned16(k_mean) ||
+        !aligned16(k_sum) || !aligned16(v_sum) || !aligned16(anchor))
+        return SPARK_ATTN_MISALIGNED;
+    launch_pool_fp8_scales(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, (uint32_t*)amax);
+    return launch_status();
+}
+
 int spark_attn_pack_fp8(const spark_attn_params* p, const void* K, const void* V, const float* k_sum,
                         const float* v_sum, const float* bias, const float* amax, void* packed, size_t packed_bytes,
                         void* stream) {
@@ -440,8 +455,7 @@ int spark_attn_forward_fp8(const spark_attn_params* p, const void* Q, const void
     float* anchor = (float*)(ws + w.anchor);
     int32_t* idx = idx_out ? idx_out : (int32_t*)(ws + w.idx);
     uint32_t* amax = amax_out ? (uint32_t*)amax_out : (uint32_t*)(ws + w.amax);
-    launch_fp8_scales(L, q, k, v, amax);
-    launch_pool(L, q, k, v, q_mean, k_mean, k_sum, v_sum, bias, anchor);
+    launch_pool_fp8_scales(L, q, k, v, q_mean, k_mean, k_sum, v_sum, bias, anchor, amax);
     launch_select(L, q_mean, k_mean, idx, (float*)(ws + w.scores));
     launch_pack_fp8(L, k, v, k_sum, v_sum, bias, amax, ws + w.packed);
     launch_attend_fp8(L, q, ws + w.packed, idx, perm, amax, O, lse);

@@ -25,6 +25,8 @@
 //    while the normaliser sums them before rounding.
 #include <type_traits>
 
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace spark {
@@ -43,14 +45,14 @@ __global__ __launch_bounds__(256) void fp8_zero_kernel(uint32_t* __restrict__ p,
 }
 
 // amax[bh][t] (float bits; non-negative floats order as unsigned integers) of tensor t = Q, K, V
-// over all N rows of (batch, head) bh.
+// raised to the largest |x| over rows row0 .. N-1 of (batch, head) bh.
 template <typename T>
 __global__ __launch_bounds__(256) void fp8_amax_kernel(const T* __restrict__ Q, const T* __restrict__ K,
-                                                       const T* __restrict__ V, int N, int d,
+                                                       const T* __restrict__ V, int N, int row0, int d,
                                                        uint32_t* __restrict__ amax) {
     const int bh = blockIdx.y, t = blockIdx.z;
-    const T* x = (t == 0 ? Q : t == 1 ? K : V) + (size_t)bh * N * d;
-    const size_t n8 = (size_t)N * d / 8;
+    const T* x = (t == 0 ? Q : t == 1 ? K : V) + ((size_t)bh * N + row0) * d;
+    const size_t n8 = (size_t)(N - row0) * d / 8;
     float m = 0.f;
     for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n8; e += (size_t)gridDim.x * 256) {
         Raw8<T> r;
@@ -553,14 +555,23 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
 // ---------------------------------------------------------------------------------------------
 // Launchers.
 
-void launch_fp8_scales(const LaunchCtx& L, const void* Q, const void* K, const void* V, uint32_t* amax) {
+// zero amax, then raise it over rows row0 .. N-1 (all rows: row0 = 0)
+void launch_fp8_amax_rows(const LaunchCtx& L, const void* Q, const void* K, const void* V, uint32_t* amax,
+                          int row0) {
     hipLaunchKernelGGL(fp8_zero_kernel, dim3((L.BH * 3 + 255) / 256), dim3(256), 0, L.stream, amax, L.BH * 3);
+    if (row0 >= L.N) return;
+    // workgroups per (batch, head, tensor): enough for the full tensor, fewer for a few sink rows
+    const int wg = (int)std::min<long long>(64, ((long long)(L.N - row0) * L.d / 8 + 255) / 256);
     if (L.dtype == SPARK_ATTN_BF16)
-        hipLaunchKernelGGL((fp8_amax_kernel<__bf16>), dim3(64, L.BH, 3), dim3(256), 0, L.stream, (const __bf16*)Q,
-                           (const __bf16*)K, (const __bf16*)V, L.N, L.d, amax);
+        hipLaunchKernelGGL((fp8_amax_kernel<__bf16>), dim3(wg, L.BH, 3), dim3(256), 0, L.stream, (const __bf16*)Q,
+                           (const __bf16*)K, (const __bf16*)V, L.N, row0, L.d, amax);
     else
-        hipLaunchKernelGGL((fp8_amax_kernel<float>), dim3(64, L.BH, 3), dim3(256), 0, L.stream, (const float*)Q,
-                           (const float*)K, (const float*)V, L.N, L.d, amax);
+        hipLaunchKernelGGL((fp8_amax_kernel<float>), dim3(wg, L.BH, 3), dim3(256), 0, L.stream, (const float*)Q,
+                           (const float*)K, (const float*)V, L.N, row0, L.d, amax);
+}
+
+void launch_fp8_scales(const LaunchCtx& L, const void* Q, const void* K, const void* V, uint32_t* amax) {
+    launch_fp8_amax_rows(L, Q, K, V, amax, 0);
 }
 
 template <typename T, int D>

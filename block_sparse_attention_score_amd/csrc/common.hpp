@@ -107,6 +107,21 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+// amax = max(amax, v) for a non-negative float v held as its bits (non-negative floats order as
+// unsigned integers).  The atomic is skipped when the current value is already as large: once the
+// running maximum is reached, most callers only read it, so many workgroups raising one value do
+// not queue on its atomic unit (a stale read only costs an extra atomic).
+__device__ __forceinline__ void raise_max_bits(uint32_t* amax, float v) {
+    const uint32_t b = __float_as_uint(v);
+    if (b > __hip_atomic_load(amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(amax, b);
+}
+
 __device__ __forceinline__ int wave_sum_int(int v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);

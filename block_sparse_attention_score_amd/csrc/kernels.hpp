@@ -43,6 +43,13 @@ PackGeom pack_geom(const LaunchCtx& L);
 
 void launch_pack(const LaunchCtx& L, const void* K, const void* V, const float* k_sum, const float* v_sum,
                  const float* bias, void* packed);
+// launch_fp8_scales restricted to rows row0 .. N-1 (amax zeroed first), and pooling that also
+// takes the amax of the video rows (launch_fp8_scales + launch_pool in one pass over Q, K, V)
+void launch_fp8_amax_rows(const LaunchCtx& L, const void* Q, const void* K, const void* V, uint32_t* amax,
+                          int row0);
+void launch_pool_fp8_scales(const LaunchCtx& L, const void* Q, const void* K, const void* V, float* q_mean,
+                            float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor, uint32_t* amax);
+
 // the sink tiles and the compressed tiles only
 void launch_pack_rest(const LaunchCtx& L, const void* K, const void* V, const float* k_sum, const float* v_sum,
                       const float* bias, void* packed);

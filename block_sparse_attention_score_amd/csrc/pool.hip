@@ -17,9 +17,11 @@ template <int D> struct PoolGeom {
     static constexpr int RG = 256 / CH;
 };
 
-template <typename T, int D, int BLK>
+// AMAX: also raise amax_q (float bits; non-negative floats order as unsigned integers) to the
+// largest |q| of the block, for the E4M3 scales.
+template <typename T, int D, int BLK, bool AMAX>
 __global__ __launch_bounds__(256) void pool_q_kernel(const T* __restrict__ Q, int N, int Nv, int M,
-                                                     float* __restrict__ q_mean) {
+                                                     float* __restrict__ q_mean, uint32_t* __restrict__ amax) {
     using G = PoolGeom<D>;
     constexpr int RPT = (BLK + G::RG - 1) / G::RG;  // rows per thread
     const int bh = blockIdx.x / M, J = blockIdx.x % M;
@@ -32,19 +34,30 @@ __global__ __launch_bounds__(256) void pool_q_kernel(const T* __restrict__ Q, in
 #pragma unroll
     for (int k = 0; k < RPT; ++k) raw[k].load(base + (size_t)min(rg + k * G::RG, n - 1) * D);
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float am = 0.f;
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
         if (rg + k * G::RG < n) {
             float v[8];
             raw[k].widen(v);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] += v[j];
+            for (int j = 0; j < 8; ++j) {
+                acc[j] += v[j];
+                if (AMAX) am = fmaxf(am, fabsf(v[j]));
+            }
         }
+    }
+    __shared__ float wmax[4];
+    if constexpr (AMAX) {
+        am = wave_max(am);
+        if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = am;
     }
     __shared__ float red[G::RG][D];
 #pragma unroll
     for (int j = 0; j < 8; ++j) red[rg][c * 8 + j] = acc[j];
     __syncthreads();
+    if (AMAX && threadIdx.x == 0)
+        raise_max_bits(&amax[(size_t)bh * 3], fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
     for (int col = threadIdx.x; col < D; col += 256) {
         float s = 0.f;
         for (int g = 0; g < G::RG; ++g) s += red[g][col];
@@ -80,16 +93,19 @@ __global__ __launch_bounds__(kAnchorThreads) void anchor_kernel(const float* __r
 // Z = sum e, k~ = sum e_i k_i / Z, v~ = sum e_i v_i / Z, bias = m + ln Z - s * a.k~.
 // MEAN: k~ = mean k, v~ = mean v, bias = ln n.  Both write the plain key mean for ranking.
 //
-// PACK: the same kernel also writes the block's keys and values into their packed 64-key tiles
-// (the layout of pack.hip: K rows as they are, bf16; V^T through LDS; additive term 0 for real
-// keys, -inf for padding), so that K and V are read from HBM once for both.
-template <typename T, int D, int BLK, bool REWEIGHT, bool PACK>
+// MODE 1 (pack): the same kernel also writes the block's keys and values into their packed 64-key
+// tiles (the layout of pack.hip: K rows as they are, bf16; V^T through LDS; additive term 0 for
+// real keys, -inf for padding), so that K and V are read from HBM once for both.
+// MODE 2 (amax): it also raises amax_k and amax_v to the block's largest |k| and |v| (E4M3 scales).
+template <typename T, int D, int BLK, bool REWEIGHT, int MODE>
 __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, const T* __restrict__ V,
                                                       const float* __restrict__ anchor, int N, int Nv,
                                                       int M, float scale, float* __restrict__ k_mean,
                                                       float* __restrict__ k_sum, float* __restrict__ v_sum,
                                                       float* __restrict__ bias, __bf16* __restrict__ packed,
-                                                      float* __restrict__ bias2, int Tall) {
+                                                      float* __restrict__ bias2, int Tall,
+                                                      uint32_t* __restrict__ amax) {
+    constexpr bool PACK = MODE == 1;
     using G = PoolGeom<D>;
     constexpr int RPT = (BLK + G::RG - 1) / G::RG;
     const int bh = blockIdx.x / M, J = blockIdx.x % M;
@@ -113,6 +129,29 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, c
         if (rg + k * G::RG >= n) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) { kr[k][j] = 0.f; vr[k][j] = 0.f; }
+        }
+    }
+
+    if constexpr (MODE == 2) {
+        float ak = 0.f, av = 0.f;  // rows past the block end are zero here
+#pragma unroll
+        for (int k = 0; k < RPT; ++k)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                ak = fmaxf(ak, fabsf(kr[k][j]));
+                av = fmaxf(av, fabsf(vr[k][j]));
+            }
+        ak = wave_max(ak);
+        av = wave_max(av);
+        __shared__ float wmax[2][4];
+        if ((threadIdx.x & 63) == 0) {
+            wmax[0][threadIdx.x >> 6] = ak;
+            wmax[1][threadIdx.x >> 6] = av;
+        }
+        __syncthreads();
+        if (threadIdx.x < 2) {
+            const float* w = wmax[threadIdx.x];
+            raise_max_bits(&amax[(size_t)bh * 3 + 1 + threadIdx.x], fmaxf(fmaxf(w[0], w[1]), fmaxf(w[2], w[3])));
         }
     }
 
@@ -270,69 +309,86 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, c
 // Query means (and the anchor) over the L.M query blocks of L.block rows; key summaries over the
 // L.Mk key blocks of L.block_k keys.
 template <typename T, int D, int BLK>
-static void launch_pool_q_t(const LaunchCtx& L, const void* Q, float* q_mean, float* anchor) {
-    hipLaunchKernelGGL((pool_q_kernel<T, D, BLK>), dim3(L.BH * L.M), dim3(256), 0, L.stream, (const T*)Q, L.N,
-                       L.Nv, L.M, q_mean);
+static void launch_pool_q_t(const LaunchCtx& L, const void* Q, float* q_mean, float* anchor, uint32_t* amax) {
+    if (amax)
+        hipLaunchKernelGGL((pool_q_kernel<T, D, BLK, true>), dim3(L.BH * L.M), dim3(256), 0, L.stream, (const T*)Q,
+                           L.N, L.Nv, L.M, q_mean, amax);
+    else
+        hipLaunchKernelGGL((pool_q_kernel<T, D, BLK, false>), dim3(L.BH * L.M), dim3(256), 0, L.stream,
+                           (const T*)Q, L.N, L.Nv, L.M, q_mean, nullptr);
     hipLaunchKernelGGL((anchor_kernel<D>), dim3(L.BH), dim3(kAnchorThreads), 0, L.stream, q_mean, L.Nv, L.M,
                        BLK, anchor);
 }
 
-template <typename T, int D, int BLK, bool PACK>
+template <typename T, int D, int BLK, int MODE>
 static void launch_pool_kv_t(const LaunchCtx& L, const void* K, const void* V, const float* anchor,
-                             float* k_mean, float* k_sum, float* v_sum, float* bias, void* packed) {
+                             float* k_mean, float* k_sum, float* v_sum, float* bias, void* packed,
+                             uint32_t* amax) {
     const dim3 grid(L.BH * L.Mk);
     __bf16* kv = nullptr;
     float* b2 = nullptr;
     int Tall = 0;
-    if (PACK) {
+    if (MODE == 1) {
         const PackGeom g = pack_geom(L);
         kv = (__bf16*)packed;
         b2 = (float*)((char*)packed + g.bias_off);
         Tall = g.Tall;
     }
     if (L.pool_mode == SPARK_ATTN_POOL_REWEIGHT)
-        hipLaunchKernelGGL((pool_kv_kernel<T, D, BLK, true, PACK>), grid, dim3(256), 0, L.stream, (const T*)K,
-                           (const T*)V, anchor, L.N, L.Nv, L.Mk, L.scale, k_mean, k_sum, v_sum, bias, kv, b2, Tall);
+        hipLaunchKernelGGL((pool_kv_kernel<T, D, BLK, true, MODE>), grid, dim3(256), 0, L.stream, (const T*)K,
+                           (const T*)V, anchor, L.N, L.Nv, L.Mk, L.scale, k_mean, k_sum, v_sum, bias, kv, b2, Tall,
+                           amax);
     else
-        hipLaunchKernelGGL((pool_kv_kernel<T, D, BLK, false, PACK>), grid, dim3(256), 0, L.stream, (const T*)K,
-                           (const T*)V, anchor, L.N, L.Nv, L.Mk, L.scale, k_mean, k_sum, v_sum, bias, kv, b2, Tall);
+        hipLaunchKernelGGL((pool_kv_kernel<T, D, BLK, false, MODE>), grid, dim3(256), 0, L.stream, (const T*)K,
+                           (const T*)V, anchor, L.N, L.Nv, L.Mk, L.scale, k_mean, k_sum, v_sum, bias, kv, b2, Tall,
+                           amax);
 }
 
 template <typename T, int D>
 static void launch_pool_t(const LaunchCtx& L, const void* Q, const void* K, const void* V, float* q_mean,
-                          float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor, void* packed) {
-    if (L.block == 64) launch_pool_q_t<T, D, 64>(L, Q, q_mean, anchor);
-    else launch_pool_q_t<T, D, 128>(L, Q, q_mean, anchor);
-    if (packed) {
-        if (L.block_k == 64) launch_pool_kv_t<T, D, 64, true>(L, K, V, anchor, k_mean, k_sum, v_sum, bias, packed);
-        else launch_pool_kv_t<T, D, 128, true>(L, K, V, anchor, k_mean, k_sum, v_sum, bias, packed);
-    } else {
-        if (L.block_k == 64) launch_pool_kv_t<T, D, 64, false>(L, K, V, anchor, k_mean, k_sum, v_sum, bias, nullptr);
-        else launch_pool_kv_t<T, D, 128, false>(L, K, V, anchor, k_mean, k_sum, v_sum, bias, nullptr);
-    }
+                          float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor, void* packed,
+                          uint32_t* amax) {
+    if (L.block == 64) launch_pool_q_t<T, D, 64>(L, Q, q_mean, anchor, amax);
+    else launch_pool_q_t<T, D, 128>(L, Q, q_mean, anchor, amax);
+#define SPARK_POOL_KV(MODE)                                                                                    \
+    if (L.block_k == 64) launch_pool_kv_t<T, D, 64, MODE>(L, K, V, anchor, k_mean, k_sum, v_sum, bias, packed, amax); \
+    else launch_pool_kv_t<T, D, 128, MODE>(L, K, V, anchor, k_mean, k_sum, v_sum, bias, packed, amax);
+    if (packed) { SPARK_POOL_KV(1) }
+    else if (amax) { SPARK_POOL_KV(2) }
+    else { SPARK_POOL_KV(0) }
+#undef SPARK_POOL_KV
 }
 
 static void launch_pool_any(const LaunchCtx& L, const void* Q, const void* K, const void* V, float* q_mean,
-                            float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor, void* packed) {
+                            float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor, void* packed,
+                            uint32_t* amax) {
     if (L.dtype == SPARK_ATTN_BF16) {
-        if (L.d == 64) launch_pool_t<__bf16, 64>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, packed);
-        else launch_pool_t<__bf16, 128>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, packed);
+        if (L.d == 64) launch_pool_t<__bf16, 64>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, packed, amax);
+        else launch_pool_t<__bf16, 128>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, packed, amax);
     } else {
-        if (L.d == 64) launch_pool_t<float, 64>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, packed);
-        else launch_pool_t<float, 128>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, packed);
+        if (L.d == 64) launch_pool_t<float, 64>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, packed, amax);
+        else launch_pool_t<float, 128>(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, packed, amax);
     }
 }
 
 void launch_pool(const LaunchCtx& L, const void* Q, const void* K, const void* V, float* q_mean,
                  float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor) {
-    launch_pool_any(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, nullptr);
+    launch_pool_any(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, nullptr, nullptr);
+}
+
+// Pooling and the per-head E4M3 amax of Q, K and V in one pass over the video rows (the sink rows,
+// which pooling does not read, by the amax kernel).
+void launch_pool_fp8_scales(const LaunchCtx& L, const void* Q, const void* K, const void* V, float* q_mean,
+                            float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor, uint32_t* amax) {
+    launch_fp8_amax_rows(L, Q, K, V, amax, L.Nv);  // zeroes amax, then the rows Nv .. N-1
+    launch_pool_any(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, nullptr, amax);
 }
 
 // Pool and pack in one pass over K and V: the video key tiles are written by the pooling kernel,
 // then the sink tiles and the compressed tiles (which need the summaries) by the pack kernels.
 void launch_pool_pack(const LaunchCtx& L, const void* Q, const void* K, const void* V, float* q_mean,
                       float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor, void* packed) {
-    launch_pool_any(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, packed);
+    launch_pool_any(L, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, packed, nullptr);
     launch_pack_rest(L, K, V, k_sum, v_sum, bias, packed);
 }
 

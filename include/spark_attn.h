@@ -269,18 +269,24 @@ int spark_attn_reblock(const spark_attn_params *p, const void *Q, const void *K,
  * are rounded to E4M3 for the value product, the normaliser sums them unrounded.
  *
  * spark_attn_fp8_scales: amax [B,H,3] fp32 (Q, K, V), written with atomics after a clear.
+ * spark_attn_pool_fp8_scales: spark_attn_pool and spark_attn_fp8_scales with Q, K, V read once
+ *   (the pooling kernels take the maxima of the video rows); the same outputs, every pointer
+ *   required.
  * spark_attn_pack_fp8: the tiles of spark_attn_pack on E4M3 carriers (same tile list and fp32
  *   bias rows; a tile is 64 key rows of d bytes, then d value rows of 64 bytes); `packed` holds
  *   spark_attn_workspace_size(p, 9) bytes.
  * spark_attn_attend_fp8: spark_attn_attend on those tiles; idx [B,H,M,K] (ascending rows), perm as
  *   in spark_attn_attend; amax as written by spark_attn_fp8_scales for the same Q, K, V.
- * spark_attn_forward_fp8: [gather by perm] -> scales -> pool -> select -> pack_fp8 -> attend_fp8;
+ * spark_attn_forward_fp8: [gather by perm] -> pool+scales -> select -> pack_fp8 -> attend_fp8;
  *   pooling and selection see the unquantized inputs (the route equals spark_attn_forward's);
  *   amax_out [B,H,3] or NULL; workspace of spark_attn_workspace_size(p, perm ? 8 : 7) bytes.
  * Errors and ownership as for the bf16 calls; every pointer is device memory.
  */
 int spark_attn_fp8_scales(const spark_attn_params *p, const void *Q, const void *K, const void *V,
                           float *amax, void *stream);
+int spark_attn_pool_fp8_scales(const spark_attn_params *p, const void *Q, const void *K,
+                               const void *V, float *q_mean, float *k_mean, float *k_sum,
+                               float *v_sum, float *bias, float *anchor, float *amax, void *stream);
 int spark_attn_pack_fp8(const spark_attn_params *p, const void *K, const void *V, const float *k_sum,
                         const float *v_sum, const float *bias, const float *amax, void *packed,
                         size_t packed_bytes, void *stream);

@@ -250,3 +250,20 @@ def test_pool_pack_validates_before_launch():
     assert L.spark_attn_pool_pack(byref(p), *mis, a, w4, None) == MISALIGNED
     assert L.spark_attn_pool_pack(byref(p), *args, bad, w4, None) == MISALIGNED
     assert L.spark_attn_pool_pack(byref(P(d=96)), *args, a, 1 << 40, None) == UNSUPPORTED
+
+
+def test_pool_fp8_scales_validates_before_launch():
+    L = sa.lib()
+    p = P()
+    a = ctypes.c_void_p(0x100000)
+    bad = ctypes.c_void_p(0x100008)
+    byref = ctypes.byref
+    args = [a] * 10  # Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, amax
+    for i in range(10):
+        miss = list(args)
+        miss[i] = None
+        assert L.spark_attn_pool_fp8_scales(byref(p), *miss, None) == INVALID
+    mis = list(args)
+    mis[0] = bad
+    assert L.spark_attn_pool_fp8_scales(byref(p), *mis, None) == MISALIGNED
+    assert L.spark_attn_pool_fp8_scales(byref(P(d=96)), *args, None) == UNSUPPORTED

@@ -155,3 +155,35 @@ def test_fp8_packed_carriers_bit_exact(orc):
             full = np.zeros((64, d), np.float32)
             full[:n] = vq
             assert (np.sort(vpart, axis=1) == np.sort(full.T, axis=1)).all(), (bh, t)
+
+
+@pytest.mark.parametrize("block_k", [0, 64])
+@pytest.mark.parametrize("pool_mode", [0, 1])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_pool_fp8_scales_equals_pool_and_scales(case, pool_mode, block_k):
+    """spark_attn_pool_fp8_scales writes the same summaries as spark_attn_pool and the same amax as
+    spark_attn_fp8_scales (maxima are exact and independent of their order)."""
+    name, B, H, nv, ns, d, b, r, dt = case
+    if block_k and b == 64:
+        pytest.skip("64-row query blocks route to key blocks of 64 already")
+    note(f"pool_fp8_scales {name} mode={pool_mode} block_k={block_k}")
+    Q, K, V = W.gaussian_qkv(B, H, nv, ns, d, seed=nv + 7 * pool_mode + block_k, dtype=dt)
+    Q[..., 0, 3] = -40.0  # a video row holds Q's largest |x|
+    if ns:
+        K[..., -1, 5] = 37.0  # a sink row holds K's
+    Qd, Kd, Vd = (dev(x, dt) for x in (Q, K, V))
+    p = sa.params(Qd, ns, b, r, pool_mode, block_k=block_k)
+    ref = sa.pool(Qd, Kd, Vd, ns, b, pool_mode, block_k=block_k)
+    amax_ref = torch.empty(B, H, 3, device="cuda", dtype=torch.float32)
+    sa.spark_attn_fp8_scales(p, Qd, Kd, Vd, amax_ref)
+    got = {k: torch.full_like(v, float("nan")) for k, v in ref.items()}
+    amax = torch.full_like(amax_ref, float("nan"))
+    sa.spark_attn_pool_fp8_scales(p, Qd, Kd, Vd, got["q_mean"], got["k_mean"], got["k_sum"], got["v_sum"],
+                                  got["bias"], got["anchor"], amax)
+    torch.cuda.synchronize()
+    for k in ref:
+        assert torch.equal(got[k], ref[k]), k
+    assert torch.equal(amax, amax_ref)
+    assert float(amax_ref[..., 0].max()) == 40.0
+    if ns:
+        assert float(amax_ref[..., 1].max()) == 37.0
