@@ -26,7 +26,8 @@
 //    then the S^T accumulator of lane (i, h) holds, for query i, exactly the keys whose values form
 //    one contiguous 16-byte chunk of a V^T row, so P feeds O^T += V^T P^T straight from registers.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: each lane holds one query's logits, so the row max
-//    and sum need one cross-half shuffle.  The running max is only raised when a tile's max exceeds
+//    and sum need one exchange between the wave's halves (a v_permlane32_swap for the max, once per
+//    tile; the sum once at the end).  The running max is only raised when a tile's max exceeds
 //    it by more than 8 (log2 units); otherwise the accumulator is not rescaled.  Probabilities are
 //    then bounded by 2^8, and the result is unchanged because O and the normaliser share the max.
 #include <type_traits>

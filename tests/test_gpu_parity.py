@@ -404,3 +404,22 @@ def test_pool_pack_equals_pool_then_pack(case, pool_mode):
     for k in ref:
         assert torch.equal(got[k], ref[k]), k
     assert torch.equal(packed, packed_ref)
+
+
+def test_forward_is_deterministic_at_scale():
+    """Two calls on the same inputs give the same bits: output, lse and route (bf16 in token order,
+    bf16 through a reblock permutation, FP8 carriers).  Every reduction runs in a fixed order; the
+    only atomics (max, integer sums, route bits) do not depend on their order."""
+    wl = W.WORKLOADS["short"]
+    note(f"determinism {wl.name}")
+    Q, K, V = (to_dev(x, wl.dtype) for x in W.make_qkv(wl))
+    perm = sa.reblock(Q, K, wl.n_sink, wl.block)
+    runs = []
+    for _ in range(2):
+        a = sa.forward(Q, K, V, wl.n_sink, wl.block, 0.1, return_lse=True, return_idx=True)
+        b = sa.forward(Q, K, V, wl.n_sink, wl.block, 0.1, perm=perm, return_lse=True, return_idx=True)
+        c = sa.forward_fp8(Q, K, V, wl.n_sink, wl.block, 0.1, return_lse=True, return_idx=True)
+        torch.cuda.synchronize()
+        runs.append([t.clone() for t in (*a, *b, *c)])
+    for x, y in zip(*runs):
+        assert torch.equal(x, y)
