@@ -198,12 +198,20 @@ __global__ __launch_bounds__(256) void tau_rows_kernel(const float* __restrict__
     int32_t* out = idx + (size_t)row * M;
     const uint64_t below = lanemask_lt();
     int pos = 0;
-    for (int J0 = 0; J0 < M; J0 += 64) {
-        const int J = J0 + lane;
-        const bool keep = J < M && (double)Sr[J] > thr;
-        const uint64_t kb = __ballot(keep);
-        if (keep) out[pos + __popcll(kb & below)] = J;
-        pos += __popcll(kb);
+    // eight column chunks at a time, loaded unconditionally (clamped column) so that the loads of a
+    // batch are in flight together
+    for (int J0 = 0; J0 < M; J0 += 64 * 8) {
+        float f[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) f[u] = Sr[min(J0 + 64 * u + lane, M - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int J = J0 + 64 * u + lane;
+            const bool keep = J < M && (double)f[u] > thr;
+            const uint64_t kb = __ballot(keep);
+            if (keep) out[pos + __popcll(kb & below)] = J;
+            pos += __popcll(kb);
+        }
     }
     if (lane == 0) {
         counts[row] = pos;
