@@ -77,9 +77,12 @@ __device__ __forceinline__ float fp8_s(uint32_t amax_bits) {
     return a > 0.f ? __fdiv_rn(a, 448.f) : 1.f;
 }
 
-// Four binary32 values to four E4M3 bytes (round to nearest even), in order.
+// Four binary32 values to four E4M3 bytes (round to nearest even), in order.  The first
+// conversion writes the low half of the word and keeps the high half of its third operand, which
+// the second conversion then replaces: any value serves there, and passing a's own bits (rather
+// than a literal 0) lets the result take a's register instead of a freshly cleared one.
 __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float e) {
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, e, lo, true);
 }
 
