@@ -117,6 +117,49 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+_DTYPES = {BF16: torch.bfloat16, FP32: torch.float32}
+
+# Buffer roles of the entry points: element count per (batch, head) from the block geometry, and
+# element type (None: the parameters' dtype).  Layouts are those the C header documents.
+_ROLES = {
+    "tok": (lambda g: g["N"] * g["d"], None),          # Q, K, V, O, X, Y [B,H,N,d]
+    "qblk": (lambda g: g["M"] * g["d"], torch.float32),   # q_mean [B,H,M,d]
+    "kblk": (lambda g: g["Mk"] * g["d"], torch.float32),  # k_mean, k_sum, v_sum [B,H,M_k,d]
+    "kbias": (lambda g: g["Mk"], torch.float32),          # bias [B,H,M_k]
+    "head": (lambda g: g["d"], torch.float32),            # anchor [B,H,d]
+    "route": (lambda g: g["M"] * g["K"], torch.int32),    # idx [B,H,M,K]
+    "route_all": (lambda g: g["M"] * g["Mk"], torch.int32),  # variable route idx [B,H,M,M_k]
+    "scores": (lambda g: g["M"] * g["Mk"], torch.float32),   # S [B,H,M,M_k]
+    "rows": (lambda g: g["N"], torch.float32),            # lse [B,H,N]
+    "perm": (lambda g: g["Nv"], torch.int32),             # perm [B,H,N_v]
+    "counts": (lambda g: g["M"], torch.int32),            # counts [B,H,M]
+    "stats": (lambda g: 2, torch.float32),                # (mu, sigma) [B,H,2]
+    "amax": (lambda g: 3, torch.float32),                 # amax [B,H,3]
+}
+
+
+def _validate(p, *args):
+    """Checks (name, tensor, role) triples against the parameters before a launch: a tensor that
+    is too small or of the wrong element type would otherwise be read or written out of bounds
+    by the kernels, which receive bare pointers.  Invalid parameters are left to the library,
+    which reports them with its own status."""
+    L = lib()
+    M, Mk = L.spark_attn_num_blocks(ctypes.byref(p)), L.spark_attn_num_key_blocks(ctypes.byref(p))
+    if M < 1 or Mk < 1 or p.dtype not in _DTYPES:
+        return
+    g = dict(N=p.N, d=p.d, M=M, Mk=Mk, K=L.spark_attn_topk_count(Mk, p.topk_ratio), Nv=p.N - p.n_sink)
+    for name, t, role in args:
+        if t is None:
+            continue
+        per_head, dtype = _ROLES[role]
+        dtype = dtype or _DTYPES[p.dtype]
+        need = p.B * p.H * per_head(g)
+        if t.dtype != dtype:
+            raise TypeError(f"{name}: element type {t.dtype}, expected {dtype}")
+        if t.numel() < need:
+            raise ValueError(f"{name}: {t.numel()} elements, expected {need}")
+
+
 def _stream(stream):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
@@ -152,12 +195,17 @@ def workspace_size(p: SparkAttnParams, what: int) -> int:
 # ---- C-named entry points (pre-allocated tensors) -------------------------------------------
 
 def spark_attn_pool(p, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, stream=None):
+    _validate(p, ("Q", Q, "tok"), ("K", K, "tok"), ("V", V, "tok"), ("q_mean", q_mean, "qblk"),
+              ("k_mean", k_mean, "kblk"), ("k_sum", k_sum, "kblk"), ("v_sum", v_sum, "kblk"),
+              ("bias", bias, "kbias"), ("anchor", anchor, "head"))
     _check("spark_attn_pool", lib().spark_attn_pool(
         ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(q_mean), _ptr(k_mean), _ptr(k_sum),
         _ptr(v_sum), _ptr(bias), _ptr(anchor), _stream(stream)))
 
 
 def spark_attn_select(p, q_mean, k_mean, idx, scores=None, workspace=None, stream=None):
+    _validate(p, ("q_mean", q_mean, "qblk"), ("k_mean", k_mean, "kblk"), ("idx", idx, "route"),
+              ("scores", scores, "scores"))
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("spark_attn_select", lib().spark_attn_select(
         ctypes.byref(p), _ptr(q_mean), _ptr(k_mean), _ptr(idx), _ptr(scores), _ptr(workspace),
@@ -169,24 +217,33 @@ def _nbytes(t):
 
 
 def spark_attn_pack(p, K, V, k_sum, v_sum, bias, packed, stream=None):
+    _validate(p, ("K", K, "tok"), ("V", V, "tok"), ("k_sum", k_sum, "kblk"), ("v_sum", v_sum, "kblk"),
+              ("bias", bias, "kbias"))
     _check("spark_attn_pack", lib().spark_attn_pack(
         ctypes.byref(p), _ptr(K), _ptr(V), _ptr(k_sum), _ptr(v_sum), _ptr(bias), _ptr(packed),
         _nbytes(packed), _stream(stream)))
 
 
 def spark_attn_pool_pack(p, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, packed, stream=None):
+    _validate(p, ("Q", Q, "tok"), ("K", K, "tok"), ("V", V, "tok"), ("q_mean", q_mean, "qblk"),
+              ("k_mean", k_mean, "kblk"), ("k_sum", k_sum, "kblk"), ("v_sum", v_sum, "kblk"),
+              ("bias", bias, "kbias"), ("anchor", anchor, "head"))
     _check("spark_attn_pool_pack", lib().spark_attn_pool_pack(
         ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(q_mean), _ptr(k_mean), _ptr(k_sum),
         _ptr(v_sum), _ptr(bias), _ptr(anchor), _ptr(packed), _nbytes(packed), _stream(stream)))
 
 
 def spark_attn_attend(p, Q, packed, idx, perm, O, lse=None, stream=None):
+    _validate(p, ("Q", Q, "tok"), ("idx", idx, "route"), ("perm", perm, "perm"), ("O", O, "tok"),
+              ("lse", lse, "rows"))
     _check("spark_attn_attend", lib().spark_attn_attend(
         ctypes.byref(p), _ptr(Q), _ptr(packed), _nbytes(packed), _ptr(idx), _ptr(perm), _ptr(O),
         _ptr(lse), _stream(stream)))
 
 
 def spark_attn_forward(p, Q, K, V, perm, O, lse, idx_out, workspace, stream=None):
+    _validate(p, ("Q", Q, "tok"), ("K", K, "tok"), ("V", V, "tok"), ("perm", perm, "perm"), ("O", O, "tok"),
+              ("lse", lse, "rows"), ("idx_out", idx_out, "route"))
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("spark_attn_forward", lib().spark_attn_forward(
         ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(perm), _ptr(O), _ptr(lse),
@@ -194,6 +251,8 @@ def spark_attn_forward(p, Q, K, V, perm, O, lse, idx_out, workspace, stream=None
 
 
 def spark_attn_forward_kv(p, Q, K, V, perm_q, perm_k, O, lse, idx_out, workspace, stream=None):
+    _validate(p, ("Q", Q, "tok"), ("K", K, "tok"), ("V", V, "tok"), ("perm_q", perm_q, "perm"),
+              ("perm_k", perm_k, "perm"), ("O", O, "tok"), ("lse", lse, "rows"), ("idx_out", idx_out, "route"))
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("spark_attn_forward_kv", lib().spark_attn_forward_kv(
         ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(perm_q), _ptr(perm_k), _ptr(O), _ptr(lse),
@@ -201,6 +260,8 @@ def spark_attn_forward_kv(p, Q, K, V, perm_q, perm_k, O, lse, idx_out, workspace
 
 
 def spark_attn_select_tau(p, tau, q_mean, k_mean, idx, counts, stats, workspace, stream=None):
+    _validate(p, ("q_mean", q_mean, "qblk"), ("k_mean", k_mean, "kblk"), ("idx", idx, "route_all"),
+              ("counts", counts, "counts"), ("stats", stats, "stats"))
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("spark_attn_select_tau", lib().spark_attn_select_tau(
         ctypes.byref(p), float(tau), _ptr(q_mean), _ptr(k_mean), _ptr(idx), _ptr(counts), _ptr(stats),
@@ -208,12 +269,16 @@ def spark_attn_select_tau(p, tau, q_mean, k_mean, idx, counts, stats, workspace,
 
 
 def spark_attn_attend_var(p, Q, packed, idx, counts, perm, O, lse, stream=None):
+    _validate(p, ("Q", Q, "tok"), ("idx", idx, "route_all"), ("counts", counts, "counts"),
+              ("perm", perm, "perm"), ("O", O, "tok"), ("lse", lse, "rows"))
     _check("spark_attn_attend_var", lib().spark_attn_attend_var(
         ctypes.byref(p), _ptr(Q), _ptr(packed), _nbytes(packed), _ptr(idx), _ptr(counts), _ptr(perm),
         _ptr(O), _ptr(lse), _stream(stream)))
 
 
 def spark_attn_forward_tau(p, tau, Q, K, V, O, lse, idx_out, counts_out, workspace, stream=None):
+    _validate(p, ("Q", Q, "tok"), ("K", K, "tok"), ("V", V, "tok"), ("O", O, "tok"), ("lse", lse, "rows"),
+              ("idx_out", idx_out, "route_all"), ("counts_out", counts_out, "counts"))
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("spark_attn_forward_tau", lib().spark_attn_forward_tau(
         ctypes.byref(p), float(tau), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(lse), _ptr(idx_out),
@@ -221,35 +286,46 @@ def spark_attn_forward_tau(p, tau, Q, K, V, O, lse, idx_out, counts_out, workspa
 
 
 def spark_attn_fp8_scales(p, Q, K, V, amax, stream=None):
+    _validate(p, ("Q", Q, "tok"), ("K", K, "tok"), ("V", V, "tok"), ("amax", amax, "amax"))
     _check("spark_attn_fp8_scales", lib().spark_attn_fp8_scales(
         ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(amax), _stream(stream)))
 
 
 def spark_attn_pool_fp8_scales(p, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor, amax, stream=None):
+    _validate(p, ("Q", Q, "tok"), ("K", K, "tok"), ("V", V, "tok"), ("q_mean", q_mean, "qblk"),
+              ("k_mean", k_mean, "kblk"), ("k_sum", k_sum, "kblk"), ("v_sum", v_sum, "kblk"),
+              ("bias", bias, "kbias"), ("anchor", anchor, "head"), ("amax", amax, "amax"))
     _check("spark_attn_pool_fp8_scales", lib().spark_attn_pool_fp8_scales(
         ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(q_mean), _ptr(k_mean), _ptr(k_sum),
         _ptr(v_sum), _ptr(bias), _ptr(anchor), _ptr(amax), _stream(stream)))
 
 
 def spark_attn_pack_fp8(p, K, V, k_sum, v_sum, bias, amax, packed, stream=None):
+    _validate(p, ("K", K, "tok"), ("V", V, "tok"), ("k_sum", k_sum, "kblk"), ("v_sum", v_sum, "kblk"),
+              ("bias", bias, "kbias"), ("amax", amax, "amax"))
     _check("spark_attn_pack_fp8", lib().spark_attn_pack_fp8(
         ctypes.byref(p), _ptr(K), _ptr(V), _ptr(k_sum), _ptr(v_sum), _ptr(bias), _ptr(amax),
         _ptr(packed), _nbytes(packed), _stream(stream)))
 
 
 def spark_attn_attend_fp8(p, Q, packed, idx, perm, amax, O, lse=None, stream=None):
+    _validate(p, ("Q", Q, "tok"), ("idx", idx, "route"), ("perm", perm, "perm"), ("amax", amax, "amax"),
+              ("O", O, "tok"), ("lse", lse, "rows"))
     _check("spark_attn_attend_fp8", lib().spark_attn_attend_fp8(
         ctypes.byref(p), _ptr(Q), _ptr(packed), _nbytes(packed), _ptr(idx), _ptr(perm), _ptr(amax),
         _ptr(O), _ptr(lse), _stream(stream)))
 
 
 def spark_attn_forward_fp8(p, Q, K, V, perm, O, lse, idx_out, amax_out, workspace, stream=None):
+    _validate(p, ("Q", Q, "tok"), ("K", K, "tok"), ("V", V, "tok"), ("perm", perm, "perm"), ("O", O, "tok"),
+              ("lse", lse, "rows"), ("idx_out", idx_out, "route"), ("amax_out", amax_out, "amax"))
     _check("spark_attn_forward_fp8", lib().spark_attn_forward_fp8(
         ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(perm), _ptr(O), _ptr(lse), _ptr(idx_out),
         _ptr(amax_out), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def spark_attn_reblock(p, Q, K, perm, workspace, stream=None):
+    _validate(p, ("Q", Q, "tok"), ("K", K, "tok"), ("perm", perm, "perm"))
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("spark_attn_reblock", lib().spark_attn_reblock(
         ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(perm), _ptr(workspace), ws_bytes,
@@ -257,6 +333,7 @@ def spark_attn_reblock(p, Q, K, perm, workspace, stream=None):
 
 
 def spark_attn_gather_rows(p, X, perm, Y, stream=None):
+    _validate(p, ("X", X, "tok"), ("perm", perm, "perm"), ("Y", Y, "tok"))
     _check("spark_attn_gather_rows", lib().spark_attn_gather_rows(
         ctypes.byref(p), _ptr(X), _ptr(perm), _ptr(Y), _stream(stream)))
 

@@ -267,3 +267,57 @@ def test_pool_fp8_scales_validates_before_launch():
     mis[0] = bad
     assert L.spark_attn_pool_fp8_scales(byref(p), *mis, None) == MISALIGNED
     assert L.spark_attn_pool_fp8_scales(byref(P(d=96)), *args, None) == UNSUPPORTED
+
+
+def test_binding_checks_tensor_sizes_and_types():
+    """The Python wrappers check every buffer against the parameters before handing bare pointers
+    to the library.  CPU tensors are used: a buffer that passes the size and type check then
+    fails the device-tensor check, so no call reaches the library's launch path."""
+    import torch
+
+    B, H, N, d, ns, b = 1, 2, 1000, 128, 8, 128
+    p = sa.params(torch.empty(B, H, N, d, dtype=torch.bfloat16), ns, b, 0.1)
+    M = sa.num_blocks(p)
+    Kk = sa.topk_count(M, 0.1)
+    f32, i32 = torch.float32, torch.int32
+    good = dict(
+        Q=torch.empty(B, H, N, d, dtype=torch.bfloat16), K=torch.empty(B, H, N, d, dtype=torch.bfloat16),
+        V=torch.empty(B, H, N, d, dtype=torch.bfloat16), q_mean=torch.empty(B, H, M, d, dtype=f32),
+        k_mean=torch.empty(B, H, M, d, dtype=f32), k_sum=torch.empty(B, H, M, d, dtype=f32),
+        v_sum=torch.empty(B, H, M, d, dtype=f32), bias=torch.empty(B, H, M, dtype=f32),
+        anchor=torch.empty(B, H, d, dtype=f32))
+    order = ["Q", "K", "V", "q_mean", "k_mean", "k_sum", "v_sum", "bias", "anchor"]
+
+    def pool(**over):
+        t = dict(good, **over)
+        sa.spark_attn_pool(p, *[t[k] for k in order])
+
+    with pytest.raises(ValueError, match="device tensors"):
+        pool()
+    with pytest.raises(TypeError, match="Q: element type"):
+        pool(Q=good["Q"].float())
+    with pytest.raises(ValueError, match="bias: 1 elements"):
+        pool(bias=torch.empty(1, dtype=f32))
+    with pytest.raises(ValueError, match="anchor"):
+        pool(anchor=torch.empty(B, H, d - 1, dtype=f32))
+    O = torch.empty(B, H, N, d, dtype=torch.bfloat16)
+    packed = torch.empty(16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match=f"idx: {M * (Kk - 1) * 2} elements, expected {B * H * M * Kk}"):
+        sa.spark_attn_attend(p, good["Q"], packed, torch.empty(B, H, M, Kk - 1, dtype=i32), None, O)
+    with pytest.raises(TypeError, match="idx: element type"):
+        sa.spark_attn_attend(p, good["Q"], packed, torch.empty(B, H, M, Kk, dtype=torch.int64), None, O)
+    with pytest.raises(ValueError, match="perm"):
+        sa.spark_attn_attend(p, good["Q"], packed, torch.empty(B, H, M, Kk, dtype=i32),
+                             torch.empty(B, H, N - ns - 1, dtype=i32), O)
+    with pytest.raises(ValueError, match="lse"):
+        sa.spark_attn_attend(p, good["Q"], packed, torch.empty(B, H, M, Kk, dtype=i32), None, O,
+                             torch.empty(B, H, N - 1, dtype=f32))
+    with pytest.raises(ValueError, match="amax"):
+        sa.spark_attn_fp8_scales(p, good["Q"], good["K"], good["V"], torch.empty(B, H, 2, dtype=f32))
+    with pytest.raises(ValueError, match="Y"):
+        sa.spark_attn_gather_rows(p, good["Q"], torch.empty(B, H, N - ns, dtype=i32),
+                                  torch.empty(B, H, N - 1, d, dtype=torch.bfloat16))
+    # invalid parameters are left to the library's own status
+    bad = sa.params(good["Q"], N, b, 0.1)  # n_sink = N
+    with pytest.raises(ValueError, match="device tensors"):
+        sa.spark_attn_pool(bad, *[torch.empty(1, dtype=f32)] * 9)
