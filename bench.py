@@ -103,7 +103,18 @@ def route_check(idx, S, rel=1e-4, floor=1e-6):
     return int((~ok).sum())
 
 
-def cpu_baseline(wl, ratio, Qh, Kh, Vh, gidx, F_sel_total, sample_blocks, block_k=0):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(wl, ratio, Qh, Kh, Vh, gidx, F_sel_total, sample_blocks, block_k=0, single_core_blocks=24):
     """The oracle as it stands, on a bounded sample: full pool, full block scores and top-K, and
     the attention of `sample_blocks` video query blocks plus a few sink query rows; the full
     forward time is extrapolated from the per-block time."""
@@ -134,6 +145,16 @@ def cpu_baseline(wl, ratio, Qh, Kh, Vh, gidx, F_sel_total, sample_blocks, block_
     per_block = (t4 - t3) / sample_blocks
     per_sink_row = (t5 - t4) / n_sq
     t_full = (t1 - t0) + (t2 - t1) + per_block * BH * M + per_sink_row * BH * wl.n_sink
+    # one host core: the attention of a few of the same query blocks, scaled the same way
+    n1 = max(1, min(sample_blocks, single_core_blocks))
+    oracle.set_num_threads(1)
+    try:
+        t6 = time.perf_counter()
+        oracle.attend_blocks(p, Qh, Kh, Vh, pooled, gidx, qb[:n1])
+        t7 = time.perf_counter()
+    finally:
+        oracle.set_num_threads(threads)
+    t_full_1 = (t7 - t6) / n1 * BH * M  # attention of every video query block on one core
     return {
         "value": F_sel_total / t_full / 1e12,
         "unit": "TFLOP/s",
@@ -144,6 +165,11 @@ def cpu_baseline(wl, ratio, Qh, Kh, Vh, gidx, F_sel_total, sample_blocks, block_
                    f"query blocks ({t4 - t3:.1f} s) and {n_sq} sink query rows ({t5 - t4:.1f} s); "
                    f"full forward extrapolated to {t_full:.0f} s"),
         "est_forward_s": t_full,
+        "cpu_model": cpu_model(),
+        "single_core": {"query_blocks": n1, "seconds": round(t7 - t6, 2),
+                        "attention_per_block_s": round((t7 - t6) / n1, 4),
+                        "est_attention_s": round(t_full_1, 1),
+                        "speedup_of_all_threads": round((t7 - t6) / n1 / per_block, 2)},
         "route_rows_violating_near_tie_rule": bad,
         "route_rows_equal_to_oracle": same,
     }
@@ -167,6 +193,9 @@ def main():
     ap.add_argument("--cpu-sample-blocks", type=int, default=600)
     ap.add_argument("--no-forward-check", action="store_true",
                     help="skip the spark_attn_forward cross-check launches (for counter runs)")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="after the timed steps, this many more steps each preceded by a 512 MiB device "
+                         "write that evicts L2 and the MALL (reported under 'cold'; 0: none)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many MiB (a kernel of "
                          "known traffic, used to scale hardware byte counters)")
@@ -290,11 +319,34 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    st = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(ns)] for e in events]).mean(axis=0)
-    stage_ms = {n: float(x) for n, x in zip(stage_names, st)}
+    per_step = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(ns)] for e in events])
+    stage_ms = {n: float(x) for n, x in zip(stage_names, per_step.mean(axis=0))}
+    stage_spread = {"median": {n: round(float(x), 4) for n, x in zip(stage_names, np.median(per_step, axis=0))},
+                    "min": {n: round(float(x), 4) for n, x in zip(stage_names, per_step.min(axis=0))}}
     ms_pool = stage_ms["pool_scales"] if fp8 else stage_ms["pool_pack"]
     ms_sel, ms_attn = stage_ms["select"], stage_ms["attend"]
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (" + ", ".join(f"{n} {v:.3f}" for n, v in stage_ms.items()) + ")")
+
+    # cold caches: a 512 MiB write before each step evicts the 4 MB L2 of every XCD and the 256 MB
+    # MALL, so the step starts with none of its inputs cached (the warm steps above keep whatever
+    # the previous step left)
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 20, device="cuda", dtype=torch.uint8)
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)] for _ in range(args.cold_steps)]
+        for k in range(args.cold_steps):
+            flush.fill_(k & 0xFF)
+            cev[k][0].record(stream)
+            step(cev[k])
+        torch.cuda.synchronize()
+        cold_steps = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(ns)] for e in cev])
+        cold = {"steps": args.cold_steps, "flush": "512 MiB device write before each step",
+                "ms_per_step_median": round(float(np.median(cold_steps.sum(axis=1))), 4),
+                "ms_per_step_min": round(float(cold_steps.sum(axis=1).min()), 4),
+                "stages_ms_median": {n: round(float(x), 4)
+                                     for n, x in zip(stage_names, np.median(cold_steps, axis=0))}}
+        del flush
+        log(f"cold caches, {args.cold_steps} steps: median {cold['ms_per_step_median']:.3f} ms/step")
 
     # cross-check: the single-call entry point over the same input
     ms_forward_call, same_out, ws, O2 = None, None, None, None
@@ -370,6 +422,8 @@ def main():
         },
         "stages_ms": dict({n: round(v, 4) for n, v in stage_ms.items()},
                           spark_attn_forward_call=ms_forward_call),
+        "stages_ms_spread": stage_spread,
+        "cold": cold,
         "forward_call_output_identical": same_out,
         "flops": {"F_sel": F_sel, "F_sink": F_sink, "F_comp": F_comp, "F_sinkq": F_sinkq},
         "roofline": {

@@ -57,6 +57,8 @@ def lib():
         L.orc_num_key_blocks.argtypes = [P]
         L.orc_topk_count.argtypes = [ctypes.c_int, ctypes.c_float]
         L.orc_num_threads.argtypes = []
+        L.orc_set_num_threads.argtypes = [ctypes.c_int]
+        L.orc_set_num_threads.restype = None
         L.orc_pool.argtypes = [P, f32, f32, f32, f64, f64, f64, f64, f64, f64]
         L.orc_scores.argtypes = [P, f64, f64, f64]
         L.orc_select.argtypes = [P, f64, i32]
@@ -112,6 +114,11 @@ def topk_count(M: int, ratio: float) -> int:
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for later calls (timing only: every result is independent of the thread count)."""
+    lib().orc_set_num_threads(int(n))
 
 
 def pool(p: Params, Q, K, V):

@@ -48,6 +48,16 @@ int orc_num_threads(void)
 #endif
 }
 
+/* Threads used by later calls (for timing a single-core sample); no effect on any result. */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Query blocks M = ceil(N_v / block) and key blocks M_k = ceil(N_v / block_k); a last block may be
  * partial.  Reading of the asymmetric route [H3O, "Manual Sparse Sage recovery": the sparse
  * backends consume a 128Q x 64KV route]: query blocks of `block` rows are routed to key blocks

@@ -617,3 +617,23 @@ def test_asymmetric_fp8_matches_brute_force(orc):
     Ob, lb, ib = brute.forward(Q, K, V, 5, 128, 0.2, 1, fp8=True, block_k=64)
     assert (idx == ib).all()
     assert np.abs(O - Ob).max() < 1e-12 and np.abs(lse - lb).max() < 1e-11
+
+
+# ---------------------------------------------------------------- thread count
+def test_results_do_not_depend_on_the_thread_count(orc):
+    """OpenMP only splits independent (batch, head, block) units, so the forward, the pool and the
+    partition are bit-identical on one thread and on all of them (the benchmark's single-core
+    sample relies on this)."""
+    Q, K, V = small(seed=11, B=2, H=2, nv=900, ns=7, d=32)
+    p = orc.params(Q, 7, 64, 0.2, 1)
+    n = orc.num_threads()
+    try:
+        orc.set_num_threads(1)
+        O1, l1, i1 = orc.forward(p, Q, K, V)
+        P1 = orc.reblock(p, Q, K)
+    finally:
+        orc.set_num_threads(n)
+    On, ln, i_n = orc.forward(p, Q, K, V)
+    Pn = orc.reblock(p, Q, K)
+    assert np.array_equal(O1, On) and np.array_equal(l1, ln) and np.array_equal(i1, i_n)
+    assert np.array_equal(P1, Pn)
