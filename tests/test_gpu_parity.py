@@ -331,6 +331,48 @@ def test_fullclip_sampled(orc):
     sampled_check(orc, W.WORKLOADS["fullclip"], 0.1, n_blocks=12, n_sink_rows=4)
 
 
+def test_maximum_block_count(orc):
+    """The largest block count the library supports (16384 query and key blocks: 1,048,555 video
+    tokens in blocks of 64, the last one ragged, d = 64, one head, 40 sinks).  At this size the
+    top-K re-reads each score row from memory instead of holding it in registers.  Sampled route
+    rows are checked against the oracle's block means with the near-tie rule, and sampled query
+    blocks (the ragged last one included) and sink rows against the oracle's attention."""
+    B, H, d, b, ns, ratio = 1, 1, 64, 64, 40, 0.1
+    M = 16384
+    nv = M * b - 21
+    Q, K, V = W.gaussian_qkv(B, H, nv, ns, d, seed=16384, dtype="bf16")
+    note(f"maximum block count M={M} N_v={nv} d={d} block={b}")
+    Qd, Kd, Vd = to_dev(Q, "bf16"), to_dev(K, "bf16"), to_dev(V, "bf16")
+    O, lse, idx = sa.forward(Qd, Kd, Vd, ns, b, ratio, return_lse=True, return_idx=True)
+    torch.cuda.synchronize()
+    del Qd, Kd, Vd
+    p = orc.params(Q, ns, b, ratio, 1)
+    assert orc.num_blocks(p) == M and idx.shape[2] == M and idx.shape[3] == sa.topk_count(M, ratio)
+    ref = orc.pool(p, Q, K, V)
+    gidx = host(idx)
+    rng = np.random.default_rng(1)
+    rows = sorted(set(rng.choice(M, 512, replace=False).tolist()) | {0, M - 1})
+    s = 1.0 / math.sqrt(d)
+    qm, km = ref["q_mean"][0, 0], ref["k_mean"][0, 0]
+    S = np.stack([s * km @ qm[I] for I in rows])
+    bad, differ = check_selection(gidx[0, 0, rows], S)
+    print(f"route rows checked {len(rows)}, outside the near-tie rule {bad}, differing {differ}", flush=True)
+    assert bad == 0
+    qb = [(0, int(I)) for I in rng.choice(M - 1, 6, replace=False)] + [(0, M - 1)]
+    qb += [(0, M + int(j)) for j in rng.choice(ns, 3, replace=False)]
+    Os, ls = orc.attend_blocks(p, Q, K, V, ref, gidx, np.array(qb))
+    Og, lg = host(O), host(lse)
+    g_rows, r_rows, gl, rl = [], [], [], []
+    for n, (bh, I) in enumerate(qb):
+        lo, hi = (I * b, min(nv, (I + 1) * b)) if I < M else (nv + I - M, nv + I - M + 1)
+        g_rows.append(Og[0, bh, lo:hi]); r_rows.append(Os[n, :hi - lo])
+        gl.append(lg[0, bh, lo:hi]); rl.append(ls[n, :hi - lo])
+    g_rows, r_rows = np.concatenate(g_rows), np.concatenate(r_rows)
+    e2, ea, el = rel_l2(g_rows, r_rows), max_abs(g_rows, r_rows), max_abs(np.concatenate(gl), np.concatenate(rl))
+    print(f"maximum M: rel-L2 {e2:.3e} max-abs {ea:.3e} lse {el:.3e}", flush=True)
+    assert e2 <= FWD_REL_L2 and ea <= FWD_MAX_ABS and el <= FWD_MAX_ABS
+
+
 def test_stage_entry_points_match_forward():
     """pool -> select -> pack -> attend through their own entry points gives exactly what
     spark_attn_forward gives (same kernels, same inputs)."""
