@@ -331,24 +331,27 @@ def test_fullclip_sampled(orc):
     sampled_check(orc, W.WORKLOADS["fullclip"], 0.1, n_blocks=12, n_sink_rows=4)
 
 
-def test_maximum_block_count(orc):
-    """The largest block count the library supports (16384 query and key blocks: 1,048,555 video
-    tokens in blocks of 64, the last one ragged, d = 64, one head, 40 sinks).  At this size the
-    top-K re-reads each score row from memory instead of holding it in registers.  Sampled route
-    rows are checked against the oracle's block means with the near-tie rule, and sampled query
-    blocks (the ragged last one included) and sink rows against the oracle's attention."""
-    B, H, d, b, ns, ratio = 1, 1, 64, 64, 40, 0.1
-    M = 16384
-    nv = M * b - 21
-    Q, K, V = W.gaussian_qkv(B, H, nv, ns, d, seed=16384, dtype="bf16")
-    note(f"maximum block count M={M} N_v={nv} d={d} block={b}")
+def max_size_check(orc, b, bk, seed):
+    """One head at the largest key-block count the library accepts (16384 key blocks of bk tokens,
+    the last one ragged; query blocks of b), d = 64, 40 sinks.  At this size the top-K re-reads
+    each score row from memory instead of holding it in registers.  Sampled route rows are checked
+    against the oracle's block means with the near-tie rule, and sampled query blocks (the ragged
+    last one included) and sink rows against the oracle's attention."""
+    B, H, d, ns, ratio = 1, 1, 64, 40, 0.1
+    Mk = 16384
+    nv = Mk * bk - 21
+    Q, K, V = W.gaussian_qkv(B, H, nv, ns, d, seed=seed, dtype="bf16")
+    note(f"maximum block count M_k={Mk} N_v={nv} d={d} block={b} block_k={bk}")
     Qd, Kd, Vd = to_dev(Q, "bf16"), to_dev(K, "bf16"), to_dev(V, "bf16")
-    O, lse, idx = sa.forward(Qd, Kd, Vd, ns, b, ratio, return_lse=True, return_idx=True)
+    O, lse, idx = sa.forward(Qd, Kd, Vd, ns, b, ratio, return_lse=True, return_idx=True,
+                             block_k=0 if bk == b else bk)
     torch.cuda.synchronize()
     del Qd, Kd, Vd
-    p = orc.params(Q, ns, b, ratio, 1)
-    assert orc.num_blocks(p) == M and idx.shape[2] == M and idx.shape[3] == sa.topk_count(M, ratio)
+    p = orc.params(Q, ns, b, ratio, 1, block_k=0 if bk == b else bk)
+    M = -(-nv // b)
+    assert orc.num_blocks(p) == M and idx.shape[2] == M and idx.shape[3] == sa.topk_count(Mk, ratio)
     ref = orc.pool(p, Q, K, V)
+    assert ref["k_mean"].shape[2] == Mk
     gidx = host(idx)
     rng = np.random.default_rng(1)
     rows = sorted(set(rng.choice(M, 512, replace=False).tolist()) | {0, M - 1})
@@ -369,8 +372,19 @@ def test_maximum_block_count(orc):
         gl.append(lg[0, bh, lo:hi]); rl.append(ls[n, :hi - lo])
     g_rows, r_rows = np.concatenate(g_rows), np.concatenate(r_rows)
     e2, ea, el = rel_l2(g_rows, r_rows), max_abs(g_rows, r_rows), max_abs(np.concatenate(gl), np.concatenate(rl))
-    print(f"maximum M: rel-L2 {e2:.3e} max-abs {ea:.3e} lse {el:.3e}", flush=True)
+    print(f"maximum M_k: rel-L2 {e2:.3e} max-abs {ea:.3e} lse {el:.3e}", flush=True)
     assert e2 <= FWD_REL_L2 and ea <= FWD_MAX_ABS and el <= FWD_MAX_ABS
+
+
+def test_maximum_block_count(orc):
+    """M = M_k = 16384 blocks of 64 (1,048,555 video tokens)."""
+    max_size_check(orc, 64, 64, seed=16384)
+
+
+def test_maximum_key_block_count_asymmetric(orc):
+    """The asymmetric route at its largest size: 8192 query blocks of 128 against 16384 key blocks
+    of 64."""
+    max_size_check(orc, 128, 64, seed=8192)
 
 
 def test_stage_entry_points_match_forward():

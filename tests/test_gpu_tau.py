@@ -145,3 +145,47 @@ def test_tau_on_the_short_clip(orc):
     e2, ea = rel_l2(Og, Oref), max_abs(Og, Oref)
     print(f"kept {gc.mean() / gc.shape[2]:.3f} of the blocks; rel-L2 {e2:.3e} max-abs {ea:.3e}")
     assert e2 <= FWD_REL_L2 and ea <= FWD_MAX_ABS
+
+
+def test_tau_at_the_maximum_block_count(orc):
+    """Adaptive-tau selection at the largest block count the library accepts (M = 16384 blocks of
+    64, the last one ragged, one head): the statistics run over 2^28 scores and a row may keep up
+    to M blocks.  The per-head (mu, sigma) and 512 sampled rows plus the first and last one are
+    checked against the binary64 rule on the oracle's block means (the attention over such a
+    route is covered at smaller sizes, where the oracle can run it)."""
+    B, H, d, b, ns, tau = 1, 1, 64, 64, 0, 1.5
+    M = 16384
+    nv = M * b - 21
+    Q, K, V = W.gaussian_qkv(B, H, nv, ns, d, seed=1234, dtype="bf16")
+    note(f"tau {tau} at the maximum block count M={M}")
+    Qd, Kd, Vd = dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16")
+    pooled = sa.pool(Qd, Kd, Vd, ns, b)
+    idx, counts, stats = sa.select_tau(pooled["q_mean"], pooled["k_mean"], Qd, ns, b, tau, with_stats=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    rows = sorted(set(rng.choice(M, 512, replace=False).tolist()) | {0, M - 1})
+    gidx = idx[0, 0, rows].cpu().numpy()
+    gcounts = counts[0, 0].cpu().numpy()
+    gstats = stats[0, 0].cpu().numpy()
+    del Qd, Kd, Vd, pooled, idx
+    p = orc.params(Q, ns, b, 1.0, 1)
+    ref = orc.pool(p, Q, K, V)
+    qm, km = ref["q_mean"][0, 0].astype(np.float64), ref["k_mean"][0, 0].astype(np.float64)
+    S = (qm @ km.T) / np.sqrt(d)
+    mu, sd = S.mean(), S.std()
+    assert abs(gstats[0] - mu) <= 1e-5 * abs(S).max() and abs(gstats[1] - sd) <= 1e-5 * sd, (gstats, mu, sd)
+    sub_counts = gcounts[rows]
+    # the threshold is the head's (all M x M scores), not that of the sampled rows
+    thr = mu + tau * sd
+    delta = 1e-4 * abs(thr) + 1e-6 * np.abs(S).max()
+    bad = 0
+    for n, I in enumerate(rows):
+        row = gidx[n, :sub_counts[n]]
+        bad += int(sub_counts[n] > 1 and not (np.diff(row) > 0).all())
+        got = np.zeros(M, bool)
+        got[row] = True
+        bad += int(((S[I] > thr + delta) & ~got).sum() + (got & ~(S[I] >= thr - delta)).sum())
+    kept = gcounts.mean() / M
+    print(f"kept fraction {kept:.4f}, rows checked {len(rows)}, decisions outside the window {bad}", flush=True)
+    assert bad == 0
+    assert 0 <= gcounts.min() and gcounts.max() <= M
