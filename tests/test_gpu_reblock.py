@@ -4,6 +4,10 @@ The permutation must equal the oracle's bit for bit (every decision is taken in 
 fixed operation order on both sides).  The forward with the partition is held to the attention
 tolerances, with the oracle attending through the GPU's validated route.
 """
+import hashlib
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -86,6 +90,32 @@ def test_reblock_is_deterministic():
     b = sa.reblock(Qd, Kd, 8, 128)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+REBLOCK_MAX = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "reblock_max.json")
+
+
+def test_reblock_at_the_largest_sizes():
+    """The partition at 2^20 video rows (its largest size: 16384 leaves of 64, 14 bisection levels)
+    and at the full clip's 245,952 rows with d = 128.  The oracle needs minutes per case there, so
+    its permutation is stored as a SHA-256 written by tests/golden/make_reblock_max.py (oracle and
+    seeded generators only); the GPU's permutation must hash the same.  It is also checked to be a
+    bijection with ascending original indices inside every leaf."""
+    cases = json.load(open(REBLOCK_MAX))["cases"]
+    for name, c in cases.items():
+        nv, b = c["n_video"], c["block"]
+        Q, K, _ = W.gaussian_qkv(1, 1, nv, c["n_sink"], c["d"], seed=c["seed"], dtype=c["dtype"])
+        note(f"reblock at {name}: N_v={nv} d={c['d']} block={b}")
+        perm = sa.reblock(dev(Q, "bf16"), dev(K, "bf16"), c["n_sink"], b)
+        torch.cuda.synchronize()
+        got = perm.cpu().numpy()
+        flat = got[0, 0]
+        assert np.array_equal(np.sort(flat), np.arange(nv, dtype=flat.dtype)), "not a bijection"
+        full = nv // b * b  # leaves of b tokens, then the ragged remainder as the last leaf
+        assert (np.diff(flat[:full].reshape(-1, b), axis=1) > 0).all() and (np.diff(flat[full:]) > 0).all(), \
+            "a leaf is not in ascending index order"
+        assert flat[:8].tolist() == c["perm_head"] and flat[-8:].tolist() == c["perm_tail"]
+        assert hashlib.sha256(got.astype("<i4").tobytes()).hexdigest() == c["perm_sha256"], name
 
 
 def test_reblock_720p_bit_exact_and_forward(orc):
