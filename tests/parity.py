@@ -68,3 +68,26 @@ def rel_l2(a, b):
 
 def max_abs(a, b):
     return float(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)).max())
+
+
+def fp8_decoded_inputs(orc, p, Q, K, V, pooled):
+    """Inputs on which the oracle's plain attention computes the FP8 forward: every carrier
+    decoded, x -> e4m3(x * r) * s per (batch, head) and tensor (the product x * r in binary32),
+    and the pseudo-keys and pseudo-values carried with the keys' and values' scales (their
+    summaries rounded to binary32 first), as the oracle's FP8 forward defines them.  A logit
+    scale * (q8 s_Q) . (k8 s_K) is then the FP8 logit scale * s_Q * s_K * (q8 . k8).  The decoded
+    rows are handed to the oracle in binary32, a relative rounding of 2^-24 far inside the FP8
+    tolerances; the decoded summaries stay binary64 (exact).  Used to sample the FP8 forward at
+    sizes where the oracle's full FP8 forward would take too long."""
+    sc = orc.fp8_scales(p, Q, K, V)  # [B, H, 6]: (r, s) for Q, K, V
+
+    def carry(X, t):
+        r = sc[..., 2 * t].astype(np.float32)[:, :, None, None]
+        s = sc[..., 2 * t + 1].astype(np.float64)[:, :, None, None]
+        return orc.e4m3((np.asarray(X, np.float32) * r).astype(np.float32)).astype(np.float64) * s
+
+    Qd, Kd, Vd = carry(Q, 0), carry(K, 1), carry(V, 2)
+    pd = dict(pooled)
+    pd["k_sum"] = carry(pooled["k_sum"], 1)
+    pd["v_sum"] = carry(pooled["v_sum"], 2)
+    return Qd, Kd, Vd, pd

@@ -187,3 +187,53 @@ def test_pool_fp8_scales_equals_pool_and_scales(case, pool_mode, block_k):
     assert float(amax_ref[..., 0].max()) == 40.0
     if ns:
         assert float(amax_ref[..., 1].max()) == 37.0
+
+
+def test_fp8_fullclip_sampled(orc):
+    """The FP8 forward at the full clip's shape (245,952 video + 512 sink tokens, 24 heads, the
+    benchmark's --fp8 launch).  For three heads the oracle checks the per-head maxima exactly,
+    sampled route rows with the near-tie rule, and sampled query blocks (the ragged last one
+    included) and sink rows through its plain attention on the decoded carriers (the oracle's
+    full FP8 forward is too long at this size; tests/test_oracle_pins.py shows the two agree)."""
+    import math
+
+    from parity import fp8_decoded_inputs
+
+    wl = W.WORKLOADS["fullclip"]
+    Q, K, V = W.make_qkv(wl)
+    note(f"fp8 forward, full clip N={wl.N} H={wl.H}")
+    O, lse, idx, amax = sa.forward_fp8(dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), wl.n_sink, wl.block,
+                                       0.1, 1, return_lse=True, return_idx=True, return_amax=True)
+    torch.cuda.synchronize()
+    heads = [0, 11, 23]
+    Qs, Ks, Vs = (np.ascontiguousarray(x[:, heads]) for x in (Q, K, V))
+    del Q, K, V
+    gidx = idx.cpu().numpy()[:, heads]
+    am = amax.cpu().numpy()[:, heads]
+    Og, lg = host(O)[:, heads], lse.cpu().numpy()[:, heads]
+    del O, lse, idx
+    assert (am == np.abs(np.stack([Qs, Ks, Vs], axis=2)).reshape(*am.shape, -1).max(axis=-1)).all()
+    p = orc.params(Qs, wl.n_sink, wl.block, 0.1, 1)
+    ref = orc.pool(p, Qs, Ks, Vs)
+    M = gidx.shape[2]
+    rng = np.random.default_rng(8)
+    s = 1.0 / math.sqrt(wl.d)
+    rows = [(h, int(I)) for h in range(len(heads)) for I in rng.choice(M, 16, replace=False)]
+    S = np.stack([s * ref["k_mean"][0, h] @ ref["q_mean"][0, h, I] for h, I in rows])
+    bad, _ = check_selection(np.stack([gidx[0, h, I] for h, I in rows]), S)
+    assert bad == 0
+    Qd, Kd, Vd, pd = fp8_decoded_inputs(orc, p, Qs, Ks, Vs, ref)
+    qb = [(int(h), int(I)) for h, I in zip(rng.integers(0, len(heads), 9), rng.integers(0, M, 9))]
+    qb += [(len(heads) - 1, M - 1)]
+    qb += [(int(h), M + int(j)) for h, j in zip(rng.integers(0, len(heads), 3), rng.integers(0, wl.n_sink, 3))]
+    Os, ls = orc.attend_blocks(p, Qd, Kd, Vd, pd, gidx, np.array(qb))
+    nv = wl.n_video
+    g_rows, r_rows, gl, rl = [], [], [], []
+    for n, (h, I) in enumerate(qb):
+        lo, hi = (I * wl.block, min(nv, (I + 1) * wl.block)) if I < M else (nv + I - M, nv + I - M + 1)
+        g_rows.append(Og[0, h, lo:hi]); r_rows.append(Os[n, :hi - lo])
+        gl.append(lg[0, h, lo:hi]); rl.append(ls[n, :hi - lo])
+    g_rows, r_rows = np.concatenate(g_rows), np.concatenate(r_rows)
+    e2, ea, el = rel_l2(g_rows, r_rows), max_abs(g_rows, r_rows), max_abs(np.concatenate(gl), np.concatenate(rl))
+    print(f"fp8 full clip: rel-L2 {e2:.3e} max-abs {ea:.3e} lse max-abs {el:.3e}", flush=True)
+    assert e2 <= FP8_REL_L2 and ea <= FP8_MAX_ABS and el <= FP8_LSE_MAX_ABS

@@ -533,6 +533,27 @@ def test_fp8_quantization_changes_the_result(orc):
     assert 1e-3 < rel < 2.0 ** -4
 
 
+@pytest.mark.parametrize("pool_mode,block_k", [(1, 0), (0, 0), (1, 32)])
+def test_fp8_forward_equals_plain_attention_on_decoded_carriers(orc, pool_mode, block_k):
+    """The sampling route of the GPU tests: the oracle's plain attention of chosen blocks, fed the
+    decoded carriers (parity.fp8_decoded_inputs), equals the oracle's FP8 forward on every video
+    block and sink row (ragged blocks, sinks, B > 1, both pool modes, unequal key blocks)."""
+    from parity import fp8_decoded_inputs
+
+    Q, K, V = small(seed=75, B=2, nv=1000 - 24, ns=5)
+    p = orc.params(Q, 5, 64, 0.2, pool_mode, block_k=block_k)
+    O8, l8, idx, _ = orc.forward_fp8(p, Q, K, V)
+    Qd, Kd, Vd, pd = fp8_decoded_inputs(orc, p, Q, K, V, orc.pool(p, Q, K, V))
+    M, BH, nv, ns = orc.num_blocks(p), 2 * 2, 1000 - 24, 5
+    qb = np.array([(bh, I) for bh in range(BH) for I in range(M + ns)])
+    Os, ls = orc.attend_blocks(p, Qd, Kd, Vd, pd, idx, qb)
+    O8f, l8f = O8.reshape(BH, -1, Q.shape[-1]), l8.reshape(BH, -1)
+    for n, (bh, I) in enumerate(qb):
+        lo, hi = (I * 64, min(nv, (I + 1) * 64)) if I < M else (nv + I - M, nv + I - M + 1)
+        assert np.abs(Os[n, :hi - lo] - O8f[bh, lo:hi]).max() < 1e-6
+        assert np.abs(ls[n, :hi - lo] - l8f[bh, lo:hi]).max() < 1e-6
+
+
 @pytest.mark.parametrize("pool_mode,ratio", [(1, 0.2), (0, 0.2), (1, 1.0)])
 def test_fp8_forward_matches_brute_force(orc, pool_mode, ratio):
     Q, K, V = small(seed=74, B=2, nv=1000 - 24, ns=5)
