@@ -1,0 +1,76 @@
+"""The benchmark's own arithmetic, on the CPU: the algorithmic work it divides by the measured
+times (one multiply-add for the logit and one for the value per query-key pair, counted from the
+actual route), and its vectorised route check against the per-row rule of the parity tests."""
+import types
+
+import numpy as np
+import pytest
+
+import bench
+from parity import check_selection
+
+
+def brute_flops(wl, idx, counts, bk):
+    """Query-key pairs of each branch counted one query block at a time."""
+    b, nv, ns, d, N = wl.block, wl.n_video, wl.n_sink, wl.d, wl.N
+    M, Mk = -(-nv // b), -(-nv // bk)
+    qsize = [min(b, nv - I * b) for I in range(M)]
+    ksize = [min(bk, nv - J * bk) for J in range(Mk)]
+    sel = comp = 0
+    for bh in range(wl.B * wl.H):
+        for I in range(M):
+            row = idx[0, bh, I] if counts is None else idx[0, bh, I, :counts[0, bh, I]]
+            sel += qsize[I] * sum(ksize[J] for J in row)
+            comp += qsize[I] * (Mk - len(row))
+    BH = wl.B * wl.H
+    return 4.0 * d * sel, 4.0 * d * nv * ns * BH, 4.0 * d * comp, 4.0 * d * ns * N * BH
+
+
+def workload(nv, ns, d, b, H):
+    return types.SimpleNamespace(block=b, n_video=nv, n_sink=ns, d=d, N=nv + ns, B=1, H=H)
+
+
+@pytest.mark.parametrize("nv,ns,b,bk,K", [(1000, 7, 64, 64, 3), (1000, 0, 128, 64, 5), (513, 3, 64, 128, 2)])
+def test_algorithmic_flops_fixed_route(nv, ns, b, bk, K):
+    wl = workload(nv, ns, 32, b, 2)
+    M, Mk = -(-nv // b), -(-nv // bk)
+    rng = np.random.default_rng(nv + bk)
+    idx = np.stack([np.sort(rng.choice(Mk, K, replace=False)) for _ in range(2 * M)]).reshape(1, 2, M, K)
+    got = bench.algorithmic_flops(idx, wl, K, None, 0 if bk == b else bk)
+    assert got == brute_flops(wl, idx, None, bk)
+
+
+def test_algorithmic_flops_variable_route():
+    nv, ns, b = 1000, 5, 64
+    wl = workload(nv, ns, 32, b, 2)
+    M = -(-nv // b)
+    rng = np.random.default_rng(2)
+    counts = rng.integers(0, M + 1, (1, 2, M)).astype(np.int32)
+    counts[0, 0, 0], counts[0, 1, M - 1] = 0, M  # nothing kept; everything kept (the ragged block)
+    idx = np.full((1, 2, M, M), -1, np.int32)
+    for bh in range(2):
+        for I in range(M):
+            idx[0, bh, I, :counts[0, bh, I]] = np.sort(rng.choice(M, counts[0, bh, I], replace=False))
+    got = bench.algorithmic_flops(idx, wl, None, counts, 0)
+    assert got == brute_flops(wl, idx, counts, b)
+
+
+def test_route_check_agrees_with_the_per_row_rule():
+    rng = np.random.default_rng(3)
+    R, M, K = 200, 40, 6
+    S = rng.standard_normal((R, M))
+    S[:20, 10] = S[:20, 11]  # exact ties at arbitrary ranks
+    idx = np.sort(np.argsort(-S, axis=1, kind="stable")[:, :K], axis=1).astype(np.int32)
+    assert bench.route_check(idx, S) == 0 == check_selection(idx, S)[0]
+    bad = idx.copy()
+    # a clearly lower block swapped in; an unsorted row; a duplicated entry
+    for r, how in ((3, "swap"), (50, "order"), (120, "dup")):
+        if how == "swap":
+            worst = int(np.argmin(S[r]))
+            bad[r] = np.sort(np.r_[bad[r, 1:], worst])
+        elif how == "order":
+            bad[r] = bad[r, ::-1]
+        else:
+            bad[r, 1] = bad[r, 0]
+    assert bench.route_check(bad, S) == 3
+    assert check_selection(bad, S)[0] == 3
