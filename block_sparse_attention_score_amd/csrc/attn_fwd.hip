@@ -25,11 +25,24 @@
 //    K rows of each 32-key group are loaded in the order pi (bits 2 and 3 of the row index swapped):
 //    then the S^T accumulator of lane (i, h) holds, for query i, exactly the keys whose values form
 //    one contiguous 16-byte chunk of a V^T row, so P feeds O^T += V^T P^T straight from registers.
-//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: each lane holds one query's logits, so the row max
-//    and sum need one exchange between the wave's halves (a v_permlane32_swap for the max, once per
-//    tile; the sum once at the end).  The running max is only raised when a tile's max exceeds
-//    it by more than 8 (log2 units); otherwise the accumulator is not rescaled.  Probabilities are
-//    then bounded by 2^8, and the result is unchanged because O and the normaliser share the max.
+//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: each lane holds one query's logits, so the row sum
+//    needs one exchange between the wave's halves at the end.
+//  * Softmax offset (FIXED pass).  A softmax is unchanged by the constant it subtracts before the
+//    exponential; the running maximum of the online formulation is one choice, and a fixed value
+//    known before the first tile is another (the "unified max value" of FlashDecoding++, Hong et
+//    al., 2023).  Here it is a Cauchy-Schwarz bound: with q' = q * scale * log2(e) rounded to bf16
+//    (the pre-scaled query the score product uses), every logit is at most
+//    U = max(|q'| * kx, |q'| * kc + bc), kx the largest exact-key norm and kc, bc the largest
+//    pseudo-key norm and additive term of the (batch, head).  The score accumulator starts at -U, so
+//    an exact tile's probability is exp2 of the accumulator with no further arithmetic, and no
+//    row maximum, exchange or rescaling runs per tile.  The bound only costs precision when the
+//    row's largest logit lies far below it: a row whose normaliser comes out below 2^-64 (its
+//    largest probability below 2^-64) marks its query tile, and the exact pass recomputes it.
+//  * Exact pass (not FIXED).  The online formulation, run only on the marked query tiles: the
+//    running max is raised when a tile's max exceeds it by more than 8 (log2 units); otherwise the
+//    accumulator is not rescaled.  Probabilities are then bounded by 2^8, and the result is
+//    unchanged because O and the normaliser share the max (one v_permlane32_swap per tile takes the
+//    max across the wave's halves).
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -107,15 +120,14 @@ __device__ __forceinline__ void issue_half(RS rs, uint32_t tile_byte,
 
 // S^T = K_tile Q^T for two chunks of 32 keys x this wave's 32 queries.  kboff[ds]: byte offset of
 // lane (i32, h)'s A operand in row i32 of the tile for k step ds (row 32 + i32 is 64*D bytes further).
+// The accumulators start at `init` (zero, or -U on the fixed-offset pass).
 template <int D>
 __device__ __forceinline__ void scores(const __bf16* Kl, const uint32_t (&kboff)[D / 16],
-                                       const bf16x8 (&qreg)[D / 16], f32x16 (&st)[2]) {
+                                       const bf16x8 (&qreg)[D / 16], const f32x16& init, f32x16 (&st)[2]) {
     const char* Kb = reinterpret_cast<const char*>(Kl);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-        f32x16 a16;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) a16[r] = 0.f;
+        f32x16 a16 = init;
 #pragma unroll
         for (int ds = 0; ds < D / 16; ++ds) {
             const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + c * 64 * D + kboff[ds]);
@@ -127,9 +139,12 @@ __device__ __forceinline__ void scores(const __bf16* Kl, const uint32_t (&kboff)
 
 template <int V> using IC = std::integral_constant<int, V>;
 
-template <typename T, int D, int BLK>
+// FIXED: the fixed-offset pass (writes flags[] for every query tile); otherwise the exact pass,
+// which runs only the query tiles whose flag is set.
+template <typename T, int D, int BLK, bool FIXED>
 __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     const T* __restrict__ Q, const __bf16* __restrict__ packed, const float* __restrict__ bias2,
+    const float4* __restrict__ bnd, int32_t* __restrict__ flags,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ counts, const int32_t* __restrict__ perm,
     T* __restrict__ O, float* __restrict__ lse, int N, int Nv, int M, int Mk, int nsh, int Ksel, int kstride, int SQ,
     int BH, int C,
@@ -157,14 +172,15 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     // its own contiguous run of C query blocks of the same head while all XCDs stay on one head:
     // neighbouring query blocks select mostly the same key blocks, so concurrent workgroups of one
     // XCD share tiles in its L2, and one head's tiles are the working set of the whole chip.
-    int bh, qrow0, nq, ntiles;
+    int bh, qrow0, nq, ntiles, qt;  // qt: query tile within the (batch, head): sink tiles, then video blocks
     bool dense;
     {
         const int wg = blockIdx.x;
         if (wg < BH * SQ) {
             dense = true;
             bh = wg / SQ;
-            qrow0 = Nv + (wg % SQ) * BLK;
+            qt = wg % SQ;
+            qrow0 = Nv + qt * BLK;
             nq = min(BLK, N - qrow0);
             ntiles = Tv + Ts;
         } else {
@@ -174,6 +190,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
             bh = slot / C;
             const int I = xcd * C + slot % C;
             if (I >= M) return;  // padding slot (uniform for the workgroup, before any barrier)
+            qt = SQ + I;
             qrow0 = I * BLK;
             nq = min(BLK, Nv - qrow0);
             // a variable route (counts given) lists counts[I] blocks in a row of kstride entries
@@ -181,6 +198,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
             ntiles = (Ksel << nsh) + Ts + Tc;
         }
     }
+    int32_t* const flag = flags + (size_t)bh * (SQ + M) + qt;
+    if (!FIXED && *flag == 0) return;  // left to the fixed-offset pass (uniform, before any barrier)
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int i32 = lane & 31, h = lane >> 5;
     const int Tall = Tv + Ts + Tc;
@@ -253,17 +272,45 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     }
 
     // Q rows of this wave as the B operand of S^T = K Q^T: lane (i32, h) holds row w*32 + i32,
-    // dims ds*16 + 8h .. +8 for each 16-wide k step ds.
+    // dims ds*16 + 8h .. +8 for each 16-wide k step ds.  On the fixed-offset pass the row is scaled
+    // into log2 units first (q * scale * log2 e, rounded to bf16), and its norm gives the offset U.
     bf16x8 qreg[D / 16];
+    f32x16 sinit;  // start value of every score accumulator: 0, or -U on the fixed-offset pass
+    float U = 0.f;
     {
         const int qr = w * 32 + i32;
         const T* src = Q + ((size_t)bh * N + qrow0 + qr) * D;
+        float ss = 0.f;
 #pragma unroll
         for (int ds = 0; ds < D / 16; ++ds) {
             u32x4 u = {0u, 0u, 0u, 0u};
-            if (qr < nq) u = load8_as_bf16<T>(src + ds * 16 + 8 * h);
+            if (qr < nq) {
+                if constexpr (FIXED) {
+                    float v[8];
+                    In<T>::load8(src + ds * 16 + 8 * h, v);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) v[j] *= c_log2;
+                    u = pack8_bf16(v);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float lo = bf16_bits_to_f32(u[j] & 0xffffu), hi = bf16_bits_to_f32(u[j] >> 16);
+                        ss = fmaf(lo, lo, ss);
+                        ss = fmaf(hi, hi, ss);
+                    }
+                } else {
+                    u = load8_as_bf16<T>(src + ds * 16 + 8 * h);
+                }
+            }
             qreg[ds] = __builtin_bit_cast(bf16x8, u);
         }
+        if constexpr (FIXED) {
+            const float qn = sqrtf(ss + __shfl_xor(ss, 32));  // the row's other half is in lane i32 + 32
+            const float4 bd = bnd[bh];
+            U = qn * bd.x;
+            if (!dense) U = fmaxf(U, fmaf(qn, bd.y, bd.z));
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sinit[r] = -U;
     }
 
     // LDS byte offsets of this lane's MFMA operands: K rows (S^T) and V^T rows (O^T), XOR-swizzled.
@@ -289,7 +336,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // K(0), K(1), V(0) and the route bits are in LDS
     f32x16 sc[2][2];  // scores of tile t live in sc[t % 2]
-    scores<D>(kbuf(IC<0>{}), kboff, qreg, sc[0]);
+    scores<D>(kbuf(IC<0>{}), kboff, qreg, sinit, sc[0]);
     bool clean_t = clean_of(tile_of(0)), clean_v = ntiles > 1 && clean_of(tl_v);  // tiles t and t+1
 
     // One pipeline step on stage parity P = t % 2.  MASKED: tile t is a compressed tile, whose
@@ -307,55 +354,77 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
         clean_t = clean_v;
         clean_v = t + 2 < ntiles && clean_of(tl_k);
         tl_v = tl_k;
-        scores<D>(kbuf(IC<P ^ 1>{}), kboff, qreg, sc[P ^ 1]);  // tile t+1 (unused after the last)
+        scores<D>(kbuf(IC<P ^ 1>{}), kboff, qreg, sinit, sc[P ^ 1]);  // tile t+1 (unused after the last)
 
         // ---- probabilities of tile t.  Register 4g+j of chunk c holds key c*32 + 16(g/2) + 8h + 4(g%2) + j.
-        // Exponent of key j: x_j * cc - m with x the raw score (cc = scale*log2 e) on a tile without
-        // an additive term, else x = raw*scale*log2 e + bias (cc = 1).
         f32x16 (&st)[2] = sc[P];
-        float mx = -INFINITY, cc;
-        if (clean) {
+        float cc = 1.f, neg_m = 0.f;  // exponent of key j: x_j * cc + neg_m
+        if constexpr (FIXED) {
+            // x = q'.k - U (the accumulator), plus the additive term on tiles that carry one
+            if (!clean) {
+                const int cbase = (t - first_cmp) * kTK;  // first pseudo-key of a compressed tile
+                const float* lb = lbias(IC<P>{});
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
+                for (int c = 0; c < 2; ++c)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[c][r]);
-            mx = half_max(mx) * c_log2;  // scale > 0: the max commutes with it
-            cc = c_log2;
+                    for (int g = 0; g < 4; ++g) {
+                        const int key = c * 32 + 16 * (g >> 1) + 8 * h + 4 * (g & 1);
+                        f32x4 bb = *reinterpret_cast<const f32x4*>(lb + key);
+                        if constexpr (MASKED) {
+                            const uint32_t selw_ = sel_bits[(cbase + key) >> 5] >> ((cbase + key) & 31);
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) bb[j] = ((selw_ >> j) & 1u) ? -INFINITY : bb[j];
+                        }
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) st[c][4 * g + j] += bb[j];
+                    }
+            }
         } else {
-            const int cbase = (t - first_cmp) * kTK;  // first pseudo-key of a compressed tile
-            const float* lb = lbias(IC<P>{});
+            // Exponent: x_j * cc - m with x the raw score (cc = scale*log2 e) on a tile without an
+            // additive term, else x = raw*scale*log2 e + bias (cc = 1).
+            float mx = -INFINITY;
+            if (clean) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
+                for (int c = 0; c < 2; ++c)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int key = c * 32 + 16 * (g >> 1) + 8 * h + 4 * (g & 1);
-                    f32x4 bb = *reinterpret_cast<const f32x4*>(lb + key);
-                    if constexpr (MASKED) {
-                        const uint32_t selw_ = sel_bits[(cbase + key) >> 5] >> ((cbase + key) & 31);
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[c][r]);
+                mx = half_max(mx) * c_log2;  // scale > 0: the max commutes with it
+                cc = c_log2;
+            } else {
+                const int cbase = (t - first_cmp) * kTK;  // first pseudo-key of a compressed tile
+                const float* lb = lbias(IC<P>{});
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) bb[j] = ((selw_ >> j) & 1u) ? -INFINITY : bb[j];
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int key = c * 32 + 16 * (g >> 1) + 8 * h + 4 * (g & 1);
+                        f32x4 bb = *reinterpret_cast<const f32x4*>(lb + key);
+                        if constexpr (MASKED) {
+                            const uint32_t selw_ = sel_bits[(cbase + key) >> 5] >> ((cbase + key) & 31);
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) bb[j] = ((selw_ >> j) & 1u) ? -INFINITY : bb[j];
+                        }
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            st[c][4 * g + j] = fmaf(st[c][4 * g + j], c_log2, bb[j]);
+                            mx = fmaxf(mx, st[c][4 * g + j]);
+                        }
                     }
+                mx = half_max(mx);
+            }
+            const bool raise = mx > m_run + kRescaleSlack;
+            if (__ballot(raise)) {
+                const float m_new = raise ? mx : m_run;
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+                l_run *= alpha;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        st[c][4 * g + j] = fmaf(st[c][4 * g + j], c_log2, bb[j]);
-                        mx = fmaxf(mx, st[c][4 * g + j]);
-                    }
-                }
-            mx = half_max(mx);
-            cc = 1.f;
+                for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+                m_run = m_new;
+            }
+            neg_m = m_run == -INFINITY ? 0.f : -m_run;
         }
-        const bool raise = mx > m_run + kRescaleSlack;
-        if (__ballot(raise)) {
-            const float m_new = raise ? mx : m_run;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-            m_run = m_new;
-        }
-        const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
         // P in bf16, 16 keys per PV step: lane (i32, h) supplies keys 16kt + 8h + e (e = 0..7).
         // The normaliser sums the same bf16 values the PV product uses.
         const char* Vb = reinterpret_cast<const char*>(vbuf(IC<P>{}));
@@ -367,7 +436,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
             bf16x8 pk;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                pk[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[kt >> 1][8 * (kt & 1) + e], cc, neg_m));
+                pk[e] = (__bf16)__builtin_amdgcn_exp2f(FIXED ? st[kt >> 1][8 * (kt & 1) + e]
+                                                             : fmaf(st[kt >> 1][8 * (kt & 1) + e], cc, neg_m));
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
                 const bf16x2 pr = {pk[e], pk[e + 1]};
@@ -406,6 +476,14 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = 1.f / l_tot;
     const int qr = w * 32 + i32;
+    if constexpr (FIXED) {
+        // the offset U lay too far above this row's logits: the exact pass redoes the query tile
+        // (written for every tile on every call, so the flags need no clearing)
+        const int under = __syncthreads_or(qr < nq && !(l_tot >= 0x1p-64f));
+        if (threadIdx.x == 0) *flag = under;
+        if (under) return;
+        m_run = U;
+    }
     if (qr < nq) {
         const int row = qrow0 + qr;
         const int orow = (!dense && perm) ? perm[(size_t)bh * Nv + row] : row;
@@ -436,14 +514,22 @@ template <typename T, int D, int BLK>
 static void launch_attend_t(const LaunchCtx& L, const void* Q, const void* packed, const int32_t* idx,
                             const int32_t* counts, const int32_t* perm, void* O, float* lse) {
     const PackGeom g = pack_geom(L);
-    const int SQ = (L.n_sink + BLK - 1) / BLK;
+    const int SQ = g.SQ;
     const int C = (L.M + 7) / 8;  // query blocks per XCD per head
     const dim3 grid(L.BH * SQ + L.BH * 8 * C);
     const float c_log2 = L.scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, BLK>), grid, dim3(BLK * 2), 0, L.stream, (const T*)Q,
-                       (const __bf16*)packed, (const float*)((const char*)packed + g.bias_off), idx, counts, perm,
-                       (T*)O, lse, L.N, L.Nv, L.M, L.Mk, L.block_k == 128 ? 1 : 0, L.K, counts ? L.Mk : L.K, SQ,
-                       L.BH, C, g.Tv, g.Ts, g.Tc, c_log2);
+    const char* pk = (const char*)packed;
+    const float* b2 = (const float*)(pk + g.bias_off);
+    const float4* bnd = (const float4*)(pk + g.bnd_off);
+    int32_t* flags = (int32_t*)(pk + g.flag_off);  // workspace the library owns inside the packed buffer
+    const int nsh = L.block_k == 128 ? 1 : 0, kstride = counts ? L.Mk : L.K;
+    // fixed-offset pass over every query tile, then the exact pass over the tiles it marked
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, BLK, true>), grid, dim3(BLK * 2), 0, L.stream, (const T*)Q,
+                       (const __bf16*)packed, b2, bnd, flags, idx, counts, perm, (T*)O, lse, L.N, L.Nv, L.M, L.Mk,
+                       nsh, L.K, kstride, SQ, L.BH, C, g.Tv, g.Ts, g.Tc, c_log2);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, BLK, false>), grid, dim3(BLK * 2), 0, L.stream, (const T*)Q,
+                       (const __bf16*)packed, b2, bnd, flags, idx, counts, perm, (T*)O, lse, L.N, L.Nv, L.M, L.Mk,
+                       nsh, L.K, kstride, SQ, L.BH, C, g.Tv, g.Ts, g.Tc, c_log2);
 }
 
 void launch_attend(const LaunchCtx& L, const void* Q, const void* packed, const int32_t* idx, const int32_t* counts,

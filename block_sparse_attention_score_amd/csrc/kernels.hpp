@@ -34,9 +34,13 @@ void launch_select_tau(const LaunchCtx& L, float tau, const float* q_mean, const
 // Packed 64-key tiles read by the attention kernel (layout in pack.hip).
 struct PackGeom {
     int Tv, Ts, Tc, Tall;  // video, sink, compressed and total tiles per (batch, head)
+    int SQ, NQT;           // sink-query tiles (of `block` rows) and all query tiles (SQ + M) per (batch, head)
     size_t tile_elems;     // bf16 elements per tile (K rows + V^T)
     size_t kv_bytes;       // all tiles of all heads
     size_t bias_off;       // byte offset of the fp32 bias rows [BH][Tall][64]
+    size_t tmax_off;       // per tile {max |k|^2, max additive term} over its valid keys, float2 [BH][Tall]
+    size_t bnd_off;        // per head {max |k| exact keys, max |k| pseudo-keys, max pseudo-key term, 0}, float4 [BH]
+    size_t flag_off;       // per query tile: 1 when the fixed-offset pass left it to the exact pass, int32 [BH][NQT]
     size_t bytes;          // total
 };
 PackGeom pack_geom(const LaunchCtx& L);
@@ -53,6 +57,8 @@ void launch_pool_fp8_scales(const LaunchCtx& L, const void* Q, const void* K, co
 // the sink tiles and the compressed tiles only
 void launch_pack_rest(const LaunchCtx& L, const void* K, const void* V, const float* k_sum, const float* v_sum,
                       const float* bias, void* packed);
+// the per-head logit-bound constants from the per-tile maxima (after every tile is written)
+void launch_bounds(const LaunchCtx& L, void* packed);
 
 // idx [B,H,M,K] with counts == NULL, or a variable route: idx [B,H,M,M] with counts [B,H,M]
 void launch_attend(const LaunchCtx& L, const void* Q, const void* packed, const int32_t* idx,

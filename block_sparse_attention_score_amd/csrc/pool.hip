@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, c
                                                       int M, float scale, float* __restrict__ k_mean,
                                                       float* __restrict__ k_sum, float* __restrict__ v_sum,
                                                       float* __restrict__ bias, __bf16* __restrict__ packed,
-                                                      float* __restrict__ bias2, int Tall,
+                                                      float* __restrict__ bias2, float2* __restrict__ tmax, int Tall,
                                                       uint32_t* __restrict__ amax) {
     constexpr bool PACK = MODE == 1;
     using G = PoolGeom<D>;
@@ -155,12 +155,17 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, c
         }
     }
 
-    // packed tiles of this key block: K rows straight from the registers, V rows into LDS
+    // packed tiles of this key block: K rows straight from the registers, V rows into LDS; per tile
+    // the largest squared norm of its keys as stored (bf16), for the attention stage's logit bound
     constexpr int TPB = BLK / 64;  // tiles per key block
     __shared__ __attribute__((aligned(16))) __bf16 vs[PACK ? BLK : 1][D + 8];
+    __shared__ float tn2[PACK ? 4 : 1][TPB];
     const size_t tile0 = (size_t)bh * Tall + (size_t)J * TPB;
     if constexpr (PACK) {
         const u32x4 zero = {0u, 0u, 0u, 0u};
+        float n2[TPB];
+#pragma unroll
+        for (int tt = 0; tt < TPB; ++tt) n2[tt] = 0.f;
 #pragma unroll
         for (int k = 0; k < RPT; ++k) {
             const int r = rg + k * G::RG;
@@ -177,7 +182,24 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, c
                 }
                 *reinterpret_cast<u32x4*>(packed + (tile0 + (r >> 6)) * (2 * 64 * D) + (r & 63) * D + c * 8) = kb;
                 *reinterpret_cast<u32x4*>(&vs[r][c * 8]) = vb;
+                float s2 = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float lo = bf16_bits_to_f32(kb[j] & 0xffffu), hi = bf16_bits_to_f32(kb[j] >> 16);
+                    s2 = fmaf(lo, lo, s2);
+                    s2 = fmaf(hi, hi, s2);
+                }
+                // the CH threads of a row are consecutive lanes of one wave
+#pragma unroll
+                for (int o = 1; o < G::CH; o <<= 1) s2 += __shfl_xor(s2, o);
+                // RG divides 64, so the tile of row rg + k*RG depends on k alone
+                n2[(k * G::RG) >> 6] = fmaxf(n2[(k * G::RG) >> 6], s2);
             }
+        }
+#pragma unroll
+        for (int tt = 0; tt < TPB; ++tt) {
+            const float v = wave_max(n2[tt]);
+            if ((threadIdx.x & 63) == 0) tn2[threadIdx.x >> 6][tt] = v;
         }
     }
 
@@ -302,6 +324,9 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, c
                 *reinterpret_cast<u32x4*>(vdst + dr * 64 + kc * 8) = o;
             }
             if (threadIdx.x < 64) bias2[(tile0 + tt) * 64 + threadIdx.x] = tt * 64 + (int)threadIdx.x < n ? 0.f : -INFINITY;
+            if (threadIdx.x == 0)
+                tmax[tile0 + tt] = make_float2(fmaxf(fmaxf(tn2[0][tt], tn2[1][tt]), fmaxf(tn2[2][tt], tn2[3][tt])),
+                                               tt * 64 < n ? 0.f : -INFINITY);
         }
     }
 }
@@ -327,21 +352,23 @@ static void launch_pool_kv_t(const LaunchCtx& L, const void* K, const void* V, c
     const dim3 grid(L.BH * L.Mk);
     __bf16* kv = nullptr;
     float* b2 = nullptr;
+    float2* tm = nullptr;
     int Tall = 0;
     if (MODE == 1) {
         const PackGeom g = pack_geom(L);
         kv = (__bf16*)packed;
         b2 = (float*)((char*)packed + g.bias_off);
+        tm = (float2*)((char*)packed + g.tmax_off);
         Tall = g.Tall;
     }
     if (L.pool_mode == SPARK_ATTN_POOL_REWEIGHT)
         hipLaunchKernelGGL((pool_kv_kernel<T, D, BLK, true, MODE>), grid, dim3(256), 0, L.stream, (const T*)K,
-                           (const T*)V, anchor, L.N, L.Nv, L.Mk, L.scale, k_mean, k_sum, v_sum, bias, kv, b2, Tall,
-                           amax);
+                           (const T*)V, anchor, L.N, L.Nv, L.Mk, L.scale, k_mean, k_sum, v_sum, bias, kv, b2, tm,
+                           Tall, amax);
     else
         hipLaunchKernelGGL((pool_kv_kernel<T, D, BLK, false, MODE>), grid, dim3(256), 0, L.stream, (const T*)K,
-                           (const T*)V, anchor, L.N, L.Nv, L.Mk, L.scale, k_mean, k_sum, v_sum, bias, kv, b2, Tall,
-                           amax);
+                           (const T*)V, anchor, L.N, L.Nv, L.Mk, L.scale, k_mean, k_sum, v_sum, bias, kv, b2, tm,
+                           Tall, amax);
 }
 
 template <typename T, int D>

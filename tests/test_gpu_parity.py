@@ -479,3 +479,25 @@ def test_forward_is_deterministic_at_scale():
         runs.append([t.clone() for t in (*a, *b, *c)])
     for x, y in zip(*runs):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("kind", ["every-tile", "mixed"])
+def test_fixed_offset_exact_pass(orc, kind):
+    """The attention stage subtracts a per-query Cauchy-Schwarz bound on the logits instead of a
+    running maximum, and recomputes with the running maximum every query tile in which a row's
+    normaliser falls below 2^-64 (its largest logit more than 64 log2 units under the bound).  A
+    sink key of norm 100 along a dimension every query has zeroed puts the bound ~140 log2 units
+    above every real logit, so without the exact pass each row's normaliser would underflow and O
+    would not be finite.  'mixed': the queries of even video blocks are scaled by 2^-6 (exact in
+    bf16), which keeps their bound close, so both passes write parts of one output."""
+    B, H, nv, ns, d, b, r = 1, 2, 6 * 128 + 37, 9, 128, 128, 0.2
+    Q, K, V = W.gaussian_qkv(B, H, nv, ns, d, seed=77, dtype="bf16")
+    Q[..., 0] = 0.0
+    K[:, :, nv + 3, :] = 0.0
+    K[:, :, nv + 3, 0] = 100.0
+    if kind == "mixed":
+        for I in range(0, -(-nv // b), 2):
+            Q[:, :, I * b:min(nv, (I + 1) * b)] *= np.float32(2.0 ** -6)
+    note(f"fixed-offset exact pass {kind}")
+    Og, _ = forward_check(orc, Q, K, V, ns, b, r, 1, "bf16")
+    assert np.isfinite(Og).all()
