@@ -74,3 +74,37 @@ def test_route_check_agrees_with_the_per_row_rule():
             bad[r, 1] = bad[r, 0]
     assert bench.route_check(bad, S) == 3
     assert check_selection(bad, S)[0] == 3
+
+
+def test_cpu_leg_checks_routes_and_sampled_rows(orc):
+    """The benchmark's CPU leg accepts rows equal to the oracle's and a route equal to its top-K,
+    and rejects a route with a demoted block or a sampled row off by more than the bounds (the
+    GPU rows are stood in for by the oracle's own, so this runs on the CPU)."""
+    import workloads as W
+
+    wl = W.WORKLOADS["tiny"]
+    Q, K, V = W.make_qkv(wl)
+    p = orc.params(Q, wl.n_sink, wl.block, 0.1, 1)
+    pooled = orc.pool(p, Q, K, V)
+    idx = orc.select(p, orc.scores(p, pooled["q_mean"], pooled["k_mean"]))
+    M = idx.shape[2]
+    qb, sq = bench.cpu_sample(wl, M, 5)
+    assert len(sq) == 0 and qb.shape == (5, 2)  # no sink rows in this workload
+    O, L = orc.attend_blocks(p, Q, K, V, pooled, idx, qb)
+    rows = bench.sample_rows(wl, M, qb)
+    G = np.concatenate([O[n, :len(r)] for n, r in enumerate(rows)])
+    GL = np.concatenate([L[n, :len(r)] for n, r in enumerate(rows)])
+    _, chk = bench.cpu_baseline(wl, 0.1, Q, K, V, idx, 1.0, qb, sq, (G, GL), single_core_blocks=1)
+    assert chk["ok"] and chk["route_rows_violating_near_tie_rule"] == 0 and chk["rel_l2"] == 0.0
+    G2 = G.copy()
+    G2[3, 7] += 0.05  # beyond the max-abs bound
+    _, chk = bench.cpu_baseline(wl, 0.1, Q, K, V, idx, 1.0, qb, sq, (G2, GL), single_core_blocks=1)
+    assert not chk["ok"] and chk["max_abs"] > bench.FWD_MAX_ABS
+    bad_idx = idx.copy()  # replace the top-scoring block of one row by the lowest-scoring one
+    S = orc.scores(p, pooled["q_mean"], pooled["k_mean"])
+    row = S[0, 1, 3]
+    top, low = int(np.argmax(row)), int(np.argmin(row))
+    sel = [j for j in bad_idx[0, 1, 3] if j != top] + [low]
+    bad_idx[0, 1, 3] = np.sort(sel)
+    _, chk = bench.cpu_baseline(wl, 0.1, Q, K, V, bad_idx, 1.0, qb, sq, (G, GL), single_core_blocks=1)
+    assert not chk["ok"] and chk["route_rows_violating_near_tie_rule"] == 1
