@@ -378,9 +378,13 @@ def select(q_mean, k_mean, Q, n_sink, block, topk_ratio, with_scores=False, scal
     K = topk_count(Mk, topk_ratio)
     B, H = q_mean.shape[:2]
     idx = torch.empty(B, H, M, K, device=q_mean.device, dtype=torch.int32)
-    S = torch.empty(B, H, M, Mk, device=q_mean.device, dtype=torch.float32)
-    spark_attn_select(p, q_mean, k_mean, idx, S, None, stream)
-    return (idx, S) if with_scores else idx
+    if with_scores:
+        S = torch.empty(B, H, M, Mk, device=q_mean.device, dtype=torch.float32)
+        spark_attn_select(p, q_mean, k_mean, idx, S, None, stream)
+        return idx, S
+    ws = torch.empty(workspace_size(p, 3), device=q_mean.device, dtype=torch.uint8)
+    spark_attn_select(p, q_mean, k_mean, idx, None, ws, stream)
+    return idx
 
 
 def pack(K, V, pooled, n_sink, block, scale=0.0, stream=None, block_k=0):

@@ -21,7 +21,7 @@ void launch_pool(const LaunchCtx& L, const void* Q, const void* K, const void* V
 void launch_pool_pack(const LaunchCtx& L, const void* Q, const void* K, const void* V, float* q_mean,
                       float* k_mean, float* k_sum, float* v_sum, float* bias, float* anchor, void* packed);
 
-// Select writes the full score matrix S [BH, M, M] (fp32) to `scores`, then the route.
+// Select writes the full score matrix S [BH, M, M_k] (fp32) to `scores`, then the route.
 size_t select_workspace_bytes(const LaunchCtx& L);
 void launch_select(const LaunchCtx& L, const float* q_mean, const float* k_mean, int32_t* idx,
                    float* scores);

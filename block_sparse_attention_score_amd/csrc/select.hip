@@ -9,9 +9,9 @@
 //     them, so no bf16 rounding is allowed here.
 //  2. topk_rows: one wave per score row.  The row's scores live in registers as order-preserving
 //     integer keys (KPL per lane); the K-th largest key is found bit by bit from the top, counting
-//     keys >= candidate with wave ballots and popcounts; ties at the threshold go to the lower
-//     block index; the chosen blocks are written in ascending order by a ballot/popcount
-//     compaction.  Deterministic, no atomics.
+//     keys >= candidate with wave ballots and popcounts, and stops early once exactly K keys lie
+//     above the candidate; ties at the threshold go to the lower block index; the chosen blocks
+//     are written in ascending order by a ballot/popcount compaction.  Deterministic, no atomics.
 #include "kernels.hpp"
 
 namespace spark {
@@ -76,6 +76,80 @@ __device__ __forceinline__ uint32_t score_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The K largest of each of R rows held as keys in registers (lane l: block l + 64 j for j < chunks,
+// padding key 0), written to out[q][0 .. K) in ascending block order (rows with a null out are
+// skipped).  The K-th largest key T of a row is found bit by bit from the top: T takes the bit when
+// at least K keys are >= T with it (counted with wave ballots and popcounts).  When exactly K keys
+// are >= that candidate, they are the K largest, so T is their minimum and the search stops there
+// (about half the passes on continuous scores).  Ties at T go to the lower block index.  The R
+// rows' searches run interleaved (independent chains).
+template <int KPL, int R>
+__device__ __forceinline__ void topk_of_rows(const uint32_t (&key)[R][KPL], int chunks, int K,
+                                             int32_t* const (&out)[R]) {
+    const int lane = threadIdx.x & 63;
+    uint32_t T[R];
+    bool done[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        T[q] = 0;
+        done[q] = out[q] == nullptr;
+    }
+    for (int bit = 31; bit >= 0; --bit) {
+        bool all = true;
+#pragma unroll
+        for (int q = 0; q < R; ++q) all = all && done[q];
+        if (all) break;
+        int cnt[R];
+#pragma unroll
+        for (int q = 0; q < R; ++q) cnt[q] = 0;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j)
+            if (j < chunks)
+#pragma unroll
+                for (int q = 0; q < R; ++q)
+                    if (!done[q]) cnt[q] += __popcll(__ballot(key[q][j] >= (T[q] | (1u << bit))));
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            if (done[q] || cnt[q] < K) continue;
+            T[q] |= 1u << bit;
+            if (cnt[q] == K) {  // exactly the K largest are >= T: the K-th largest is their minimum
+                uint32_t m = 0xffffffffu;
+#pragma unroll
+                for (int j = 0; j < KPL; ++j)
+                    if (j < chunks && key[q][j] >= T[q]) m = min(m, key[q][j]);
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) m = min(m, (uint32_t)__shfl_xor((int)m, o));
+                T[q] = m;
+                done[q] = true;
+            }
+        }
+    }
+    const uint64_t below = lanemask_lt();
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        if (!out[q]) continue;
+        int gt = 0;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j)
+            if (j < chunks) gt += __popcll(__ballot(key[q][j] > T[q]));
+        const int need = K - gt;  // keys equal to T still to take, lowest block index first
+        int pos = 0, eq_seen = 0;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+            if (j < chunks) {
+                const uint32_t kk = key[q][j];
+                const uint64_t eqb = __ballot(kk == T[q]);
+                const int eq_rank = eq_seen + __popcll(eqb & below);
+                const bool sel = kk > T[q] || (kk == T[q] && eq_rank < need);
+                const uint64_t sb = __ballot(sel);
+                if (sel) out[q][pos + __popcll(sb & below)] = lane + 64 * j;
+                pos += __popcll(sb);
+                eq_seen += __popcll(eqb);
+            }
+        }
+    }
+}
+
 // KPL > 0: the row is held in KPL registers per lane (M <= 64 * KPL).  KPL == 0: the row is
 // re-read from memory on every pass (any M).
 template <int KPL>
@@ -85,48 +159,48 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict_
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
     const float* Sr = S + (size_t)row * M;
-    constexpr int NREG = KPL > 0 ? KPL : 1;
-    uint32_t key[NREG];
-    if (KPL > 0) {
+    int32_t* const out[1] = {idx + (size_t)row * K};
+    if constexpr (KPL > 0) {
         // every load is unconditional (from a clamped column) so that all of them are in flight
         // together; columns past the row end are then replaced by the padding key
-        float f[NREG];
+        float f[KPL];
 #pragma unroll
-        for (int j = 0; j < NREG; ++j) f[j] = Sr[min(lane + 64 * j, M - 1)];
+        for (int j = 0; j < KPL; ++j) f[j] = Sr[min(lane + 64 * j, M - 1)];
+        uint32_t key[1][KPL];
 #pragma unroll
-        for (int j = 0; j < NREG; ++j) key[j] = lane + 64 * j < M ? score_key(f[j]) : 0u;
-    }
-    auto key_at = [&](int j) -> uint32_t {  // key of block lane + 64 j
-        if (KPL > 0) return key[j];
-        const int J = lane + 64 * j;
-        return J < M ? score_key(Sr[J]) : 0u;
-    };
-    const int chunks = KPL > 0 ? KPL : (M + 63) / 64;
-
-    // largest T with #{J : key_J >= T} >= K, i.e. the K-th largest key
-    uint32_t T = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = T | (1u << bit);
-        int cnt = 0;
-        for (int j = 0; j < chunks; ++j) cnt += __popcll(__ballot(key_at(j) >= cand));
-        if (cnt >= K) T = cand;
-    }
-    int gt = 0;
-    for (int j = 0; j < chunks; ++j) gt += __popcll(__ballot(key_at(j) > T));
-    const int need = K - gt;  // keys equal to T still to take, lowest block index first
-
-    const uint64_t below = lanemask_lt();
-    int32_t* out = idx + (size_t)row * K;
-    int pos = 0, eq_seen = 0;
-    for (int j = 0; j < chunks; ++j) {
-        const uint32_t kk = key_at(j);
-        const uint64_t eqb = __ballot(kk == T);
-        const int eq_rank = eq_seen + __popcll(eqb & below);
-        const bool sel = kk > T || (kk == T && eq_rank < need);
-        const uint64_t sb = __ballot(sel);
-        if (sel) out[pos + __popcll(sb & below)] = lane + 64 * j;
-        pos += __popcll(sb);
-        eq_seen += __popcll(eqb);
+        for (int j = 0; j < KPL; ++j) key[0][j] = lane + 64 * j < M ? score_key(f[j]) : 0u;
+        topk_of_rows<KPL, 1>(key, KPL, K, out);
+        return;
+    } else {
+        // the row is re-read from memory on every pass (any M)
+        auto key_at = [&](int j) -> uint32_t {  // key of block lane + 64 j
+            const int J = lane + 64 * j;
+            return J < M ? score_key(Sr[J]) : 0u;
+        };
+        const int chunks = (M + 63) / 64;
+        // largest T with #{J : key_J >= T} >= K, i.e. the K-th largest key
+        uint32_t T = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = T | (1u << bit);
+            int cnt = 0;
+            for (int j = 0; j < chunks; ++j) cnt += __popcll(__ballot(key_at(j) >= cand));
+            if (cnt >= K) T = cand;
+        }
+        int gt = 0;
+        for (int j = 0; j < chunks; ++j) gt += __popcll(__ballot(key_at(j) > T));
+        const int need = K - gt;  // keys equal to T still to take, lowest block index first
+        const uint64_t below = lanemask_lt();
+        int pos = 0, eq_seen = 0;
+        for (int j = 0; j < chunks; ++j) {
+            const uint32_t kk = key_at(j);
+            const uint64_t eqb = __ballot(kk == T);
+            const int eq_rank = eq_seen + __popcll(eqb & below);
+            const bool sel = kk > T || (kk == T && eq_rank < need);
+            const uint64_t sb = __ballot(sel);
+            if (sel) out[0][pos + __popcll(sb & below)] = lane + 64 * j;
+            pos += __popcll(sb);
+            eq_seen += __popcll(eqb);
+        }
     }
 }
 

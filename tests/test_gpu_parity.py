@@ -501,3 +501,45 @@ def test_fixed_offset_exact_pass(orc, kind):
     note(f"fixed-offset exact pass {kind}")
     Og, _ = forward_check(orc, Q, K, V, ns, b, r, 1, "bf16")
     assert np.isfinite(Og).all()
+
+
+ROUTE_CASES = [(c[0], c[1], c[2], c[3], d) for c in TOPK_CASES for d in (64, 128)]
+
+
+@pytest.mark.parametrize("case", ROUTE_CASES, ids=[f"{c[0]}-d{c[4]}" for c in ROUTE_CASES])
+def test_select_route_against_binary64(orc, case):
+    """spark_attn_select without a score matrix requested (the score matrix in the workspace), its
+    route against binary64 scores of the same block means: exactly the lexsort top-K where the
+    scores are exact in fp32 (integer-valued means, all-zero queries), and within the near-tie rule
+    otherwise (including rows of tied key means, whose fp32 scores tie exactly too)."""
+    name, M, r, kind, d = case
+    B, H, b = 1, 2, 64
+    rng = np.random.default_rng(M + d)
+    qm = rng.standard_normal((B, H, M, d)).astype(np.float32)
+    km = rng.standard_normal((B, H, M, d)).astype(np.float32)
+    if kind == "ties":
+        km = rng.standard_normal((B, H, 5, d)).astype(np.float32)[:, :, rng.integers(0, 5, M)]
+    elif kind == "zero-q":
+        qm[:] = 0.0
+    elif kind == "few":
+        qm = rng.integers(-2, 3, (B, H, M, d)).astype(np.float32)
+        km = rng.integers(-1, 2, (B, H, M, d)).astype(np.float32)
+    Q = torch.zeros(B, H, M * b, d, device="cuda", dtype=torch.bfloat16)  # shapes only
+    note(f"select route {name} d={d}")
+    qm, km = np.ascontiguousarray(qm), np.ascontiguousarray(km)
+    idx = sa.select(torch.from_numpy(qm).cuda(), torch.from_numpy(km).cuda(), Q, 0, b, r)
+    torch.cuda.synchronize()
+    gi = host(idx)
+    S = (qm.astype(np.float64) @ np.swapaxes(km.astype(np.float64), -1, -2)) / math.sqrt(d)
+    K = gi.shape[-1]
+    assert K == sa.topk_count(M, r)
+    if kind in ("few", "zero-q"):  # every score exact in fp32
+        for bb in range(B):
+            for h in range(H):
+                for I in range(M):
+                    top = np.sort(np.lexsort((np.arange(M), -S[bb, h, I]))[:K])
+                    assert (gi[bb, h, I] == top).all(), (bb, h, I)
+    else:
+        bad, differ = check_selection(gi, S)
+        assert bad == 0
+        print(f"rows differing from the binary64 top-K (inside the near-tie window): {differ}")
