@@ -16,7 +16,9 @@ import os
 import torch  # loaded first so the library binds to the HIP runtime torch already uses
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libspark_attn.so")
+# SPARK_ATTN_LIB names another build of the library to load (the sanitizer test loads one whose
+# host code is instrumented)
+LIB_PATH = os.environ.get("SPARK_ATTN_LIB") or os.path.join(_PKG, "libspark_attn.so")
 
 BF16, FP32 = 0, 1
 POOL_MEAN, POOL_REWEIGHT = 0, 1
@@ -133,9 +135,50 @@ _ROLES = {
     "rows": (lambda g: g["N"], torch.float32),            # lse [B,H,N]
     "perm": (lambda g: g["Nv"], torch.int32),             # perm [B,H,N_v]
     "counts": (lambda g: g["M"], torch.int32),            # counts [B,H,M]
+    # the same, as inputs whose contents the kernels follow
+    "route_in": (lambda g: g["M"] * g["K"], torch.int32),
+    "route_all_in": (lambda g: g["M"] * g["Mk"], torch.int32),
+    "perm_in": (lambda g: g["Nv"], torch.int32),
+    "counts_in": (lambda g: g["M"], torch.int32),
     "stats": (lambda g: 2, torch.float32),                # (mu, sigma) [B,H,2]
     "amax": (lambda g: 3, torch.float32),                 # amax [B,H,3]
 }
+
+
+# SPARK_ATTN_CHECK=1: also check the contents of the index inputs the kernels follow (routes,
+# counts, permutations) before every launch.  This costs a device-to-host synchronisation per
+# call, so it is off by default.  The kernels themselves clamp route entries and counts to the
+# key blocks and skip output rows with a permutation entry out of range, so bad indices give
+# wrong values rather than memory faults; the check turns them into an error.
+CHECK_CONTENTS = os.environ.get("SPARK_ATTN_CHECK", "0") == "1"
+
+
+def check_contents(p, idx=None, counts=None, perm=None):
+    """Raises ValueError unless the index inputs are what the C header documents: a route
+    idx [B,H,M,K] of strictly ascending key blocks in [0, M_k) (with counts [B,H,M] in [0, M_k]:
+    a variable route, whose row I holds counts[I] such entries), and a permutation perm [B,H,N_v]
+    of row indices in [0, N_v).  Works on tensors of any device."""
+    L = lib()
+    M, Mk = L.spark_attn_num_blocks(ctypes.byref(p)), L.spark_attn_num_key_blocks(ctypes.byref(p))
+    Nv = p.N - p.n_sink
+    if perm is not None:
+        pv = perm.reshape(p.B * p.H, -1)[:, :Nv]
+        if pv.numel() and (int(pv.min()) < 0 or int(pv.max()) >= Nv):
+            raise ValueError(f"perm: entries outside [0, {Nv})")
+    if counts is not None:
+        c = counts.reshape(-1)[:p.B * p.H * M]
+        if c.numel() and (int(c.min()) < 0 or int(c.max()) > Mk):
+            raise ValueError(f"counts: entries outside [0, {Mk}]")
+    if idx is not None:
+        width = Mk if counts is not None else L.spark_attn_topk_count(Mk, p.topk_ratio)
+        rows = idx.reshape(p.B * p.H * M, -1)[:, :width].long()
+        valid = torch.ones_like(rows, dtype=torch.bool)
+        if counts is not None:
+            valid = torch.arange(width, device=rows.device)[None, :] < counts.reshape(-1)[:rows.shape[0], None].long()
+        if bool(((rows < 0) | (rows >= Mk))[valid].any()):
+            raise ValueError(f"idx: route entries outside [0, {Mk})")
+        if width > 1 and bool(((rows[:, 1:] <= rows[:, :-1]) & valid[:, 1:]).any()):
+            raise ValueError("idx: route rows not strictly ascending")
 
 
 def _validate(p, *args):
@@ -158,6 +201,12 @@ def _validate(p, *args):
             raise TypeError(f"{name}: element type {t.dtype}, expected {dtype}")
         if t.numel() < need:
             raise ValueError(f"{name}: {t.numel()} elements, expected {need}")
+    if CHECK_CONTENTS:  # index inputs the kernels follow (roles ending in _in)
+        d = {role: t for _, t, role in args if t is not None and role != "perm_in"}
+        check_contents(p, idx=d.get("route_in", d.get("route_all_in")), counts=d.get("counts_in"))
+        for _, t, role in args:
+            if t is not None and role == "perm_in":
+                check_contents(p, perm=t)
 
 
 def _stream(stream):
@@ -234,7 +283,7 @@ def spark_attn_pool_pack(p, Q, K, V, q_mean, k_mean, k_sum, v_sum, bias, anchor,
 
 
 def spark_attn_attend(p, Q, packed, idx, perm, O, lse=None, stream=None):
-    _validate(p, ("Q", Q, "tok"), ("idx", idx, "route"), ("perm", perm, "perm"), ("O", O, "tok"),
+    _validate(p, ("Q", Q, "tok"), ("idx", idx, "route_in"), ("perm", perm, "perm_in"), ("O", O, "tok"),
               ("lse", lse, "rows"))
     _check("spark_attn_attend", lib().spark_attn_attend(
         ctypes.byref(p), _ptr(Q), _ptr(packed), _nbytes(packed), _ptr(idx), _ptr(perm), _ptr(O),
@@ -242,7 +291,7 @@ def spark_attn_attend(p, Q, packed, idx, perm, O, lse=None, stream=None):
 
 
 def spark_attn_forward(p, Q, K, V, perm, O, lse, idx_out, workspace, stream=None):
-    _validate(p, ("Q", Q, "tok"), ("K", K, "tok"), ("V", V, "tok"), ("perm", perm, "perm"), ("O", O, "tok"),
+    _validate(p, ("Q", Q, "tok"), ("K", K, "tok"), ("V", V, "tok"), ("perm", perm, "perm_in"), ("O", O, "tok"),
               ("lse", lse, "rows"), ("idx_out", idx_out, "route"))
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("spark_attn_forward", lib().spark_attn_forward(
@@ -251,8 +300,8 @@ def spark_attn_forward(p, Q, K, V, perm, O, lse, idx_out, workspace, stream=None
 
 
 def spark_attn_forward_kv(p, Q, K, V, perm_q, perm_k, O, lse, idx_out, workspace, stream=None):
-    _validate(p, ("Q", Q, "tok"), ("K", K, "tok"), ("V", V, "tok"), ("perm_q", perm_q, "perm"),
-              ("perm_k", perm_k, "perm"), ("O", O, "tok"), ("lse", lse, "rows"), ("idx_out", idx_out, "route"))
+    _validate(p, ("Q", Q, "tok"), ("K", K, "tok"), ("V", V, "tok"), ("perm_q", perm_q, "perm_in"),
+              ("perm_k", perm_k, "perm_in"), ("O", O, "tok"), ("lse", lse, "rows"), ("idx_out", idx_out, "route"))
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("spark_attn_forward_kv", lib().spark_attn_forward_kv(
         ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(perm_q), _ptr(perm_k), _ptr(O), _ptr(lse),
@@ -269,8 +318,8 @@ def spark_attn_select_tau(p, tau, q_mean, k_mean, idx, counts, stats, workspace,
 
 
 def spark_attn_attend_var(p, Q, packed, idx, counts, perm, O, lse, stream=None):
-    _validate(p, ("Q", Q, "tok"), ("idx", idx, "route_all"), ("counts", counts, "counts"),
-              ("perm", perm, "perm"), ("O", O, "tok"), ("lse", lse, "rows"))
+    _validate(p, ("Q", Q, "tok"), ("idx", idx, "route_all_in"), ("counts", counts, "counts_in"),
+              ("perm", perm, "perm_in"), ("O", O, "tok"), ("lse", lse, "rows"))
     _check("spark_attn_attend_var", lib().spark_attn_attend_var(
         ctypes.byref(p), _ptr(Q), _ptr(packed), _nbytes(packed), _ptr(idx), _ptr(counts), _ptr(perm),
         _ptr(O), _ptr(lse), _stream(stream)))
@@ -309,7 +358,7 @@ def spark_attn_pack_fp8(p, K, V, k_sum, v_sum, bias, amax, packed, stream=None):
 
 
 def spark_attn_attend_fp8(p, Q, packed, idx, perm, amax, O, lse=None, stream=None):
-    _validate(p, ("Q", Q, "tok"), ("idx", idx, "route"), ("perm", perm, "perm"), ("amax", amax, "amax"),
+    _validate(p, ("Q", Q, "tok"), ("idx", idx, "route_in"), ("perm", perm, "perm_in"), ("amax", amax, "amax"),
               ("O", O, "tok"), ("lse", lse, "rows"))
     _check("spark_attn_attend_fp8", lib().spark_attn_attend_fp8(
         ctypes.byref(p), _ptr(Q), _ptr(packed), _nbytes(packed), _ptr(idx), _ptr(perm), _ptr(amax),
@@ -317,7 +366,7 @@ def spark_attn_attend_fp8(p, Q, packed, idx, perm, amax, O, lse=None, stream=Non
 
 
 def spark_attn_forward_fp8(p, Q, K, V, perm, O, lse, idx_out, amax_out, workspace, stream=None):
-    _validate(p, ("Q", Q, "tok"), ("K", K, "tok"), ("V", V, "tok"), ("perm", perm, "perm"), ("O", O, "tok"),
+    _validate(p, ("Q", Q, "tok"), ("K", K, "tok"), ("V", V, "tok"), ("perm", perm, "perm_in"), ("O", O, "tok"),
               ("lse", lse, "rows"), ("idx_out", idx_out, "route"), ("amax_out", amax_out, "amax"))
     _check("spark_attn_forward_fp8", lib().spark_attn_forward_fp8(
         ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(perm), _ptr(O), _ptr(lse), _ptr(idx_out),
@@ -333,7 +382,7 @@ def spark_attn_reblock(p, Q, K, perm, workspace, stream=None):
 
 
 def spark_attn_gather_rows(p, X, perm, Y, stream=None):
-    _validate(p, ("X", X, "tok"), ("perm", perm, "perm"), ("Y", Y, "tok"))
+    _validate(p, ("X", X, "tok"), ("perm", perm, "perm_in"), ("Y", Y, "tok"))
     _check("spark_attn_gather_rows", lib().spark_attn_gather_rows(
         ctypes.byref(p), _ptr(X), _ptr(perm), _ptr(Y), _stream(stream)))
 

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
             qrow0 = I * BLK;
             nq = min(BLK, Nv - qrow0);
             // a variable route (counts given) lists counts[I] blocks in a row of kstride entries
-            if (counts) Ksel = counts[(size_t)bh * M + I];
+            if (counts) Ksel = min(max(counts[(size_t)bh * M + I], 0), Mk);  // clamped: a bad count cannot run past the row
             ntiles = (Ksel << nsh) + Ts + Tc;
         }
     }
@@ -126,8 +126,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     // next 64 are loaded one window ahead, so moving to them never waits for memory.
     int win_base = 0, selw = 0, selw_next = 0;
     if (!dense) {
-        selw = lane < Ksel ? sel[lane] : 0;
-        selw_next = 64 + lane < Ksel ? sel[64 + lane] : 0;
+        selw = lane < Ksel ? clamp_block(sel[lane], Mk) : 0;
+        selw_next = 64 + lane < Ksel ? clamp_block(sel[64 + lane], Mk) : 0;
     }
     // packed tile of list entry t (called with increasing t): selected blocks, sinks, compressed
     auto tile_of = [&](int t) __attribute__((always_inline)) -> int {
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
         if (k >= win_base + 64) {  // k grows by at most one per call: this is the next window
             win_base += 64;
             selw = selw_next;
-            selw_next = win_base + 64 + lane < Ksel ? sel[win_base + 64 + lane] : 0;
+            selw_next = win_base + 64 + lane < Ksel ? clamp_block(sel[win_base + 64 + lane], Mk) : 0;
         }
         return (__builtin_amdgcn_readlane(selw, k - win_base) << nsh) + (t & ((1 << nsh) - 1));
     };
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
         for (int j = threadIdx.x; j < (Mk + 63) / 32 + 1; j += NT) sel_bits[j] = 0u;
         __syncthreads();
         for (int k = threadIdx.x; k < Ksel; k += NT) {
-            const int J = sel[k];
+            const int J = clamp_block(sel[k], Mk);
             atomicOr(&sel_bits[J >> 5], 1u << (J & 31));
         }
     }
@@ -386,6 +386,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     if (qr < nq) {
         const int row = qrow0 + qr;
         const int orow = (!dense && perm) ? perm[(size_t)bh * Nv + row] : row;
+        if (!dense && perm && (unsigned)orow >= (unsigned)Nv) return;  // a permutation entry out of range: row not written
         T* dst = O + ((size_t)bh * N + orow) * D;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)

@@ -319,8 +319,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
     // loaded one ahead so that moving to it never waits for memory
     int win_base = 0, selw = 0, selw_next = 0;
     if (!dense) {
-        selw = lane < Ksel ? sel[lane] : 0;
-        selw_next = 64 + lane < Ksel ? sel[64 + lane] : 0;
+        selw = lane < Ksel ? clamp_block(sel[lane], Mk) : 0;
+        selw_next = 64 + lane < Ksel ? clamp_block(sel[64 + lane], Mk) : 0;
     }
     auto tile_of = [&](int t) __attribute__((always_inline)) -> int {
         if (dense) return t;
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
         if (k >= win_base + 64) {  // k grows by at most one per call: this is the next window
             win_base += 64;
             selw = selw_next;
-            selw_next = win_base + 64 + lane < Ksel ? sel[win_base + 64 + lane] : 0;
+            selw_next = win_base + 64 + lane < Ksel ? clamp_block(sel[win_base + 64 + lane], Mk) : 0;
         }
         return (__builtin_amdgcn_readlane(selw, k - win_base) << nsh) + (t & ((1 << nsh) - 1));
     };
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
         for (int j = threadIdx.x; j < (Mk + 63) / 32 + 1; j += NT) sel_bits[j] = 0u;
         __syncthreads();
         for (int k = threadIdx.x; k < Ksel; k += NT) {
-            const int J = sel[k];
+            const int J = clamp_block(sel[k], Mk);
             atomicOr(&sel_bits[J >> 5], 1u << (J & 31));
         }
     }
@@ -532,6 +532,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
     if (qr < nq) {
         const int row = qrow0 + qr;
         const int orow = (!dense && perm) ? perm[(size_t)bh * Nv + row] : row;
+        if (!dense && perm && (unsigned)orow >= (unsigned)Nv) return;  // a permutation entry out of range: row not written
         T* dst = O + ((size_t)bh * N + orow) * D;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)

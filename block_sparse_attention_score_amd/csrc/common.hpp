@@ -27,6 +27,10 @@ __device__ __forceinline__ float half_max(float v) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// A route entry read from caller memory, clamped to the key blocks [0, Mk): a bad entry then selects
+// a wrong block rather than reading or writing out of bounds.
+__device__ __forceinline__ int clamp_block(int J, int Mk) { return min(max(J, 0), Mk - 1); }
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }

@@ -14,7 +14,8 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restric
         const int c = (int)(e % CPR);
         const size_t bh = row / N;
         const int r = (int)(row % N);
-        const int src = r < Nv ? perm[bh * Nv + r] : r;
+        // a permutation entry out of range is clamped to the video rows (no read out of bounds)
+        const int src = r < Nv ? min(max(perm[bh * Nv + r], 0), Nv - 1) : r;
         Y[e] = X[(bh * N + src) * CPR + c];
     }
 }

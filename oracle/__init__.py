@@ -44,11 +44,16 @@ _lib = None
 
 
 def lib():
+    """The loaded C oracle, built first when missing or stale.  SPARK_ORACLE_LIB names another
+    build of spark_oracle.c to load instead (the sanitizer test loads an instrumented one)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        L = ctypes.CDLL(_LIB)
+        path = os.environ.get("SPARK_ORACLE_LIB")
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+        L = ctypes.CDLL(path)
         P = ctypes.POINTER(Params)
         f32, f64, i32 = (np.ctypeslib.ndpointer(t, flags="C_CONTIGUOUS")
                          for t in (np.float32, np.float64, np.int32))

@@ -324,3 +324,40 @@ def test_binding_checks_tensor_sizes_and_types():
     bad = sa.params(good["Q"], N, b, 0.1)  # n_sink = N
     with pytest.raises(ValueError, match="device tensors"):
         sa.spark_attn_pool(bad, *[torch.empty(1, dtype=f32)] * 9)
+
+
+def test_content_checks_of_index_inputs():
+    """sa.check_contents (run before every launch under SPARK_ATTN_CHECK=1) accepts routes,
+    variable routes and permutations as the header documents them and rejects entries the
+    kernels would otherwise clamp or skip: route entries outside [0, M_k), rows not strictly
+    ascending, counts outside [0, M_k], permutation entries outside [0, N_v).  CPU tensors."""
+    import torch
+
+    p = P(N=1000, n_sink=8, block=128, topk_ratio=0.3)  # N_v = 992: M = M_k = 8, K = 2
+    M, K, Nv = 8, 2, 992
+    idx = torch.tensor([[0, 5]] * M, dtype=torch.int32).expand(2, M, K).reshape(1, 2, M, K).contiguous()
+    sa.check_contents(p, idx=idx)
+    for bad, msg in ((7 + 1, "outside"), (-1, "outside")):
+        b = idx.clone()
+        b[0, 1, 3, 1] = bad
+        with pytest.raises(ValueError, match=msg):
+            sa.check_contents(p, idx=b)
+    b = idx.clone()
+    b[0, 0, 2] = torch.tensor([4, 4], dtype=torch.int32)
+    with pytest.raises(ValueError, match="ascending"):
+        sa.check_contents(p, idx=b)
+    # variable route: entries past counts[I] are not looked at
+    var = torch.full((1, 2, M, M), 99, dtype=torch.int32)
+    counts = torch.zeros(1, 2, M, dtype=torch.int32)
+    var[0, 0, 1, :3] = torch.tensor([1, 2, 7], dtype=torch.int32)
+    counts[0, 0, 1] = 3
+    sa.check_contents(p, idx=var, counts=counts)
+    counts[0, 1, 0] = M + 1
+    with pytest.raises(ValueError, match="counts"):
+        sa.check_contents(p, idx=var, counts=counts)
+    perm = torch.arange(Nv, dtype=torch.int32).flip(0).expand(2, Nv).reshape(1, 2, Nv).contiguous()
+    sa.check_contents(p, perm=perm)
+    b = perm.clone()
+    b[0, 1, 10] = Nv
+    with pytest.raises(ValueError, match="perm"):
+        sa.check_contents(p, perm=b)
