@@ -45,7 +45,7 @@ EXPORTS = (
     "spark_attn_attend", "spark_attn_forward", "spark_attn_forward_kv", "spark_attn_reblock",
     "spark_attn_gather_rows", "spark_attn_select_tau", "spark_attn_attend_var", "spark_attn_forward_tau",
     "spark_attn_fp8_scales", "spark_attn_pack_fp8", "spark_attn_attend_fp8", "spark_attn_forward_fp8",
-    "spark_attn_pool_fp8_scales",
+    "spark_attn_pool_fp8_scales", "spark_attn_select_noalloc",
 )
 
 _lib = None
@@ -69,6 +69,7 @@ def lib():
             "spark_attn_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "spark_attn_pool": ([P] + [vp] * 9 + [vp], ctypes.c_int),
             "spark_attn_select": ([P, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "spark_attn_select_noalloc": ([P, vp, vp, vp, vp], ctypes.c_int),
             "spark_attn_pack": ([P, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "spark_attn_pool_pack": ([P] + [vp] * 10 + [sz, vp], ctypes.c_int),
             "spark_attn_attend": ([P, vp, vp, sz, vp, vp, vp, vp, vp], ctypes.c_int),
@@ -259,6 +260,13 @@ def spark_attn_select(p, q_mean, k_mean, idx, scores=None, workspace=None, strea
     _check("spark_attn_select", lib().spark_attn_select(
         ctypes.byref(p), _ptr(q_mean), _ptr(k_mean), _ptr(idx), _ptr(scores), _ptr(workspace),
         ws_bytes, _stream(stream)))
+
+
+def spark_attn_select_noalloc(p, q_mean, k_mean, idx, stream=None):
+    """spark_attn_select with the score matrix in the library's static scratch (no workspace)."""
+    _validate(p, ("q_mean", q_mean, "qblk"), ("k_mean", k_mean, "kblk"), ("idx", idx, "route"))
+    _check("spark_attn_select_noalloc", lib().spark_attn_select_noalloc(
+        ctypes.byref(p), _ptr(q_mean), _ptr(k_mean), _ptr(idx), _stream(stream)))
 
 
 def _nbytes(t):

@@ -3,7 +3,14 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kernels.hpp"
+
+// Scratch of spark_attn_select_noalloc: the score matrix, in a static device array each device
+// holds until the process ends.  In host code `scratch` is only a stand-in for the symbol: its
+// device address (per device) comes from hipGetSymbolAddress, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[SPARK_ATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace spark {
 
@@ -51,6 +58,24 @@ static int make_ctx(const spark_attn_params* p, void* stream, LaunchCtx* L) {
     L->dtype = p->dtype;
     L->scale = p->scale != 0.f ? p->scale : 1.0f / sqrtf((float)p->d);
     L->stream = (hipStream_t)stream;
+    return SPARK_ATTN_OK;
+}
+
+// Device address of `scratch` on the current device, looked up once per device.
+constexpr int kMaxDevices = 64;
+static std::once_flag g_scratch_once[kMaxDevices];
+static void* g_scratch_ptr[kMaxDevices];
+static hipError_t g_scratch_err[kMaxDevices];
+
+static int scratch_on_current_device(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SPARK_ATTN_HIP_ERROR;
+    if (dev < 0 || dev >= kMaxDevices) return SPARK_ATTN_UNSUPPORTED;
+    std::call_once(g_scratch_once[dev], [dev] {
+        g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return SPARK_ATTN_HIP_ERROR;
+    *out = g_scratch_ptr[dev];
     return SPARK_ATTN_OK;
 }
 
@@ -186,6 +211,7 @@ const char* spark_attn_status_str(int status) {
         case SPARK_ATTN_WORKSPACE_TOO_SMALL: return "workspace too small";
         case SPARK_ATTN_HIP_ERROR: return "HIP launch error";
         case SPARK_ATTN_MISALIGNED: return "pointer not 16-byte aligned";
+        case SPARK_ATTN_SCRATCH_TOO_SMALL: return "problem exceeds the library's static scratch";
         default: return "unknown status";
     }
 }
@@ -218,6 +244,21 @@ int spark_attn_select(const spark_attn_params* p, const float* q_mean, const flo
         S = (float*)workspace;
     }
     launch_select(L, q_mean, k_mean, idx, S);
+    return launch_status();
+}
+
+int spark_attn_select_noalloc(const spark_attn_params* p, const float* q_mean, const float* k_mean,
+                              int32_t* idx, void* stream) {
+    LaunchCtx L;
+    int s = make_ctx(p, stream, &L);
+    if (s < 0) return s;
+    if (!q_mean || !k_mean || !idx) return SPARK_ATTN_INVALID_ARGUMENT;
+    if (!aligned16(q_mean) || !aligned16(k_mean)) return SPARK_ATTN_MISALIGNED;
+    if (select_workspace_bytes(L) > SPARK_ATTN_NOALLOC_SCRATCH_BYTES) return SPARK_ATTN_SCRATCH_TOO_SMALL;
+    void* ws = nullptr;
+    s = scratch_on_current_device(&ws);
+    if (s < 0) return s;
+    launch_select(L, q_mean, k_mean, idx, (float*)ws);
     return launch_status();
 }
 

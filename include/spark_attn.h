@@ -53,7 +53,8 @@ enum spark_attn_status {
     SPARK_ATTN_UNSUPPORTED = -2,        /* d, block, dtype or size outside the supported set */
     SPARK_ATTN_WORKSPACE_TOO_SMALL = -3,
     SPARK_ATTN_HIP_ERROR = -4,          /* a kernel launch failed */
-    SPARK_ATTN_MISALIGNED = -5          /* a pointer is not 16-byte aligned */
+    SPARK_ATTN_MISALIGNED = -5,         /* a pointer is not 16-byte aligned */
+    SPARK_ATTN_SCRATCH_TOO_SMALL = -6   /* the problem exceeds the library's static scratch */
 };
 
 enum spark_attn_dtype { SPARK_ATTN_BF16 = 0, SPARK_ATTN_FP32 = 1 };
@@ -132,6 +133,24 @@ int spark_attn_pool(const spark_attn_params *p, const void *Q, const void *K, co
  */
 int spark_attn_select(const spark_attn_params *p, const float *q_mean, const float *k_mean,
                       int32_t *idx, float *scores, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * spark_attn_select without a workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation).  The same
+ * kernels and the same route as spark_attn_select with scores = NULL; the score matrix lives in
+ * a static scratch array the library holds on each device until the process ends
+ * (SPARK_ATTN_NOALLOC_SCRATCH_BYTES, 64 MiB: up to 16,777,216 scores, B*H*M*M_k; the 720p
+ * workload, 24 x 591 x 591, takes 33.5 MB).  The scratch of a device is looked up once, on the
+ * first call made with that device current; pass a stream of the current device.
+ * In:  q_mean, k_mean as for spark_attn_select.  Out: idx [B,H,M,K] as for spark_attn_select.
+ * Errors: as spark_attn_select; SPARK_ATTN_SCRATCH_TOO_SMALL (nothing launched) when
+ * B*H*M*M_k*4 exceeds the scratch; SPARK_ATTN_HIP_ERROR when the scratch cannot be located.
+ * Calls that overlap on one device (different streams, or threads) share the scratch and race;
+ * calls on one stream are ordered and safe.  The entry point allocates and frees nothing.
+ */
+#define SPARK_ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int spark_attn_select_noalloc(const spark_attn_params *p, const float *q_mean, const float *k_mean,
+                              int32_t *idx, void *stream);
 
 /*
  * Packing of the keys and values the attention stage reads.  `packed` (device memory of at least

@@ -361,3 +361,17 @@ def test_content_checks_of_index_inputs():
     b[0, 1, 10] = Nv
     with pytest.raises(ValueError, match="perm"):
         sa.check_contents(p, perm=b)
+
+
+def test_noalloc_select_rejects_before_any_launch():
+    """spark_attn_select_noalloc validates before touching the device: a score matrix larger than
+    the static scratch (64 MiB) is SCRATCH_TOO_SMALL, null pointers INVALID_ARGUMENT (fake,
+    never-dereferenced addresses)."""
+    L = sa.lib()
+    a = ctypes.c_void_p(0x100000)
+    big = P(N=245952 + 512, n_sink=512, H=24)  # 24 x 1922 x 1922 scores = 355 MB
+    assert L.spark_attn_select_noalloc(ctypes.byref(big), a, a, a, None) == -6
+    assert L.spark_attn_status_str(-6) == b"problem exceeds the library's static scratch"
+    small = P(N=75600 + 512, n_sink=512, H=24)  # 24 x 591 x 591 scores = 33.5 MB: fits
+    assert L.spark_attn_select_noalloc(ctypes.byref(small), None, a, a, None) == INVALID
+    assert L.spark_attn_select_noalloc(ctypes.byref(small), a, a, None, None) == INVALID
