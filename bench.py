@@ -84,15 +84,26 @@ def committed_traffic(workload, kernel="attn_fwd"):
     import re
 
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.md")
-    src = os.path.join(ROOT, "block_sparse_attention_score_amd", "csrc", f"{kernel}.hip")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     h = re.search(kernel + r"_kernel_source_sha256_16: ([0-9a-f]+)", text)
     t = re.search(kernel + r"_kernel_traffic_bytes_per_launch: ([0-9.]+)", text)
-    if not h or not t or hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != h.group(1):
+    if not h or not t or kernel_source_hash(kernel) != h.group(1):
         return None
     return float(t.group(1))
+
+
+def kernel_source_hash(kernel):
+    """sha256 (16 hex digits) of an attention kernel's source file and the headers it includes."""
+    import hashlib
+
+    csrc = os.path.join(ROOT, "block_sparse_attention_score_amd", "csrc")
+    files = [f"{kernel}.hip", "common.hpp", "kernels.hpp"] + (["attn_tile.hpp"] if kernel == "attn_fwd" else [])
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def route_check(idx, S, rel=1e-4, floor=1e-6):
