@@ -80,9 +80,10 @@ def lib():
         L.orc_forward_fp8.argtypes = [P, f32, f32, f32, vp, vp, f64, f64, vp, vp]
         L.orc_reblock_metric.argtypes = [P, f32, f32, f64, f64]
         L.orc_reblock.argtypes = [P, f32, f32, i32]
+        L.orc_reblock_given_sigma.argtypes = [P, f32, f64, i32]
         for fn in (L.orc_pool, L.orc_scores, L.orc_select, L.orc_dense, L.orc_attend_blocks,
                    L.orc_forward, L.orc_select_tau, L.orc_forward_tau, L.orc_reblock_metric,
-                   L.orc_reblock):
+                   L.orc_reblock, L.orc_reblock_given_sigma):
             fn.restype = None
         _lib = L
     return _lib
@@ -290,4 +291,12 @@ def reblock(p: Params, Q, K):
     Nv = p.N - p.n_sink
     perm = np.empty((p.B, p.H, Nv), np.int32)
     lib().orc_reblock(ctypes.byref(p), _f32(Q), _f32(K), perm)
+    return perm
+
+
+def reblock_given_sigma(p: Params, Q, Sigma):
+    """The partition (readings R2..R6) from a caller's Sigma [B,H,d,d] in place of R1's."""
+    Nv = p.N - p.n_sink
+    perm = np.empty((p.B, p.H, Nv), np.int32)
+    lib().orc_reblock_given_sigma(ctypes.byref(p), _f32(Q), np.ascontiguousarray(Sigma, np.float64), perm)
     return perm

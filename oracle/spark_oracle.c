@@ -854,6 +854,20 @@ static void reblock_split(rb_ctx *x, int *tok, int n, int c, int leaf0)
     reblock_split(x, tok + nl, n - nl, c - cl, leaf0 + cl);
 }
 
+/* R2 for every video query of one head, from that head's Sigma. */
+static void reblock_norms(const float *Qh, int Nv, int d, const double *Sg, double *nrm)
+{
+    double *t = (double *)malloc(sizeof(double) * d);
+    for (int i = 0; i < Nv; ++i) {
+        const float *q = Qh + (size_t)i * d;
+        sigma_times(Sg, q, d, t);
+        double r = 0.0;
+        for (int a = 0; a < d; ++a) r = fma((double)q[a], t[a], r);
+        nrm[i] = r > 0.0 ? sqrt(r) : 0.0;
+    }
+    free(t);
+}
+
 /* Exposed for tests: Sigma [B*H][d][d] and norms [B*H][N_v]. */
 void orc_reblock_metric(const orc_params *p, const float *Q, const float *K, double *Sigma,
                         double *nrm)
@@ -864,26 +878,19 @@ void orc_reblock_metric(const orc_params *p, const float *Q, const float *K, dou
     for (int bh = 0; bh < p->B * p->H; ++bh) {
         double *Sg = Sigma + (size_t)bh * d * d;
         reblock_sigma(K + bh * row, Nv, d, Sg);
-        double *t = (double *)malloc(sizeof(double) * d);
-        for (int i = 0; i < Nv; ++i) {
-            const float *q = Q + bh * row + (size_t)i * d;
-            sigma_times(Sg, q, d, t);
-            double r = 0.0;
-            for (int a = 0; a < d; ++a) r = fma((double)q[a], t[a], r);
-            nrm[(size_t)bh * Nv + i] = r > 0.0 ? sqrt(r) : 0.0;
-        }
-        free(t);
+        reblock_norms(Q + bh * row, Nv, d, Sg, nrm + (size_t)bh * Nv);
     }
 }
 
-/* perm [B*H][N_v]: position q of the reblocked layout holds token perm[q]. */
-void orc_reblock(const orc_params *p, const float *Q, const float *K, int32_t *perm)
+/* R2..R6 for every (batch, head) from the given Sigma [B*H][d][d]. */
+static void reblock_from_sigma(const orc_params *p, const float *Q, const double *Sigma, int32_t *perm)
 {
     const int d = p->d, Nv = n_video(p), M = orc_num_blocks(p), b = p->block;
     const size_t row = (size_t)p->N * d, BH = (size_t)p->B * p->H;
-    double *Sigma = (double *)malloc(sizeof(double) * BH * d * d);
     double *nrm = (double *)malloc(sizeof(double) * BH * Nv);
-    orc_reblock_metric(p, Q, K, Sigma, nrm);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < (int)BH; ++bh)
+        reblock_norms(Q + bh * row, Nv, d, Sigma + (size_t)bh * d * d, nrm + (size_t)bh * Nv);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int bh = 0; bh < (int)BH; ++bh) {
         rb_ctx x;
@@ -906,5 +913,24 @@ void orc_reblock(const orc_params *p, const float *Q, const float *K, int32_t *p
         }
         free(fill); free(tok); free(x.g); free(x.cosA); free(x.cosB); free(x.tmp); free(x.leaf);
     }
-    free(Sigma); free(nrm);
+    free(nrm);
+}
+
+/* perm [B*H][N_v]: position q of the reblocked layout holds token perm[q]. */
+void orc_reblock(const orc_params *p, const float *Q, const float *K, int32_t *perm)
+{
+    const int d = p->d, Nv = n_video(p);
+    const size_t row = (size_t)p->N * d, BH = (size_t)p->B * p->H;
+    double *Sigma = (double *)malloc(sizeof(double) * BH * d * d);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < (int)BH; ++bh) reblock_sigma(K + bh * row, Nv, d, Sigma + (size_t)bh * d * d);
+    reblock_from_sigma(p, Q, Sigma, perm);
+    free(Sigma);
+}
+
+/* Exposed for tests: R2..R6 from a caller's Sigma [B*H][d][d] in place of R1's (to measure how the
+ * partition depends on the reading of Sigma). */
+void orc_reblock_given_sigma(const orc_params *p, const float *Q, const double *Sigma, int32_t *perm)
+{
+    reblock_from_sigma(p, Q, Sigma, perm);
 }
