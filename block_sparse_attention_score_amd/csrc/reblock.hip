@@ -8,7 +8,7 @@
 // exact and reproducible (this file is compiled with -ffp-contract=off and every multiply-add
 // below is an explicit fma):
 //   Sigma  = K^T K / N_v in fixed point: k^ = rint(k 2^s) (s = 21 - E, max|k| < 2^E), exact int64
-//            sums of k^_a k^_b (binary64 partial sums over 2048 rows are exact), scaled back;
+//            sums of k^_a k^_b (exact integer products of base-256 digits on int8 MFMA), scaled back;
 //   n_i    = sqrt(q_i^T Sigma q_i): t_a = fma(Sigma_ab, q_b, t_a) over b, r = fma(q_a, t_a, r) over a;
 //   g(P)   = t(P) / n_P;  cos(i, P) = (fma chain over a of q_ia g_a(P)) / n_i  (0 when a norm is 0);
 //   split  : P0 = lowest index, A = argmin cos(., P0), B = argmin cos(., A) (ties: lower index),
@@ -37,9 +37,9 @@
 namespace spark {
 
 typedef double f64x2 __attribute__((ext_vector_type(2)));
-typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kRbSigmaRows = 2048;  // rows per exact binary64 partial sum (2^42 * 2^11 = 2^53)
 constexpr int kRbMaxRows = 1 << 20; // int64 sums of <= 2^20 products of magnitude <= 2^42
 constexpr int kRbChunk = 2048;      // order positions per workgroup of a chunked cos pass
 constexpr int kRbChunkThreads = 256;
@@ -142,85 +142,169 @@ __device__ __forceinline__ int fixed_point_shift(uint32_t kmax_bits) {
     return 21 - E;
 }
 
-// Tiles of Sigma on or above the diagonal: TB*(TB+1)/2 of 4x4, one per thread.
-template <int D>
-struct RbSigmaTiles {
-    static constexpr int TB = D / 4;
-    static constexpr int NTILE = TB * (TB + 1) / 2;
-    static constexpr int NTH = (NTILE + 63) / 64 * 64;
+// Exact fixed-point K^T K on int8 MFMA.  Every key entry k^ = rint(k 2^s) (|k^| <= 2^21) is
+// written as three balanced base-256 digits, k^ = d0 + 256 d1 + 65536 d2 with d0, d1 in [-128, 127]
+// and d2 in [-32, 32]; then sum_i k^_ia k^_ib = sum_{p,q} 256^(p+q) sum_i d_p(i,a) d_q(i,b), whose
+// inner sums are exact integer products (v_mfma_i32_32x32x32_i8).  Digit pairs with the same p + q
+// share one int32 accumulator: at most three products of magnitude <= 2^14 per row and entry, so
+// the sums stay exact for the kRbSigRows rows of a workgroup; they are combined in int64 at the end
+// and added to the int64 sums of the (batch, head).  Workgroup (bh, row chunk): each wave owns one
+// 32 x 32 tile of Sigma on or above the diagonal.  Rows are converted 64 at a time into digit
+// planes in LDS (plane p: feature rows of 64 bytes, one byte per row of K), which give both MFMA
+// operands: lane l reads 16 bytes of feature 32t + l % 32, rows 16 (l / 32) .. of a 32-row step,
+// the same rows for the A and the B side, so the products pair the digits of one row.
+template <int D> struct RbSig {
+    static constexpr int TB = D / 32;               // 32-feature blocks
+    static constexpr int NTL = TB * (TB + 1) / 2;   // tiles on or above the diagonal: one per wave
+    static constexpr int NT = 64 * NTL;
+    static constexpr int FPI = D == 128 ? 4 : 8;    // features per conversion item (4 rows each)
+    static constexpr int ITEMS = 16 * (D / FPI);    // conversion items per step of 64 rows
+    static_assert(ITEMS <= NT, "one conversion item per thread and step");
+};
+constexpr int kRbSigRows = 4096;  // rows per workgroup: 3 * 2^14 * 4096 < 2^31
+constexpr int kRbSigStep = 64;    // rows per LDS step (two MFMA k-steps of 32)
+static_assert(3 * (1 << 14) * (long long)kRbSigRows < (1ll << 31), "int32 digit sums must stay exact");
+
+// dword of digit-plane row f (16 dwords: 64 rows of K, one byte each) holding rows 16c + 4w ..
+// 16c + 4w + 3; the 16-byte chunks are rotated by (f / 4) % 4 so that lanes reading one chunk of
+// 32 consecutive feature rows spread over the banks
+__device__ __forceinline__ int rb_plane_dw(int f, int c, int w) { return f * 16 + 4 * (c ^ ((f >> 2) & 3)) + w; }
+
+// W consecutive elements of a row of K, kept raw until converted.
+template <typename T, int W> struct RbRaw;
+template <typename T> struct RbRaw<T, 8> : Raw8<T> {};
+template <> struct RbRaw<__bf16, 4> {
+    uint2 u;
+    __device__ __forceinline__ void load(const __bf16* p) { u = *reinterpret_cast<const uint2*>(p); }
+    __device__ __forceinline__ void widen(float (&v)[4]) const {
+        v[0] = __uint_as_float(u.x << 16);
+        v[1] = __uint_as_float(u.x & 0xffff0000u);
+        v[2] = __uint_as_float(u.y << 16);
+        v[3] = __uint_as_float(u.y & 0xffff0000u);
+    }
+};
+template <> struct RbRaw<float, 4> {
+    f32x4 a;
+    __device__ __forceinline__ void load(const float* p) { a = *reinterpret_cast<const f32x4*>(p); }
+    __device__ __forceinline__ void widen(float (&v)[4]) const {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = a[j];
+    }
 };
 
-// Exact fixed-point K^T K: workgroup (bh, row chunk of 2048 rows), one thread per 4x4 tile of
-// Sigma on or above the diagonal.  Rows are staged 64 at a time as k^ = rint(k 2^s) (exact in
-// fp32, |k^| <= 2^21); products and the chunk's partial sums are exact in binary64.
+// k^ = rint(k 2^s) as the three balanced base-256 digits in bytes 0..2: with x = k^, the bytes of
+// x + 0x808080 are d_i + 128 (each in [0, 255]: |x| <= 2^21), and flipping their top bits leaves
+// d_i as a signed byte.  In binary32 when s <= 100 (k 2^s is then exact, or below 2^-26 in
+// magnitude and rounds to 0 whether or not a subnormal k is kept), else in binary64.
+template <bool F32>
+__device__ __forceinline__ uint32_t rb_digits(float v, int sh) {
+    const int x = F32 ? (int)rintf(ldexpf(v, sh)) : (int)rint(ldexp((double)v, sh));
+    return (uint32_t)(x + 0x808080) ^ 0x808080u;
+}
+
+// Two buffers of digit planes: while the waves multiply one step's planes, the next step's rows
+// (loaded a step earlier) are converted into the other.
 template <typename T, int D>
-__global__ __launch_bounds__(RbSigmaTiles<D>::NTH) void rb_sigma_kernel(const T* __restrict__ K, int N, int Nv,
-                                                                       const uint32_t* __restrict__ kmax,
-                                                                       long long* __restrict__ sint) {
-    constexpr int TB = RbSigmaTiles<D>::TB, NTILE = RbSigmaTiles<D>::NTILE, NTH = RbSigmaTiles<D>::NTH;
-    __shared__ __attribute__((aligned(16))) float ks[64][D];
+__global__ __launch_bounds__(RbSig<D>::NT) void rb_sigma_kernel(const T* __restrict__ K, int N, int Nv,
+                                                               const uint32_t* __restrict__ kmax,
+                                                               long long* __restrict__ sint) {
+    using S = RbSig<D>;
+    constexpr int PL = 3 * D * 16;  // dwords of one buffer's three planes
+    __shared__ __attribute__((aligned(16))) uint32_t pl[2 * PL];
     const int bh = blockIdx.y;
-    const int r0 = blockIdx.x * kRbSigmaRows, r1 = min(Nv, r0 + kRbSigmaRows);
+    const int r0 = blockIdx.x * kRbSigRows, r1 = min(Nv, r0 + kRbSigRows);
     const int sh = fixed_point_shift(kmax[bh]);
-    // tile p -> (ta, tc), ta <= tc, rows of the upper triangle one after another
-    const int p = threadIdx.x;
-    const bool live = p < NTILE;
-    int ta = 0, tc = 0;
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const T* kh = K + (size_t)bh * N * D;
+
+    // this wave's tile of the upper triangle (rows of blocks one after another)
+    int ta = 0, tb;
     {
-        int rest = live ? p : 0;
-        while (rest >= TB - ta) {
-            rest -= TB - ta;
+        int rest = wv;
+        while (rest >= S::TB - ta) {
+            rest -= S::TB - ta;
             ++ta;
         }
-        tc = ta + rest;
+        tb = ta + rest;
     }
-    double acc[4][4] = {};
-    const T* kh = K + (size_t)bh * N * D;
-    // the next 64 rows are in flight in registers while the current 64 are multiplied
-    constexpr int NC = (64 * D / 8 + NTH - 1) / NTH;  // eight-element chunks per thread and batch
-    Raw8<T> nxt[NC];
+    i32x16 acc[5];
+#pragma unroll
+    for (int q = 0; q < 5; ++q)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[q][r] = 0;
+
+    // conversion item of this thread: rows 4*tk4 .. +3, features FPI*fc .. of a step
+    constexpr int FPI = S::FPI;
+    const bool conv = (int)threadIdx.x < S::ITEMS;
+    const int tk4 = (int)threadIdx.x / (D / FPI), fc = (int)threadIdx.x % (D / FPI);
+    const bool f32 = sh <= 100;
+    RbRaw<T, FPI> nx[4];  // rows of the next step to convert
     auto fetch = [&](int rs) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < NC; ++u) {
-            const int e = threadIdx.x + u * NTH, r = rs + e / (D / 8);
-            if (e < 64 * D / 8 && r < r1) nxt[u].load(kh + (size_t)r * D + (e % (D / 8)) * 8);
+        for (int u = 0; u < 4; ++u) {
+            const int r = rs + 4 * tk4 + u;
+            if (conv && r < r1) nx[u].load(kh + (size_t)r * D + FPI * fc);
+        }
+    };
+    auto convert = [&](int rs, uint32_t* buf) __attribute__((always_inline)) {
+        if (!conv) return;
+        uint32_t z[4][FPI];  // digits of row u, feature j
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float v[FPI] = {};
+            if (rs + 4 * tk4 + u < r1) nx[u].widen(v);
+#pragma unroll
+            for (int j = 0; j < FPI; ++j) z[u][j] = f32 ? rb_digits<true>(v[j], sh) : rb_digits<false>(v[j], sh);
+        }
+        // per feature, byte p of the four rows' digit words into one dword of plane p
+#pragma unroll
+        for (int j = 0; j < FPI; ++j) {
+            const uint32_t a = __builtin_amdgcn_perm(z[1][j], z[0][j], 0x05010400u);  // r0.d0 r1.d0 r0.d1 r1.d1
+            const uint32_t b = __builtin_amdgcn_perm(z[3][j], z[2][j], 0x05010400u);  // r2.d0 r3.d0 r2.d1 r3.d1
+            const uint32_t c = __builtin_amdgcn_perm(z[1][j], z[0][j], 0x0c0c0602u);  // r0.d2 r1.d2
+            const uint32_t e = __builtin_amdgcn_perm(z[3][j], z[2][j], 0x0c0c0602u);  // r2.d2 r3.d2
+            const int dw = rb_plane_dw(FPI * fc + j, tk4 >> 2, tk4 & 3);
+            buf[dw] = __builtin_amdgcn_perm(b, a, 0x05040100u);
+            buf[D * 16 + dw] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+            buf[2 * D * 16 + dw] = __builtin_amdgcn_perm(e, c, 0x05040100u);
         }
     };
     fetch(r0);
-    for (int rs = r0; rs < r1; rs += 64) {
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < NC; ++u) {
-            const int e = threadIdx.x + u * NTH;
-            if (e >= 64 * D / 8) continue;
-            const int r = rs + e / (D / 8), c8 = (e % (D / 8)) * 8;
-            float v[8] = {};
-            if (r < r1) nxt[u].widen(v);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = (float)rint(ldexp((double)v[j], sh));
-            *reinterpret_cast<f32x4*>(&ks[e / (D / 8)][c8]) = f32x4{v[0], v[1], v[2], v[3]};
-            *reinterpret_cast<f32x4*>(&ks[e / (D / 8)][c8 + 4]) = f32x4{v[4], v[5], v[6], v[7]};
+    convert(r0, pl);
+    if (r0 + kRbSigStep < r1) fetch(r0 + kRbSigStep);
+    __syncthreads();
+    for (int rs = r0, cur = 0; rs < r1; rs += kRbSigStep, cur ^= 1) {
+        const uint32_t* bp = pl + cur * PL;
+        if (rs + kRbSigStep < r1) {
+            convert(rs + kRbSigStep, pl + (cur ^ 1) * PL);
+            if (rs + 2 * kRbSigStep < r1) fetch(rs + 2 * kRbSigStep);
         }
-        __syncthreads();
-        if (rs + 64 < r1) fetch(rs + 64);
-        if (live) {
-            for (int r = 0; r < 64; ++r) {
-                const f32x4 a = *reinterpret_cast<const f32x4*>(&ks[r][ta * 4]);
-                const f32x4 c = *reinterpret_cast<const f32x4*>(&ks[r][tc * 4]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+        for (int ks = 0; ks < 2; ++ks) {
+            i32x4 A[3], B[3];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[i][j] = fma((double)a[i], (double)c[j], acc[i][j]);
+            for (int p = 0; p < 3; ++p) {
+                A[p] = *reinterpret_cast<const i32x4*>(bp + p * D * 16 + rb_plane_dw(32 * ta + (lane & 31), 2 * ks + (lane >> 5), 0));
+                B[p] = *reinterpret_cast<const i32x4*>(bp + p * D * 16 + rb_plane_dw(32 * tb + (lane & 31), 2 * ks + (lane >> 5), 0));
             }
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+#pragma unroll
+                for (int q = 0; q < 3; ++q)
+                    acc[p + q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[p], B[q], acc[p + q], 0, 0, 0);
         }
+        __syncthreads();
     }
-    if (live) {
+    // accumulator register r of lane l: Sigma row 32 ta + 8 (r / 4) + 4 (l / 32) + r % 4, column
+    // 32 tb + l % 32; the entries on or above the diagonal are added
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int r = 0; r < 16; ++r) {
+        const int a = 32 * ta + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), c = 32 * tb + (lane & 31);
+        if (a > c) continue;
+        long long v = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                atomicAdd((unsigned long long*)&sint[((size_t)bh * D + ta * 4 + i) * D + tc * 4 + j],
-                          (unsigned long long)(long long)acc[i][j]);
+        for (int q = 0; q < 5; ++q) v += (long long)acc[q][r] << (8 * q);
+        atomicAdd((unsigned long long*)&sint[((size_t)bh * D + a) * D + c], (unsigned long long)v);
     }
 }
 
@@ -806,12 +890,38 @@ __global__ __launch_bounds__(NT) void rb_chunk_split_kernel(int Nv, int BLK, int
 // and subgroup: P0 is the lowest member index; the thread holding a pivot publishes its row for
 // g(P); the argmins are lexicographic minima in LDS (least key, then least index among that key);
 // a member goes left when fewer than ceil(c/2)*block members precede it in (dk, index) order,
-// exactly the membership the radix select and stable partition give.  At the end a token's
+// exactly the membership the radix select and stable partition give.  That rank is the member's
+// place in its subgroup's run after one bitonic sort of all (subgroup, dk, index) triples in LDS.  At the end a token's
 // position is its leaf's start plus the number of members of the same leaf with a lower index.
 // Members are in ascending index with the thread number, so thread numbers stand in for indexes
 // in every tie-break.  Workgroups are laid out so that each XCD (every eighth workgroup id) takes
 // a contiguous range of (head, group) and so reads only a few heads' data.
 constexpr int kRbSubThreads = 512;  // largest subtree: threads = tokens
+
+// Sort NT (key, val) pairs in LDS ascending by (val >> 16, key, val & 0xffff), one pair per thread:
+// a bitonic network, one barrier per stage.
+template <int NT>
+__device__ __forceinline__ void rb_bitonic_sort(uint64_t* key, uint32_t* val) {
+    const int t = threadIdx.x;
+    for (int k = 2; k <= NT; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const int l = t ^ j;
+            if (l > t) {
+                const uint64_t ka = key[t], kb = key[l];
+                const uint32_t va = val[t], vb = val[l];
+                const uint32_t ga = va >> 16, gb = vb >> 16;
+                const bool a_after = ga > gb || (ga == gb && (ka > kb || (ka == kb && (va & 0xffffu) > (vb & 0xffffu))));
+                if (a_after == ((t & k) == 0)) {  // ascending runs where bit k of t is clear
+                    key[t] = kb;
+                    key[l] = ka;
+                    val[t] = vb;
+                    val[l] = va;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
 
 __host__ __device__ constexpr int rb_tri(int a, int D) { return a * (2 * D - a + 1) / 2; }
 
@@ -831,8 +941,10 @@ __global__ __launch_bounds__(NT) void rb_subtree_kernel(const T* __restrict__ Q,
     __shared__ double spn[SG];
     __shared__ unsigned long long skey[SG];
     __shared__ int sown[SG], sarg[SG];
-    __shared__ __attribute__((aligned(16))) uint64_t tkey[NT];
-    __shared__ __attribute__((aligned(8))) signed char tgrp[NT];
+    __shared__ uint64_t tkey[NT];  // sort keys dk ...
+    __shared__ uint32_t tval[NT];  // ... and (subgroup << 16 | thread), members not splitting last;
+                                   // after the sort, a member's rank in its subgroup
+    __shared__ int sstart[SG];
     __shared__ int lcnt[NT / 64][NT / 64];
 
     const int G = 1 << lev0, total = G * BH, per = (total + 7) / 8;
@@ -939,23 +1051,18 @@ __global__ __launch_bounds__(NT) void rb_subtree_kernel(const T* __restrict__ Q,
             }
         }
         tkey[t] = dk;
-        tgrp[t] = split ? (signed char)sid : (signed char)-1;
+        tval[t] = ((split ? (uint32_t)sid : 0xffffu) << 16) | (uint32_t)t;
         __syncthreads();
+        rb_bitonic_sort<NT>(tkey, tval);  // ascending (subgroup, dk, thread)
+        {
+            const uint32_t v = tval[t], grp = v >> 16;
+            if (grp != 0xffffu && (t == 0 || (tval[t - 1] >> 16) != grp)) sstart[grp] = t;
+            __syncthreads();  // every sorted entry has been read: tval now takes the ranks
+            if (grp != 0xffffu) tval[v & 0xffffu] = (uint32_t)(t - sstart[grp]);
+            __syncthreads();
+        }
         if (split) {
-            // entries past n carry subgroup -1; eight entries per step
-            int rank = 0;
-            for (int u0 = 0; u0 < n; u0 += 8) {
-                const uint64_t gg = *reinterpret_cast<const uint64_t*>(&tgrp[u0]);
-                u64x2 kk[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) kk[q] = *reinterpret_cast<const u64x2*>(&tkey[u0 + 2 * q]);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint64_t k2 = kk[j / 2][j % 2];
-                    const int gj = (int)(signed char)(gg >> (8 * j));
-                    rank += gj == sid && (k2 < dk || (k2 == dk && u0 + j < t));
-                }
-            }
+            const int rank = (int)tval[t];
             const int cl = (sc + 1) / 2;
             if (rank < cl * BLK) {
                 sc = cl;
@@ -1003,8 +1110,8 @@ static void launch_reblock_t(const LaunchCtx& L, const void* Q, const void* K, i
     const size_t zero_words = (lay.sigma - lay.kmax) / 8;
     hipLaunchKernelGGL(rb_zero_kernel, dim3(256), dim3(256), 0, L.stream, (uint64_t*)(w + lay.kmax), zero_words);
     hipLaunchKernelGGL((rb_kmax_kernel<T>), dim3(128, L.BH), dim3(256), 0, L.stream, (const T*)K, L.N, L.Nv, D, kmax);
-    hipLaunchKernelGGL((rb_sigma_kernel<T, D>), dim3((L.Nv + kRbSigmaRows - 1) / kRbSigmaRows, L.BH),
-                       dim3(RbSigmaTiles<D>::NTH), 0, L.stream, (const T*)K, L.N, L.Nv, kmax, sint);
+    hipLaunchKernelGGL((rb_sigma_kernel<T, D>), dim3((L.Nv + kRbSigRows - 1) / kRbSigRows, L.BH),
+                       dim3(RbSig<D>::NT), 0, L.stream, (const T*)K, L.N, L.Nv, kmax, sint);
     hipLaunchKernelGGL(rb_sigma_finalize_kernel, dim3((D * D + 255) / 256, L.BH), dim3(256), 0, L.stream, sint, kmax,
                        D, L.Nv, sigma);
     hipLaunchKernelGGL((rb_norms_kernel<T, D>), dim3((L.Nv + 256 * kRbNormTPL - 1) / (256 * kRbNormTPL), L.BH),
