@@ -358,68 +358,67 @@ __device__ __forceinline__ double rb_dot(const RbRow<T, D>& r, const double* gv)
     return acc;
 }
 
-// n_i for every video query: TPL tokens per thread; t in chunks of QC accumulators, each t_a
-// still one chain over b = 0..D-1.  The workgroup stages the chunk's columns of Sigma in LDS
-// (Sigma_ab read as Sigma[b][a]); every value read there feeds the TPL tokens of a thread, and
-// each token's next row elements are in flight while the current eight b steps run.  Then r over
-// a in ascending order across the chunks.
-constexpr int kRbNormQC = 32;
-constexpr int kRbNormTPL = 2;
-constexpr int kRbNormAhead = 3;  // row chunks of eight elements in flight per token
+// n_i for every video query, two bf16 rows (or one fp32 row) per thread held in registers.  t in
+// chunks of QC accumulators, each t_a one fma chain over b = 0..D-1; Sigma_ab is read as
+// Sigma[b][a] (exactly symmetric) at wave-uniform addresses, so it arrives by scalar loads and
+// feeds the FMAs from scalar registers (no LDS traffic).  Then r over a in ascending order across
+// the chunks, with the chunk's q_a read again (from cache).
+constexpr int kRbNormQC = 16;
+template <typename T> constexpr int rb_norm_tpl() { return sizeof(T) == 2 ? 2 : 1; }  // tokens per thread
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void rb_norms_kernel(const T* __restrict__ Q, int N, int Nv,
                                                        const double* __restrict__ sigma, double* __restrict__ nrm) {
-    constexpr int QC = kRbNormQC, TPL = kRbNormTPL, PD = kRbNormAhead, NK = D / 8;
-    __shared__ __attribute__((aligned(16))) double sl[D * QC];
+    constexpr int QC = kRbNormQC, TPL = rb_norm_tpl<T>(), NK = D / 8;
     const int bh = blockIdx.y, i0 = blockIdx.x * 256 * TPL + threadIdx.x;
     const T* q[TPL];
+    RbRow<T, D> row[TPL];
 #pragma unroll
-    for (int u = 0; u < TPL; ++u) q[u] = Q + ((size_t)bh * N + min(i0 + 256 * u, Nv - 1)) * D;
+    for (int u = 0; u < TPL; ++u) {
+        q[u] = Q + ((size_t)bh * N + min(i0 + 256 * u, Nv - 1)) * D;
+        row[u].load(q[u]);
+    }
     const double* S = sigma + (size_t)bh * D * D;
     double r[TPL];
 #pragma unroll
     for (int u = 0; u < TPL; ++u) r[u] = 0.0;
 #pragma unroll 1
     for (int h0 = 0; h0 < D; h0 += QC) {
-        __syncthreads();
-        for (int e2 = threadIdx.x; e2 < D * QC / 2; e2 += 256) {
-            const int b = e2 / (QC / 2), a2 = e2 % (QC / 2);
-            *reinterpret_cast<f64x2*>(&sl[b * QC + 2 * a2]) =
-                *reinterpret_cast<const f64x2*>(&S[(size_t)b * D + h0 + 2 * a2]);
-        }
-        __syncthreads();
         double t[TPL][QC];
 #pragma unroll
         for (int u = 0; u < TPL; ++u)
 #pragma unroll
             for (int a = 0; a < QC; ++a) t[u][a] = 0.0;
-        Raw8<T> ring[TPL][PD];
+        // row b+1 of the chunk's Sigma columns is requested before row b is used (two rows in
+        // scalar registers); the scheduling barriers keep the compiler from hoisting every row's
+        // loads to the top, which would spill the scalar registers
+        double sr[2][QC];
+#pragma unroll
+        for (int a = 0; a < QC; ++a) sr[0][a] = S[h0 + a];
+        // widen the rows again in every chunk rather than keep them widened in four times the registers
 #pragma unroll
         for (int u = 0; u < TPL; ++u)
 #pragma unroll
-            for (int j = 0; j < PD; ++j) ring[u][j].load(q[u] + 8 * j);
-#pragma unroll 1
+            for (int k = 0; k < NK; ++k) rb_launder(row[u].p[k]);
+#pragma unroll
         for (int k = 0; k < NK; ++k) {
             float v[TPL][8];
 #pragma unroll
-            for (int u = 0; u < TPL; ++u) {
-                ring[u][0].widen(v[u]);
-#pragma unroll
-                for (int j = 0; j + 1 < PD; ++j) ring[u][j] = ring[u][j + 1];
-                if (k + PD < NK) ring[u][PD - 1].load(q[u] + 8 * (k + PD));
-            }
+            for (int u = 0; u < TPL; ++u) row[u].p[k].widen(v[u]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const double* Sb = sl + (8 * k + e) * QC;
+                const int b = 8 * k + e;
+                __builtin_amdgcn_sched_barrier(0);
+                if (b + 1 < D)
 #pragma unroll
-                for (int a = 0; a < QC; ++a) {
-                    const double sab = Sb[a];
+                    for (int a = 0; a < QC; ++a) sr[(b + 1) & 1][a] = S[(size_t)(b + 1) * D + h0 + a];
 #pragma unroll
-                    for (int u = 0; u < TPL; ++u) t[u][a] = fma(sab, (double)v[u][e], t[u][a]);
-                }
+                for (int a = 0; a < QC; ++a)
+#pragma unroll
+                    for (int u = 0; u < TPL; ++u) t[u][a] = fma(sr[b & 1][a], (double)v[u][e], t[u][a]);
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < TPL; ++u) {
             Raw8<T> qa[QC / 8];
@@ -1114,7 +1113,7 @@ static void launch_reblock_t(const LaunchCtx& L, const void* Q, const void* K, i
                        dim3(RbSig<D>::NT), 0, L.stream, (const T*)K, L.N, L.Nv, kmax, sint);
     hipLaunchKernelGGL(rb_sigma_finalize_kernel, dim3((D * D + 255) / 256, L.BH), dim3(256), 0, L.stream, sint, kmax,
                        D, L.Nv, sigma);
-    hipLaunchKernelGGL((rb_norms_kernel<T, D>), dim3((L.Nv + 256 * kRbNormTPL - 1) / (256 * kRbNormTPL), L.BH),
+    hipLaunchKernelGGL((rb_norms_kernel<T, D>), dim3((L.Nv + 256 * rb_norm_tpl<T>() - 1) / (256 * rb_norm_tpl<T>()), L.BH),
                        dim3(256), 0, L.stream, (const T*)Q,
                        L.N, L.Nv, sigma, nrm);
     int32_t* ord[2] = {(int32_t*)(w + lay.ord0), (int32_t*)(w + lay.ord1)};
