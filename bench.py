@@ -38,10 +38,7 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (no sparsity)
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak (no sparsity)
 HBM_PEAK_GBS = 8000.0
-# fp32 vector peak, 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2 (packed FMA) x 2.4 GHz; the
-# kernels are built without packed fp32 instructions, which halves what they can reach
-VALU_FP32_PEAK_TFLOPS = 157.3
-VALU_FP32_UNPACKED_TFLOPS = 78.6
+MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
 # the forward tolerances of the parity tests (bf16 matrix-core attention against the binary64 oracle)
 FWD_REL_L2, FWD_MAX_ABS = 1e-2, 2e-2
 
@@ -582,12 +579,12 @@ def main():
                 "frac_own_bytes": round(stage_bytes / (ms_pool * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "frac_pool_bytes": round(pool_bytes / (ms_pool * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         },
-        # select = block-score product (fp32, 2*M*M_k*d flops per head) + row top-K in one kernel; its
-        # compulsory bytes (block means in, route out) are small next to the product, so the fp32
-        # arithmetic bounds it
-        "select_roofline": {"bound": "alu", "achieved": round(sel_flops / (ms_sel * 1e-3) / 1e12, 2),
-                            "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": round(sel_flops / (ms_sel * 1e-3) / 1e12 / VALU_FP32_PEAK_TFLOPS, 4),
+        # select = block-score product (fp32 on the matrix cores, 2*M*M_k*d flops per head) + row
+        # top-K; its compulsory bytes (block means in, route out) are small next to the product, so
+        # the fp32 matrix rate bounds it
+        "select_roofline": {"bound": "mfma", "achieved": round(sel_flops / (ms_sel * 1e-3) / 1e12, 2),
+                            "peak": MFMA_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(sel_flops / (ms_sel * 1e-3) / 1e12 / MFMA_FP32_PEAK_TFLOPS, 4),
                             "bytes": sel_bytes,
                             "hbm_achieved_GBs": round(sel_bytes / (ms_sel * 1e-3) / 1e9, 1),
                             "hbm_frac": round(sel_bytes / (ms_sel * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},

@@ -3,10 +3,10 @@
 // mode keeps a fixed fraction of them; Spark-H3 page, "ワークフロー": topk_mode=topk_ratio).
 //
 // Two kernels:
-//  1. block_scores: S_IJ = s * q_mean_I . k_mean_J for every (batch, head), a batched fp32 GEMM
-//     (64 x 64 output tile per workgroup, 4 x 4 per thread, d staged through LDS 32 at a time).
-//     Scores must be fp32-accurate: a near-tie between the K-th and (K+1)-th block is decided by
-//     them, so no bf16 rounding is allowed here.
+//  1. block_scores: S_IJ = s * q_mean_I . k_mean_J for every (batch, head), a batched fp32 GEMM on
+//     the fp32 matrix cores (v_mfma_f32_32x32x2_f32; 64 x 64 output tile per workgroup, 32 x 32
+//     per wave, d staged through LDS 32 at a time).  Scores must be fp32-accurate: a near-tie between the K-th and (K+1)-th block is
+//     decided by them, so no bf16 rounding is allowed here.
 //  2. topk_rows: one wave per score row.  The row's scores live in registers as order-preserving
 //     integer keys (KPL per lane); the K-th largest key is found bit by bit from the top, counting
 //     keys >= candidate with wave ballots and popcounts, and stops early once exactly K keys lie
@@ -16,20 +16,30 @@
 
 namespace spark {
 
-constexpr int kGT = 64;   // score tile (rows and columns)
+constexpr int kGT = 64;   // score tile (rows and columns) of a workgroup
 constexpr int kGD = 32;   // d per LDS stage
 
-// S [BH][Mq][Mk]: query-block means against key-block means.
+// S [BH][Mq][Mk]: query-block means against key-block means.  The workgroup stages 64 rows of
+// each operand, 32 d at a time, in LDS (coalesced row reads); wave w computes the 32 x 32 tile
+// (rows 32 (w / 2), columns 32 (w % 2) of the workgroup's).  Lane (i, h) feeds row i of both
+// operands (A: a query-block mean, B: a key-block mean) with the four d values 8t + 4h .. +3 of
+// step t from one 16-byte LDS read each; MFMA j of the step takes element j, so its two k slots
+// hold d = 8t + j and 8t + 4 + j for both operands alike, and over a step every d of the eight
+// comes once.  Accumulator register r of lane (i, h) is row 8 (r / 4) + 4 h + r % 4, column i.
 __global__ __launch_bounds__(256) void block_scores_kernel(const float* __restrict__ q_mean,
                                                            const float* __restrict__ k_mean, int Mq, int M,
                                                            int D, float scale, float* __restrict__ S) {
-    __shared__ float Qs[kGD][kGT + 4];
-    __shared__ float Ks[kGD][kGT + 4];
+    constexpr int LD = kGD + 4;  // padded LDS row (floats)
+    __shared__ __attribute__((aligned(16))) float Qs[kGT * LD];
+    __shared__ __attribute__((aligned(16))) float Ks[kGT * LD];
     const int bh = blockIdx.z, I0 = blockIdx.y * kGT, J0 = blockIdx.x * kGT;
-    const int t = threadIdx.x, ty = t / 16, tx = t % 16;
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63, i = lane & 31, h = lane >> 5;
     const float* qb = q_mean + (size_t)bh * Mq * D;
     const float* kb = k_mean + (size_t)bh * M * D;
-    float acc[4][4] = {};
+    const int qrow = 32 * (w >> 1) + i, krow = 32 * (w & 1) + i;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
     for (int d0 = 0; d0 < D; d0 += kGD) {
         __syncthreads();
 #pragma unroll
@@ -38,33 +48,24 @@ __global__ __launch_bounds__(256) void block_scores_kernel(const float* __restri
             f32x4 qv = {0.f, 0.f, 0.f, 0.f}, kv = {0.f, 0.f, 0.f, 0.f};
             if (I0 + r < Mq) qv = *reinterpret_cast<const f32x4*>(qb + (size_t)(I0 + r) * D + d0 + c);
             if (J0 + r < M) kv = *reinterpret_cast<const f32x4*>(kb + (size_t)(J0 + r) * D + d0 + c);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                Qs[c + m][r] = qv[m];
-                Ks[c + m][r] = kv[m];
-            }
+            *reinterpret_cast<f32x4*>(&Qs[r * LD + c]) = qv;
+            *reinterpret_cast<f32x4*>(&Ks[r * LD + c]) = kv;
         }
         __syncthreads();
-#pragma unroll 8
-        for (int dd = 0; dd < kGD; ++dd) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(&Qs[dd][ty * 4]);
-            const f32x4 b = *reinterpret_cast<const f32x4*>(&Ks[dd][tx * 4]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+        for (int s8 = 0; s8 < kGD / 8; ++s8) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(&Qs[qrow * LD + 8 * s8 + 4 * h]);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(&Ks[krow * LD + 8 * s8 + 4 * h]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], acc, 0, 0, 0);
         }
     }
+    const int J = J0 + krow;
+    if (J >= M) return;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int I = I0 + ty * 4 + i;
-        if (I >= Mq) break;
-        float* dst = S + ((size_t)bh * Mq + I) * M;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int J = J0 + tx * 4 + j;
-            if (J < M) dst[J] = scale * acc[i][j];
-        }
+    for (int r = 0; r < 16; ++r) {
+        const int I = I0 + 32 * (w >> 1) + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (I < Mq) S[((size_t)bh * Mq + I) * M + J] = scale * acc[r];
     }
 }
 
