@@ -44,6 +44,28 @@ def check_selection_row(sel, S_row, K):
     return must <= G <= allowed
 
 
+def check_selection_rows(idx, S):
+    """Vectorised form of check_selection_row over rows: idx [R, K] GPU routes, S [R, M] oracle
+    scores; returns the boolean validity of every row."""
+    idx = np.asarray(idx)
+    S = np.asarray(S, np.float64)
+    K, M = idx.shape[-1], S.shape[-1]
+    part = -np.sort(-S, axis=1)
+    sK = part[:, K - 1]
+    sK1 = part[:, K] if K < M else np.full_like(sK, -np.inf)
+    delta = SEL_REL * np.maximum(np.abs(sK), np.where(np.isfinite(sK1), np.abs(sK1), 0.0)) \
+        + SEL_FLOOR * np.abs(S).max(1)
+    inrange = (idx >= 0).all(1) & (idx < M).all(1)
+    chosen = np.zeros(S.shape, dtype=bool)
+    np.put_along_axis(chosen, np.clip(idx, 0, M - 1).astype(np.int64), True, axis=1)
+    must = S > (sK + delta)[:, None]
+    allowed = S >= (sK - delta)[:, None]
+    ok = inrange & (chosen.sum(1) == K) & ~(must & ~chosen).any(1) & ~(chosen & ~allowed).any(1)
+    if K > 1:
+        ok &= (np.diff(idx, axis=1) > 0).all(1)
+    return ok
+
+
 def check_selection(idx, S):
     """idx [..., M, K] GPU route vs oracle scores S [..., M, M]; returns (#rows bad, #rows not
     equal to the oracle's exact top-K)."""
