@@ -358,18 +358,20 @@ __device__ __forceinline__ double rb_dot(const RbRow<T, D>& r, const double* gv)
     return acc;
 }
 
-// n_i for every video query, two bf16 rows (or one fp32 row) per thread held in registers.  t in
+// n_i for every video query, one row per thread held in registers.  t in
 // chunks of QC accumulators, each t_a one fma chain over b = 0..D-1; Sigma_ab is read as
 // Sigma[b][a] (exactly symmetric) at wave-uniform addresses, so it arrives by scalar loads and
 // feeds the FMAs from scalar registers (no LDS traffic).  Then r over a in ascending order across
 // the chunks, with the chunk's q_a read again (from cache).
 constexpr int kRbNormQC = 16;
-template <typename T> constexpr int rb_norm_tpl() { return sizeof(T) == 2 ? 2 : 1; }  // tokens per thread
+// rows per thread: with one the kernel needs ~115 VGPRs, so four waves per SIMD hide each other's
+// scalar-load waits (two rows: ~221 VGPRs, two waves, 1.58 ms against 1.35 ms at 720p)
+constexpr int kRbNormTPL = 1;
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void rb_norms_kernel(const T* __restrict__ Q, int N, int Nv,
                                                        const double* __restrict__ sigma, double* __restrict__ nrm) {
-    constexpr int QC = kRbNormQC, TPL = rb_norm_tpl<T>(), NK = D / 8;
+    constexpr int QC = kRbNormQC, TPL = kRbNormTPL, NK = D / 8;
     const int bh = blockIdx.y, i0 = blockIdx.x * 256 * TPL + threadIdx.x;
     const T* q[TPL];
     RbRow<T, D> row[TPL];
@@ -1113,7 +1115,7 @@ static void launch_reblock_t(const LaunchCtx& L, const void* Q, const void* K, i
                        dim3(RbSig<D>::NT), 0, L.stream, (const T*)K, L.N, L.Nv, kmax, sint);
     hipLaunchKernelGGL(rb_sigma_finalize_kernel, dim3((D * D + 255) / 256, L.BH), dim3(256), 0, L.stream, sint, kmax,
                        D, L.Nv, sigma);
-    hipLaunchKernelGGL((rb_norms_kernel<T, D>), dim3((L.Nv + 256 * rb_norm_tpl<T>() - 1) / (256 * rb_norm_tpl<T>()), L.BH),
+    hipLaunchKernelGGL((rb_norms_kernel<T, D>), dim3((L.Nv + 256 * kRbNormTPL - 1) / (256 * kRbNormTPL), L.BH),
                        dim3(256), 0, L.stream, (const T*)Q,
                        L.N, L.Nv, sigma, nrm);
     int32_t* ord[2] = {(int32_t*)(w + lay.ord0), (int32_t*)(w + lay.ord1)};
