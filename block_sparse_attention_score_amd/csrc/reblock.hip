@@ -463,9 +463,9 @@ __device__ __forceinline__ void rb_pivot(const double* __restrict__ sigma, const
 }
 
 // cos(i, P) = (fma chain over a of q_ia g_a(P)) / n_i (0 when n_i = 0) for the positions
-// jb + tid, jb + tid + NT, ... below je of an order segment; f(j, i, cos) sees each one.  The next
-// position's row and norm are in flight while the current dot product runs, and the order entry
-// after that one is loaded a step earlier still.
+// jb + tid, jb + tid + NT, ... below je of an order segment; f(j, i, cos) sees each one.  One row
+// per thread is live (no row loaded ahead), so the kernels that use this fit 4-5 waves per SIMD;
+// loading the next row ahead instead, at 3 waves, took the same time.
 template <typename T, int D, int NT, typename F>
 __device__ __forceinline__ void rb_cos_range(const T* __restrict__ Qh, const double* __restrict__ nrm,
                                              const int32_t* __restrict__ seg, int jb, int je, const double* gv,
@@ -473,28 +473,18 @@ __device__ __forceinline__ void rb_cos_range(const T* __restrict__ Qh, const dou
     int j = jb + (int)threadIdx.x;
     if (j >= je) return;
     int i = seg[j];
-    int i1 = j + NT < je ? seg[j + NT] : 0;
-    RbRow<T, D> r;
-    r.load(Qh + (size_t)i * D);
-    double ni = nrm[i];
     for (;;) {
         const int jn = j + NT;
         const bool more = jn < je;
-        RbRow<T, D> rn;
-        double nn = 0.0;
-        if (more) {
-            rn.load(Qh + (size_t)i1 * D);
-            nn = nrm[i1];
-        }
-        const int i2 = jn + NT < je ? seg[jn + NT] : 0;
+        RbRow<T, D> r;
+        r.load(Qh + (size_t)i * D);
+        const double ni = nrm[i];
+        const int i1 = more ? seg[jn] : 0;
         const double acc = rb_dot<T, D>(r, gv + rb_opaque_zero());
         f(j, i, ni == 0.0 ? 0.0 : acc / ni);
         if (!more) break;
         j = jn;
         i = i1;
-        i1 = i2;
-        r = rn;
-        ni = nn;
     }
 }
 
