@@ -167,6 +167,23 @@ def test_reblock_720p_bit_exact_and_forward(orc):
     assert e2 <= FWD_REL_L2 and ea <= FWD_MAX_ABS and el <= FWD_MAX_ABS
 
 
+def test_reblock_720p_every_head_as_if_alone():
+    """Heads are partitioned independently: the 720p-like latent's 24-head partition equals, head
+    by head, the partition of that head passed on its own.  Every head of the batch (with its
+    offsets into the per-head workspace) is pinned against a single-head call, and the oracle pins
+    the single-head path."""
+    wl = W.WORKLOADS["reblock720p"]
+    Q, K, _ = W.make_qkv(wl)
+    note("reblock 720p: all heads vs each head alone")
+    Qd, Kd = dev(Q, "bf16"), dev(K, "bf16")
+    full = sa.reblock(Qd, Kd, wl.n_sink, wl.block)
+    alone = [sa.reblock(Qd[:, h:h + 1].contiguous(), Kd[:, h:h + 1].contiguous(), wl.n_sink, wl.block)
+             for h in range(Qd.shape[1])]
+    torch.cuda.synchronize()
+    for h, a in enumerate(alone):
+        assert torch.equal(full[:, h:h + 1], a), f"head {h}"
+
+
 # ---- separate key partition: keys bisected under the queries' second moment (the same
 # partitioner with the roles of Q and K exchanged), keys and values in their own order
 KV_CASES = [
