@@ -547,13 +547,17 @@ struct RbSplitShared {
     unsigned hist[NT / 64][256];
     int wc[2][kRbU * (NT / 64)];
     int tot[2];
-    int sel_digit, sel_rem;
+    int sel_digit, sel_rem, sel_cnt;
+    uint64_t thr_key;
+    uint32_t thr_idx;
 };
 
 // Split a group of n order entries with keys dk (order (dk, index) ascending = (cos(., A) -
 // cos(., B)) descending, index ascending): a radix select finds the nl-th smallest (dk, index)
 // (8 digits of dk, then 3 of the index, which is below 2^24); a stable partition writes the nl
-// smallest, in their current order, to out[0 .. nl) and the rest to out[nl .. n).
+// smallest, in their current order, to out[0 .. nl) and the rest to out[nl .. n).  Once the
+// chosen digit's bin holds a single entry, that entry is the nl-th smallest: one more sweep
+// reads its key and index and the remaining digits are skipped.
 template <int NT>
 __device__ void rb_split(const uint64_t* __restrict__ dk, const int32_t* __restrict__ seg, int n, int nl,
                          int32_t* __restrict__ out, RbSplitShared<NT>& sh) {
@@ -616,25 +620,45 @@ __device__ void rb_split(const uint64_t* __restrict__ dk, const int32_t* __restr
             const unsigned before = inc - tot;  // count of bins below 4*lane
             // the lane whose range holds the rem-th element picks the bin
             if ((int)before < rem && rem <= (int)inc) {
-                unsigned cum = before;
+                unsigned cum = before, csel = cnt[3];
                 int dsel = 4 * lane + 3;
                 for (int q = 0; q < 4; ++q) {
                     if ((int)(cum + cnt[q]) >= rem) {
                         dsel = 4 * lane + q;
+                        csel = cnt[q];
                         break;
                     }
                     cum += cnt[q];
                 }
                 sh.sel_digit = dsel;
                 sh.sel_rem = rem - (int)cum;
+                sh.sel_cnt = (int)csel;
             }
         }
         __syncthreads();
         const unsigned dsel = (unsigned)sh.sel_digit;
+        const int csel = sh.sel_cnt;
         rem = sh.sel_rem;
         if (pass < 8) pre_hi = (pre_hi << 8) | dsel;
         else pre_lo = (pre_lo << 8) | dsel;
         __syncthreads();
+        if (csel == 1 && pass < 10) {
+            // the one entry with this prefix is the threshold: take its whole key and index
+            for (int j = tid; j < n; j += NT) {
+                const uint64_t k = dk[j];
+                const uint32_t i = (uint32_t)seg[j];
+                const bool match = pass < 8 ? (k >> (56 - 8 * pass)) == pre_hi
+                                            : k == pre_hi && (i >> (16 - 8 * (pass - 8))) == pre_lo;
+                if (match) {
+                    sh.thr_key = k;
+                    sh.thr_idx = i;
+                }
+            }
+            __syncthreads();
+            pre_hi = sh.thr_key;
+            pre_lo = sh.thr_idx;
+            break;
+        }
     }
     // stable partition, U*NT positions per tile: position t0 + u*NT + tid is the (u, wave, lane)-th
     const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
