@@ -906,34 +906,47 @@ __global__ __launch_bounds__(NT) void rb_chunk_split_kernel(int Nv, int BLK, int
 // g(P); the argmins are lexicographic minima in LDS (least key, then least index among that key);
 // a member goes left when fewer than ceil(c/2)*block members precede it in (dk, index) order,
 // exactly the membership the radix select and stable partition give.  That rank is the member's
-// place in its subgroup's run after one bitonic sort of all (subgroup, dk, index) triples in LDS.  At the end a token's
+// place in its subgroup's run after one bitonic sort of all (subgroup, dk, index) triples.  At the end a token's
 // position is its leaf's start plus the number of members of the same leaf with a lower index.
 // Members are in ascending index with the thread number, so thread numbers stand in for indexes
-// in every tie-break.  Workgroups are laid out so that each XCD (every eighth workgroup id) takes
-// a contiguous range of (head, group) and so reads only a few heads' data.
+// in every tie-break.  Workgroups run group-major (id = group * heads + head) and every eighth id
+// runs on the same XCD: at each dispatch step the XCDs take neighbouring (head, group) items, whose
+// lengths depend on the group's leaf count only, so every XCD sees the same run of lengths and
+// none holds the in-order dispatch back while the others idle; with a multiple of 8 heads an XCD
+// also reads only its own heads' data (head h on XCD h mod 8).
 constexpr int kRbSubThreads = 512;  // largest subtree: threads = tokens
 
-// Sort NT (key, val) pairs in LDS ascending by (val >> 16, key, val & 0xffff), one pair per thread:
-// a bitonic network, one barrier per stage.
+// Sort NT (key, val) pairs ascending by (val >> 16, key, val & 0xffff), thread t holding pair t in
+// registers: a bitonic network.  A stage whose partners are lanes of one wave exchanges through
+// shuffles; one whose partners sit in other waves goes through LDS (skey, sval), two barriers.
 template <int NT>
-__device__ __forceinline__ void rb_bitonic_sort(uint64_t* key, uint32_t* val) {
+__device__ __forceinline__ void rb_bitonic_sort(uint64_t& key, uint32_t& val, uint64_t* skey, uint32_t* sval) {
     const int t = threadIdx.x;
+#pragma unroll 1
     for (int k = 2; k <= NT; k <<= 1) {
+#pragma unroll 1
         for (int j = k >> 1; j > 0; j >>= 1) {
-            const int l = t ^ j;
-            if (l > t) {
-                const uint64_t ka = key[t], kb = key[l];
-                const uint32_t va = val[t], vb = val[l];
-                const uint32_t ga = va >> 16, gb = vb >> 16;
-                const bool a_after = ga > gb || (ga == gb && (ka > kb || (ka == kb && (va & 0xffffu) > (vb & 0xffffu))));
-                if (a_after == ((t & k) == 0)) {  // ascending runs where bit k of t is clear
-                    key[t] = kb;
-                    key[l] = ka;
-                    val[t] = vb;
-                    val[l] = va;
-                }
+            uint64_t kp;
+            uint32_t vp;
+            if (j >= 64) {
+                skey[t] = key;
+                sval[t] = val;
+                __syncthreads();
+                kp = skey[t ^ j];
+                vp = sval[t ^ j];
+                __syncthreads();
+            } else {
+                kp = __shfl_xor(key, j);
+                vp = __shfl_xor(val, j);
             }
-            __syncthreads();
+            const uint32_t g = val >> 16, gp = vp >> 16;
+            const bool after = g > gp || (g == gp && (key > kp || (key == kp && (val & 0xffffu) > (vp & 0xffffu))));
+            // ascending runs where bit k of t is clear: there the lower partner keeps the smaller
+            const bool keep_smaller = ((t & j) == 0) == ((t & k) == 0);
+            if (after == keep_smaller) {
+                key = kp;
+                val = vp;
+            }
         }
     }
 }
@@ -956,16 +969,15 @@ __global__ __launch_bounds__(NT) void rb_subtree_kernel(const T* __restrict__ Q,
     __shared__ double spn[SG];
     __shared__ unsigned long long skey[SG];
     __shared__ int sown[SG], sarg[SG];
-    __shared__ uint64_t tkey[NT];  // sort keys dk ...
-    __shared__ uint32_t tval[NT];  // ... and (subgroup << 16 | thread), members not splitting last;
-                                   // after the sort, a member's rank in its subgroup
+    __shared__ uint64_t tkey[NT];  // the sort's exchange of keys dk ...
+    __shared__ uint32_t tval[NT];  // ... and of (subgroup << 16 | thread), members not splitting
+                                   // last; then the sorted entries; then a member's rank in its
+                                   // subgroup
     __shared__ int sstart[SG];
     __shared__ int lcnt[NT / 64][NT / 64];
+    __shared__ int sany;  // some member splits at this sublevel (read from the second one on)
 
-    const int G = 1 << lev0, total = G * BH, per = (total + 7) / 8;
-    const int wi = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-    if (wi >= total) return;
-    const int bh = wi / G, g = wi % G, t = threadIdx.x;
+    const int bh = (int)(blockIdx.x % BH), g = (int)(blockIdx.x / BH), t = threadIdx.x;
     int L0, c;
     rb_group(g, lev0, M, L0, c);
     if (c <= 0) return;
@@ -1002,7 +1014,12 @@ __global__ __launch_bounds__(NT) void rb_subtree_kernel(const T* __restrict__ Q,
         const int ng = 1 << k;
         const bool split = act && sc >= 2;
         if (t < ng) sown[t] = INT_MAX;
+        if (split) sany = 1;
         __syncthreads();
+        // once every subgroup is a single leaf, no later sublevel splits either (subgroups only
+        // shrink) and the leaves are final; the first sublevel splits when the group has two
+        // leaves or more, and the flag is cleared at the end of each sublevel for the next
+        if (k == 0 ? c < 2 : sany == 0) break;
         if (split) atomicMin(&sown[sid], t);
         __syncthreads();
         double cA = 0.0;
@@ -1065,10 +1082,13 @@ __global__ __launch_bounds__(NT) void rb_subtree_kernel(const T* __restrict__ Q,
                 dk = ~asc_key(cA - cs);
             }
         }
-        tkey[t] = dk;
-        tval[t] = ((split ? (uint32_t)sid : 0xffffu) << 16) | (uint32_t)t;
-        __syncthreads();
-        rb_bitonic_sort<NT>(tkey, tval);  // ascending (subgroup, dk, thread)
+        {
+            uint64_t key = dk;
+            uint32_t val = ((split ? (uint32_t)sid : 0xffffu) << 16) | (uint32_t)t;
+            rb_bitonic_sort<NT>(key, val, tkey, tval);  // ascending (subgroup, dk, thread)
+            tval[t] = val;
+            __syncthreads();
+        }
         {
             const uint32_t v = tval[t], grp = v >> 16;
             if (grp != 0xffffu && (t == 0 || (tval[t - 1] >> 16) != grp)) sstart[grp] = t;
@@ -1090,6 +1110,7 @@ __global__ __launch_bounds__(NT) void rb_subtree_kernel(const T* __restrict__ Q,
         } else {
             sid = 2 * sid;
         }
+        if (t == 0) sany = 0;  // every thread read it many barriers ago
         __syncthreads();
     }
     // position inside the leaf: members of the leaf in lower waves, then lower lanes of this wave
@@ -1177,8 +1198,7 @@ static void launch_reblock_t(const LaunchCtx& L, const void* Q, const void* K, i
                            dst, dk);
     }
     if (ls < levels) {
-        const int total = (1 << ls) * L.BH;
-        hipLaunchKernelGGL((rb_subtree_kernel<T, D, kRbSubThreads>), dim3(8 * ((total + 7) / 8)), dim3(kRbSubThreads), 0,
+        hipLaunchKernelGGL((rb_subtree_kernel<T, D, kRbSubThreads>), dim3((1 << ls) * L.BH), dim3(kRbSubThreads), 0,
                            L.stream, Qt, L.N, L.Nv, L.block, L.M, ls, levels - ls, L.BH, sigma, nrm, ord[ls & 1], perm);
     }
 }
