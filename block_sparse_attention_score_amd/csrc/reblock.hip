@@ -954,7 +954,7 @@ __device__ __forceinline__ void rb_bitonic_sort(uint64_t& key, uint32_t& val, ui
 __host__ __device__ constexpr int rb_tri(int a, int D) { return a * (2 * D - a + 1) / 2; }
 
 template <typename T, int D, int NT>
-__global__ __launch_bounds__(NT) void rb_subtree_kernel(const T* __restrict__ Q, int N, int Nv, int BLK,
+__global__ __launch_bounds__(NT, sizeof(T) == 2 || D == 64 ? 4 : 1) void rb_subtree_kernel(const T* __restrict__ Q, int N, int Nv, int BLK,
                                                                    int M, int lev0, int nsub, int BH,
                                                                    const double* __restrict__ sigma_all,
                                                                    const double* __restrict__ nrm_all,
@@ -1043,15 +1043,23 @@ __global__ __launch_bounds__(NT) void rb_subtree_kernel(const T* __restrict__ Q,
                 const double nP = spn[slot];
                 double gval = 0.0;
                 if (nP != 0.0) {
-                    // Sigma_ab from the triangle: row min(a, b), column max(a, b)
+                    // Sigma_ab from the triangle: row min(a, b), column max(a, b).  Four values
+                    // are read ahead of their four FMAs (same order), so the chain waits on one
+                    // LDS round trip per four steps.
                     const int ta = rb_tri(a, D);
                     int tb = 0;
                     double acc = 0.0;
-#pragma unroll 8
-                    for (int b = 0; b < D; ++b) {
-                        const int off = b <= a ? tb + a - b : ta + b - a;
-                        acc = fma(stri[off], (double)qpv[slot][b], acc);
-                        tb += D - b;
+#pragma unroll 2
+                    for (int b0 = 0; b0 < D; b0 += 4) {
+                        double sv[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int b = b0 + j;
+                            sv[j] = stri[b <= a ? tb + a - b : ta + b - a];
+                            tb += D - b;
+                        }
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc = fma(sv[j], (double)qpv[slot][b0 + j], acc);
                     }
                     gval = acc / nP;
                 }
