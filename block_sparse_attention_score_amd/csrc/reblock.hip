@@ -123,7 +123,22 @@ __global__ __launch_bounds__(256) void rb_kmax_kernel(const T* __restrict__ K, i
     const T* kh = K + (size_t)bh * N * d;
     const size_t n8 = (size_t)Nv * d / 8;
     float m = 0.f;
-    for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n8; e += (size_t)gridDim.x * 256) {
+    const size_t stride = (size_t)gridDim.x * 256;
+    size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+    // four loads in flight per thread, then the remainder one at a time
+    for (; e + 3 * stride < n8; e += 4 * stride) {
+        Raw8<T> r[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r[u].load(kh + 8 * (e + u * stride));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float v[8];
+            r[u].widen(v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+        }
+    }
+    for (; e < n8; e += stride) {
         Raw8<T> r;
         r.load(kh + 8 * e);
         float v[8];
