@@ -55,7 +55,7 @@ constexpr float kRescaleSlack = 8.f;  // log2-domain slack before the running ma
 template <typename T, int D, int BLK, bool FIXED>
 __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     const T* __restrict__ Q, const __bf16* __restrict__ packed, const float* __restrict__ bias2,
-    const float4* __restrict__ bnd, int32_t* __restrict__ flags,
+    const float4* __restrict__ bnd, int32_t* __restrict__ flags, int32_t* __restrict__ queue,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ counts, const int32_t* __restrict__ perm,
     T* __restrict__ O, float* __restrict__ lse, int N, int Nv, int M, int Mk, int nsh, int Ksel, int kstride, int SQ,
     int BH, int C,
@@ -82,7 +82,12 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     // query blocks are remapped so that each of the 8 XCDs (workgroup id w runs on XCD w % 8) walks
     // its own contiguous run of C query blocks of the same head while all XCDs stay on one head:
     // neighbouring query blocks select mostly the same key blocks, so concurrent workgroups of one
-    // XCD share tiles in its L2, and one head's tiles are the working set of the whole chip.
+    // XCD share tiles in its L2, and one head's tiles are the working set of the whole chip.  In
+    // the fixed-offset pass a workgroup claims the next tile of its XCD's run from a counter, and
+    // once that run is spent, the next tile of another XCD's run: XCDs that go faster than others
+    // (their routes hit L2 more often) take over the slower ones' last tiles instead of idling.
+    // The grid holds as many video workgroups as there are (XCD, slot) items, so every workgroup
+    // claims exactly one, and every item is claimed once.
     int bh, qrow0, nq, ntiles, qt;  // qt: query tile within the (batch, head): sink tiles, then video blocks
     bool dense;
     {
@@ -97,7 +102,24 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
         } else {
             dense = false;
             const int v = wg - BH * SQ;
-            const int xcd = wg & 7, slot = v >> 3;
+            int xcd = wg & 7, slot = v >> 3;
+            if constexpr (FIXED) {
+                __shared__ int s_claim;
+                if (threadIdx.x == 0) {
+                    int c = -1;
+                    for (int k = 0; k < 8 && c < 0; ++k) {
+                        const int x2 = (xcd + k) & 7;
+                        const int j = atomicAdd(&queue[x2], 1);
+                        if (j < BH * C) c = x2 * BH * C + j;
+                    }
+                    s_claim = c;
+                }
+                __syncthreads();
+                const int c = s_claim;
+                if (c < 0) return;  // none left (not reached: items = workgroups); uniform
+                xcd = c / (BH * C);
+                slot = c % (BH * C);
+            }
             bh = slot / C;
             const int I = xcd * C + slot % C;
             if (I >= M) return;  // padding slot (uniform for the workgroup, before any barrier)
@@ -410,6 +432,12 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
 #endif
 }
 
+// The fixed-offset pass's tile counters start at zero on every call (a kernel, not a memset, so
+// that a captured graph replays it).
+__global__ __launch_bounds__(64) void attn_queue_zero_kernel(int32_t* __restrict__ queue) {
+    if (threadIdx.x < 8) queue[threadIdx.x] = 0;
+}
+
 template <typename T, int D, int BLK>
 static void launch_attend_t(const LaunchCtx& L, const void* Q, const void* packed, const int32_t* idx,
                             const int32_t* counts, const int32_t* perm, void* O, float* lse) {
@@ -422,13 +450,15 @@ static void launch_attend_t(const LaunchCtx& L, const void* Q, const void* packe
     const float* b2 = (const float*)(pk + g.bias_off);
     const float4* bnd = (const float4*)(pk + g.bnd_off);
     int32_t* flags = (int32_t*)(pk + g.flag_off);  // workspace the library owns inside the packed buffer
+    int32_t* queue = (int32_t*)(pk + g.queue_off);  // likewise
     const int nsh = L.block_k == 128 ? 1 : 0, kstride = counts ? L.Mk : L.K;
     // fixed-offset pass over every query tile, then the exact pass over the tiles it marked
+    hipLaunchKernelGGL(attn_queue_zero_kernel, dim3(1), dim3(64), 0, L.stream, queue);
     hipLaunchKernelGGL((attn_fwd_kernel<T, D, BLK, true>), grid, dim3(BLK * 2), 0, L.stream, (const T*)Q,
-                       (const __bf16*)packed, b2, bnd, flags, idx, counts, perm, (T*)O, lse, L.N, L.Nv, L.M, L.Mk,
+                       (const __bf16*)packed, b2, bnd, flags, queue, idx, counts, perm, (T*)O, lse, L.N, L.Nv, L.M, L.Mk,
                        nsh, L.K, kstride, SQ, L.BH, C, g.Tv, g.Ts, g.Tc, c_log2);
     hipLaunchKernelGGL((attn_fwd_kernel<T, D, BLK, false>), grid, dim3(BLK * 2), 0, L.stream, (const T*)Q,
-                       (const __bf16*)packed, b2, bnd, flags, idx, counts, perm, (T*)O, lse, L.N, L.Nv, L.M, L.Mk,
+                       (const __bf16*)packed, b2, bnd, flags, nullptr, idx, counts, perm, (T*)O, lse, L.N, L.Nv, L.M, L.Mk,
                        nsh, L.K, kstride, SQ, L.BH, C, g.Tv, g.Ts, g.Tc, c_log2);
 }
 

@@ -41,6 +41,7 @@ struct PackGeom {
     size_t tmax_off;       // per tile {max |k|^2, max additive term} over its valid keys, float2 [BH][Tall]
     size_t bnd_off;        // per head {max |k| exact keys, max |k| pseudo-keys, max pseudo-key term, 0}, float4 [BH]
     size_t flag_off;       // per query tile: 1 when the fixed-offset pass left it to the exact pass, int32 [BH][NQT]
+    size_t queue_off;      // the fixed-offset pass's tile counters, one per XCD, int32 [8]
     size_t bytes;          // total
 };
 PackGeom pack_geom(const LaunchCtx& L);

@@ -37,7 +37,8 @@ PackGeom pack_geom(const LaunchCtx& L) {
     g.tmax_off = a256(g.bias_off + (size_t)L.BH * g.Tall * 64 * 4);
     g.bnd_off = a256(g.tmax_off + (size_t)L.BH * g.Tall * 8);
     g.flag_off = a256(g.bnd_off + (size_t)L.BH * 16);
-    g.bytes = a256(g.flag_off + (size_t)L.BH * g.NQT * 4);
+    g.queue_off = a256(g.flag_off + (size_t)L.BH * g.NQT * 4);
+    g.bytes = a256(g.queue_off + 8 * 4);
     return g;
 }
 

@@ -186,6 +186,9 @@ int spark_attn_pool_pack(const spark_attn_params *p, const void *Q, const void *
  * Video query i of block I attends in one softmax to every key of its K selected blocks, to
  * every sink row, and to one pseudo-key per unselected block J (logit s*q.k_sum_J + bias_J,
  * value v_sum_J).  Sink query rows attend densely to all N keys.
+ * The call also writes a small region at the end of `packed` that the library keeps for itself
+ * (a flag per query tile and eight tile counters): calls that share one packed buffer must not
+ * overlap in time; the tiles themselves are only read.
  */
 int spark_attn_attend(const spark_attn_params *p, const void *Q, const void *packed,
                       size_t packed_bytes, const int32_t *idx, const int32_t *perm, void *O,
