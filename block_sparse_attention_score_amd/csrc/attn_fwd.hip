@@ -84,8 +84,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_kernel(
     // neighbouring query blocks select mostly the same key blocks, so concurrent workgroups of one
     // XCD share tiles in its L2, and one head's tiles are the working set of the whole chip.  In
     // the fixed-offset pass a workgroup claims the next tile of its XCD's run from a counter, and
-    // once that run is spent, the next tile of another XCD's run: XCDs that go faster than others
-    // (their routes hit L2 more often) take over the slower ones' last tiles instead of idling.
+    // once that run is spent, the next tile of another XCD's run: the XCDs do not run at one speed
+    // (mean workgroup times up to 5% apart on the full clip), and the faster ones take over the
+    // slower ones' last tiles instead of idling.
     // The grid holds as many video workgroups as there are (XCD, slot) items, so every workgroup
     // claims exactly one, and every item is claimed once.
     int bh, qrow0, nq, ntiles, qt;  // qt: query tile within the (batch, head): sink tiles, then video blocks

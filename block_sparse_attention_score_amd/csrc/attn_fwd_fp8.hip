@@ -98,7 +98,8 @@ PackGeom pack_geom_fp8(const LaunchCtx& L) {
     g.tile_elems = (size_t)2 * 64 * L.d;  // bytes of a tile (one byte per element)
     g.kv_bytes = (size_t)L.BH * g.Tall * g.tile_elems;
     g.bias_off = (g.kv_bytes + 255) & ~(size_t)255;
-    g.bytes = g.bias_off + (size_t)L.BH * g.Tall * 64 * 4;
+    g.queue_off = (g.bias_off + (size_t)L.BH * g.Tall * 64 * 4 + 255) & ~(size_t)255;
+    g.bytes = g.queue_off + 8 * 4;
     return g;
 }
 
@@ -264,6 +265,7 @@ template <typename T, int D, int BLK>
 __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
     const T* __restrict__ Q, const uint8_t* __restrict__ packed, const float* __restrict__ bias2,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ perm, const uint32_t* __restrict__ amax,
+    int32_t* __restrict__ queue,
     T* __restrict__ O, float* __restrict__ lse, int N, int Nv, int M, int Mk, int nsh, int Ksel, int SQ, int BH, int C,
     int Tv,
     int Ts, int Tc, float c_log2) {
@@ -282,7 +284,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
     auto lbias = [&](auto s) __attribute__((always_inline)) -> float* { if constexpr (decltype(s)::value == 0) return lbias0; else return lbias1; };
 
     // which query tile: sink-query tiles first; video query blocks laid out per XCD as in the bf16
-    // kernel (each XCD walks a contiguous run of one head's query blocks)
+    // kernel (each XCD walks a contiguous run of one head's query blocks), claimed from the XCD's
+    // counter and, once its run is spent, from another XCD's (the grid holds one workgroup per
+    // item, so each claims exactly one)
     int bh, qrow0, nq, ntiles;
     bool dense;
     {
@@ -296,7 +300,22 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_fp8_kernel(
         } else {
             dense = false;
             const int v = wg - BH * SQ;
-            const int xcd = wg & 7, slot = v >> 3;
+            int xcd = wg & 7, slot = v >> 3;
+            __shared__ int s_claim;
+            if (threadIdx.x == 0) {
+                int c = -1;
+                for (int k = 0; k < 8 && c < 0; ++k) {
+                    const int x2 = (xcd + k) & 7;
+                    const int j = atomicAdd(&queue[x2], 1);
+                    if (j < BH * C) c = x2 * BH * C + j;
+                }
+                s_claim = c;
+            }
+            __syncthreads();
+            const int c = s_claim;
+            if (c < 0) return;  // none left (not reached: items = workgroups); uniform
+            xcd = c / (BH * C);
+            slot = c % (BH * C);
             bh = slot / C;
             const int I = xcd * C + slot % C;
             if (I >= M) return;
@@ -609,9 +628,12 @@ static void launch_attend_fp8_t(const LaunchCtx& L, const void* Q, const void* p
     const int C = (L.M + 7) / 8;
     const dim3 grid(L.BH * SQ + L.BH * 8 * C);
     const float c_log2 = L.scale * 1.4426950408889634f;
+    // the tile counters start at zero on every call (a kernel, so that a captured graph replays it)
+    int32_t* queue = (int32_t*)((char*)packed + g.queue_off);  // workspace the library owns inside the packed buffer
+    hipLaunchKernelGGL(fp8_zero_kernel, dim3(1), dim3(256), 0, L.stream, (uint32_t*)queue, 8);
     hipLaunchKernelGGL((attn_fwd_fp8_kernel<T, D, BLK>), grid, dim3(BLK * 2), 0, L.stream, (const T*)Q,
                        (const uint8_t*)packed, (const float*)((const char*)packed + g.bias_off), idx, perm, amax,
-                       (T*)O, lse, L.N, L.Nv, L.M, L.Mk, L.block_k == 128 ? 1 : 0, L.K, SQ, L.BH, C, g.Tv, g.Ts,
+                       queue, (T*)O, lse, L.N, L.Nv, L.M, L.Mk, L.block_k == 128 ? 1 : 0, L.K, SQ, L.BH, C, g.Tv, g.Ts,
                        g.Tc, c_log2);
 }
 

@@ -298,7 +298,9 @@ int spark_attn_reblock(const spark_attn_params *p, const void *Q, const void *K,
  *   bias rows; a tile is 64 key rows of d bytes, then d value rows of 64 bytes); `packed` holds
  *   spark_attn_workspace_size(p, 9) bytes.
  * spark_attn_attend_fp8: spark_attn_attend on those tiles; idx [B,H,M,K] (ascending rows), perm as
- *   in spark_attn_attend; amax as written by spark_attn_fp8_scales for the same Q, K, V.
+ *   in spark_attn_attend; amax as written by spark_attn_fp8_scales for the same Q, K, V.  Like
+ *   spark_attn_attend it writes eight tile counters the library keeps at the end of `packed`:
+ *   calls that share one packed buffer must not overlap in time.
  * spark_attn_forward_fp8: [gather by perm] -> pool+scales -> select -> pack_fp8 -> attend_fp8;
  *   pooling and selection see the unquantized inputs (the route equals spark_attn_forward's);
  *   amax_out [B,H,3] or NULL; workspace of spark_attn_workspace_size(p, perm ? 8 : 7) bytes.
