@@ -59,7 +59,7 @@ static int rb_chunks(const LaunchCtx& L, int lev) {
 }
 
 struct RbLayout {
-    size_t kmax, sint, sigma, nrm, ord0, ord1, cbuf, dk, gbuf, pkey, pidx, total;
+    size_t kmax, sint, subq, sigma, nrm, ord0, ord1, cbuf, dk, gbuf, pkey, pidx, total;
 };
 
 static RbLayout rb_layout(const LaunchCtx& L) {
@@ -80,6 +80,7 @@ static RbLayout rb_layout(const LaunchCtx& L) {
     };
     r.kmax = take(BH * 4);
     r.sint = take(BH * d * d * 8);
+    r.subq = take(BH * 4);  // the subtree kernel's per-head group counters
     r.sigma = take(BH * d * d * 8);
     r.nrm = take(BH * Nv * 8);
     r.ord0 = take(BH * Nv * 4);
@@ -968,13 +969,29 @@ __device__ __forceinline__ void rb_bitonic_sort(uint64_t& key, uint32_t& val, ui
 
 __host__ __device__ constexpr int rb_tri(int a, int D) { return a * (2 * D - a + 1) / 2; }
 
+// After head bh's groups are all claimed: the next head, in rotation from bh, with groups left
+// (one read of every head's counter), or -1 when none has.  Every thread gets the same answer.
+template <int NT>
+__device__ int rb_next_head(const int32_t* hq, int BH, int G, int bh, int* s_pick) {
+    if (threadIdx.x == 0) *s_pick = INT_MAX;
+    __syncthreads();
+    for (int j = 1 + (int)threadIdx.x; j < BH; j += NT)
+        if (__hip_atomic_load(&hq[(bh + j) % BH], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < G)
+            atomicMin(s_pick, j);
+    __syncthreads();
+    const int j = *s_pick;
+    __syncthreads();  // read by every thread before it is written again
+    return j == INT_MAX ? -1 : (bh + j) % BH;
+}
+
 template <typename T, int D, int NT>
 __global__ __launch_bounds__(NT, sizeof(T) == 2 || D == 64 ? 4 : 1) void rb_subtree_kernel(const T* __restrict__ Q, int N, int Nv, int BLK,
                                                                    int M, int lev0, int nsub, int BH,
                                                                    const double* __restrict__ sigma_all,
                                                                    const double* __restrict__ nrm_all,
                                                                    const int32_t* __restrict__ ord_in_all,
-                                                                   int32_t* __restrict__ perm_all) {
+                                                                   int32_t* __restrict__ perm_all,
+                                                                   int32_t* __restrict__ hq) {
     // a subtree holds at most NT/64 leaves (block >= 64), so at most NT/128 subgroups split at
     // one sub-level
     constexpr int SG = NT / 128;
@@ -991,164 +1008,181 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 || D == 64 ? 4 : 1) void rb_subt
     __shared__ int sstart[SG];
     __shared__ int lcnt[NT / 64][NT / 64];
     __shared__ int sany;  // some member splits at this sublevel (read from the second one on)
+    __shared__ int s_claim;
 
-    const int bh = (int)(blockIdx.x % BH), g = (int)(blockIdx.x / BH), t = threadIdx.x;
-    int L0, c;
-    rb_group(g, lev0, M, L0, c);
-    if (c <= 0) return;
-    const int s0 = L0 * BLK, n = min(s0 + c * BLK, Nv) - s0;
-    const bool act = t < n;
-    const T* Qh = Q + (size_t)bh * N * D;
-    const double* sigma = sigma_all + (size_t)bh * D * D;
-    const int idx = act ? ord_in_all[(size_t)bh * Nv + s0 + t] : INT_MAX;
-    RbRow<T, D> row;
-    double ni = 0.0;
-    if (act) {
-        row.load(Qh + (size_t)idx * D);
-        ni = nrm_all[(size_t)bh * Nv + idx];
-    }
-    if (c >= 2) {
-        // Sigma as pairs, eight pairs per thread in flight at a time
-        constexpr int NP = D * D / 2 / NT, HALF = NP / 2;
-        const f64x2* s2 = reinterpret_cast<const f64x2*>(sigma);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            f64x2 v[HALF];
-#pragma unroll
-            for (int k = 0; k < HALF; ++k) v[k] = s2[t + (h * HALF + k) * NT];
-#pragma unroll
-            for (int k = 0; k < HALF; ++k) {
-                const int e = 2 * (t + (h * HALF + k) * NT), ra = e / D, cb = e % D;
-                if (cb >= ra) stri[rb_tri(ra, D) + cb - ra] = v[k][0];
-                if (cb + 1 >= ra) stri[rb_tri(ra, D) + cb + 1 - ra] = v[k][1];
-            }
-        }
-    }
-    int sL0 = L0, sc = c, sid = 0;
-    for (int k = 0; k < nsub; ++k) {
-        const int ng = 1 << k;
-        const bool split = act && sc >= 2;
-        if (t < ng) sown[t] = INT_MAX;
-        if (split) sany = 1;
-        __syncthreads();
-        // once every subgroup is a single leaf, no later sublevel splits either (subgroups only
-        // shrink) and the leaves are final; the first sublevel splits when the group has two
-        // leaves or more, and the flag is cleared at the end of each sublevel for the next
-        if (k == 0 ? c < 2 : sany == 0) break;
-        if (split) atomicMin(&sown[sid], t);
-        __syncthreads();
-        double cA = 0.0;
-        uint64_t dk = 0;
-        for (int step = 0; step < 3; ++step) {
-            // the pivot's thread publishes its row and norm; then g(P) of every splitting subgroup
-            if (split && sown[sid] == t) {
-#pragma unroll
-                for (int q = 0; q < D / 8; ++q) {
-                    float v[8];
-                    row.p[q].widen(v);
-                    *reinterpret_cast<f32x4*>(&qpv[sid][8 * q]) = f32x4{v[0], v[1], v[2], v[3]};
-                    *reinterpret_cast<f32x4*>(&qpv[sid][8 * q + 4]) = f32x4{v[4], v[5], v[6], v[7]};
-                }
-                spn[sid] = ni;
-            }
+    const int G = 1 << lev0;
+    int staged = -1;  // the head whose Sigma triangle is in LDS
+    for (int bh = (int)(blockIdx.x % BH); bh >= 0; bh = rb_next_head<NT>(hq, BH, G, bh, &s_claim)) {
+        for (;;) {
+            if (threadIdx.x == 0) s_claim = atomicAdd(&hq[bh], 1);
             __syncthreads();
-            for (int e = t; e < ng * D; e += NT) {
-                const int slot = e / D, a = e % D;
-                if (sown[slot] == INT_MAX) continue;
-                const double nP = spn[slot];
-                double gval = 0.0;
-                if (nP != 0.0) {
-                    // Sigma_ab from the triangle: row min(a, b), column max(a, b).  Four values
-                    // are read ahead of their four FMAs (same order), so the chain waits on one
-                    // LDS round trip per four steps.
-                    const int ta = rb_tri(a, D);
-                    int tb = 0;
-                    double acc = 0.0;
-#pragma unroll 2
-                    for (int b0 = 0; b0 < D; b0 += 4) {
-                        double sv[4];
+            const int g = s_claim;
+            __syncthreads();  // read by every thread before it is written again
+            if (g >= G) break;
+            int L0, c;
+            rb_group(g, lev0, M, L0, c);
+            if (c <= 0) continue;
+            // the thread number, opaque to the compiler: what derives from it is computed per group
+            // instead of being hoisted out of the loop and held in registers across it
+            const int t = (int)(threadIdx.x + rb_opaque_zero());
+            const int s0 = L0 * BLK, n = min(s0 + c * BLK, Nv) - s0;
+            const bool act = t < n;
+            const T* Qh = Q + (size_t)bh * N * D;
+            const double* sigma = sigma_all + (size_t)bh * D * D;
+            const int idx = act ? ord_in_all[(size_t)bh * Nv + s0 + t] : INT_MAX;
+            RbRow<T, D> row;
+            double ni = 0.0;
+            if (act) {
+                row.load(Qh + (size_t)idx * D);
+                ni = nrm_all[(size_t)bh * Nv + idx];
+            }
+            if (c >= 2 && staged != bh) {
+                staged = bh;
+                // Sigma as pairs, four pairs per thread in flight at a time (once per head and
+                // workgroup, so its registers matter more than its latency)
+                constexpr int NP = D * D / 2 / NT, PF = 4;
+#pragma unroll 1
+                for (int h = 0; h < NP / PF; ++h) {
+                    f64x2 v[PF];
+                    const f64x2* s2 = reinterpret_cast<const f64x2*>(sigma) + rb_opaque_zero();
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int b = b0 + j;
-                            sv[j] = stri[b <= a ? tb + a - b : ta + b - a];
-                            tb += D - b;
-                        }
+                    for (int k = 0; k < PF; ++k) v[k] = s2[t + (h * PF + k) * NT];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) acc = fma(sv[j], (double)qpv[slot][b0 + j], acc);
+                    for (int k = 0; k < PF; ++k) {
+                        const int e = 2 * (t + (h * PF + k) * NT), ra = e / D, cb = e % D;
+                        if (cb >= ra) stri[rb_tri(ra, D) + cb - ra] = v[k][0];
+                        if (cb + 1 >= ra) stri[rb_tri(ra, D) + cb + 1 - ra] = v[k][1];
                     }
-                    gval = acc / nP;
                 }
-                gvs[slot][a] = gval;
             }
-            if (t < ng) {
-                skey[t] = ~0ull;
-                sarg[t] = INT_MAX;
-            }
-            __syncthreads();
-            double cs = 0.0;
-            if (split) {
+            int sL0 = L0, sc = c, sid = 0;
+            for (int k = 0; k < nsub; ++k) {
+                const int ng = 1 << k;
+                const bool split = act && sc >= 2;
+                if (t < ng) sown[t] = INT_MAX;
+                if (split) sany = 1;
+                __syncthreads();
+                // once every subgroup is a single leaf, no later sublevel splits either (subgroups only
+                // shrink) and the leaves are final; the first sublevel splits when the group has two
+                // leaves or more, and the flag is cleared at the end of each sublevel for the next
+                if (k == 0 ? c < 2 : sany == 0) break;
+                if (split) atomicMin(&sown[sid], t);
+                __syncthreads();
+                double cA = 0.0;
+                uint64_t dk = 0;
+                for (int step = 0; step < 3; ++step) {
+                    // the pivot's thread publishes its row and norm; then g(P) of every splitting subgroup
+                    if (split && sown[sid] == t) {
 #pragma unroll
-                for (int q = 0; q < D / 8; ++q) rb_launder(row.p[q]);
-                const double acc = rb_dot<T, D>(row, &gvs[sid][0]);
-                cs = ni == 0.0 ? 0.0 : acc / ni;
+                        for (int q = 0; q < D / 8; ++q) {
+                            float v[8];
+                            row.p[q].widen(v);
+                            *reinterpret_cast<f32x4*>(&qpv[sid][8 * q]) = f32x4{v[0], v[1], v[2], v[3]};
+                            *reinterpret_cast<f32x4*>(&qpv[sid][8 * q + 4]) = f32x4{v[4], v[5], v[6], v[7]};
+                        }
+                        spn[sid] = ni;
+                    }
+                    __syncthreads();
+                    for (int e = t; e < ng * D; e += NT) {
+                        const int slot = e / D, a = e % D;
+                        if (sown[slot] == INT_MAX) continue;
+                        const double nP = spn[slot];
+                        double gval = 0.0;
+                        if (nP != 0.0) {
+                            // Sigma_ab from the triangle: row min(a, b), column max(a, b).  Four values
+                            // are read ahead of their four FMAs (same order), so the chain waits on one
+                            // LDS round trip per four steps.
+                            const int ta = rb_tri(a, D);
+                            int tb = 0;
+                            double acc = 0.0;
+#pragma unroll 2
+                            for (int b0 = 0; b0 < D; b0 += 4) {
+                                double sv[4];
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) {
+                                    const int b = b0 + j;
+                                    sv[j] = stri[b <= a ? tb + a - b : ta + b - a];
+                                    tb += D - b;
+                                }
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) acc = fma(sv[j], (double)qpv[slot][b0 + j], acc);
+                            }
+                            gval = acc / nP;
+                        }
+                        gvs[slot][a] = gval;
+                    }
+                    if (t < ng) {
+                        skey[t] = ~0ull;
+                        sarg[t] = INT_MAX;
+                    }
+                    __syncthreads();
+                    double cs = 0.0;
+                    if (split) {
+#pragma unroll
+                        for (int q = 0; q < D / 8; ++q) rb_launder(row.p[q]);
+                        const double acc = rb_dot<T, D>(row, &gvs[sid][0]);
+                        cs = ni == 0.0 ? 0.0 : acc / ni;
+                    }
+                    if (step < 2) {
+                        const uint64_t kk = asc_key(cs);
+                        if (split) atomicMin(&skey[sid], (unsigned long long)kk);
+                        __syncthreads();
+                        if (split && kk == skey[sid]) atomicMin(&sarg[sid], t);
+                        __syncthreads();
+                        if (step == 1) cA = cs;
+                        if (t < ng) sown[t] = sarg[t];
+                        __syncthreads();
+                    } else {
+                        dk = ~asc_key(cA - cs);
+                    }
+                }
+                {
+                    uint64_t key = dk;
+                    uint32_t val = ((split ? (uint32_t)sid : 0xffffu) << 16) | (uint32_t)t;
+                    rb_bitonic_sort<NT>(key, val, tkey, tval);  // ascending (subgroup, dk, thread)
+                    tval[t] = val;
+                    __syncthreads();
+                }
+                {
+                    const uint32_t v = tval[t], grp = v >> 16;
+                    if (grp != 0xffffu && (t == 0 || (tval[t - 1] >> 16) != grp)) sstart[grp] = t;
+                    __syncthreads();  // every sorted entry has been read: tval now takes the ranks
+                    if (grp != 0xffffu) tval[v & 0xffffu] = (uint32_t)(t - sstart[grp]);
+                    __syncthreads();
+                }
+                if (split) {
+                    const int rank = (int)tval[t];
+                    const int cl = (sc + 1) / 2;
+                    if (rank < cl * BLK) {
+                        sc = cl;
+                        sid = 2 * sid;
+                    } else {
+                        sL0 += cl;
+                        sc -= cl;
+                        sid = 2 * sid + 1;
+                    }
+                } else {
+                    sid = 2 * sid;
+                }
+                if (t == 0) sany = 0;  // every thread read it many barriers ago
+                __syncthreads();
             }
-            if (step < 2) {
-                const uint64_t kk = asc_key(cs);
-                if (split) atomicMin(&skey[sid], (unsigned long long)kk);
-                __syncthreads();
-                if (split && kk == skey[sid]) atomicMin(&sarg[sid], t);
-                __syncthreads();
-                if (step == 1) cA = cs;
-                if (t < ng) sown[t] = sarg[t];
-                __syncthreads();
-            } else {
-                dk = ~asc_key(cA - cs);
+            // position inside the leaf: members of the leaf in lower waves, then lower lanes of this wave
+            const int lane = t & 63, w = t >> 6, lj = sL0 - L0;
+            uint64_t mine = 0;
+            for (int j = 0; j < c; ++j) {
+                const uint64_t m = __ballot(act && lj == j);
+                if (lane == 0) lcnt[j][w] = __popcll(m);
+                if (lj == j) mine = m;
             }
-        }
-        {
-            uint64_t key = dk;
-            uint32_t val = ((split ? (uint32_t)sid : 0xffffu) << 16) | (uint32_t)t;
-            rb_bitonic_sort<NT>(key, val, tkey, tval);  // ascending (subgroup, dk, thread)
-            tval[t] = val;
             __syncthreads();
-        }
-        {
-            const uint32_t v = tval[t], grp = v >> 16;
-            if (grp != 0xffffu && (t == 0 || (tval[t - 1] >> 16) != grp)) sstart[grp] = t;
-            __syncthreads();  // every sorted entry has been read: tval now takes the ranks
-            if (grp != 0xffffu) tval[v & 0xffffu] = (uint32_t)(t - sstart[grp]);
-            __syncthreads();
-        }
-        if (split) {
-            const int rank = (int)tval[t];
-            const int cl = (sc + 1) / 2;
-            if (rank < cl * BLK) {
-                sc = cl;
-                sid = 2 * sid;
-            } else {
-                sL0 += cl;
-                sc -= cl;
-                sid = 2 * sid + 1;
+            if (act) {
+                int r = __popcll(mine & (lane == 0 ? 0ull : (~0ull >> (64 - lane))));
+                for (int v = 0; v < w; ++v) r += lcnt[lj][v];
+                perm_all[(size_t)bh * Nv + (size_t)sL0 * BLK + r] = idx;
             }
-        } else {
-            sid = 2 * sid;
+            __syncthreads();  // this group's LDS is free for the next one
         }
-        if (t == 0) sany = 0;  // every thread read it many barriers ago
-        __syncthreads();
-    }
-    // position inside the leaf: members of the leaf in lower waves, then lower lanes of this wave
-    const int lane = t & 63, w = t >> 6, lj = sL0 - L0;
-    uint64_t mine = 0;
-    for (int j = 0; j < c; ++j) {
-        const uint64_t m = __ballot(act && lj == j);
-        if (lane == 0) lcnt[j][w] = __popcll(m);
-        if (lj == j) mine = m;
-    }
-    __syncthreads();
-    if (act) {
-        int r = __popcll(mine & (lane == 0 ? 0ull : (~0ull >> (64 - lane))));
-        for (int v = 0; v < w; ++v) r += lcnt[lj][v];
-        perm_all[(size_t)bh * Nv + (size_t)sL0 * BLK + r] = idx;
     }
 }
 
@@ -1165,7 +1199,7 @@ static void launch_reblock_t(const LaunchCtx& L, const void* Q, const void* K, i
     long long* sint = (long long*)(w + lay.sint);
     double* sigma = (double*)(w + lay.sigma);
     double* nrm = (double*)(w + lay.nrm);
-    // zero max|k| and the integer sums (one contiguous span at the start of the layout)
+    // zero max|k|, the integer sums and the group counters (one contiguous span at the start)
     const size_t zero_words = (lay.sigma - lay.kmax) / 8;
     hipLaunchKernelGGL(rb_zero_kernel, dim3(256), dim3(256), 0, L.stream, (uint64_t*)(w + lay.kmax), zero_words);
     hipLaunchKernelGGL((rb_kmax_kernel<T>), dim3(128, L.BH), dim3(256), 0, L.stream, (const T*)K, L.N, L.Nv, D, kmax);
@@ -1221,8 +1255,19 @@ static void launch_reblock_t(const LaunchCtx& L, const void* Q, const void* K, i
                            dst, dk);
     }
     if (ls < levels) {
-        hipLaunchKernelGGL((rb_subtree_kernel<T, D, kRbSubThreads>), dim3((1 << ls) * L.BH), dim3(kRbSubThreads), 0,
-                           L.stream, Qt, L.N, L.Nv, L.block, L.M, ls, levels - ls, L.BH, sigma, nrm, ord[ls & 1], perm);
+        // as many workgroups as stay resident at once; they claim the (head, group) items
+        const auto kern = rb_subtree_kernel<T, D, kRbSubThreads>;
+        const long long items = (1ll << ls) * L.BH;
+        int dev = 0, ncu = 0, per_cu = 0;
+        long long resident = 1024;  // used only if the queries fail
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kRbSubThreads, 0) == hipSuccess &&
+            ncu > 0 && per_cu > 0)
+            resident = (long long)ncu * per_cu;
+        const int grid = (int)std::min(items, resident);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(kRbSubThreads), 0, L.stream, Qt, L.N, L.Nv, L.block, L.M, ls,
+                           levels - ls, L.BH, sigma, nrm, ord[ls & 1], perm, (int32_t*)(w + lay.subq));
     }
 }
 
