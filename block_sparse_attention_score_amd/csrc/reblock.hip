@@ -922,14 +922,15 @@ __global__ __launch_bounds__(NT) void rb_chunk_split_kernel(int Nv, int BLK, int
 // g(P); the argmins are lexicographic minima in LDS (least key, then least index among that key);
 // a member goes left when fewer than ceil(c/2)*block members precede it in (dk, index) order,
 // exactly the membership the radix select and stable partition give.  That rank is the member's
-// place in its subgroup's run after one bitonic sort of all (subgroup, dk, index) triples.  At the end a token's
-// position is its leaf's start plus the number of members of the same leaf with a lower index.
+// place in its subgroup's run after one bitonic sort of all (subgroup, dk, index) triples.  At the
+// end a token's position is its leaf's start plus the number of members of the same leaf with a
+// lower index.
 // Members are in ascending index with the thread number, so thread numbers stand in for indexes
-// in every tie-break.  Workgroups run group-major (id = group * heads + head) and every eighth id
-// runs on the same XCD: at each dispatch step the XCDs take neighbouring (head, group) items, whose
-// lengths depend on the group's leaf count only, so every XCD sees the same run of lengths and
-// none holds the in-order dispatch back while the others idle; with a multiple of 8 heads an XCD
-// also reads only its own heads' data (head h on XCD h mod 8).
+// in every tie-break.  The grid holds as many workgroups as stay resident; each claims (head,
+// group) items from per-head counters, starting at head (id mod heads) so that with a multiple of 8
+// heads an XCD (every eighth workgroup id) works on its own heads, and moves to any head with
+// groups left once its own are spent.  The upper triangle of Sigma is staged once per head and
+// workgroup.
 constexpr int kRbSubThreads = 512;  // largest subtree: threads = tokens
 
 // Sort NT (key, val) pairs ascending by (val >> 16, key, val & 0xffff), thread t holding pair t in
