@@ -41,7 +41,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kRbMaxRows = 1 << 20; // int64 sums of <= 2^20 products of magnitude <= 2^42
-constexpr int kRbChunk = 2048;      // order positions per workgroup of a chunked cos pass
+constexpr int kRbChunk = 2048;      // most order positions per workgroup of a chunked cos pass
 constexpr int kRbChunkThreads = 256;
 
 static int rb_levels(int M) {
@@ -59,7 +59,7 @@ static int rb_chunks(const LaunchCtx& L, int lev) {
 }
 
 struct RbLayout {
-    size_t kmax, sint, subq, sigma, nrm, ord0, ord1, cbuf, dk, gbuf, pkey, pidx, total;
+    size_t kmax, sint, subq, sigma, nrm, ord0, ord1, cbuf, dk, c0, gbuf, pkey, pidx, total;
 };
 
 static RbLayout rb_layout(const LaunchCtx& L) {
@@ -87,6 +87,7 @@ static RbLayout rb_layout(const LaunchCtx& L) {
     r.ord1 = take(BH * Nv * 4);
     r.cbuf = take(BH * Nv * 8);
     r.dk = take(BH * Nv * 8);
+    r.c0 = take(BH * Nv * 8);  // per token: cos(., P0) of its group at the last chunked level
     r.gbuf = take(BH * gmax * d * 8);
     r.pkey = take(BH * pmax * 8);
     r.pidx = take(BH * pmax * 4);
@@ -828,10 +829,9 @@ __global__ __launch_bounds__(D) void rb_chunk_pivot_kernel(const T* __restrict__
         P = ord_in_all[(size_t)bh * Nv + s0];
     } else {
         const size_t base = ((size_t)bh * G + g) * nch;
-        const int nc = (n + kRbChunk - 1) / kRbChunk;
         uint64_t k = ~0ull;
         P = INT_MAX;
-        for (int ch = threadIdx.x; ch < nc; ch += D) {
+        for (int ch = threadIdx.x; ch < nch; ch += D) {
             const uint64_t k2 = pkey[base + ch];
             const int i2 = pidx[base + ch];
             if (rb_before(k2, i2, k, P)) {
@@ -846,11 +846,17 @@ __global__ __launch_bounds__(D) void rb_chunk_pivot_kernel(const T* __restrict__
 }
 
 // MODE 0: argmin partial of cos(., P0); 1: cos(., A) kept and argmin partial; 2: the key dk.
+// MODE 0 also keeps cos(., P0) per token in c0.  A group's P0, its first entry, is the first entry
+// of its parent too for one of the two children of every split (the partition is stable and P0
+// has the parent's lowest index); that child reads c0 instead of its rows.  ord_prev is the order
+// of the previous level (the buffer this level's split overwrites only after the cos passes), or
+// null at level 0.
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(kRbChunkThreads) void rb_chunk_cos_kernel(
     const T* __restrict__ Q, int N, int Nv, int BLK, int M, int lev, int nch, const double* __restrict__ nrm_all,
     const int32_t* __restrict__ ord_in_all, const double* __restrict__ gbuf, double* __restrict__ cbuf_all,
-    uint64_t* __restrict__ dk_all, uint64_t* __restrict__ pkey, int* __restrict__ pidx) {
+    uint64_t* __restrict__ dk_all, uint64_t* __restrict__ pkey, int* __restrict__ pidx,
+    const int32_t* __restrict__ ord_prev, double* __restrict__ c0_all) {
     constexpr int NT = kRbChunkThreads;
     __shared__ double gv[D];
     __shared__ uint64_t skey[NT / 64];
@@ -860,9 +866,17 @@ __global__ __launch_bounds__(kRbChunkThreads) void rb_chunk_cos_kernel(
     rb_group(g, lev, M, L0, c);
     if (c <= 1) return;
     const int s0 = L0 * BLK, n = min(s0 + c * BLK, Nv) - s0;
-    const int jb = ch * kRbChunk;
-    if (jb >= n) return;
-    const int je = min(n, jb + kRbChunk);
+    // the group's positions split evenly over its nch chunks (at most kRbChunk each), so that no
+    // workgroup of the pass holds many more positions than the others
+    const int jb = (int)((long long)ch * n / nch), je = (int)((long long)(ch + 1) * n / nch);
+    if (jb >= je) {  // no positions (not met at the sizes that run chunked): a neutral partial
+        if (MODE != 2 && threadIdx.x == 0) {
+            const size_t at = ((size_t)bh * G + g) * nch + ch;
+            pkey[at] = ~0ull;
+            pidx[at] = INT_MAX;
+        }
+        return;
+    }
     const double* gsrc = gbuf + ((size_t)bh * G + g) * D;
     for (int a = threadIdx.x; a < D; a += NT) gv[a] = gsrc[a];
     __syncthreads();
@@ -878,14 +892,34 @@ __global__ __launch_bounds__(kRbChunkThreads) void rb_chunk_cos_kernel(
     }
     uint64_t kmin = ~0ull;
     int P = INT_MAX;
-    rb_cos_range<T, D, NT>(Qh, nrm, seg, jb, je, gv, [&](int j, int i, double cs) {
-        if (MODE == 1) cb[j] = cs;
-        const uint64_t k = asc_key(cs);
-        if (rb_before(k, i, kmin, P)) {
-            kmin = k;
-            P = i;
+    double* c0 = MODE == 0 ? c0_all + (size_t)bh * Nv : nullptr;
+    bool inherited = false;
+    if (MODE == 0 && ord_prev) {
+        int L0p, cp;
+        rb_group(g >> 1, lev - 1, M, L0p, cp);
+        inherited = ord_prev[(size_t)bh * Nv + (size_t)L0p * BLK] == seg[0];
+    }
+    if (inherited) {
+        // the same P0 as the parent's: cos(., P0) of every member is in c0 already
+        for (int j = jb + (int)threadIdx.x; j < je; j += NT) {
+            const int i = seg[j];
+            const uint64_t k = asc_key(c0[i]);
+            if (rb_before(k, i, kmin, P)) {
+                kmin = k;
+                P = i;
+            }
         }
-    });
+    } else {
+        rb_cos_range<T, D, NT>(Qh, nrm, seg, jb, je, gv, [&](int j, int i, double cs) {
+            if (MODE == 0) c0[i] = cs;
+            if (MODE == 1) cb[j] = cs;
+            const uint64_t k = asc_key(cs);
+            if (rb_before(k, i, kmin, P)) {
+                kmin = k;
+                P = i;
+            }
+        });
+    }
     rb_argmin<NT>(kmin, P, skey, sidx);
     if (threadIdx.x == 0) {
         const size_t at = ((size_t)bh * G + g) * nch + ch;
@@ -1214,6 +1248,7 @@ static void launch_reblock_t(const LaunchCtx& L, const void* Q, const void* K, i
     int32_t* ord[2] = {(int32_t*)(w + lay.ord0), (int32_t*)(w + lay.ord1)};
     double* cbuf = (double*)(w + lay.cbuf);
     uint64_t* dk = (uint64_t*)(w + lay.dk);
+    double* c0 = (double*)(w + lay.c0);
     double* gbuf = (double*)(w + lay.gbuf);
     uint64_t* pkey = (uint64_t*)(w + lay.pkey);
     int* pidx = (int*)(w + lay.pidx);
@@ -1242,16 +1277,18 @@ static void launch_reblock_t(const LaunchCtx& L, const void* Q, const void* K, i
         const dim3 gp(G, L.BH), gc(G * nch, L.BH);
         hipLaunchKernelGGL((rb_chunk_pivot_kernel<T, D>), gp, dim3(D), 0, L.stream, Qt, L.N, L.Nv, L.block, L.M, lev,
                            nch, sigma, nrm, src, pkey, pidx, gbuf, 1);
+        // dst still holds the previous level's order (the split below is the first to write it)
         hipLaunchKernelGGL((rb_chunk_cos_kernel<T, D, 0>), gc, dim3(kRbChunkThreads), 0, L.stream, Qt, L.N, L.Nv,
-                           L.block, L.M, lev, nch, nrm, src, gbuf, cbuf, dk, pkey, pidx);
+                           L.block, L.M, lev, nch, nrm, src, gbuf, cbuf, dk, pkey, pidx, lev > 0 ? dst : nullptr,
+                           c0);
         hipLaunchKernelGGL((rb_chunk_pivot_kernel<T, D>), gp, dim3(D), 0, L.stream, Qt, L.N, L.Nv, L.block, L.M, lev,
                            nch, sigma, nrm, src, pkey, pidx, gbuf, 0);
         hipLaunchKernelGGL((rb_chunk_cos_kernel<T, D, 1>), gc, dim3(kRbChunkThreads), 0, L.stream, Qt, L.N, L.Nv,
-                           L.block, L.M, lev, nch, nrm, src, gbuf, cbuf, dk, pkey, pidx);
+                           L.block, L.M, lev, nch, nrm, src, gbuf, cbuf, dk, pkey, pidx, nullptr, nullptr);
         hipLaunchKernelGGL((rb_chunk_pivot_kernel<T, D>), gp, dim3(D), 0, L.stream, Qt, L.N, L.Nv, L.block, L.M, lev,
                            nch, sigma, nrm, src, pkey, pidx, gbuf, 0);
         hipLaunchKernelGGL((rb_chunk_cos_kernel<T, D, 2>), gc, dim3(kRbChunkThreads), 0, L.stream, Qt, L.N, L.Nv,
-                           L.block, L.M, lev, nch, nrm, src, gbuf, cbuf, dk, pkey, pidx);
+                           L.block, L.M, lev, nch, nrm, src, gbuf, cbuf, dk, pkey, pidx, nullptr, nullptr);
         hipLaunchKernelGGL((rb_chunk_split_kernel<1024>), gp, dim3(1024), 0, L.stream, L.Nv, L.block, L.M, lev, src,
                            dst, dk);
     }
