@@ -734,6 +734,18 @@ __device__ void rb_split(const uint64_t* __restrict__ dk, const int32_t* __restr
     }
 }
 
+// Whether group g of level lev has its parent's P0 (never at level 0).  The parent's segment is
+// the two children's segments one after the other, each in ascending index, so the parent's P0 (its
+// lowest index) is the lower of the two children's first entries; the child whose first entry that
+// is keeps it as its own P0, and cos(., P0) of its members is in c0 already.  It reads this level's
+// order only, which no pass of the level writes.
+__device__ __forceinline__ bool rb_keeps_p0(const int32_t* ord, int g, int lev, int M, int BLK, int first) {
+    if (lev == 0) return false;
+    int L0s, cs;
+    rb_group(g ^ 1, lev, M, L0s, cs);  // the sibling: not empty, since the parent was split
+    return first < ord[(size_t)L0s * BLK];
+}
+
 // One level for groups that fit one workgroup: workgroup (group g of this level, (batch, head)).
 // A group of one leaf is copied; a group of more leaves is split.  Every group's order segment
 // is in ascending token index (the start is the identity and every partition is stable), so
@@ -823,7 +835,7 @@ __global__ __launch_bounds__(D) void rb_chunk_pivot_kernel(const T* __restrict__
     int L0, c;
     rb_group(g, lev, M, L0, c);
     if (c <= 1) return;
-    const int s0 = L0 * BLK, n = min(s0 + c * BLK, Nv) - s0;
+    const int s0 = L0 * BLK;
     int P;
     if (first) {
         P = ord_in_all[(size_t)bh * Nv + s0];
@@ -846,17 +858,13 @@ __global__ __launch_bounds__(D) void rb_chunk_pivot_kernel(const T* __restrict__
 }
 
 // MODE 0: argmin partial of cos(., P0); 1: cos(., A) kept and argmin partial; 2: the key dk.
-// MODE 0 also keeps cos(., P0) per token in c0.  A group's P0, its first entry, is the first entry
-// of its parent too for one of the two children of every split (the partition is stable and P0
-// has the parent's lowest index); that child reads c0 instead of its rows.  ord_prev is the order
-// of the previous level (the buffer this level's split overwrites only after the cos passes), or
-// null at level 0.
+// MODE 0 also keeps cos(., P0) per token in c0 (see rb_keeps_p0).
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(kRbChunkThreads) void rb_chunk_cos_kernel(
     const T* __restrict__ Q, int N, int Nv, int BLK, int M, int lev, int nch, const double* __restrict__ nrm_all,
     const int32_t* __restrict__ ord_in_all, const double* __restrict__ gbuf, double* __restrict__ cbuf_all,
     uint64_t* __restrict__ dk_all, uint64_t* __restrict__ pkey, int* __restrict__ pidx,
-    const int32_t* __restrict__ ord_prev, double* __restrict__ c0_all) {
+    double* __restrict__ c0_all) {
     constexpr int NT = kRbChunkThreads;
     __shared__ double gv[D];
     __shared__ uint64_t skey[NT / 64];
@@ -893,13 +901,7 @@ __global__ __launch_bounds__(kRbChunkThreads) void rb_chunk_cos_kernel(
     uint64_t kmin = ~0ull;
     int P = INT_MAX;
     double* c0 = MODE == 0 ? c0_all + (size_t)bh * Nv : nullptr;
-    bool inherited = false;
-    if (MODE == 0 && ord_prev) {
-        int L0p, cp;
-        rb_group(g >> 1, lev - 1, M, L0p, cp);
-        inherited = ord_prev[(size_t)bh * Nv + (size_t)L0p * BLK] == seg[0];
-    }
-    if (inherited) {
+    if (MODE == 0 && rb_keeps_p0(ord_in_all + (size_t)bh * Nv, g, lev, M, BLK, seg[0])) {
         // the same P0 as the parent's: cos(., P0) of every member is in c0 already
         for (int j = jb + (int)threadIdx.x; j < je; j += NT) {
             const int i = seg[j];
@@ -1277,18 +1279,16 @@ static void launch_reblock_t(const LaunchCtx& L, const void* Q, const void* K, i
         const dim3 gp(G, L.BH), gc(G * nch, L.BH);
         hipLaunchKernelGGL((rb_chunk_pivot_kernel<T, D>), gp, dim3(D), 0, L.stream, Qt, L.N, L.Nv, L.block, L.M, lev,
                            nch, sigma, nrm, src, pkey, pidx, gbuf, 1);
-        // dst still holds the previous level's order (the split below is the first to write it)
         hipLaunchKernelGGL((rb_chunk_cos_kernel<T, D, 0>), gc, dim3(kRbChunkThreads), 0, L.stream, Qt, L.N, L.Nv,
-                           L.block, L.M, lev, nch, nrm, src, gbuf, cbuf, dk, pkey, pidx, lev > 0 ? dst : nullptr,
-                           c0);
+                           L.block, L.M, lev, nch, nrm, src, gbuf, cbuf, dk, pkey, pidx, c0);
         hipLaunchKernelGGL((rb_chunk_pivot_kernel<T, D>), gp, dim3(D), 0, L.stream, Qt, L.N, L.Nv, L.block, L.M, lev,
                            nch, sigma, nrm, src, pkey, pidx, gbuf, 0);
         hipLaunchKernelGGL((rb_chunk_cos_kernel<T, D, 1>), gc, dim3(kRbChunkThreads), 0, L.stream, Qt, L.N, L.Nv,
-                           L.block, L.M, lev, nch, nrm, src, gbuf, cbuf, dk, pkey, pidx, nullptr, nullptr);
+                           L.block, L.M, lev, nch, nrm, src, gbuf, cbuf, dk, pkey, pidx, nullptr);
         hipLaunchKernelGGL((rb_chunk_pivot_kernel<T, D>), gp, dim3(D), 0, L.stream, Qt, L.N, L.Nv, L.block, L.M, lev,
                            nch, sigma, nrm, src, pkey, pidx, gbuf, 0);
         hipLaunchKernelGGL((rb_chunk_cos_kernel<T, D, 2>), gc, dim3(kRbChunkThreads), 0, L.stream, Qt, L.N, L.Nv,
-                           L.block, L.M, lev, nch, nrm, src, gbuf, cbuf, dk, pkey, pidx, nullptr, nullptr);
+                           L.block, L.M, lev, nch, nrm, src, gbuf, cbuf, dk, pkey, pidx, nullptr);
         hipLaunchKernelGGL((rb_chunk_split_kernel<1024>), gp, dim3(1024), 0, L.stream, L.Nv, L.block, L.M, lev, src,
                            dst, dk);
     }
