@@ -969,38 +969,81 @@ __global__ __launch_bounds__(NT) void rb_chunk_split_kernel(int Nv, int BLK, int
 // workgroup.
 constexpr int kRbSubThreads = 512;  // largest subtree: threads = tokens
 
+// Lane l ^ J's value of v (J = 1 .. 32, a constant), by VALU cross-lane moves where one exists:
+// DPP quad permutes for 1 and 2, v_permlane16/32_swap for 16 and 32 (the swap's outputs are told
+// apart by swapping the lane numbers alongside, so the choice does not rest on their order), the
+// swizzle's bit mode for 4 and 8.
+struct RbXorLanes {
+    bool first16, first32;
+    __device__ __forceinline__ RbXorLanes() {
+        const uint32_t l = threadIdx.x & 63;
+        first16 = __builtin_amdgcn_permlane16_swap(l, l, false, false)[0] == (l ^ 16u);
+        first32 = __builtin_amdgcn_permlane32_swap(l, l, false, false)[0] == (l ^ 32u);
+    }
+    template <int J>
+    __device__ __forceinline__ uint32_t get(uint32_t v) const {
+        if constexpr (J == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+        else if constexpr (J == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+        else if constexpr (J == 4 || J == 8) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (J << 10) | 0x1F);
+        else if constexpr (J == 16) {
+            const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+            return first16 ? r[0] : r[1];
+        } else {
+            static_assert(J == 32, "lane distance");
+            const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+            return first32 ? r[0] : r[1];
+        }
+    }
+};
+
+// One compare-exchange of a bitonic network between thread t and t ^ j, given the partner's pair.
+__device__ __forceinline__ void rb_bitonic_step(uint64_t& key, uint32_t& val, uint64_t kp, uint32_t vp, int t, int j,
+                                                int k) {
+    const uint32_t g = val >> 16, gp = vp >> 16;
+    const bool after = g > gp || (g == gp && (key > kp || (key == kp && (val & 0xffffu) > (vp & 0xffffu))));
+    // ascending runs where bit k of t is clear: there the lower partner keeps the smaller
+    const bool keep_smaller = ((t & j) == 0) == ((t & k) == 0);
+    if (after == keep_smaller) {
+        key = kp;
+        val = vp;
+    }
+}
+
+template <int J>
+__device__ __forceinline__ void rb_bitonic_lane_step(uint64_t& key, uint32_t& val, const RbXorLanes& xl, int t,
+                                                     int k) {
+    const uint64_t kp = ((uint64_t)xl.get<J>((uint32_t)(key >> 32)) << 32) | xl.get<J>((uint32_t)key);
+    rb_bitonic_step(key, val, kp, xl.get<J>(val), t, J, k);
+}
+
 // Sort NT (key, val) pairs ascending by (val >> 16, key, val & 0xffff), thread t holding pair t in
-// registers: a bitonic network.  A stage whose partners are lanes of one wave exchanges through
-// shuffles; one whose partners sit in other waves goes through LDS (skey, sval), two barriers.
+// registers: a bitonic network.  Stages whose partners are lanes of one wave exchange through
+// cross-lane moves; stages whose partners sit in other waves go through LDS (skey, sval), two
+// barriers each.
 template <int NT>
 __device__ __forceinline__ void rb_bitonic_sort(uint64_t& key, uint32_t& val, uint64_t* skey, uint32_t* sval) {
     const int t = threadIdx.x;
+    const RbXorLanes xl;
 #pragma unroll 1
     for (int k = 2; k <= NT; k <<= 1) {
+        int j = k >> 1;
 #pragma unroll 1
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            uint64_t kp;
-            uint32_t vp;
-            if (j >= 64) {
-                skey[t] = key;
-                sval[t] = val;
-                __syncthreads();
-                kp = skey[t ^ j];
-                vp = sval[t ^ j];
-                __syncthreads();
-            } else {
-                kp = __shfl_xor(key, j);
-                vp = __shfl_xor(val, j);
-            }
-            const uint32_t g = val >> 16, gp = vp >> 16;
-            const bool after = g > gp || (g == gp && (key > kp || (key == kp && (val & 0xffffu) > (vp & 0xffffu))));
-            // ascending runs where bit k of t is clear: there the lower partner keeps the smaller
-            const bool keep_smaller = ((t & j) == 0) == ((t & k) == 0);
-            if (after == keep_smaller) {
-                key = kp;
-                val = vp;
-            }
+        for (; j >= 64; j >>= 1) {
+            skey[t] = key;
+            sval[t] = val;
+            __syncthreads();
+            const uint64_t kp = skey[t ^ j];
+            const uint32_t vp = sval[t ^ j];
+            __syncthreads();
+            rb_bitonic_step(key, val, kp, vp, t, j, k);
         }
+        // j = min(k / 2, 32) down to 1
+        if (j >= 32) rb_bitonic_lane_step<32>(key, val, xl, t, k);
+        if (j >= 16) rb_bitonic_lane_step<16>(key, val, xl, t, k);
+        if (j >= 8) rb_bitonic_lane_step<8>(key, val, xl, t, k);
+        if (j >= 4) rb_bitonic_lane_step<4>(key, val, xl, t, k);
+        if (j >= 2) rb_bitonic_lane_step<2>(key, val, xl, t, k);
+        rb_bitonic_lane_step<1>(key, val, xl, t, k);
     }
 }
 
