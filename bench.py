@@ -579,15 +579,20 @@ def main():
                 "frac_own_bytes": round(stage_bytes / (ms_pool * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "frac_pool_bytes": round(pool_bytes / (ms_pool * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         },
-        # select = block-score product (fp32 on the matrix cores, 2*M*M_k*d flops per head) + row
-        # top-K; its compulsory bytes (block means in, route out) are small next to the product, so
-        # the fp32 matrix rate bounds it
+        # select = block-score product (2*M*M_k*d fp32-accurate flops per head, run as six bf16
+        # part products on the matrix cores) + row top-K.  Its compulsory bytes (block means in,
+        # route out) are small next to the product, so the roofline is the product's fp32 rate;
+        # the score matrix the stage writes and reads back is reported beside it.
         "select_roofline": {"bound": "mfma", "achieved": round(sel_flops / (ms_sel * 1e-3) / 1e12, 2),
                             "peak": MFMA_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(sel_flops / (ms_sel * 1e-3) / 1e12 / MFMA_FP32_PEAK_TFLOPS, 4),
+                            "executed_bf16_TFLOPs": round(6 * sel_flops / (ms_sel * 1e-3) / 1e12, 2),
                             "bytes": sel_bytes,
                             "hbm_achieved_GBs": round(sel_bytes / (ms_sel * 1e-3) / 1e9, 1),
-                            "hbm_frac": round(sel_bytes / (ms_sel * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                            "hbm_frac": round(sel_bytes / (ms_sel * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "bytes_with_score_matrix": sel_bytes + 8.0 * B * H * M * Mk,
+                            "hbm_frac_with_score_matrix": round((sel_bytes + 8.0 * B * H * M * Mk) / (ms_sel * 1e-3)
+                                                                / 1e9 / HBM_PEAK_GBS, 4)},
         "check": check,
         "timed_output_identical_to_checked": timed_identical,
         "cpu_baseline": cpu_out,

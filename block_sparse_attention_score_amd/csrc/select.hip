@@ -3,69 +3,139 @@
 // mode keeps a fixed fraction of them; Spark-H3 page, "ワークフロー": topk_mode=topk_ratio).
 //
 // Two kernels:
-//  1. block_scores: S_IJ = s * q_mean_I . k_mean_J for every (batch, head), a batched fp32 GEMM on
-//     the fp32 matrix cores (v_mfma_f32_32x32x2_f32; 64 x 64 output tile per workgroup, 32 x 32
-//     per wave, d staged through LDS 32 at a time).  Scores must be fp32-accurate: a near-tie between the K-th and (K+1)-th block is
-//     decided by them, so no bf16 rounding is allowed here.
+//  1. block_scores: S_IJ = s * q_mean_I . k_mean_J for every (batch, head), a batched GEMM on the
+//     bf16 matrix cores (v_mfma_f32_32x32x16_bf16; 128 x 128 output tile per workgroup, 64 x 64 per
+//     wave).  Scores must be fp32-accurate: a near-tie between the K-th and (K+1)-th block is decided
+//     by them, so one bf16 rounding of the means is not allowed.  Each fp32 mean is written exactly
+//     as the sum of three bf16 parts (x = h + m + l), and the six part products whose weight is at
+//     least 2^-18 of h*h are accumulated (small ones first), which leaves an error below 2^-26 of
+//     sum |q||k| from the dropped ones: below the fp32 rounding of the sum itself.
 //  2. topk_rows: one wave per score row.  The row's scores live in registers as order-preserving
-//     integer keys (KPL per lane); the K-th largest key is found bit by bit from the top, counting
-//     keys >= candidate with wave ballots and popcounts, and stops early once exactly K keys lie
-//     above the candidate; ties at the threshold go to the lower block index; the chosen blocks
-//     are written in ascending order by a ballot/popcount compaction.  Deterministic, no atomics.
+//     integer keys (KPL per lane); the K-th largest key is found by counting keys >= a candidate
+//     with wave ballots and popcounts: first at candidates guessed from the row's mean and spread
+//     (they bracket the threshold and usually hit a candidate with exactly K keys above it, which
+//     ends the search), then bit by bit inside the bracket; ties at the threshold go to the lower
+//     block index; the chosen blocks are written in ascending order by a ballot/popcount
+//     compaction.  Deterministic, no atomics.
+#include <cmath>
+
 #include "kernels.hpp"
 
 namespace spark {
 
-constexpr int kGT = 64;   // score tile (rows and columns) of a workgroup
-constexpr int kGD = 32;   // d per LDS stage
+constexpr int kST = 128;      // score tile (rows and columns) of a workgroup
+constexpr int kSD = 32;       // d per LDS stage
+constexpr int kSP = kSD + 8;  // LDS row of a bf16 part plane (elements; 80 bytes, so the 16-byte
+                              // operand reads of 32 rows spread over the banks)
 
-// S [BH][Mq][Mk]: query-block means against key-block means.  The workgroup stages 64 rows of
-// each operand, 32 d at a time, in LDS (coalesced row reads); wave w computes the 32 x 32 tile
-// (rows 32 (w / 2), columns 32 (w % 2) of the workgroup's).  Lane (i, h) feeds row i of both
-// operands (A: a query-block mean, B: a key-block mean) with the four d values 8t + 4h .. +3 of
-// step t from one 16-byte LDS read each; MFMA j of the step takes element j, so its two k slots
-// hold d = 8t + j and 8t + 4 + j for both operands alike, and over a step every d of the eight
-// comes once.  Accumulator register r of lane (i, h) is row 8 (r / 4) + 4 h + r % 4, column i.
-__global__ __launch_bounds__(256) void block_scores_kernel(const float* __restrict__ q_mean,
-                                                           const float* __restrict__ k_mean, int Mq, int M,
-                                                           int D, float scale, float* __restrict__ S) {
-    constexpr int LD = kGD + 4;  // padded LDS row (floats)
-    __shared__ __attribute__((aligned(16))) float Qs[kGT * LD];
-    __shared__ __attribute__((aligned(16))) float Ks[kGT * LD];
-    const int bh = blockIdx.z, I0 = blockIdx.y * kGT, J0 = blockIdx.x * kGT;
-    const int t = threadIdx.x, w = t >> 6, lane = t & 63, i = lane & 31, h = lane >> 5;
+// x = h + m + l exactly, each part bf16 (round to nearest even at every step).  h is x rounded to 8
+// significant bits, so x - h is exact (Sterbenz) and holds at most 16 significant bits; m rounds that
+// to 8, and the remainder holds at most 8, so l is exact: the three parts carry every bit of x.
+// (Parts that fall below the smallest normal number may be flushed; that moves x by < 2^-126.)
+__device__ __forceinline__ void split3(float x, __bf16& h, __bf16& m, __bf16& l) {
+    h = (__bf16)x;
+    const float r1 = x - (float)h;
+    m = (__bf16)r1;
+    l = (__bf16)(r1 - (float)m);
+}
+
+// S [BH][Mq][Mk]: query-block means (A, rows) against key-block means (B, columns).  The workgroup
+// stages 128 rows of each operand, 32 d at a time: the fp32 values are read with coalesced 16-byte
+// loads, split into their three bf16 parts once, and stored as three planes.  Wave w computes rows
+// 64 (w / 2) and columns 64 (w % 2) of the tile as 2 x 2 MFMA tiles of 32 x 32.  For each 16-d step,
+// lane (i, g) feeds the 8 d values 8g .. 8g+7 of row i of A and of B (the same d for both operands,
+// as the MFMA pairs them); the part products go into one accumulator in the order l.h, m.m, h.l,
+// m.h, h.m, h.h (the dropped m.l, l.m and l.l are below 2^-26 of h.h).  Accumulator register r of
+// lane (i, g) is row 8 (r / 4) + 4 g + r % 4, column i of its 32 x 32 tile.
+__global__ __launch_bounds__(256, 2) void block_scores_kernel(const float* __restrict__ q_mean,
+                                                              const float* __restrict__ k_mean, int Mq, int M,
+                                                              int D, float scale, float* __restrict__ S) {
+    __shared__ __attribute__((aligned(16))) __bf16 As[3][kST * kSP];
+    __shared__ __attribute__((aligned(16))) __bf16 Bs[3][kST * kSP];
+    const int bh = blockIdx.z, I0 = blockIdx.y * kST, J0 = blockIdx.x * kST;
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63, i = lane & 31, g = lane >> 5;
     const float* qb = q_mean + (size_t)bh * Mq * D;
     const float* kb = k_mean + (size_t)bh * M * D;
-    const int qrow = 32 * (w >> 1) + i, krow = 32 * (w & 1) + i;
-    f32x16 acc;
+    const int r0 = 64 * (w >> 1), c0 = 64 * (w & 1);
+    f32x16 acc[2][2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    for (int d0 = 0; d0 < D; d0 += kGD) {
-        __syncthreads();
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {  // 64 rows x 32 d = 512 float4 per operand
-            const int e = t + 256 * k, r = e / 8, c = (e % 8) * 4;
-            f32x4 qv = {0.f, 0.f, 0.f, 0.f}, kv = {0.f, 0.f, 0.f, 0.f};
-            if (I0 + r < Mq) qv = *reinterpret_cast<const f32x4*>(qb + (size_t)(I0 + r) * D + d0 + c);
-            if (J0 + r < M) kv = *reinterpret_cast<const f32x4*>(kb + (size_t)(J0 + r) * D + d0 + c);
-            *reinterpret_cast<f32x4*>(&Qs[r * LD + c]) = qv;
-            *reinterpret_cast<f32x4*>(&Ks[r * LD + c]) = kv;
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+    // 128 rows x 32 d = 1024 float4 per operand, four per thread; the next stage's values are
+    // loaded before the current stage's products are issued, so the loads run under them
+    f32x4 qv[4], kv[4];
+    auto load_stage = [&](int d0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int e = t + 256 * k, r = e >> 3, c = (e & 7) * 4;
+            qv[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+            kv[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (I0 + r < Mq) qv[k] = *reinterpret_cast<const f32x4*>(qb + (size_t)(I0 + r) * D + d0 + c);
+            if (J0 + r < M) kv[k] = *reinterpret_cast<const f32x4*>(kb + (size_t)(J0 + r) * D + d0 + c);
+        }
+    };
+    load_stage(0);
+    for (int d0 = 0; d0 < D; d0 += kSD) {
+        __syncthreads();  // every wave is done with the previous stage's planes
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int e = t + 256 * k, r = e >> 3, c = (e & 7) * 4;
+            bf16x4 qh, qm, ql, kh, km, kl;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                __bf16 x0, x1, x2;
+                split3(qv[k][j], x0, x1, x2);
+                qh[j] = x0, qm[j] = x1, ql[j] = x2;
+                split3(kv[k][j], x0, x1, x2);
+                kh[j] = x0, km[j] = x1, kl[j] = x2;
+            }
+            *reinterpret_cast<bf16x4*>(&As[0][r * kSP + c]) = qh;
+            *reinterpret_cast<bf16x4*>(&As[1][r * kSP + c]) = qm;
+            *reinterpret_cast<bf16x4*>(&As[2][r * kSP + c]) = ql;
+            *reinterpret_cast<bf16x4*>(&Bs[0][r * kSP + c]) = kh;
+            *reinterpret_cast<bf16x4*>(&Bs[1][r * kSP + c]) = km;
+            *reinterpret_cast<bf16x4*>(&Bs[2][r * kSP + c]) = kl;
         }
         __syncthreads();
+        if (d0 + kSD < D) load_stage(d0 + kSD);
 #pragma unroll
-        for (int s8 = 0; s8 < kGD / 8; ++s8) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(&Qs[qrow * LD + 8 * s8 + 4 * h]);
-            const f32x4 b = *reinterpret_cast<const f32x4*>(&Ks[krow * LD + 8 * s8 + 4 * h]);
+        for (int ks = 0; ks < kSD / 16; ++ks) {
+            bf16x8 a[2][3], b[2][3];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], acc, 0, 0, 0);
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int p = 0; p < 3; ++p) {
+                    a[x][p] = *reinterpret_cast<const bf16x8*>(&As[p][(r0 + 32 * x + i) * kSP + 16 * ks + 8 * g]);
+                    b[x][p] = *reinterpret_cast<const bf16x8*>(&Bs[p][(c0 + 32 * x + i) * kSP + 16 * ks + 8 * g]);
+                }
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int y = 0; y < 2; ++y) {
+                    f32x16 c = acc[x][y];
+                    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x][2], b[y][0], c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x][1], b[y][1], c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x][0], b[y][2], c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x][1], b[y][0], c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x][0], b[y][1], c, 0, 0, 0);
+                    acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x][0], b[y][0], c, 0, 0, 0);
+                }
         }
     }
-    const int J = J0 + krow;
-    if (J >= M) return;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int I = I0 + 32 * (w >> 1) + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (I < Mq) S[((size_t)bh * Mq + I) * M + J] = scale * acc[r];
+    for (int y = 0; y < 2; ++y) {
+        const int J = J0 + c0 + 32 * y + i;
+        if (J >= M) continue;
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int I = I0 + r0 + 32 * x + 8 * (r >> 2) + 4 * g + (r & 3);
+                if (I < Mq) S[((size_t)bh * Mq + I) * M + J] = scale * acc[x][y][r];
+            }
     }
 }
 
@@ -77,77 +147,118 @@ __device__ __forceinline__ uint32_t score_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// The K largest of each of R rows held as keys in registers (lane l: block l + 64 j for j < chunks,
-// padding key 0), written to out[q][0 .. K) in ascending block order (rows with a null out are
-// skipped).  The K-th largest key T of a row is found bit by bit from the top: T takes the bit when
-// at least K keys are >= T with it (counted with wave ballots and popcounts).  When exactly K keys
-// are >= that candidate, they are the K largest, so T is their minimum and the search stops there
-// (about half the passes on continuous scores).  Ties at T go to the lower block index.  The R
-// rows' searches run interleaved (independent chains).
-template <int KPL, int R>
-__device__ __forceinline__ void topk_of_rows(const uint32_t (&key)[R][KPL], int chunks, int K,
-                                             int32_t* const (&out)[R]) {
+// Number of keys >= c in the row (c wave-uniform and >= 1, so the padding key 0 never counts).
+template <int KPL>
+__device__ __forceinline__ int count_ge(const uint32_t (&key)[KPL], uint32_t c) {
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) n += __popcll(__ballot(key[j] >= c));
+    return n;
+}
+
+__device__ __forceinline__ float uniform_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
+// The K largest of a row of M scores held in registers (lane l: block l + 64 j; f the scores, key
+// their order-preserving keys, padding key 0 past the row end), written to out[0 .. K) in ascending
+// block order.  T, the K-th largest key, is max{t : #{keys >= t} >= K}.  The search keeps a bracket
+// lo < hi of counted candidates, #{>= lo} >= K > #{>= hi}, and stops as soon as a candidate has
+// exactly K keys at or above it: those are the K largest, and T is their minimum.
+//  1. Guesses.  The row's mean mu and standard deviation sd (fp32) place the first candidate at
+//     mu + zk * sd, zk the standard normal quantile of 1 - K / M; then Newton steps with the normal
+//     density at zk (dens_c = 1 / (M * phi(zk))) until the bracket closes on both sides, then secant
+//     steps between its ends.  On block scores, whose upper tail is close to normal, this lands on
+//     an exact count after about four counts.  The guesses only choose which candidates get counted:
+//     any row distribution (ties, constant rows, NaN statistics) still ends in the exact T.
+//  2. Bit-serial completion (when no guess hit an exact count): T takes each bit from the top when at
+//     least K keys are >= T with it; candidates at or below lo take the bit and candidates at or
+//     above hi do not, without a count; the exact-count stop applies here too.
+// Ties at T go to the lower block index.
+template <int KPL>
+__device__ __forceinline__ void topk_of_row(const uint32_t (&key)[KPL], const float (&f)[KPL], int M, int K,
+                                            float zk, float dens_c, int32_t* out) {
     const int lane = threadIdx.x & 63;
-    uint32_t T[R];
-    bool done[R];
+    float s = 0.f, s2 = 0.f;
 #pragma unroll
-    for (int q = 0; q < R; ++q) {
-        T[q] = 0;
-        done[q] = out[q] == nullptr;
+    for (int j = 0; j < KPL; ++j)
+        if (lane + 64 * j < M) {
+            s += f[j];
+            s2 = fmaf(f[j], f[j], s2);
+        }
+    const float mu = uniform_f32(wave_sum(s) / (float)M);
+    const float sd = uniform_f32(sqrtf(fmaxf(wave_sum(s2) / (float)M - mu * mu, 0.f)));
+    uint32_t lo = 0;                 // #{>= 0} = M >= K
+    uint64_t hi = 1ull << 32;        // #{>= 2^32} = 0 < K
+    int c_lo = M, c_hi = 0;
+    float x_lo = 0.f, x_hi = 0.f;
+    bool has_xlo = false, has_xhi = false, exact = false;
+    float x = fmaf(zk, sd, mu);
+    for (int it = 0; it < 8; ++it) {
+        const uint32_t cand = max(score_key(x), 1u);
+        if (!(cand > lo && (uint64_t)cand < hi)) break;  // also a NaN guess
+        const int c = count_ge(key, cand);
+        if (c >= K) {
+            lo = cand, c_lo = c, x_lo = x, has_xlo = true;
+            if (c == K) {
+                exact = true;
+                break;
+            }
+        } else {
+            hi = cand, c_hi = c, x_hi = x, has_xhi = true;
+        }
+        if (has_xlo && has_xhi)
+            x = fmaf((float)(c_lo - K) / (float)(c_lo - c_hi), x_hi - x_lo, x_lo);
+        else
+            x = fmaf((float)(c - K) * dens_c, sd, x);
+        x = uniform_f32(x);
     }
-    for (int bit = 31; bit >= 0; --bit) {
-        bool all = true;
-#pragma unroll
-        for (int q = 0; q < R; ++q) all = all && done[q];
-        if (all) break;
-        int cnt[R];
-#pragma unroll
-        for (int q = 0; q < R; ++q) cnt[q] = 0;
-#pragma unroll
-        for (int j = 0; j < KPL; ++j)
-            if (j < chunks)
-#pragma unroll
-                for (int q = 0; q < R; ++q)
-                    if (!done[q]) cnt[q] += __popcll(__ballot(key[q][j] >= (T[q] | (1u << bit))));
-#pragma unroll
-        for (int q = 0; q < R; ++q) {
-            if (done[q] || cnt[q] < K) continue;
-            T[q] |= 1u << bit;
-            if (cnt[q] == K) {  // exactly the K largest are >= T: the K-th largest is their minimum
-                uint32_t m = 0xffffffffu;
-#pragma unroll
-                for (int j = 0; j < KPL; ++j)
-                    if (j < chunks && key[q][j] >= T[q]) m = min(m, key[q][j]);
-#pragma unroll
-                for (int o = 32; o >= 1; o >>= 1) m = min(m, (uint32_t)__shfl_xor((int)m, o));
-                T[q] = m;
-                done[q] = true;
+    uint32_t T = 0;
+    if (!exact) {
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = T | (1u << bit);
+            if (cand <= lo) {
+                T = cand;
+                continue;
+            }
+            if ((uint64_t)cand >= hi) continue;
+            const int c = count_ge(key, cand);
+            if (c >= K) {
+                T = lo = cand;
+                if (c == K) {
+                    exact = true;
+                    break;
+                }
+            } else {
+                hi = cand;
             }
         }
+    }
+    if (exact) {  // exactly the K largest are >= lo: the K-th largest is their minimum
+        uint32_t m = 0xffffffffu;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j)
+            if (key[j] >= lo) m = min(m, key[j]);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) m = min(m, (uint32_t)__shfl_xor((int)m, o));
+        T = m;
     }
     const uint64_t below = lanemask_lt();
+    int gt = 0;
 #pragma unroll
-    for (int q = 0; q < R; ++q) {
-        if (!out[q]) continue;
-        int gt = 0;
+    for (int j = 0; j < KPL; ++j) gt += __popcll(__ballot(key[j] > T));
+    const int need = K - gt;  // keys equal to T still to take, lowest block index first
+    int pos = 0, eq_seen = 0;
 #pragma unroll
-        for (int j = 0; j < KPL; ++j)
-            if (j < chunks) gt += __popcll(__ballot(key[q][j] > T[q]));
-        const int need = K - gt;  // keys equal to T still to take, lowest block index first
-        int pos = 0, eq_seen = 0;
-#pragma unroll
-        for (int j = 0; j < KPL; ++j) {
-            if (j < chunks) {
-                const uint32_t kk = key[q][j];
-                const uint64_t eqb = __ballot(kk == T[q]);
-                const int eq_rank = eq_seen + __popcll(eqb & below);
-                const bool sel = kk > T[q] || (kk == T[q] && eq_rank < need);
-                const uint64_t sb = __ballot(sel);
-                if (sel) out[q][pos + __popcll(sb & below)] = lane + 64 * j;
-                pos += __popcll(sb);
-                eq_seen += __popcll(eqb);
-            }
-        }
+    for (int j = 0; j < KPL; ++j) {
+        const uint32_t kk = key[j];
+        const uint64_t eqb = __ballot(kk == T);
+        const int eq_rank = eq_seen + __popcll(eqb & below);
+        const bool sel = kk > T || (kk == T && eq_rank < need);
+        const uint64_t sb = __ballot(sel);
+        if (sel) out[pos + __popcll(sb & below)] = lane + 64 * j;
+        pos += __popcll(sb);
+        eq_seen += __popcll(eqb);
     }
 }
 
@@ -155,22 +266,22 @@ __device__ __forceinline__ void topk_of_rows(const uint32_t (&key)[R][KPL], int 
 // re-read from memory on every pass (any M).
 template <int KPL>
 __global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict__ S, int rows, int M, int K,
-                                                        int32_t* __restrict__ idx) {
+                                                        float zk, float dens_c, int32_t* __restrict__ idx) {
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
     const float* Sr = S + (size_t)row * M;
-    int32_t* const out[1] = {idx + (size_t)row * K};
+    int32_t* const out = idx + (size_t)row * K;
     if constexpr (KPL > 0) {
         // every load is unconditional (from a clamped column) so that all of them are in flight
         // together; columns past the row end are then replaced by the padding key
         float f[KPL];
 #pragma unroll
         for (int j = 0; j < KPL; ++j) f[j] = Sr[min(lane + 64 * j, M - 1)];
-        uint32_t key[1][KPL];
+        uint32_t key[KPL];
 #pragma unroll
-        for (int j = 0; j < KPL; ++j) key[0][j] = lane + 64 * j < M ? score_key(f[j]) : 0u;
-        topk_of_rows<KPL, 1>(key, KPL, K, out);
+        for (int j = 0; j < KPL; ++j) key[j] = lane + 64 * j < M ? score_key(f[j]) : 0u;
+        topk_of_row<KPL>(key, f, M, K, zk, dens_c, out);
         return;
     } else {
         // the row is re-read from memory on every pass (any M)
@@ -198,7 +309,7 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict_
             const int eq_rank = eq_seen + __popcll(eqb & below);
             const bool sel = kk > T || (kk == T && eq_rank < need);
             const uint64_t sb = __ballot(sel);
-            if (sel) out[0][pos + __popcll(sb & below)] = lane + 64 * j;
+            if (sel) out[pos + __popcll(sb & below)] = lane + 64 * j;
             pos += __popcll(sb);
             eq_seen += __popcll(eqb);
         }
@@ -299,7 +410,7 @@ __global__ __launch_bounds__(256) void tau_rows_kernel(const float* __restrict__
 
 void launch_select_tau(const LaunchCtx& L, float tau, const float* q_mean, const float* k_mean, int32_t* idx,
                        int32_t* counts, float* stats, float* scores, double* partials) {
-    const dim3 sgrid((L.M + kGT - 1) / kGT, (L.M + kGT - 1) / kGT, L.BH);
+    const dim3 sgrid((L.M + kST - 1) / kST, (L.M + kST - 1) / kST, L.BH);
     hipLaunchKernelGGL(block_scores_kernel, sgrid, dim3(256), 0, L.stream, q_mean, k_mean, L.M, L.M, L.d, L.scale,
                        scores);
     hipLaunchKernelGGL(tau_partial_kernel, dim3(kTauParts, L.BH), dim3(256), 0, L.stream, scores, L.M, partials);
@@ -311,14 +422,25 @@ void launch_select_tau(const LaunchCtx& L, float tau, const float* q_mean, const
 size_t select_workspace_bytes(const LaunchCtx& L) { return (size_t)L.BH * L.M * L.Mk * 4; }
 
 void launch_select(const LaunchCtx& L, const float* q_mean, const float* k_mean, int32_t* idx, float* scores) {
-    const dim3 sgrid((L.Mk + kGT - 1) / kGT, (L.M + kGT - 1) / kGT, L.BH);
+    const dim3 sgrid((L.Mk + kST - 1) / kST, (L.M + kST - 1) / kST, L.BH);
     hipLaunchKernelGGL(block_scores_kernel, sgrid, dim3(256), 0, L.stream, q_mean, k_mean, L.M, L.Mk, L.d,
                        L.scale, scores);
     const int rows = L.BH * L.M;
     const dim3 tgrid((rows + 3) / 4);
     const int need = (L.Mk + 63) / 64;
-#define SPARK_TOPK(KPL) \
-    hipLaunchKernelGGL((topk_rows_kernel<KPL>), tgrid, dim3(256), 0, L.stream, scores, rows, L.Mk, L.K, idx)
+    // search hints for the register-resident top-K: the standard normal quantile zk of 1 - K / Mk and
+    // 1 / (Mk * phi(zk)), phi the standard normal density (they steer the search, not its result)
+    const double p = 1.0 - (double)L.K / (double)L.Mk;
+    double zlo = -8.0, zhi = 8.0;  // Phi(z) = p by bisection on Phi(z) = erfc(-z / sqrt 2) / 2
+    for (int it = 0; it < 60; ++it) {
+        const double zm = 0.5 * (zlo + zhi);
+        (0.5 * std::erfc(-zm / std::sqrt(2.0)) < p ? zlo : zhi) = zm;
+    }
+    const double zk = 0.5 * (zlo + zhi);
+    const double dens_c = 1.0 / ((double)L.Mk * std::exp(-0.5 * zk * zk) / std::sqrt(2.0 * M_PI));
+#define SPARK_TOPK(KPL)                                                                                      \
+    hipLaunchKernelGGL((topk_rows_kernel<KPL>), tgrid, dim3(256), 0, L.stream, scores, rows, L.Mk, L.K, (float)zk, \
+                       (float)dens_c, idx)
     if (need <= 1) SPARK_TOPK(1);
     else if (need <= 2) SPARK_TOPK(2);
     else if (need <= 4) SPARK_TOPK(4);
