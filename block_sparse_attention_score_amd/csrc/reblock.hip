@@ -375,87 +375,91 @@ __device__ __forceinline__ double rb_dot(const RbRow<T, D>& r, const double* gv)
     return acc;
 }
 
-// n_i for every video query, one row per thread held in registers.  t in
-// chunks of QC accumulators, each t_a one fma chain over b = 0..D-1; Sigma_ab is read as
-// Sigma[b][a] (exactly symmetric) at wave-uniform addresses, so it arrives by scalar loads and
-// feeds the FMAs from scalar registers (no LDS traffic).  Then r over a in ascending order across
-// the chunks, with the chunk's q_a read again (from cache).
-constexpr int kRbNormQC = 16;
-// rows per thread: with one the kernel needs ~115 VGPRs, so four waves per SIMD hide each other's
-// scalar-load waits (two rows: ~221 VGPRs, two waves, 1.58 ms against 1.35 ms at 720p)
-constexpr int kRbNormTPL = 1;
+// One element of a token row as raw bits (bf16 in the low half, or fp32), and its binary64 value.
+template <typename T> __device__ __forceinline__ uint32_t rb_elem_bits(const T* p);
+template <> __device__ __forceinline__ uint32_t rb_elem_bits<__bf16>(const __bf16* p) {
+    return *reinterpret_cast<const uint16_t*>(p);
+}
+template <> __device__ __forceinline__ uint32_t rb_elem_bits<float>(const float* p) {
+    return *reinterpret_cast<const uint32_t*>(p);
+}
+template <typename T> __device__ __forceinline__ double rb_bits_f64(uint32_t v) {
+    return (double)__uint_as_float(sizeof(T) == 2 ? v << 16 : v);
+}
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// n_i for every video query on the binary64 matrix cores.  v_mfma_f64_16x16x4f64 accumulates its
+// four products into C one fused multiply-add at a time, in k order (a probe on the device matched
+// the chain fma(a3 b3, fma(a2 b2, fma(a1 b1, fma(a0 b0, c)))) on 131,072 of 131,072 outputs of
+// random operands spanning 20 binades, and no other order), so a chain of these instructions over
+// k-steps 0, 1, ... is the fixed binary64 order of the norm bit for bit:
+//  * t_a = fma(Sigma_ab, q_b, t_a) over b ascending: D1 = A1 B1 with A1[i][k] = Sigma[4s+k][16c+i] (c the
+//    16-column tile of a) and B1[k][j] = q_j[4s+k], s = 0 .. D/4-1, so D1[i][j] = t_{16c+i} of row j;
+//  * r = fma(q_a, t_a, r) over a ascending: D2 = A2 B2 with A2[i][k] = q_i[4s+k] and B2[k][j] =
+//    t_{4s+k} of row j; its diagonal D2[j][j] is r of row j (the rest is not used).
+// Operand layouts (lane l, one fp64 each): A[l % 16][l / 16], B[l / 16][l % 16]; accumulator register
+// r of lane l is D[4r + l / 16][l % 16].  So B2 of step s is D1 register s % 4 of tile s / 4 in the
+// same lane, and A2 is B1: no data moves between lanes.  A wave takes 16 rows at a time (lane l:
+// row l % 16, its elements b = l / 16 mod 4); Sigma of the (batch, head) sits in LDS (128 KB at
+// d = 128), staged once per head; the resident workgroups split the (head, 16-row block) items
+// evenly.
+constexpr int kRbNrmWaves = 8;
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void rb_norms_kernel(const T* __restrict__ Q, int N, int Nv,
-                                                       const double* __restrict__ sigma, double* __restrict__ nrm) {
-    constexpr int QC = kRbNormQC, TPL = kRbNormTPL, NK = D / 8;
-    const int bh = blockIdx.y, i0 = blockIdx.x * 256 * TPL + threadIdx.x;
-    const T* q[TPL];
-    RbRow<T, D> row[TPL];
+__global__ __launch_bounds__(64 * kRbNrmWaves) void rb_norms_kernel(const T* __restrict__ Q, int N, int Nv, int BH,
+                                                                    const double* __restrict__ sigma,
+                                                                    double* __restrict__ nrm) {
+    __shared__ __attribute__((aligned(16))) double sS[D * D];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, jr = lane & 15, kq = lane >> 4;
+    const long long nb = (Nv + 15) / 16, items = nb * BH;
+    const long long i0 = items * blockIdx.x / gridDim.x, i1 = items * (blockIdx.x + 1) / gridDim.x;
+    for (long long seg = i0; seg < i1;) {
+        const int bh = (int)(seg / nb);
+        const long long seg_end = min(i1, (long long)(bh + 1) * nb);
+        __syncthreads();  // the previous head's Sigma is no longer read
+        const f64x2* src = reinterpret_cast<const f64x2*>(sigma + (size_t)bh * D * D);
+        for (int e = threadIdx.x; e < D * D / 2; e += 64 * kRbNrmWaves) reinterpret_cast<f64x2*>(sS)[e] = src[e];
+        __syncthreads();
+        // lane l needs only the elements b = 4s + l / 16 of its row: D / 4 loads per block, and the
+        // next block's are in flight while this block's products run
+        uint32_t qc[D / 4], qn[D / 4];
+        auto load_q = [&](uint32_t (&dst)[D / 4], long long item) __attribute__((always_inline)) {
+            const int rw = min((int)(item - (long long)bh * nb) * 16 + jr, Nv - 1);
+            const T* src = Q + ((size_t)bh * N + rw) * D + kq;
 #pragma unroll
-    for (int u = 0; u < TPL; ++u) {
-        q[u] = Q + ((size_t)bh * N + min(i0 + 256 * u, Nv - 1)) * D;
-        row[u].load(q[u]);
-    }
-    const double* S = sigma + (size_t)bh * D * D;
-    double r[TPL];
+            for (int s = 0; s < D / 4; ++s) dst[s] = rb_elem_bits<T>(src + 4 * s);
+        };
+        if (seg + w < seg_end) load_q(qc, seg + w);
+        for (long long it = seg + w; it < seg_end; it += kRbNrmWaves) {
+            const int row = (int)(it - (long long)bh * nb) * 16 + jr;
+            if (it + kRbNrmWaves < seg_end) load_q(qn, it + kRbNrmWaves);
+            f64x4 t[D / 16];
 #pragma unroll
-    for (int u = 0; u < TPL; ++u) r[u] = 0.0;
-#pragma unroll 1
-    for (int h0 = 0; h0 < D; h0 += QC) {
-        double t[TPL][QC];
+            for (int c = 0; c < D / 16; ++c) t[c] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int u = 0; u < TPL; ++u)
-#pragma unroll
-            for (int a = 0; a < QC; ++a) t[u][a] = 0.0;
-        // row b+1 of the chunk's Sigma columns is requested before row b is used (two rows in
-        // scalar registers); the scheduling barriers keep the compiler from hoisting every row's
-        // loads to the top, which would spill the scalar registers
-        double sr[2][QC];
-#pragma unroll
-        for (int a = 0; a < QC; ++a) sr[0][a] = S[h0 + a];
-        // widen the rows again in every chunk rather than keep them widened in four times the registers
-#pragma unroll
-        for (int u = 0; u < TPL; ++u)
-#pragma unroll
-            for (int k = 0; k < NK; ++k) rb_launder(row[u].p[k]);
-#pragma unroll
-        for (int k = 0; k < NK; ++k) {
-            float v[TPL][8];
-#pragma unroll
-            for (int u = 0; u < TPL; ++u) row[u].p[k].widen(v[u]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int b = 8 * k + e;
+            for (int s = 0; s < D / 4; ++s) {
+                // keeps the compiler from hoisting the LDS reads of every step to the top (they
+                // would need 2 * D * D / 64 registers)
                 __builtin_amdgcn_sched_barrier(0);
-                if (b + 1 < D)
+                const double qb = rb_bits_f64<T>(qc[s]);
 #pragma unroll
-                    for (int a = 0; a < QC; ++a) sr[(b + 1) & 1][a] = S[(size_t)(b + 1) * D + h0 + a];
-#pragma unroll
-                for (int a = 0; a < QC; ++a)
-#pragma unroll
-                    for (int u = 0; u < TPL; ++u) t[u][a] = fma(sr[b & 1][a], (double)v[u][e], t[u][a]);
+                for (int c = 0; c < D / 16; ++c)
+                    t[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(sS[(4 * s + kq) * D + 16 * c + jr], qb, t[c], 0, 0, 0);
             }
-        }
-        __builtin_amdgcn_sched_barrier(0);
+            f64x4 r = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int u = 0; u < TPL; ++u) {
-            Raw8<T> qa[QC / 8];
-#pragma unroll
-            for (int k = 0; k < QC / 8; ++k) qa[k].load(q[u] + h0 + 8 * k);
-#pragma unroll
-            for (int k = 0; k < QC / 8; ++k) {
-                float v[8];
-                qa[k].widen(v);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) r[u] = fma((double)v[e], t[u][8 * k + e], r[u]);
+            for (int s = 0; s < D / 4; ++s)
+                r = __builtin_amdgcn_mfma_f64_16x16x4f64(rb_bits_f64<T>(qc[s]), t[s >> 2][s & 3], r, 0, 0, 0);
+            // the diagonal: row jr's r is register jr / 4 of the lane with l / 16 = jr % 4
+            if ((jr & 3) == kq && row < Nv) {
+                const double v = r[jr >> 2];
+                nrm[(size_t)bh * Nv + row] = v > 0.0 ? sqrt(v) : 0.0;
             }
-        }
-    }
 #pragma unroll
-    for (int u = 0; u < TPL; ++u) {
-        const int i = i0 + 256 * u;
-        if (i < Nv) nrm[(size_t)bh * Nv + i] = r[u] > 0.0 ? sqrt(r[u]) : 0.0;
+            for (int s = 0; s < D / 4; ++s) qc[s] = qn[s];
+        }
+        seg = seg_end;
     }
 }
 
@@ -1287,9 +1291,22 @@ static void launch_reblock_t(const LaunchCtx& L, const void* Q, const void* K, i
                        dim3(RbSig<D>::NT), 0, L.stream, (const T*)K, L.N, L.Nv, kmax, sint);
     hipLaunchKernelGGL(rb_sigma_finalize_kernel, dim3((D * D + 255) / 256, L.BH), dim3(256), 0, L.stream, sint, kmax,
                        D, L.Nv, sigma);
-    hipLaunchKernelGGL((rb_norms_kernel<T, D>), dim3((L.Nv + 256 * kRbNormTPL - 1) / (256 * kRbNormTPL), L.BH),
-                       dim3(256), 0, L.stream, (const T*)Q,
-                       L.N, L.Nv, sigma, nrm);
+    {
+        // as many workgroups as stay resident at once (one per CU at d = 128: Sigma fills the LDS),
+        // each an even share of the (head, 16-row block) items
+        const auto kern = rb_norms_kernel<T, D>;
+        const long long items = (long long)L.BH * ((L.Nv + 15) / 16);
+        int dev = 0, ncu = 0, per_cu = 0;
+        long long resident = 256;  // used only if the queries fail
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * kRbNrmWaves, 0) == hipSuccess &&
+            ncu > 0 && per_cu > 0)
+            resident = (long long)ncu * per_cu;
+        const int grid = (int)std::min(items, resident);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kRbNrmWaves), 0, L.stream, (const T*)Q, L.N, L.Nv, L.BH, sigma,
+                           nrm);
+    }
     int32_t* ord[2] = {(int32_t*)(w + lay.ord0), (int32_t*)(w + lay.ord1)};
     double* cbuf = (double*)(w + lay.cbuf);
     uint64_t* dk = (uint64_t*)(w + lay.dk);
