@@ -7,9 +7,10 @@
 //     bf16 matrix cores (v_mfma_f32_32x32x16_bf16; 128 x 128 output tile per workgroup, 64 x 64 per
 //     wave).  Scores must be fp32-accurate: a near-tie between the K-th and (K+1)-th block is decided
 //     by them, so one bf16 rounding of the means is not allowed.  Each fp32 mean is written exactly
-//     as the sum of three bf16 parts (x = h + m + l), and the six part products whose weight is at
-//     least 2^-18 of h*h are accumulated (small ones first), which leaves an error below 2^-26 of
-//     sum |q||k| from the dropped ones: below the fp32 rounding of the sum itself.
+//     as the sum of three bf16 parts (x = h + m + l, |m| <= 2^-8 |x|, |l| <= 2^-16 |x|), and the
+//     six part products of weight at least 2^-16 are accumulated (small ones first).  The dropped
+//     ones (m.l, l.m, l.l) stay below 2^-23 of sum |q||k|, under the worst-case fp32 rounding of
+//     a d-term sum (about d * 2^-24).
 //  2. topk_rows: one wave per score row.  The row's scores live in registers as order-preserving
 //     integer keys (KPL per lane); the K-th largest key is found by counting keys >= a candidate
 //     with wave ballots and popcounts: first at candidates guessed from the row's mean and spread
@@ -45,7 +46,7 @@ __device__ __forceinline__ void split3(float x, __bf16& h, __bf16& m, __bf16& l)
 // 64 (w / 2) and columns 64 (w % 2) of the tile as 2 x 2 MFMA tiles of 32 x 32.  For each 16-d step,
 // lane (i, g) feeds the 8 d values 8g .. 8g+7 of row i of A and of B (the same d for both operands,
 // as the MFMA pairs them); the part products go into one accumulator in the order l.h, m.m, h.l,
-// m.h, h.m, h.h (the dropped m.l, l.m and l.l are below 2^-26 of h.h).  Accumulator register r of
+// m.h, h.m, h.h (the dropped m.l, l.m and l.l are below 2^-23 of h.h).  Accumulator register r of
 // lane (i, g) is row 8 (r / 4) + 4 g + r % 4, column i of its 32 x 32 tile.
 __global__ __launch_bounds__(256, 2) void block_scores_kernel(const float* __restrict__ q_mean,
                                                               const float* __restrict__ k_mean, int Mq, int M,
