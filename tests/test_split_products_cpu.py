@@ -4,7 +4,7 @@ parts, and the three part products the matrix-core kernel drops stay below 2^-23
 The block scores decide the route, so they must be fp32-accurate (near-tie window 1e-4 relative).
 The kernel runs them on bf16 MFMA by splitting each fp32 mean x into h = bf16(x),
 m = bf16(x - h), l = bf16(x - h - m) (round to nearest even at each step) and accumulating the six
-part products h.h, h.m, m.h, h.l, m.m, l.h.  These tests check both facts that makes the product
+part products h.h, h.m, m.h, h.l, m.m, l.h.  These tests check the facts that make the product
 fp32-accurate, in binary64 where every sum below is exact.
 """
 import os
