@@ -165,7 +165,8 @@ __device__ __forceinline__ float uniform_f32(float v) {
 // their order-preserving keys, padding key 0 past the row end), written to out[0 .. K) in ascending
 // block order.  T, the K-th largest key, is max{t : #{keys >= t} >= K}.  The search keeps a bracket
 // lo < hi of counted candidates, #{>= lo} >= K > #{>= hi}, and stops as soon as a candidate has
-// exactly K keys at or above it: those are the K largest, and T is their minimum.
+// exactly K keys at or above it: those are the K largest, written out as they are (no key outside
+// them equals one inside, so no tie is left to break).
 //  1. Guesses.  The row's mean mu and standard deviation sd (fp32) place the first candidate at
 //     mu + zk * sd, zk the standard normal quantile of 1 - K / M; then Newton steps with the normal
 //     density at zk (dens_c = 1 / (M * phi(zk))) until the bracket closes on both sides, then secant
@@ -175,7 +176,7 @@ __device__ __forceinline__ float uniform_f32(float v) {
 //  2. Bit-serial completion (when no guess hit an exact count): T takes each bit from the top when at
 //     least K keys are >= T with it; candidates at or below lo take the bit and candidates at or
 //     above hi do not, without a count; the exact-count stop applies here too.
-// Ties at T go to the lower block index.
+// Otherwise T is exact and ties at T go to the lower block index.
 template <int KPL>
 __device__ __forceinline__ void topk_of_row(const uint32_t (&key)[KPL], const float (&f)[KPL], int M, int K,
                                             float zk, float dens_c, int32_t* out) {
@@ -235,16 +236,17 @@ __device__ __forceinline__ void topk_of_row(const uint32_t (&key)[KPL], const fl
             }
         }
     }
-    if (exact) {  // exactly the K largest are >= lo: the K-th largest is their minimum
-        uint32_t m = 0xffffffffu;
+    if (exact) {  // exactly the K largest are >= lo: they are the output, with no tie to break
+        int pos = 0;
 #pragma unroll
-        for (int j = 0; j < KPL; ++j)
-            if (key[j] >= lo) m = min(m, key[j]);
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) m = min(m, (uint32_t)__shfl_xor((int)m, o));
-        T = m;
+        for (int j = 0; j < KPL; ++j) {
+            const bool sel = key[j] >= lo;
+            const uint64_t sb = __ballot(sel);
+            if (sel) out[pos + rank_below(sb)] = lane + 64 * j;
+            pos += __popcll(sb);
+        }
+        return;
     }
-    const uint64_t below = lanemask_lt();
     int gt = 0;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) gt += __popcll(__ballot(key[j] > T));
@@ -254,10 +256,10 @@ __device__ __forceinline__ void topk_of_row(const uint32_t (&key)[KPL], const fl
     for (int j = 0; j < KPL; ++j) {
         const uint32_t kk = key[j];
         const uint64_t eqb = __ballot(kk == T);
-        const int eq_rank = eq_seen + __popcll(eqb & below);
+        const int eq_rank = eq_seen + rank_below(eqb);
         const bool sel = kk > T || (kk == T && eq_rank < need);
         const uint64_t sb = __ballot(sel);
-        if (sel) out[pos + __popcll(sb & below)] = lane + 64 * j;
+        if (sel) out[pos + rank_below(sb)] = lane + 64 * j;
         pos += __popcll(sb);
         eq_seen += __popcll(eqb);
     }
@@ -269,16 +271,20 @@ template <int KPL>
 __global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict__ S, int rows, int M, int K,
                                                         float zk, float dens_c, int32_t* __restrict__ idx) {
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));  // one row per wave
     if (row >= rows) return;
     const float* Sr = S + (size_t)row * M;
     int32_t* const out = idx + (size_t)row * K;
     if constexpr (KPL > 0) {
-        // every load is unconditional (from a clamped column) so that all of them are in flight
-        // together; columns past the row end are then replaced by the padding key
+        // every load is unconditional so that all of them are in flight together: buffer loads with
+        // the row as the buffer's extent (a column past the row end reads 0), one offset register
+        // and the column step in the instruction; those columns then take the padding key
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(Sr), (short)0, M * 4, 0x00020000);
         float f[KPL];
 #pragma unroll
-        for (int j = 0; j < KPL; ++j) f[j] = Sr[min(lane + 64 * j, M - 1)];
+        for (int j = 0; j < KPL; ++j)
+            f[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4 + 256 * j, 0, 0));
         uint32_t key[KPL];
 #pragma unroll
         for (int j = 0; j < KPL; ++j) key[j] = lane + 64 * j < M ? score_key(f[j]) : 0u;
