@@ -137,9 +137,4 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// number of set bits of a wave mask m in the lanes below this one (two mbcnt instructions)
-__device__ __forceinline__ int rank_below(uint64_t m) {
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
 }  // namespace spark

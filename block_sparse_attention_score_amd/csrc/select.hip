@@ -53,7 +53,14 @@ __global__ __launch_bounds__(256, 2) void block_scores_kernel(const float* __res
                                                               int D, float scale, float* __restrict__ S) {
     __shared__ __attribute__((aligned(16))) __bf16 As[3][kST * kSP];
     __shared__ __attribute__((aligned(16))) __bf16 Bs[3][kST * kSP];
-    const int bh = blockIdx.z, I0 = blockIdx.y * kST, J0 = blockIdx.x * kST;
+    // Workgroup w runs on XCD w % 8.  Tiles are numbered row band by row band (column tile fastest)
+    // and each XCD takes one contiguous run of them, so the column tiles of a band run side by side
+    // on one XCD: the cache lines that straddle two column tiles (rows are not line-aligned) are
+    // completed in that XCD's L2 and written back once, and a head's operands stay in one L2.
+    const int n = gridDim.x, q8 = n >> 3, r8 = n & 7, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int tile = xcd < r8 ? xcd * (q8 + 1) + slot : r8 * (q8 + 1) + (xcd - r8) * q8 + slot;
+    const int gx = (M + kST - 1) / kST, gy = (Mq + kST - 1) / kST;
+    const int bh = tile / (gx * gy), I0 = (tile / gx % gy) * kST, J0 = (tile % gx) * kST;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63, i = lane & 31, g = lane >> 5;
     const float* qb = q_mean + (size_t)bh * Mq * D;
     const float* kb = k_mean + (size_t)bh * M * D;
@@ -149,6 +156,11 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 }
 
 // Number of keys >= c in the row (c wave-uniform and >= 1, so the padding key 0 never counts).
+// number of set bits of a wave mask m in the lanes below this one (two mbcnt instructions)
+__device__ __forceinline__ int rank_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 template <int KPL>
 __device__ __forceinline__ int count_ge(const uint32_t (&key)[KPL], uint32_t c) {
     int n = 0;
@@ -417,7 +429,7 @@ __global__ __launch_bounds__(256) void tau_rows_kernel(const float* __restrict__
 
 void launch_select_tau(const LaunchCtx& L, float tau, const float* q_mean, const float* k_mean, int32_t* idx,
                        int32_t* counts, float* stats, float* scores, double* partials) {
-    const dim3 sgrid((L.M + kST - 1) / kST, (L.M + kST - 1) / kST, L.BH);
+    const dim3 sgrid(((L.M + kST - 1) / kST) * ((L.M + kST - 1) / kST) * L.BH);
     hipLaunchKernelGGL(block_scores_kernel, sgrid, dim3(256), 0, L.stream, q_mean, k_mean, L.M, L.M, L.d, L.scale,
                        scores);
     hipLaunchKernelGGL(tau_partial_kernel, dim3(kTauParts, L.BH), dim3(256), 0, L.stream, scores, L.M, partials);
@@ -429,7 +441,7 @@ void launch_select_tau(const LaunchCtx& L, float tau, const float* q_mean, const
 size_t select_workspace_bytes(const LaunchCtx& L) { return (size_t)L.BH * L.M * L.Mk * 4; }
 
 void launch_select(const LaunchCtx& L, const float* q_mean, const float* k_mean, int32_t* idx, float* scores) {
-    const dim3 sgrid((L.Mk + kST - 1) / kST, (L.M + kST - 1) / kST, L.BH);
+    const dim3 sgrid(((L.Mk + kST - 1) / kST) * ((L.M + kST - 1) / kST) * L.BH);
     hipLaunchKernelGGL(block_scores_kernel, sgrid, dim3(256), 0, L.stream, q_mean, k_mean, L.M, L.Mk, L.d,
                        L.scale, scores);
     const int rows = L.BH * L.M;
