@@ -26,8 +26,12 @@ namespace spark {
 
 constexpr int kST = 128;      // score tile (rows and columns) of a workgroup
 constexpr int kSD = 32;       // d per LDS stage
-constexpr int kSP = kSD + 8;  // LDS row of a bf16 part plane (elements; 80 bytes, so the 16-byte
-                              // operand reads of 32 rows spread over the banks)
+constexpr int kSP = kSD;      // LDS row of a bf16 part plane (elements, 64 bytes, four 16-byte chunks)
+
+// LDS element offset of element c of row r in a part plane: the 16-byte chunk index is XORed with
+// bits 1..2 of the row, so the 16-byte operand reads of 8 consecutive rows at one chunk touch 8
+// different 16-byte bank groups (two rows per 128 bytes, four chunk positions each)
+__device__ __forceinline__ int plane_at(int r, int c) { return r * kSP + ((((c >> 3) ^ (r >> 1)) & 3) << 3) + (c & 7); }
 
 // x = h + m + l exactly, each part bf16 (round to nearest even at every step).  h is x rounded to 8
 // significant bits, so x - h is exact (Sterbenz) and holds at most 16 significant bits; m rounds that
@@ -48,7 +52,7 @@ __device__ __forceinline__ void split3(float x, __bf16& h, __bf16& m, __bf16& l)
 // as the MFMA pairs them); the part products go into one accumulator in the order l.h, m.m, h.l,
 // m.h, h.m, h.h (the dropped m.l, l.m and l.l are below 2^-23 of h.h).  Accumulator register r of
 // lane (i, g) is row 8 (r / 4) + 4 g + r % 4, column i of its 32 x 32 tile.
-__global__ __launch_bounds__(256, 2) void block_scores_kernel(const float* __restrict__ q_mean,
+__global__ __launch_bounds__(256, 3) void block_scores_kernel(const float* __restrict__ q_mean,
                                                               const float* __restrict__ k_mean, int Mq, int M,
                                                               int D, float scale, float* __restrict__ S) {
     __shared__ __attribute__((aligned(16))) __bf16 As[3][kST * kSP];
@@ -100,12 +104,13 @@ __global__ __launch_bounds__(256, 2) void block_scores_kernel(const float* __res
                 split3(kv[k][j], x0, x1, x2);
                 kh[j] = x0, km[j] = x1, kl[j] = x2;
             }
-            *reinterpret_cast<bf16x4*>(&As[0][r * kSP + c]) = qh;
-            *reinterpret_cast<bf16x4*>(&As[1][r * kSP + c]) = qm;
-            *reinterpret_cast<bf16x4*>(&As[2][r * kSP + c]) = ql;
-            *reinterpret_cast<bf16x4*>(&Bs[0][r * kSP + c]) = kh;
-            *reinterpret_cast<bf16x4*>(&Bs[1][r * kSP + c]) = km;
-            *reinterpret_cast<bf16x4*>(&Bs[2][r * kSP + c]) = kl;
+            const int o = plane_at(r, c);
+            *reinterpret_cast<bf16x4*>(&As[0][o]) = qh;
+            *reinterpret_cast<bf16x4*>(&As[1][o]) = qm;
+            *reinterpret_cast<bf16x4*>(&As[2][o]) = ql;
+            *reinterpret_cast<bf16x4*>(&Bs[0][o]) = kh;
+            *reinterpret_cast<bf16x4*>(&Bs[1][o]) = km;
+            *reinterpret_cast<bf16x4*>(&Bs[2][o]) = kl;
         }
         __syncthreads();
         if (d0 + kSD < D) load_stage(d0 + kSD);
@@ -116,8 +121,8 @@ __global__ __launch_bounds__(256, 2) void block_scores_kernel(const float* __res
             for (int x = 0; x < 2; ++x)
 #pragma unroll
                 for (int p = 0; p < 3; ++p) {
-                    a[x][p] = *reinterpret_cast<const bf16x8*>(&As[p][(r0 + 32 * x + i) * kSP + 16 * ks + 8 * g]);
-                    b[x][p] = *reinterpret_cast<const bf16x8*>(&Bs[p][(c0 + 32 * x + i) * kSP + 16 * ks + 8 * g]);
+                    a[x][p] = *reinterpret_cast<const bf16x8*>(&As[p][plane_at(r0 + 32 * x + i, 16 * ks + 8 * g)]);
+                    b[x][p] = *reinterpret_cast<const bf16x8*>(&Bs[p][plane_at(c0 + 32 * x + i, 16 * ks + 8 * g)]);
                 }
 #pragma unroll
             for (int x = 0; x < 2; ++x)
