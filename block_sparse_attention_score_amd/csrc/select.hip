@@ -179,7 +179,7 @@ __device__ __forceinline__ float uniform_f32(float v) {
 }
 
 // The K largest of a row of M scores held in registers (lane l: block l + 64 j; f the scores, key
-// their order-preserving keys, padding key 0 past the row end), written to out[0 .. K) in ascending
+// their order-preserving keys; past the row end f holds 0 and key the padding key 0), written to out[0 .. K) in ascending
 // block order.  T, the K-th largest key, is max{t : #{keys >= t} >= K}.  The search keeps a bracket
 // lo < hi of counted candidates, #{>= lo} >= K > #{>= hi}, and stops as soon as a candidate has
 // exactly K keys at or above it: those are the K largest, written out as they are (no key outside
@@ -198,13 +198,12 @@ template <int KPL>
 __device__ __forceinline__ void topk_of_row(const uint32_t (&key)[KPL], const float (&f)[KPL], int M, int K,
                                             float zk, float dens_c, int32_t* out) {
     const int lane = threadIdx.x & 63;
-    float s = 0.f, s2 = 0.f;
+    float s = 0.f, s2 = 0.f;  // columns past the row end hold 0 in f and add nothing
 #pragma unroll
-    for (int j = 0; j < KPL; ++j)
-        if (lane + 64 * j < M) {
-            s += f[j];
-            s2 = fmaf(f[j], f[j], s2);
-        }
+    for (int j = 0; j < KPL; ++j) {
+        s += f[j];
+        s2 = fmaf(f[j], f[j], s2);
+    }
     const float mu = uniform_f32(wave_sum(s) / (float)M);
     const float sd = uniform_f32(sqrtf(fmaxf(wave_sum(s2) / (float)M - mu * mu, 0.f)));
     uint32_t lo = 0;                 // #{>= 0} = M >= K
