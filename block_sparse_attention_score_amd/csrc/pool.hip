@@ -17,6 +17,17 @@ template <int D> struct PoolGeom {
     static constexpr int RG = 256 / CH;
 };
 
+// Element j of eight loaded consecutive elements, as fp32; and the eight set to zero.
+__device__ __forceinline__ float raw_elem(const Raw8<__bf16>& r, int j) {
+    return bf16_bits_to_f32((j & 1) ? r.u[j >> 1] >> 16 : r.u[j >> 1] & 0xffffu);
+}
+__device__ __forceinline__ float raw_elem(const Raw8<float>& r, int j) { return j < 4 ? r.a[j] : r.b[j - 4]; }
+__device__ __forceinline__ void raw_zero(Raw8<__bf16>& r) { r.u = u32x4{0u, 0u, 0u, 0u}; }
+__device__ __forceinline__ void raw_zero(Raw8<float>& r) {
+    r.a = f32x4{0.f, 0.f, 0.f, 0.f};
+    r.b = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
 // AMAX: also raise amax_q (float bits; non-negative floats order as unsigned integers) to the
 // largest |q| of the block, for the E4M3 scales.
 template <typename T, int D, int BLK, bool AMAX>
@@ -98,7 +109,7 @@ __global__ __launch_bounds__(kAnchorThreads) void anchor_kernel(const float* __r
 // real keys, -inf for padding), so that K and V are read from HBM once for both.
 // MODE 2 (amax): it also raises amax_k and amax_v to the block's largest |k| and |v| (E4M3 scales).
 template <typename T, int D, int BLK, bool REWEIGHT, int MODE>
-__global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, const T* __restrict__ V,
+__global__ __launch_bounds__(256, 3) void pool_kv_kernel(const T* __restrict__ K, const T* __restrict__ V,
                                                       const float* __restrict__ anchor, int N, int Nv,
                                                       int M, float scale, float* __restrict__ k_mean,
                                                       float* __restrict__ k_sum, float* __restrict__ v_sum,
@@ -121,16 +132,16 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, c
         kraw[k].load(K + off + ro);
         vraw[k].load(V + off + ro);
     }
-    float kr[RPT][8], vr[RPT][8];
+    // rows past the block end are zero from here on; element j of a row is widened where it is used
+    // (a shift or a mask for bf16), so the rows stay in registers at their loaded width
 #pragma unroll
-    for (int k = 0; k < RPT; ++k) {
-        kraw[k].widen(kr[k]);
-        vraw[k].widen(vr[k]);
+    for (int k = 0; k < RPT; ++k)
         if (rg + k * G::RG >= n) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) { kr[k][j] = 0.f; vr[k][j] = 0.f; }
+            raw_zero(kraw[k]);
+            raw_zero(vraw[k]);
         }
-    }
+    auto kr = [&](int k, int j) __attribute__((always_inline)) { return raw_elem(kraw[k], j); };
+    auto vr = [&](int k, int j) __attribute__((always_inline)) { return raw_elem(vraw[k], j); };
 
     if constexpr (MODE == 2) {
         float ak = 0.f, av = 0.f;  // rows past the block end are zero here
@@ -138,8 +149,8 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, c
         for (int k = 0; k < RPT; ++k)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                ak = fmaxf(ak, fabsf(kr[k][j]));
-                av = fmaxf(av, fabsf(vr[k][j]));
+                ak = fmaxf(ak, fabsf(kr(k, j)));
+                av = fmaxf(av, fabsf(vr(k, j)));
             }
         ak = wave_max(ak);
         av = wave_max(av);
@@ -176,8 +187,11 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, c
                         kb = kraw[k].u;  // the input bits, unchanged
                         vb = vraw[k].u;
                     } else {
-                        kb = pack8_bf16(kr[k]);
-                        vb = pack8_bf16(vr[k]);
+                        float kf[8], vf[8];
+                        kraw[k].widen(kf);
+                        vraw[k].widen(vf);
+                        kb = pack8_bf16(kf);
+                        vb = pack8_bf16(vf);
                     }
                 }
                 *reinterpret_cast<u32x4*>(packed + (tile0 + (r >> 6)) * (2 * 64 * D) + (r & 63) * D + c * 8) = kb;
@@ -203,9 +217,10 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, c
         }
     }
 
-    __shared__ float red_k[G::RG][D];
-    __shared__ float red_w[G::RG][D];
-    __shared__ float red_v[G::RG][D];
+    // column sums: first over the row groups of a wave (shuffles), then over the 4 waves (LDS)
+    __shared__ float red_k[4][D];
+    __shared__ float red_w[4][D];
+    __shared__ float red_v[4][D];
     __shared__ float red_s[G::RG];
     __shared__ float bcast[2];
 
@@ -214,7 +229,7 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, c
     for (int j = 0; j < 8; ++j) {
         ks[j] = 0.f;
 #pragma unroll
-        for (int k = 0; k < RPT; ++k) ks[j] += kr[k][j];
+        for (int k = 0; k < RPT; ++k) ks[j] += kr(k, j);
     }
 
     float m = 0.f, Z = (float)n;
@@ -227,7 +242,7 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, c
         for (int k = 0; k < RPT; ++k) {
             float pd = 0.f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) pd += a[j] * kr[k][j];
+            for (int j = 0; j < 8; ++j) pd += a[j] * kr(k, j);
             // the CH threads of one row group are consecutive lanes of one wave
 #pragma unroll
             for (int o = 1; o < G::CH; o <<= 1) pd += __shfl_xor(pd, o);
@@ -252,7 +267,7 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, c
             const float e = rg + k * G::RG < n ? expf(x[k] - m) : 0.f;
             zloc += e;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) { wk[j] += e * kr[k][j]; wv[j] += e * vr[k][j]; }
+            for (int j = 0; j < 8; ++j) { wk[j] += e * kr(k, j); wv[j] += e * vr(k, j); }
         }
         __syncthreads();  // red_s reuse
         if (c == 0) red_s[rg] = zloc;
@@ -262,14 +277,24 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, c
             wk[j] = ks[j];
             wv[j] = 0.f;
 #pragma unroll
-            for (int k = 0; k < RPT; ++k) wv[j] += vr[k][j];
+            for (int k = 0; k < RPT; ++k) wv[j] += vr(k, j);
         }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        red_k[rg][c * 8 + j] = ks[j];
-        red_w[rg][c * 8 + j] = wk[j];
-        red_v[rg][c * 8 + j] = wv[j];
+    for (int o = G::CH; o < 64; o <<= 1)  // lanes c + CH * r of a wave hold chunk c of its row groups
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            ks[j] += __shfl_xor(ks[j], o);
+            wk[j] += __shfl_xor(wk[j], o);
+            wv[j] += __shfl_xor(wv[j], o);
+        }
+    if ((threadIdx.x & 63) < G::CH) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            red_k[threadIdx.x >> 6][c * 8 + j] = ks[j];
+            red_w[threadIdx.x >> 6][c * 8 + j] = wk[j];
+            red_v[threadIdx.x >> 6][c * 8 + j] = wv[j];
+        }
     }
     __syncthreads();
     if (REWEIGHT) {
@@ -285,7 +310,7 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ K, c
     float dot = 0.f;  // a . k~ partial over this thread's columns
     for (int col = threadIdx.x; col < D; col += 256) {
         float sk = 0.f, sw = 0.f, sv = 0.f;
-        for (int g = 0; g < G::RG; ++g) { sk += red_k[g][col]; sw += red_w[g][col]; sv += red_v[g][col]; }
+        for (int g = 0; g < 4; ++g) { sk += red_k[g][col]; sw += red_w[g][col]; sv += red_v[g][col]; }
         const float kt = sw / Z;
         k_mean[o + col] = sk / (float)n;
         k_sum[o + col] = kt;
